@@ -1,0 +1,184 @@
+"""ctypes wrapper around the fp64 CPU oracle (ssd_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU-baseline
+leg may import this module; the GPU library and its Python binding never do.
+
+Every array is converted to contiguous float64 before the call.  Shapes follow the
+oracle's header comment:
+    x, z        [B, L, H, P]      dt_raw      [B, L, H]
+    Bm, Cm      [B, L, G, N]      h0          [B, H, P, N]
+    conv input  [B, L, Cd]        conv state  [B, K-1, Cd]     conv weight [Cd, K]
+
+The mixer helpers compose the conv and the SSD the way a Mamba-2 mixer wires
+them: the conv output row is split into x (H*P channels), then B (G*N), then
+C (G*N) -- the channel order of the Mamba-2 block that the Video-Ma2mba and
+Vamba pages build on.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    """Compile ssd_oracle.c into liboracle.so (gcc, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB)
+        for name in ("oracle_conv1d_fwd", "oracle_conv1d_bwd", "oracle_ssd_fwd", "oracle_ssd_bwd"):
+            getattr(_lib, name).restype = None
+        _lib.oracle_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def _c(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_dp)
+
+
+# --------------------------------------------------------------------------- conv
+
+def conv1d_fwd(xraw, w, bias=None, state_in=None, silu=True):
+    """Causal depthwise conv (+SiLU).  Returns (out [B,L,Cd], state_out [B,K-1,Cd])."""
+    xraw, w, bias, state_in = _c(xraw), _c(w), _c(bias), _c(state_in)
+    Bsz, L, Cd = xraw.shape
+    K = w.shape[1]
+    out = np.empty((Bsz, L, Cd))
+    st = np.empty((Bsz, K - 1, Cd))
+    lib().oracle_conv1d_fwd(_i64(Bsz), _i64(L), _i64(Cd), ctypes.c_int(K), _p(xraw),
+                            _p(state_in), _p(w), _p(bias), ctypes.c_int(int(silu)),
+                            _p(out), _p(st))
+    return out, st
+
+
+def conv1d_bwd(xraw, w, bias, state_in, silu, dout, dstate_out=None):
+    """Returns (dxraw, dw, db, dstate_in)."""
+    xraw, w, bias, state_in = _c(xraw), _c(w), _c(bias), _c(state_in)
+    dout, dstate_out = _c(dout), _c(dstate_out)
+    Bsz, L, Cd = xraw.shape
+    K = w.shape[1]
+    dx = np.empty((Bsz, L, Cd))
+    dw = np.empty((Cd, K))
+    db = np.empty((Cd,))
+    dst = np.empty((Bsz, K - 1, Cd))
+    lib().oracle_conv1d_bwd(_i64(Bsz), _i64(L), _i64(Cd), ctypes.c_int(K), _p(xraw),
+                            _p(state_in), _p(w), _p(bias), ctypes.c_int(int(silu)), _p(dout),
+                            _p(dstate_out), _p(dx), _p(dw), _p(db), _p(dst))
+    return dx, dw, db, dst
+
+
+# --------------------------------------------------------------------------- ssd
+
+def _dims(x, Bm):
+    Bsz, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    return Bsz, L, H, P, N, G
+
+
+def ssd_fwd(x, dt_raw, A, Bm, Cm, dt_bias=None, softplus=True, D=None, z=None, h0=None):
+    """Sequential recurrence.  Returns (out, y_pre_gate, h_final)."""
+    x, dt_raw, A, Bm, Cm = _c(x), _c(dt_raw), _c(A), _c(Bm), _c(Cm)
+    dt_bias, D, z, h0 = _c(dt_bias), _c(D), _c(z), _c(h0)
+    Bsz, L, H, P, N, G = _dims(x, Bm)
+    out = np.empty((Bsz, L, H, P))
+    y = np.empty((Bsz, L, H, P))
+    hf = np.empty((Bsz, H, P, N))
+    lib().oracle_ssd_fwd(_i64(Bsz), _i64(L), _i64(H), _i64(P), _i64(N), _i64(G), _p(x),
+                         _p(dt_raw), _p(dt_bias), ctypes.c_int(int(softplus)), _p(A), _p(Bm),
+                         _p(Cm), _p(D), _p(z), _p(h0), _p(out), _p(y), _p(hf))
+    return out, y, hf
+
+
+def ssd_bwd(x, dt_raw, A, Bm, Cm, dout, dt_bias=None, softplus=True, D=None, z=None, h0=None,
+            dh_final=None, block=4096):
+    """Reverse sweep with time-blocked exact recompute (block=0: literal full storage).
+
+    Returns a dict with dx, ddt (w.r.t. dt_raw), dB, dC, dz, dA, dD, ddt_bias, dh0."""
+    x, dt_raw, A, Bm, Cm, dout = _c(x), _c(dt_raw), _c(A), _c(Bm), _c(Cm), _c(dout)
+    dt_bias, D, z, h0, dh_final = _c(dt_bias), _c(D), _c(z), _c(h0), _c(dh_final)
+    Bsz, L, H, P, N, G = _dims(x, Bm)
+    r = dict(dx=np.empty((Bsz, L, H, P)), ddt=np.empty((Bsz, L, H)),
+             dB=np.empty((Bsz, L, G, N)), dC=np.empty((Bsz, L, G, N)),
+             dz=np.empty((Bsz, L, H, P)) if z is not None else None,
+             dA=np.empty((H,)), dD=np.empty((H,)), ddt_bias=np.empty((H,)),
+             dh0=np.empty((Bsz, H, P, N)))
+    lib().oracle_ssd_bwd(_i64(Bsz), _i64(L), _i64(H), _i64(P), _i64(N), _i64(G), _p(x),
+                         _p(dt_raw), _p(dt_bias), ctypes.c_int(int(softplus)), _p(A), _p(Bm),
+                         _p(Cm), _p(D), _p(z), _p(h0), _p(dout), _p(dh_final), _p(r["dx"]),
+                         _p(r["ddt"]), _p(r["dB"]), _p(r["dC"]), _p(r["dz"]), _p(r["dA"]),
+                         _p(r["dD"]), _p(r["ddt_bias"]), _p(r["dh0"]), _i64(int(block)))
+    if D is None:
+        r["dD"] = None
+    if dt_bias is None:
+        r["ddt_bias"] = None
+    return r
+
+
+# --------------------------------------------------------------------------- mixer
+
+def split_xbc(xbc, H, P, G, N):
+    """[B, L, H*P + 2*G*N] -> x [B,L,H,P], B [B,L,G,N], C [B,L,G,N] (copies)."""
+    Bsz, L, _ = xbc.shape
+    hp, gn = H * P, G * N
+    x = xbc[..., :hp].reshape(Bsz, L, H, P)
+    Bm = xbc[..., hp:hp + gn].reshape(Bsz, L, G, N)
+    Cm = xbc[..., hp + gn:hp + 2 * gn].reshape(Bsz, L, G, N)
+    return x, Bm, Cm
+
+
+def mixer_fwd(xbc_raw, conv_w, conv_b, dt_raw, A, H, P, G, N, dt_bias=None, D=None, z=None,
+              h0=None, conv_state=None, softplus=True):
+    """conv1d+SiLU -> SSD -> SiLU(z) gate.  Returns dict(out, y, h_final, conv_state_out, xbc)."""
+    xbc, st_out = conv1d_fwd(xbc_raw, conv_w, conv_b, conv_state, silu=True)
+    x, Bm, Cm = split_xbc(xbc, H, P, G, N)
+    out, y, hf = ssd_fwd(x, dt_raw, A, Bm, Cm, dt_bias, softplus, D, z, h0)
+    return dict(out=out, y=y, h_final=hf, conv_state_out=st_out, xbc=xbc)
+
+
+def mixer_bwd(xbc_raw, conv_w, conv_b, dt_raw, A, H, P, G, N, dout, dt_bias=None, D=None, z=None,
+              h0=None, conv_state=None, dh_final=None, dconv_state_out=None, softplus=True,
+              block=4096):
+    """Backward of mixer_fwd.  Returns the ssd_bwd dict plus dxbc_raw, dconv_w, dconv_b,
+    dconv_state (w.r.t. the carried-in conv state) and dxbc (post-conv)."""
+    xbc, _ = conv1d_fwd(xbc_raw, conv_w, conv_b, conv_state, silu=True)
+    x, Bm, Cm = split_xbc(xbc, H, P, G, N)
+    r = ssd_bwd(x, dt_raw, A, Bm, Cm, dout, dt_bias, softplus, D, z, h0, dh_final, block)
+    Bsz, L = x.shape[:2]
+    dxbc = np.concatenate([r["dx"].reshape(Bsz, L, H * P), r["dB"].reshape(Bsz, L, G * N),
+                           r["dC"].reshape(Bsz, L, G * N)], axis=-1)
+    dxr, dw, db, dst = conv1d_bwd(xbc_raw, conv_w, conv_b, conv_state, True, dxbc, dconv_state_out)
+    r.update(dxbc=dxbc, dxbc_raw=dxr, dconv_w=dw, dconv_b=db, dconv_state=dst)
+    return r
