@@ -1,0 +1,197 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 mixer hot path:
+ *
+ *     causal depthwise conv1d + SiLU  ->  selective SSD recurrence  ->  SiLU(z) gate
+ *
+ * and its backward pass.
+ *
+ * What is computed (sources: the pith.science review of Video-Ma2mba, arXiv
+ * 2411.19460 -- skeptic critique and referee report, Eq. (1) and the Conv1d-buffer
+ * critique; the Mamba / Mamba-2 papers in the arXiv index page's reference list for
+ * the selective form of Eq. (1)):
+ *
+ *   conv:  pre[t,c] = b[c] + sum_{k<K} w[c,k] * xin[t-K+1+k, c]      (xin[t<0] = carried state)
+ *          xbc[t,c] = silu(pre[t,c]);   conv state out = the last K-1 rows of xin
+ *   split: x[t,h,p] = xbc[t, h*P+p],  B[t,g,n] = xbc[t, H*P+g*N+n],
+ *          C[t,g,n] = xbc[t, H*P+G*N+g*N+n],   head h uses group g = h / (H/G)
+ *   dt:    dt[t,h] = softplus(dt_raw[t,h] + dt_bias[h])   (or dt_raw + dt_bias)
+ *   Eq.(1) selective form, per head h:
+ *          h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t B_t^T        (state P x N)
+ *          y_t = h_t C_t + D_h x_t
+ *   gate:  out_t = y_t * silu(z_t)
+ *
+ * The state needed to resume a sequence at step s is (h_s, the last K-1 conv
+ * inputs) -- the review's point that checkpointing h alone is not exact when a
+ * causal conv precedes the SSD.  Every entry point takes both in and returns both,
+ * so a long sequence can be run and trained segment by segment (multi-axis
+ * gradient checkpointing along the sequence axis).
+ *
+ * Conventions
+ *   Pointers   All tensor pointers are caller-owned *device* pointers (hipMalloc /
+ *              torch device memory).  The library allocates nothing, keeps no
+ *              pointer after return, and never synchronises.  Scratch memory comes
+ *              from the caller through (ws, ws_bytes), sized by the *_workspace
+ *              queries; its contents need not be initialised.
+ *   Streams    `stream` is a hipStream_t (NULL = the legacy default stream).  All
+ *              work is enqueued asynchronously on it; results are valid once the
+ *              stream has been synchronised.  Calls that overlap on one device and
+ *              share a workspace race.
+ *   Views      ssd_view = {ptr, stride_b, stride_t}: a [batch, time, channels]
+ *              tensor whose channel dim is contiguous; strides are in *elements*.
+ *              A view with ptr == NULL means "absent" where the argument is optional.
+ *              Activations use the I/O dtype `io`; base pointers must be 16-byte
+ *              aligned and stride_b, stride_t multiples of 16 bytes, except the dt /
+ *              ddt views, which need only element alignment.
+ *   Dtypes     Activations, conv states and activation gradients: `io` (bf16 or
+ *              fp32).  Parameters (A, D, dt_bias, conv w and b), SSD states (h0,
+ *              h_final, checkpoints, dh) and parameter gradients: fp32.  All
+ *              arithmetic accumulates in fp32; bf16 results are rounded to nearest
+ *              even.
+ *   Layouts    h0 / h_final / dh: [B][H][P][N] (n contiguous) fp32.
+ *              conv state:        [B][K-1][Cd] rows, oldest first -- the same layout
+ *                                 as xbc rows, so the previous segment's last K-1
+ *                                 input rows can be passed as a view.
+ *              conv weight:       [Cd][K]; w[c][K-1] multiplies the current token.
+ *   Errors     Every call returns ssd_status.  All validation happens before any
+ *              launch; nothing is enqueued on error.  Launch failures return
+ *              SSD_ERR_HIP with detail in ssd_last_error() (thread-local).
+ *              Unsupported shapes return SSD_ERR_UNSUPPORTED; there is no fallback.
+ *   Preconditions (documented, not checked on the device): A <= 0 and dt >= 0
+ *              (always true with dt_softplus = 1).
+ *   Supported  headdim P in {32, 64}; dstate N in {16, 32, 64, 128}; conv width
+ *              K in {0 (no conv), 2, 3, 4}; chunk in {0, 64} (0 selects 64); any
+ *              seqlen >= 1, any batch >= 1, nheads % ngroups == 0.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = -1,        /* a required pointer is NULL */
+  SSD_ERR_SHAPE = -2,       /* a dimension is out of range or inconsistent */
+  SSD_ERR_DTYPE = -3,       /* unknown dtype */
+  SSD_ERR_ALIGN = -4,       /* a pointer or stride breaks the alignment rule */
+  SSD_ERR_UNSUPPORTED = -5, /* valid but not implemented (P, N, K or chunk) */
+  SSD_ERR_WORKSPACE = -6,   /* ws too small (or NULL with ws_bytes > 0 needed) */
+  SSD_ERR_HIP = -7          /* a HIP call or kernel launch failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+  int64_t batch;      /* B */
+  int64_t seqlen;     /* L, tokens in this call (a segment of a longer stream) */
+  int64_t nheads;     /* H */
+  int64_t headdim;    /* P */
+  int64_t dstate;     /* N */
+  int64_t ngroups;    /* G (B and C shared by the H/G heads of a group) */
+  int64_t chunk;      /* Q, intra-chunk length of the chunked evaluation (0 = 64) */
+  int64_t conv_width; /* K; 0 = no conv: xbc already holds x|B|C */
+} ssd_dims;
+
+typedef struct {
+  void* ptr;
+  int64_t stride_b; /* elements between batches */
+  int64_t stride_t; /* elements between time steps */
+} ssd_view;
+
+/* ABI version of this header (bumped on any signature change). */
+#define SSD_ABI_VERSION 1
+int ssd_abi_version(void);
+
+/* Static text of a status code. */
+const char* ssd_status_string(int status);
+
+/* Detail of the last error on this thread (empty string if none). */
+const char* ssd_last_error(void);
+
+/* Scratch bytes ssd_fwd / ssd_bwd need for these dims (0 is possible). */
+ssd_status ssd_fwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes);
+ssd_status ssd_bwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes);
+
+/*
+ * ssd_fwd -- conv1d+SiLU (when d->conv_width > 0), SSD recurrence, SiLU(z) gate.
+ *
+ *   xbc             [B,L,Cd], Cd = H*P + 2*G*N, channel order x | B | C.  Raw
+ *                   (pre-conv) rows when conv_width > 0, else the SSD inputs.
+ *   conv_w, conv_b  [Cd,K] and [Cd] (conv_b may be NULL); ignored without conv.
+ *   conv_state_in   [B,K-1,Cd] carried conv inputs (ptr NULL = zeros).
+ *   conv_state_out  [B,K-1,Cd] receives the last K-1 conv inputs (ptr NULL = skip).
+ *                   May not alias xbc.
+ *   dt              [B,L,H] raw dt;  dt_bias [H] or NULL;  dt_softplus 0/1.
+ *   A               [H] (<= 0);  D [H] or NULL.
+ *   z               [B,L,H*P] gate input (ptr NULL = no gate: out = y).
+ *   h0              [B,H,P,N] initial state, NULL = zeros.
+ *   out             [B,L,H*P] output.  May alias z (read before written per tile)
+ *                   only if z and out have identical views.
+ *   h_final         [B,H,P,N] state after the last token, NULL = skip.
+ *   h_ckpt          optional sequence checkpoints: [ceil(L/ckpt_every),B,H,P,N];
+ *                   entry j is the state before token j*ckpt_every (entry 0 = h0).
+ *                   ckpt_every must be a positive multiple of 64 when h_ckpt != NULL.
+ */
+ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                   const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                   ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                   const float* D, ssd_view z, const float* h0, ssd_view out, float* h_final,
+                   float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ssd_bwd -- gradients of ssd_fwd (same inputs) given dout = dLoss/dout, the
+ * gradient dh_final of the returned state and dconv_state_out of the returned conv
+ * state (both optional: NULL / ptr NULL = zero).  Recomputes the forward from
+ * (h0, conv_state_in): with these set to a segment checkpoint this is the
+ * per-segment backward of sequence-axis gradient checkpointing.
+ *
+ *   dxbc            [B,L,Cd] gradient w.r.t. xbc (raw rows when conv_width > 0).
+ *   ddt             [B,L,H] gradient w.r.t. dt_raw.
+ *   dz              [B,L,H*P] (required iff z is given).
+ *   dA, dD, ddt_bias [H]; dconv_w [Cd,K]; dconv_b [Cd]: parameter gradients, fp32,
+ *                   overwritten (accumulate = 0) or added to (accumulate = 1).
+ *                   dD, ddt_bias, dconv_w, dconv_b may be NULL (not computed).
+ *   dh0             [B,H,P,N] gradient w.r.t. h0 (NULL = skip).
+ *   dconv_state_in  [B,K-1,Cd] gradient w.r.t. conv_state_in (ptr NULL = skip).
+ */
+ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                   const float* conv_b, ssd_view conv_state_in, ssd_view dt, const float* dt_bias,
+                   int dt_softplus, const float* A, const float* D, ssd_view z, const float* h0,
+                   ssd_view dout, const float* dh_final, ssd_view dconv_state_out, ssd_view dxbc,
+                   ssd_view ddt, ssd_view dz, float* dA, float* dD, float* ddt_bias,
+                   float* dconv_w, float* dconv_b, float* dh0, ssd_view dconv_state_in,
+                   int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * conv1d_fwd -- causal depthwise conv of width K in [2,4] over [B,L,C] rows, plus
+ * bias and optional SiLU (the first stage of the hot path, as a standalone call).
+ *   x [B,L,C] -> out [B,L,C];  state_in / state_out [B,K-1,C] as in ssd_fwd.
+ */
+ssd_status conv1d_fwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                      ssd_dtype io, ssd_view x, const float* w, const float* b, int silu,
+                      ssd_view state_in, ssd_view out, ssd_view state_out, void* stream);
+
+/* Scratch bytes conv1d_bwd needs (per-tile partial sums of dw and db). */
+ssd_status conv1d_bwd_workspace(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                                size_t* bytes);
+
+/*
+ * conv1d_bwd -- gradients of conv1d_fwd given dout [B,L,C] and the gradient
+ * dstate_out of the returned state (ptr NULL = zero).
+ *   dx [B,L,C]; dw [C,K] and db [C] (fp32, db may be NULL; overwritten or added to
+ *   per `accumulate`); dstate_in [B,K-1,C] (ptr NULL = skip).
+ */
+ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                      ssd_dtype io, ssd_view x, const float* w, const float* b, int silu,
+                      ssd_view state_in, ssd_view dout, ssd_view dstate_out, ssd_view dx,
+                      float* dw, float* db, ssd_view dstate_in, int accumulate, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_H */

@@ -1,0 +1,273 @@
+// C ABI of the mixer hot path (declarations and contract in include/ssd.h).
+//
+// This layer only validates arguments, sizes scratch memory and enqueues kernels on
+// the caller's stream; it allocates nothing and never synchronises.  Every check
+// runs before the first launch, so an error leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssd.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ssd_status fail(ssd_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ssd_status fail(ssd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ssd_status hip_fail(hipError_t e, const char* where) {
+  return fail(SSD_ERR_HIP, "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+int esize(ssd_dtype io) { return io == SSD_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A [B, T, C] activation view.  vec: 16-byte rule (vector loads); else element rule.
+ssd_status check_view(const ssd_view& v, const char* name, ssd_dtype io, bool required, bool vec,
+                      int64_t T, int64_t C) {
+  if (!v.ptr) {
+    if (required) return fail(SSD_ERR_NULL, "%s: NULL pointer", name);
+    return SSD_OK;
+  }
+  const int es = esize(io);
+  if (v.stride_t < C && T > 1) return fail(SSD_ERR_SHAPE, "%s: stride_t %lld < channels %lld", name,
+                                           (long long)v.stride_t, (long long)C);
+  if (v.stride_b < 0 || v.stride_t < 0) return fail(SSD_ERR_SHAPE, "%s: negative stride", name);
+  if (vec) {
+    if (!aligned16(v.ptr)) return fail(SSD_ERR_ALIGN, "%s: base pointer not 16-byte aligned", name);
+    if ((v.stride_b * es) % 16 || (v.stride_t * es) % 16)
+      return fail(SSD_ERR_ALIGN, "%s: strides (%lld, %lld) elements are not multiples of 16 bytes",
+                  name, (long long)v.stride_b, (long long)v.stride_t);
+  } else if (reinterpret_cast<uintptr_t>(v.ptr) % es) {
+    return fail(SSD_ERR_ALIGN, "%s: base pointer not element-aligned", name);
+  }
+  return SSD_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    ssd_status _st = (x);           \
+    if (_st != SSD_OK) return _st;  \
+  } while (0)
+
+ssd_status check_dims(const ssd_dims* d, ssd_dtype io) {
+  if (!d) return fail(SSD_ERR_NULL, "dims: NULL");
+  if (io != SSD_F32 && io != SSD_BF16) return fail(SSD_ERR_DTYPE, "unknown dtype %d", (int)io);
+  if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+      d->ngroups < 1)
+    return fail(SSD_ERR_SHAPE, "dims must be >= 1 (B=%lld L=%lld H=%lld P=%lld N=%lld G=%lld)",
+                (long long)d->batch, (long long)d->seqlen, (long long)d->nheads,
+                (long long)d->headdim, (long long)d->dstate, (long long)d->ngroups);
+  if (d->nheads % d->ngroups)
+    return fail(SSD_ERR_SHAPE, "nheads %lld not a multiple of ngroups %lld", (long long)d->nheads,
+                (long long)d->ngroups);
+  if (d->batch > (1 << 20) || d->nheads > 4096 || d->seqlen > (int64_t(1) << 40))
+    return fail(SSD_ERR_SHAPE, "dims out of range");
+  if (d->headdim != 32 && d->headdim != 64)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim %lld (supported: 32, 64)", (long long)d->headdim);
+  if (d->dstate != 16 && d->dstate != 32 && d->dstate != 64 && d->dstate != 128)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate %lld (supported: 16, 32, 64, 128)",
+                (long long)d->dstate);
+  if (d->chunk != 0 && d->chunk != ssd::kQ)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk %lld (supported: 0 or %d)", (long long)d->chunk, ssd::kQ);
+  if (d->conv_width != 0 && (d->conv_width < 2 || d->conv_width > 4))
+    return fail(SSD_ERR_UNSUPPORTED, "conv_width %lld (supported: 0, 2, 3, 4)",
+                (long long)d->conv_width);
+  return SSD_OK;
+}
+
+ssd::View cv(const ssd_view& v) { return ssd::View{v.ptr, v.stride_b, v.stride_t}; }
+ssd::MView mv(const ssd_view& v) { return ssd::MView{v.ptr, v.stride_b, v.stride_t}; }
+
+ssd::Problem make_problem(const ssd_dims* d, ssd_dtype io) {
+  ssd::Problem pr{};
+  pr.bf16 = io == SSD_BF16;
+  pr.B = d->batch;
+  pr.L = d->seqlen;
+  pr.H = static_cast<int>(d->nheads);
+  pr.P = static_cast<int>(d->headdim);
+  pr.N = static_cast<int>(d->dstate);
+  pr.G = static_cast<int>(d->ngroups);
+  pr.K = static_cast<int>(d->conv_width);
+  return pr;
+}
+
+int64_t cdim(const ssd_dims* d) { return d->nheads * d->headdim + 2 * d->ngroups * d->dstate; }
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: a dimension is out of range or inconsistent";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown dtype";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer or stride breaks the alignment rule";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape not implemented";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace too small";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown ssd_status";
+  }
+}
+
+const char* ssd_last_error(void) { return g_last_error.c_str(); }
+
+ssd_status ssd_fwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes) {
+  TRY(check_dims(d, io));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes: NULL");
+  const ssd::Problem pr = make_problem(d, io);
+  *bytes = ssd::fwd_workspace_bytes(pr, ssd::make_plan(pr.B, pr.L, pr.H));
+  return SSD_OK;
+}
+
+ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                   const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                   ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                   const float* D, ssd_view z, const float* h0, ssd_view out, float* h_final,
+                   float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  TRY(check_dims(d, io));
+  const int64_t L = d->seqlen, Cd = cdim(d), HP = d->nheads * d->headdim;
+  const int64_t K = d->conv_width;
+  TRY(check_view(xbc, "xbc", io, true, true, L, Cd));
+  TRY(check_view(dt, "dt", io, true, false, L, d->nheads));
+  TRY(check_view(z, "z", io, false, true, L, HP));
+  TRY(check_view(out, "out", io, true, true, L, HP));
+  if (!A) return fail(SSD_ERR_NULL, "A: NULL");
+  if (K > 0) {
+    if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+    TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));
+    TRY(check_view(conv_state_out, "conv_state_out", io, false, true, K - 1, Cd));
+  }
+  if (h_ckpt && (ckpt_every <= 0 || ckpt_every % ssd::kQ))
+    return fail(SSD_ERR_SHAPE, "ckpt_every %lld must be a positive multiple of %d",
+                (long long)ckpt_every, ssd::kQ);
+  ssd::Problem pr = make_problem(d, io);
+  const ssd::Plan pl = ssd::make_plan(pr.B, pr.L, pr.H);
+  const size_t need = ssd::fwd_workspace_bytes(pr, pl);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  pr.xbc = cv(xbc);
+  pr.conv_w = K > 0 ? conv_w : nullptr;
+  pr.conv_b = K > 0 ? conv_b : nullptr;
+  pr.cs_in = K > 0 ? cv(conv_state_in) : ssd::View{nullptr, 0, 0};
+  pr.dt = cv(dt);
+  pr.dt_bias = dt_bias;
+  pr.softplus = dt_softplus ? 1 : 0;
+  pr.A = A;
+  pr.D = D;
+  pr.z = cv(z);
+  pr.h0 = h0;
+  ssd::FwdOut o{};
+  o.out = mv(out);
+  o.h_final = h_final;
+  o.h_ckpt = h_ckpt;
+  o.ckpt_every = ckpt_every;
+  o.cs_out = K > 0 ? mv(conv_state_out) : ssd::MView{nullptr, 0, 0};
+  const hipError_t e = ssd::launch_fwd(pr, o, pl, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ssd_fwd launch");
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes) {
+  TRY(check_dims(d, io));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes: NULL");
+  *bytes = 0;
+  return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd not built yet");
+}
+
+ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                   const float* conv_b, ssd_view conv_state_in, ssd_view dt, const float* dt_bias,
+                   int dt_softplus, const float* A, const float* D, ssd_view z, const float* h0,
+                   ssd_view dout, const float* dh_final, ssd_view dconv_state_out, ssd_view dxbc,
+                   ssd_view ddt, ssd_view dz, float* dA, float* dD, float* ddt_bias,
+                   float* dconv_w, float* dconv_b, float* dh0, ssd_view dconv_state_in,
+                   int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  TRY(check_dims(d, io));
+  return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd not built yet");
+}
+
+namespace {
+ssd_status check_conv(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                      ssd_dtype io) {
+  if (io != SSD_F32 && io != SSD_BF16) return fail(SSD_ERR_DTYPE, "unknown dtype %d", (int)io);
+  if (batch < 1 || seqlen < 1 || channels < 1 || batch > (1 << 20) || seqlen > (int64_t(1) << 40) ||
+      channels > (1 << 24))
+    return fail(SSD_ERR_SHAPE, "conv dims out of range (B=%lld L=%lld C=%lld)", (long long)batch,
+                (long long)seqlen, (long long)channels);
+  if (width < 2 || width > 4)
+    return fail(SSD_ERR_UNSUPPORTED, "conv width %d (supported: 2, 3, 4)", (int)width);
+  const int vec = io == SSD_BF16 ? 8 : 4;
+  if (channels % vec)
+    return fail(SSD_ERR_UNSUPPORTED, "channels %lld not a multiple of %d", (long long)channels, vec);
+  return SSD_OK;
+}
+
+ssd::ConvProblem make_conv(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                           ssd_dtype io, ssd_view x, const float* w, const float* b, int silu,
+                           ssd_view state_in) {
+  ssd::ConvProblem cp{};
+  cp.bf16 = io == SSD_BF16;
+  cp.B = batch;
+  cp.L = seqlen;
+  cp.C = channels;
+  cp.K = width;
+  cp.silu = silu ? 1 : 0;
+  cp.x = cv(x);
+  cp.w = w;
+  cp.b = b;
+  cp.state_in = cv(state_in);
+  return cp;
+}
+}  // namespace
+
+ssd_status conv1d_fwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                      ssd_dtype io, ssd_view x, const float* w, const float* b, int silu,
+                      ssd_view state_in, ssd_view out, ssd_view state_out, void* stream) {
+  g_last_error.clear();
+  TRY(check_conv(batch, seqlen, channels, width, io));
+  TRY(check_view(x, "x", io, true, true, seqlen, channels));
+  TRY(check_view(out, "out", io, true, true, seqlen, channels));
+  TRY(check_view(state_in, "state_in", io, false, true, width - 1, channels));
+  TRY(check_view(state_out, "state_out", io, false, true, width - 1, channels));
+  if (!w) return fail(SSD_ERR_NULL, "w: NULL");
+  const ssd::ConvProblem cp = make_conv(batch, seqlen, channels, width, io, x, w, b, silu, state_in);
+  const hipError_t e = ssd::launch_conv_fwd(cp, mv(out), mv(state_out), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "conv1d_fwd launch");
+  return SSD_OK;
+}
+
+ssd_status conv1d_bwd_workspace(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                                size_t* bytes) {
+  return fail(SSD_ERR_UNSUPPORTED, "conv1d_bwd not built yet");
+}
+
+ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
+                      ssd_dtype io, ssd_view x, const float* w, const float* b, int silu,
+                      ssd_view state_in, ssd_view dout, ssd_view dstate_out, ssd_view dx,
+                      float* dw, float* db, ssd_view dstate_in, int accumulate, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  return fail(SSD_ERR_UNSUPPORTED, "conv1d_bwd not built yet");
+}
+
+}  // extern "C"

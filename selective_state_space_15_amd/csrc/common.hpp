@@ -1,0 +1,252 @@
+// Device-side building blocks shared by the gfx950 kernels of the mixer hot path.
+//
+//  * I/O element traits (bf16 stored as raw uint16 bits, or fp32).
+//  * bf16 <-> fp32 conversion (round to nearest even).
+//  * A wave-level MFMA tile product reading both operands from LDS, in either
+//    orientation, for the two instantiations the library supports:
+//      bf16 I/O: v_mfma_f32_16x16x32_bf16 (gfx950), 8 K-values per lane;
+//      fp32 I/O: v_mfma_f32_16x16x4_f32, 1 K-value per lane.
+//    Both accumulate a 16x16 fp32 tile; lane l holds rows 4*(l/16)+r (r = 0..3)
+//    of column l%16.  Each lane feeds row l%16 of A and column l%16 of B with the
+//    K-slice owned by its lane group l/16; A and B use the same slice mapping, so
+//    the product does not depend on how the hardware orders K inside an
+//    instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two fp32 -> packed bf16 pair (low half = a), one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- I/O traits
+template <typename IO>
+struct io_traits;
+
+template <>
+struct io_traits<bf16_t> {
+  using elem = uint16_t;   // global element
+  using lds = uint16_t;    // LDS operand element (bf16 bits)
+  static constexpr int kstep = 32;  // K per MFMA
+  static constexpr int kpl = 8;     // K-values per lane
+  static constexpr int vec = 8;     // elements per 16-byte vector
+  __device__ static __forceinline__ float to_f(elem v) { return bf2f(v); }
+  __device__ static __forceinline__ elem from_f(float v) { return f2bf(v); }
+  __device__ static __forceinline__ lds to_lds(float v) { return f2bf(v); }
+  __device__ static __forceinline__ float lds_to_f(lds v) { return bf2f(v); }
+};
+
+template <>
+struct io_traits<float> {
+  using elem = float;
+  using lds = float;
+  static constexpr int kstep = 4;
+  static constexpr int kpl = 1;
+  static constexpr int vec = 4;
+  __device__ static __forceinline__ float to_f(elem v) { return v; }
+  __device__ static __forceinline__ elem from_f(float v) { return v; }
+  __device__ static __forceinline__ lds to_lds(float v) { return v; }
+  __device__ static __forceinline__ float lds_to_f(lds v) { return v; }
+};
+
+// 16-byte vector of I/O elements held as floats.
+template <typename IO>
+struct vec16 {
+  static constexpr int n = io_traits<IO>::vec;
+  float v[n];
+};
+
+template <typename IO>
+__device__ __forceinline__ void load_vec16(vec16<IO>& out, const typename io_traits<IO>::elem* p) {
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  if constexpr (io_traits<IO>::vec == 8) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out.v[2 * i] = __uint_as_float(w[i] << 16);
+      out.v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    out.v[0] = __uint_as_float(raw.x);
+    out.v[1] = __uint_as_float(raw.y);
+    out.v[2] = __uint_as_float(raw.z);
+    out.v[3] = __uint_as_float(raw.w);
+  }
+}
+
+// Element v of a raw 16-byte vector of I/O elements, as float (v is a
+// compile-time constant after unrolling, so this is a register select).
+template <typename IO>
+__device__ __forceinline__ float raw_elem(const uint4& raw, int v) {
+  constexpr int per_word = io_traits<IO>::vec / 4;  // 2 (bf16) or 1 (fp32)
+  const int wi = v / per_word;
+  const uint32_t w = wi == 0 ? raw.x : wi == 1 ? raw.y : wi == 2 ? raw.z : raw.w;
+  if constexpr (per_word == 2)
+    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
+  else
+    return __uint_as_float(w);
+}
+
+template <typename IO>
+__device__ __forceinline__ void zero_vec16(vec16<IO>& out) {
+#pragma unroll
+  for (int i = 0; i < vec16<IO>::n; ++i) out.v[i] = 0.f;
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_vec16(typename io_traits<IO>::elem* p, const float* v) {
+  uint4 raw;
+  if constexpr (io_traits<IO>::vec == 8) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f2bf2(v[2 * i], v[2 * i + 1]);
+    raw = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    raw = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3]));
+  }
+  *reinterpret_cast<uint4*>(p) = raw;
+}
+
+// ---------------------------------------------------------------- math
+// Logistic function with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division: exp, add, rcp.
+__device__ __forceinline__ float sigmoidf_(float u) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-u));
+}
+__device__ __forceinline__ float siluf_(float u) { return u * sigmoidf_(u); }
+__device__ __forceinline__ float softplusf_(float u) {
+  return fmaxf(u, 0.f) + log1pf(__expf(-fabsf(u)));
+}
+__device__ __forceinline__ float dsiluf_(float u) {
+  const float s = sigmoidf_(u);
+  return s * (1.f + u * (1.f - s));
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- MFMA tiles
+__device__ __forceinline__ f32x4 mfma_step(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_step(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Operand fetch for one MFMA step.  `kc` (K-contiguous): element (row, k) at
+// base[row * ld + k]; otherwise at base[k * ld + row].
+template <typename L, bool kc>
+struct frag;
+
+template <bool kc>
+struct frag<uint16_t, kc> {
+  using type = bf16x8;
+  __device__ static __forceinline__ type zero() { return __builtin_bit_cast(bf16x8, u16x8{}); }
+  __device__ static __forceinline__ type get(const uint16_t* base, int ld, int row, int k) {
+    if constexpr (kc) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(base + row * ld + k);
+      return __builtin_bit_cast(bf16x8, raw);
+    } else {
+      u16x8 u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) u[e] = base[(k + e) * ld + row];
+      return __builtin_bit_cast(bf16x8, u);
+    }
+  }
+};
+
+template <bool kc>
+struct frag<float, kc> {
+  using type = float;
+  __device__ static __forceinline__ type zero() { return 0.f; }
+  __device__ static __forceinline__ type get(const float* base, int ld, int row, int k) {
+    return kc ? base[row * ld + k] : base[k * ld + row];
+  }
+};
+
+// acc[j] += A(16 x K) * B_j(K x 16) for NJ column tiles sharing one 16-row A strip.
+//   A rows m0..m0+15 of an operand stored per `akc`;
+//   B tile j: columns n0 + 16*j .. +15, stored per `bkc`.
+// K must be a multiple of the per-lane K-slice (8 for bf16); when it is not a
+// multiple of the MFMA K-step, lanes whose slice lies at or past K feed zeros.
+// Executed by one full wave.
+template <typename L, bool akc, bool bkc, int NJ>
+__device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda, int m0, const L* B,
+                                          int ldb, int n0, int K) {
+  constexpr int kstep = sizeof(L) == 2 ? 32 : 4;
+  constexpr int kpl = sizeof(L) == 2 ? 8 : 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  const int kg = lane >> 4;
+  // one K-step at a time: a fully unrolled K loop lets the scheduler hoist every
+  // fragment read of every tile ahead of the MFMAs, which costs more registers
+  // than two waves per SIMD have
+#pragma unroll 1
+  for (int k0 = 0; k0 < K; k0 += kstep) {
+    const int k = k0 + kpl * kg;
+    const bool kin = k < K;
+    const auto a = kin ? frag<L, akc>::get(A, lda, m0 + r, k) : frag<L, akc>::zero();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const auto b = kin ? frag<L, bkc>::get(B, ldb, n0 + 16 * j + r, k) : frag<L, bkc>::zero();
+      acc[j] = mfma_step(a, b, acc[j]);
+    }
+  }
+}
+
+// Row / column of accumulator element e (0..3) of this lane inside a 16x16 tile.
+__device__ __forceinline__ int acc_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
+__device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
+
+// Map a hardware workgroup id to a logical id so that consecutive logical ids
+// run on the same XCD (dispatch places workgroup i on XCD i % 8).  Bijective for
+// any grid size.
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t total) {
+  constexpr int64_t kXcd = 8;
+  const int64_t xcd = i % kXcd, slot = i / kXcd;
+  const int64_t per = total / kXcd, rem = total % kXcd;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace ssd

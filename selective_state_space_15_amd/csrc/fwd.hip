@@ -1,0 +1,525 @@
+// Forward pass of the mixer hot path on gfx950:
+//   causal depthwise conv1d + SiLU (fused into the chunk loads)
+//   -> chunked evaluation of the selective recurrence (Eq. (1) of the Video-Ma2mba
+//      review, pith.science verdict for arXiv 2411.19460; selective form of the
+//      Mamba-2 paper in that page's reference list)
+//   -> SiLU(z) gate.
+//
+// Decomposition (obtained by unrolling the recurrence inside a chunk of Q steps,
+// with cs_t the chunk-local cumulative sum of l = dt * A):
+//   h_t = exp(cs_t) H_{c-1} + sum_{s <= t in chunk} exp(cs_t - cs_s) dt_s x_s B_s^T
+//   y_t = sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s      (intra-chunk, MFMA)
+//       + exp(cs_t) H_{c-1} C_t                                  (carried state, MFMA)
+//       + D x_t
+//   H_c = exp(cs_{Q-1}) H_{c-1} + sum_s exp(cs_{Q-1} - cs_s) dt_s x_s B_s^T   (MFMA)
+//
+// Work split (the sequence is cut into sub-segments of `cps` chunks):
+//   1. walk_kernel<STATE>: one workgroup per (batch, sub-segment, head) walks its
+//      chunks from a zero state and writes the sub-segment's end state S_k and
+//      its total log-decay.
+//   2. scan_kernel: per state element, H_in(k+1) = exp(lsum_k) H_in(k) + S_k over
+//      the sub-segments (a short sequential scan; 256 steps at L = 1M).
+//   3. walk_kernel<OUT>: the same walk started from H_in(k), now producing y,
+//      the gated output, the optional sequence checkpoints and h_final.
+// The state stays in registers (MFMA accumulator layout) along each walk, so
+// the only state traffic through memory is one state per sub-segment.
+#include "chunk_io.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+struct WalkArgs {
+  Problem pr;
+  int64_t cps, n_sub;
+  float* ws_state;          // STATE: [B][n_sub][H][P][N] end states
+  float* ws_lsum;           // STATE: [B][n_sub][H] total log-decay
+  const float* init;        // OUT: initial states (null = zeros)
+  int64_t init_sb, init_sk; // OUT: element strides of init per batch / sub-segment
+  MView out;
+  float* h_final;
+  float* h_ckpt;
+  int64_t ckpt_every;
+};
+
+constexpr int kModeState = 0;
+constexpr int kModeOut = 1;
+
+// Launch shape of the walks: two 4-wave workgroups per CU (2 waves per SIMD, up to
+// 256 registers each; the output pass needs ~80 KB of LDS per workgroup).
+// Independent workgroups on a CU overlap one's memory phase with the other's
+// MFMA phase, which one larger workgroup cannot do across its own barriers.
+template <int MODE>
+struct WalkShape;
+template <>
+struct WalkShape<0> {
+  static constexpr int waves = 4, waves_per_simd = 2;
+};
+template <>
+struct WalkShape<1> {
+  static constexpr int waves = 4, waves_per_simd = 2;
+};
+
+template <typename IO, int P, int N, int MODE>
+__global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
+    __attribute__((amdgpu_waves_per_eu(WalkShape<MODE>::waves_per_simd, WalkShape<MODE>::waves_per_simd)))
+    walk_kernel(WalkArgs a) {
+  constexpr int NW = WalkShape<MODE>::waves;
+  constexpr int NTHR = NW * 64;
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  using Lt = typename T::lds;
+  constexpr bool OUT = MODE == kModeOut;
+  constexpr int V = T::vec;
+  constexpr int PADK = 16 / sizeof(Lt);
+  constexpr int ldN = N + PADK, ldQ = kQ + PADK;
+  __shared__ __align__(16) Lt sB[kQ * ldN];
+  __shared__ __align__(16) Lt sXwT[P * ldQ];
+  __shared__ __align__(16) Lt sC[OUT ? kQ * ldN : 8];
+  __shared__ __align__(16) Lt sXT[OUT ? P * ldQ : 8];
+  __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
+  __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
+  __shared__ float s_dt[kQ], s_cs[kQ], s_w[kQ];
+
+  const Problem& pr = a.pr;
+  const int64_t total = static_cast<int64_t>(pr.B) * a.n_sub * pr.H;
+  const int64_t lid = xcd_remap(blockIdx.x, total);
+  const int h = static_cast<int>(lid % pr.H);
+  const int64_t k = (lid / pr.H) % a.n_sub;
+  const int b = static_cast<int>(lid / (static_cast<int64_t>(pr.H) * a.n_sub));
+  const int g = h / (pr.H / pr.G);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const float Ah = pr.A[h];
+  const float bias_h = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+  const bool gate = OUT && pr.z.p != nullptr;
+
+  // Output tiles (16x16) of the 64-row chunk products: row tile rt = wave % 4; with
+  // 8 waves the columns are split in halves between waves w and w + 4.
+  constexpr int HALVES = NW / 4;
+  const int rt = wave % 4;
+  const int m0 = rt * 16;
+  const int half = wave / 4;
+  constexpr int CBJ = 4 / HALVES;        // column tiles of C B^T per wave
+  constexpr int YJ = (P / 16) / HALVES;  // column tiles of y per wave
+  // State tiles (16x16 of the P x N state) owned by this wave
+  constexpr int PT = P / 16, NT = N / 16, WPP = NW / PT, NJS = (NT + WPP - 1) / WPP;
+  const int s_pi = wave % PT;
+  const int s_nj0 = (wave / PT) * NJS;
+  const bool s_owns = s_nj0 < NT;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+
+  f32x4 accH[NJS];
+  {
+    const float* init = nullptr;
+    if constexpr (OUT)
+      if (a.init) init = a.init + b * a.init_sb + k * a.init_sk + h * PN;
+#pragma unroll
+    for (int j = 0; j < NJS; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = s_pi * 16 + acc_row(e);
+        const int n = (s_nj0 + j) * 16 + acc_col();
+        accH[j][e] = (init && s_owns) ? init[p * N + n] : 0.f;
+      }
+  }
+  if constexpr (OUT) {
+    if (s_owns)
+#pragma unroll
+      for (int j = 0; j < NJS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
+  }
+
+  // Everything a chunk reads from global memory (raw x rows, post-conv B/C rows,
+  // dt, z) is prefetched into registers one chunk ahead, so those loads are in
+  // flight while the previous chunk computes.
+  const E* dtp = static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + h;
+  const E* zp = OUT && gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+  const int64_t tbeg = k * a.cps * kQ;
+  constexpr int RXL = HALVES == 1 ? 2 : 1;  // x rows per loader task: all threads busy
+  constexpr int RBL = 8 / HALVES;           // B/C rows per loader task
+  ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL> ld;
+  float dt_raw = 0.f;
+  // gate inputs of this lane's output elements (rows m0 + 4*(lane/16) + e,
+  // columns 16*(YJ*half + j) + lane%16), kept as raw I/O bits (bf16: two per register)
+  constexpr int ZPR = sizeof(E) == 2 ? 2 : 1;
+  uint32_t zv[OUT ? YJ : 1][4 / ZPR];
+  auto prefetch_z = [&](int64_t tn) {
+    if constexpr (OUT) {
+#pragma unroll
+      for (int j = 0; j < YJ; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 4 / ZPR; ++e2) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int q = 0; q < ZPR; ++q) {
+            const int64_t tg = tn + m0 + acc_row(e2 * ZPR + q);
+            const E v = (zp && tg < pr.L) ? zp[tg * pr.z.st + 16 * (YJ * half + j) + acc_col()] : E(0);
+            if constexpr (ZPR == 2)
+              word |= static_cast<uint32_t>(v) << (16 * q);
+            else
+              word = __float_as_uint(v);
+          }
+          zv[j][e2] = word;
+        }
+    }
+  };
+  auto zval = [&](int j, int e) -> float {
+    const uint32_t w = zv[j][e / ZPR];
+    if constexpr (ZPR == 2)
+      return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    else
+      return __uint_as_float(w);
+  };
+  // dt is prefetched one chunk ahead; the row loads are issued right before use
+  // (holding them across the MFMA phase costs more registers than 2 waves/SIMD allow)
+  auto prefetch = [&](int64_t tn) {
+    if (wave == 0 && tn + lane < pr.L) dt_raw = T::to_f(dtp[(tn + lane) * pr.dt.st]);
+  };
+  prefetch(tbeg);
+
+  float lsum = 0.f;
+  for (int64_t c = 0; c < a.cps; ++c) {
+    const int64_t t0 = tbeg + c * kQ;
+    if (t0 >= pr.L) break;
+    if constexpr (OUT) {
+      if (a.h_ckpt && t0 % a.ckpt_every == 0 && s_owns) {
+        float* dst = a.h_ckpt + ((t0 / a.ckpt_every) * pr.B + b) * pr.H * PN + h * PN;
+#pragma unroll
+        for (int j = 0; j < NJS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
+      }
+    }
+    // (1) dt = softplus(dt_raw + bias), l = dt * A, chunk-local cumsum (wave 0)
+    if (wave == 0) {
+      float dtv = 0.f;
+      if (t0 + lane < pr.L) {
+        const float u = dt_raw + bias_h;
+        dtv = pr.softplus ? softplusf_(u) : u;
+      }
+      const float cs = wave_incl_scan(dtv * Ah);
+      const float csl = __shfl(cs, kWave - 1, kWave);
+      s_dt[lane] = dtv;
+      s_cs[lane] = cs;
+      s_w[lane] = dtv * __expf(csl - cs);
+    }
+    __syncthreads();
+    const float cs_last = s_cs[kQ - 1];
+    lsum += cs_last;
+    // (2) conv + stores into LDS
+    //   sXT[p][s] = x (OUT only), sXwT[p][s] = x * w_s, sB[s][n], sC[s][n] (OUT only)
+    prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
+    ld.issue(pr, b, h, g, t0);
+    ld.consume(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
+      if (seg == 0) {
+        const float ws = s_w[s];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          if constexpr (OUT) sXT[(cl + v) * ldQ + s] = T::to_lds(o[v]);
+          sXwT[(cl + v) * ldQ + s] = T::to_lds(o[v] * ws);
+        }
+      } else {
+        lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
+      }
+    });
+    // next chunk's loads go in flight now
+    if (c + 1 < a.cps && t0 + kQ < pr.L) prefetch(t0 + kQ);
+    __syncthreads();
+
+    if constexpr (OUT) {
+      // C B^T -> masked, decayed, dt-scaled intra-chunk matrix Mt
+      {
+        f32x4 cb[CBJ];
+#pragma unroll
+        for (int j = 0; j < CBJ; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mma_strip<Lt, true, true, CBJ>(cb, sC, ldN, m0, sB, ldN, 16 * CBJ * half, N);
+#pragma unroll
+        for (int j = 0; j < CBJ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = m0 + acc_row(e);
+            const int s = 16 * CBJ * half + 16 * j + acc_col();
+            const float v = s <= t ? cb[j][e] * __expf(s_cs[t] - s_cs[s]) * s_dt[s] : 0.f;
+            sM[t * ldQ + s] = T::to_lds(v);
+          }
+      }
+      // carried-state term with H_{c-1}, rows scaled by exp(cs_t) in place, then the
+      // intra-chunk term accumulated on top by the same MFMA accumulators
+      f32x4 yacc[YJ];
+#pragma unroll
+      for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, true, YJ>(yacc, sC, ldN, m0, sH, ldN, 16 * YJ * half, N);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ecs = __expf(s_cs[m0 + acc_row(e)]);
+#pragma unroll
+        for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
+      }
+      __syncthreads();
+      mma_strip<Lt, true, true, YJ>(yacc, sM, ldQ, m0, sXT, ldQ, 16 * YJ * half, kQ);
+      // y = Ydiag + exp(cs_t) Yoff + D x;  out = y * silu(z)
+      const float Dh = pr.D ? pr.D[h] : 0.f;
+      E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = m0 + acc_row(e);
+        const int64_t tg = t0 + t;
+#pragma unroll
+        for (int j = 0; j < YJ; ++j) {
+          const int p = 16 * (YJ * half + j) + acc_col();
+          float y = yacc[j][e] + Dh * T::lds_to_f(sXT[p * ldQ + t]);
+          if (gate) y *= siluf_(zval(j, e));
+          if (tg < pr.L) op[tg * a.out.st + p] = T::from_f(y);
+        }
+      }
+    }
+    // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B
+    if (s_owns) {
+      const float decay = __expf(cs_last);
+#pragma unroll
+      for (int j = 0; j < NJS; ++j) accH[j] *= decay;
+      mma_strip<Lt, true, false, NJS>(accH, sXwT, ldQ, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+    }
+    __syncthreads();
+    if constexpr (OUT) {
+      if (s_owns)
+#pragma unroll
+        for (int j = 0; j < NJS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (!OUT) {
+    float* dst = a.ws_state + ((b * a.n_sub + k) * pr.H + h) * PN;
+    if (s_owns)
+#pragma unroll
+      for (int j = 0; j < NJS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
+    if (threadIdx.x == 0) a.ws_lsum[(b * a.n_sub + k) * pr.H + h] = lsum;
+  } else {
+    if (a.h_final && k == a.n_sub - 1 && s_owns) {
+      float* dst = a.h_final + (static_cast<int64_t>(b) * pr.H + h) * PN;
+#pragma unroll
+      for (int j = 0; j < NJS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
+    }
+  }
+}
+
+// Exclusive scan of the affine sub-segment maps: ws_state[k] <- H_in(k).
+__global__ void __launch_bounds__(256) scan_kernel(const float* h0, float* ws_state,
+                                                   const float* ws_lsum, int64_t B, int H,
+                                                   int64_t PN, int64_t n_sub) {
+  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t per_b = H * PN;
+  if (e >= B * per_b) return;
+  const int64_t b = e / per_b, rem = e % per_b;
+  const int h = static_cast<int>(rem / PN);
+  float hc = h0 ? h0[e] : 0.f;
+  float* base = ws_state + b * n_sub * per_b + rem;
+  const float* lb = ws_lsum + b * n_sub * H + h;
+  int64_t k = 0;
+  for (; k + 8 <= n_sub; k += 8) {
+    float s[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[i] = base[(k + i) * per_b];
+      l[i] = lb[(k + i) * H];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      base[(k + i) * per_b] = hc;
+      hc = __expf(l[i]) * hc + s[i];
+    }
+  }
+  for (; k < n_sub; ++k) {
+    const float s = base[k * per_b];
+    base[k * per_b] = hc;
+    hc = __expf(lb[k * H]) * hc + s;
+  }
+}
+
+template <typename IO>
+__global__ void conv_state_out_kernel(Problem pr, MView dst) {
+  using E = typename io_traits<IO>::elem;
+  const int64_t km1 = pr.K - 1;
+  const int64_t cd = static_cast<int64_t>(pr.H) * pr.P + 2LL * pr.G * pr.N;
+  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (e >= pr.B * km1 * cd) return;
+  const int64_t c = e % cd, j = (e / cd) % km1, b = e / (cd * km1);
+  const int64_t tau = pr.L - km1 + j;
+  E v;
+  if (tau >= 0)
+    v = static_cast<const E*>(pr.xbc.p)[b * pr.xbc.sb + tau * pr.xbc.st + c];
+  else if (pr.cs_in.p)
+    v = static_cast<const E*>(pr.cs_in.p)[b * pr.cs_in.sb + (tau + km1) * pr.cs_in.st + c];
+  else
+    v = E(0);
+  static_cast<E*>(dst.p)[b * dst.sb + j * dst.st + c] = v;
+}
+
+template <typename IO, int P, int N>
+hipError_t run_walks(const Problem& pr, const FwdOut& o, const Plan& pl, float* ws_state,
+                     float* ws_lsum, hipStream_t s) {
+  WalkArgs a{};
+  a.pr = pr;
+  a.cps = pl.cps;
+  a.n_sub = pl.n_sub;
+  a.ws_state = ws_state;
+  a.ws_lsum = ws_lsum;
+  a.out = o.out;
+  a.h_final = o.h_final;
+  a.h_ckpt = o.h_ckpt;
+  a.ckpt_every = o.ckpt_every > 0 ? o.ckpt_every : 1;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  const dim3 grid(static_cast<unsigned>(pr.B * pl.n_sub * pr.H));
+  if (pl.n_sub > 1) {
+    hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeState>), grid, dim3(WalkShape<kModeState>::waves * 64), 0, s, a);
+    const int64_t ne = pr.B * pr.H * PN;
+    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+                       pr.h0, ws_state, ws_lsum, pr.B, pr.H, PN, pl.n_sub);
+    a.init = ws_state;
+    a.init_sb = pl.n_sub * pr.H * PN;
+    a.init_sk = pr.H * PN;
+  } else {
+    a.init = pr.h0;
+    a.init_sb = pr.H * PN;
+    a.init_sk = 0;
+  }
+  hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeOut>), grid, dim3(WalkShape<kModeOut>::waves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t dispatch_pn(const Problem& pr, const FwdOut& o, const Plan& pl, float* st, float* ls,
+                       hipStream_t s) {
+#define SSD_CASE(PP, NN) \
+  if (pr.P == PP && pr.N == NN) return run_walks<IO, PP, NN>(pr, o, pl, st, ls, s);
+  SSD_CASE(64, 128)
+  SSD_CASE(64, 64)
+  SSD_CASE(64, 32)
+  SSD_CASE(64, 16)
+  SSD_CASE(32, 128)
+  SSD_CASE(32, 64)
+  SSD_CASE(32, 32)
+  SSD_CASE(32, 16)
+#undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+Plan make_plan(int64_t B, int64_t L, int H) {
+  Plan pl{};
+  pl.nchunks = (L + kQ - 1) / kQ;
+  const int64_t target = 2048;  // workgroups: 8 per CU on 256 CUs
+  int64_t want = (target + B * H - 1) / (B * H);
+  if (want < 1) want = 1;
+  int64_t cps = (pl.nchunks + want - 1) / want;
+  if (cps < 1) cps = 1;
+  if (cps > 64) cps = 64;
+  pl.cps = cps;
+  pl.n_sub = (pl.nchunks + cps - 1) / cps;
+  return pl;
+}
+
+// Scratch layout: [B|C post-conv rows][sub-segment states][sub-segment log-decays]
+size_t fwd_workspace_bytes(const Problem& pr, const Plan& pl) {
+  size_t n = bc_prepass_bytes(pr);
+  if (pl.n_sub > 1) {
+    const size_t st = static_cast<size_t>(pr.B) * pl.n_sub * pr.H * pr.P * pr.N * sizeof(float);
+    const size_t ls = static_cast<size_t>(pr.B) * pl.n_sub * pr.H * sizeof(float);
+    n += align256(st) + align256(ls);
+  }
+  return n;
+}
+
+hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, void* ws,
+                      hipStream_t s) {
+  Problem pr = pr_in;
+  char* w = static_cast<char*>(ws);
+  hipError_t err = hipSuccess;
+  if (pr.K > 0) {
+    err = launch_bc_prepass(pr, w, s);
+    if (err != hipSuccess) return err;
+    const int64_t gn2 = 2LL * pr.G * pr.N;
+    pr.bc = View{w, pr.L * gn2, gn2};
+    w += bc_prepass_bytes(pr);
+  }
+  float* st = reinterpret_cast<float*>(w);
+  float* ls = nullptr;
+  if (pl.n_sub > 1) {
+    const size_t stb = static_cast<size_t>(pr.B) * pl.n_sub * pr.H * pr.P * pr.N * sizeof(float);
+    ls = reinterpret_cast<float*>(w + align256(stb));
+  }
+  err = pr.bf16 ? dispatch_pn<bf16_t>(pr, o, pl, st, ls, s) : dispatch_pn<float>(pr, o, pl, st, ls, s);
+  if (err != hipSuccess) return err;
+  if (o.cs_out.p && pr.K > 1) err = launch_conv_state_out(pr, o.cs_out, s);
+  return err;
+}
+
+// Chunk-start states for the backward pass: the walk in state mode with one
+// chunk per sub-segment gives each chunk's local end state and log-decay; the
+// exclusive scan (from h0) turns them into H_{c-1}, the state entering chunk c.
+hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
+                               hipStream_t s) {
+  WalkArgs a{};
+  a.pr = pr;
+  a.cps = 1;
+  a.n_sub = nch;
+  a.ws_state = ws_H;
+  a.ws_lsum = ws_lsum;
+  a.ckpt_every = 1;
+  const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
+  const dim3 grid(static_cast<unsigned>(pr.B * nch * pr.H));
+#define SSD_CASE(IO, PP, NN)                                                                    \
+  if (pr.P == PP && pr.N == NN) {                                                               \
+    hipLaunchKernelGGL((walk_kernel<IO, PP, NN, kModeState>), grid, dim3(WalkShape<kModeState>::waves * 64), 0, s, a); \
+    launched = true;                                                                            \
+  }
+  bool launched = false;
+  if (pr.bf16) {
+    SSD_CASE(bf16_t, 64, 128) else SSD_CASE(bf16_t, 64, 64) else SSD_CASE(bf16_t, 64, 32)
+    else SSD_CASE(bf16_t, 64, 16) else SSD_CASE(bf16_t, 32, 128) else SSD_CASE(bf16_t, 32, 64)
+    else SSD_CASE(bf16_t, 32, 32) else SSD_CASE(bf16_t, 32, 16)
+  } else {
+    SSD_CASE(float, 64, 128) else SSD_CASE(float, 64, 64) else SSD_CASE(float, 64, 32)
+    else SSD_CASE(float, 64, 16) else SSD_CASE(float, 32, 128) else SSD_CASE(float, 32, 64)
+    else SSD_CASE(float, 32, 32) else SSD_CASE(float, 32, 16)
+  }
+#undef SSD_CASE
+  if (!launched) return hipErrorInvalidValue;
+  const int64_t ne = pr.B * pr.H * PN;
+  hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+                     pr.h0, ws_H, ws_lsum, pr.B, pr.H, PN, nch);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s) {
+  const int64_t cd = static_cast<int64_t>(pr.H) * pr.P + 2LL * pr.G * pr.N;
+  const int64_t ne = pr.B * (pr.K - 1) * cd;
+  if (ne <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((ne + 255) / 256));
+  if (pr.bf16)
+    hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, dim3(256), 0, s, pr, dst);
+  else
+    hipLaunchKernelGGL(conv_state_out_kernel<float>, grid, dim3(256), 0, s, pr, dst);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,108 @@
+// Internal host-side interface between the C ABI layer (api.hip) and the kernel
+// translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kQ = 64;         // chunk length of the chunked evaluation
+constexpr int kThreads = 256;  // threads per workgroup of the chunk kernels
+
+struct View {
+  const void* p;
+  int64_t sb, st;  // element strides (batch, time)
+};
+struct MView {
+  void* p;
+  int64_t sb, st;
+};
+
+// Sub-segment plan of the forward pass: each workgroup walks `cps` chunks of one
+// head; the states at sub-segment starts come from a scan over sub-segments.
+struct Plan {
+  int64_t nchunks;  // ceil(L / kQ)
+  int64_t cps;      // chunks per sub-segment
+  int64_t n_sub;    // sub-segments
+};
+
+struct Problem {
+  int bf16;  // 1 = bf16 I/O, 0 = fp32 I/O
+  int64_t B, L;
+  int H, P, N, G, K;
+  View xbc;
+  const float* conv_w;
+  const float* conv_b;
+  View cs_in;  // conv state in (p may be null)
+  View dt;
+  const float* dt_bias;
+  int softplus;
+  const float* A;
+  const float* D;
+  View z;  // p may be null
+  const float* h0;
+  View bc;  // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
+};
+
+struct FwdOut {
+  MView out;
+  float* h_final;
+  float* h_ckpt;
+  int64_t ckpt_every;
+  MView cs_out;  // p may be null
+};
+
+Plan make_plan(int64_t B, int64_t L, int H);
+size_t fwd_workspace_bytes(const Problem& pr, const Plan& pl);
+hipError_t launch_fwd(const Problem& pr, const FwdOut& o, const Plan& pl, void* ws,
+                      hipStream_t s);
+
+// conv-state copy: dst rows j < K-1 = conv inputs at t = L-(K-1)+j
+hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s);
+
+// ws_H[b][c][h] <- state entering chunk c (fp32), ws_lsum[b][c][h] <- chunk log-decay
+hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
+                               hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+struct BwdIn {
+  View dout;                // [B,L,H*P]
+  const float* dh_final;    // [B,H,P,N] or null
+  View dcs_out;             // [B,K-1,Cd] gradient of the returned conv state (p may be null)
+};
+struct BwdOut {
+  MView dxbc;               // [B,L,Cd]
+  MView ddt;                // [B,L,H]
+  MView dz;                 // [B,L,H*P] (p null without gate)
+  float *dA, *dD, *ddt_bias, *dconv_w, *dconv_b, *dh0;
+  MView dcs_in;             // [B,K-1,Cd] (p may be null)
+  int accumulate;
+};
+size_t bwd_workspace_bytes(const Problem& pr);
+hipError_t launch_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, void* ws,
+                      hipStream_t s);
+
+// ---------------------------------------------------------------- standalone conv
+struct ConvProblem {
+  int bf16;
+  int64_t B, L, C;
+  int K, silu;
+  View x;
+  const float* w;
+  const float* b;
+  View state_in;
+};
+hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s);
+hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, int silu, View x,
+                                 int x_c0, View st, int st_c0, const float* w, const float* bias,
+                                 MView out, int o_c0, hipStream_t s);
+// B|C post-conv pre-pass of the SSD entry points: channels [H*P, Cd) of xbc -> dst
+hipError_t launch_bc_prepass(const Problem& pr, void* dst, hipStream_t s);
+size_t bc_prepass_bytes(const Problem& pr);
+size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);
+hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,
+                           float* db, MView dstate_in, int accumulate, void* ws, hipStream_t s);
+
+}  // namespace ssd
