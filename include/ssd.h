@@ -129,8 +129,7 @@ ssd_status ssd_bwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes);
  *   A               [H] (<= 0);  D [H] or NULL.
  *   z               [B,L,H*P] gate input (ptr NULL = no gate: out = y).
  *   h0              [B,H,P,N] initial state, NULL = zeros.
- *   out             [B,L,H*P] output.  May alias z (read before written per tile)
- *                   only if z and out have identical views.
+ *   out             [B,L,H*P] output; must not overlap any input.
  *   h_final         [B,H,P,N] state after the last token, NULL = skip.
  *   h_ckpt          optional sequence checkpoints: [ceil(L/ckpt_every),B,H,P,N];
  *                   entry j is the state before token j*ckpt_every (entry 0 = h0).
@@ -190,6 +189,20 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
                       ssd_view state_in, ssd_view dout, ssd_view dstate_out, ssd_view dx,
                       float* dw, float* db, ssd_view dstate_in, int accumulate, void* ws,
                       size_t ws_bytes, void* stream);
+
+/*
+ * Timing instrumentation (off by default).  While enabled, every kernel the
+ * library enqueues is bracketed by HIP events on the caller's stream.
+ *   ssd_timing_enable(1) clears the totals and starts recording; (0) stops.
+ *   ssd_timing_read(kind, ...) waits for the recorded events and returns the
+ *     summed device time (ms) and launch count of kernel kind `kind`
+ *     (0 .. ssd_timing_kinds()-1; ssd_timing_name gives its name).
+ * Host-side state is process-wide; enable it only around work you measure.
+ */
+ssd_status ssd_timing_enable(int on);
+ssd_status ssd_timing_read(int kind, double* total_ms, int64_t* launches);
+const char* ssd_timing_name(int kind);
+int ssd_timing_kinds(void);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,10 @@ _SIGS = {
     "conv1d_bwd_workspace": ([_I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(_SZ)], _I),
     "conv1d_bwd": ([_I64, _I64, _I64, ctypes.c_int32, _I, _V, _F, _F, _I, _V, _V, _V, _V, _F, _F, _V,
                     _I, _P, _SZ, _P], _I),
+    "ssd_timing_enable": ([_I], _I),
+    "ssd_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I),
+    "ssd_timing_name": ([_I], ctypes.c_char_p),
+    "ssd_timing_kinds": ([], _I),
 }
 
 _lib = None
@@ -205,3 +209,19 @@ def conv1d_bwd(x, w, dout, dx, dw, *, b=None, silu=True, state_in=None, dstate_o
                           fptr(dw), fptr(db), view(dstate_in), int(bool(accumulate)), wsp, wsn,
                           stream_ptr(stream))
     _check(st, "conv1d_bwd")
+
+
+# ------------------------------------------------------------------ timing instrumentation
+
+def ssd_timing_enable(on: bool) -> None:
+    _check(lib().ssd_timing_enable(int(bool(on))), "ssd_timing_enable")
+
+
+def ssd_timing_read() -> dict:
+    """{kernel name: (total_ms, launches)} for every kind recorded since enable."""
+    out = {}
+    for k in range(lib().ssd_timing_kinds()):
+        ms, n = ctypes.c_double(0.0), _I64(0)
+        _check(lib().ssd_timing_read(k, ctypes.byref(ms), ctypes.byref(n)), "ssd_timing_read")
+        out[lib().ssd_timing_name(k).decode()] = (ms.value, n.value)
+    return out

@@ -190,8 +190,11 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
 ssd_status ssd_bwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes) {
   TRY(check_dims(d, io));
   if (!bytes) return fail(SSD_ERR_NULL, "bytes: NULL");
-  *bytes = 0;
-  return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd not built yet");
+  const ssd::Problem pr = make_problem(d, io);
+  if (!ssd::bwd_supported(pr))
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd with fp32 I/O supports dstate <= 64");
+  *bytes = ssd::bwd_workspace_bytes(pr);
+  return SSD_OK;
 }
 
 ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
@@ -203,7 +206,59 @@ ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
                    int accumulate, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   TRY(check_dims(d, io));
-  return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd not built yet");
+  const int64_t L = d->seqlen, Cd = cdim(d), HP = d->nheads * d->headdim;
+  const int64_t K = d->conv_width;
+  TRY(check_view(xbc, "xbc", io, true, true, L, Cd));
+  TRY(check_view(dt, "dt", io, true, false, L, d->nheads));
+  TRY(check_view(z, "z", io, false, true, L, HP));
+  TRY(check_view(dout, "dout", io, true, true, L, HP));
+  TRY(check_view(dxbc, "dxbc", io, true, true, L, Cd));
+  TRY(check_view(ddt, "ddt", io, true, false, L, d->nheads));
+  TRY(check_view(dz, "dz", io, z.ptr != nullptr, true, L, HP));
+  if (!A) return fail(SSD_ERR_NULL, "A: NULL");
+  if (!dA) return fail(SSD_ERR_NULL, "dA: NULL");
+  if (K > 0) {
+    if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+    TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));
+    TRY(check_view(dconv_state_out, "dconv_state_out", io, false, true, K - 1, Cd));
+    TRY(check_view(dconv_state_in, "dconv_state_in", io, false, true, K - 1, Cd));
+  }
+  ssd::Problem pr = make_problem(d, io);
+  if (!ssd::bwd_supported(pr))
+    return fail(SSD_ERR_UNSUPPORTED, "ssd_bwd with fp32 I/O supports dstate <= 64");
+  const size_t need = ssd::bwd_workspace_bytes(pr);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  pr.xbc = cv(xbc);
+  pr.conv_w = K > 0 ? conv_w : nullptr;
+  pr.conv_b = K > 0 ? conv_b : nullptr;
+  pr.cs_in = K > 0 ? cv(conv_state_in) : ssd::View{nullptr, 0, 0};
+  pr.dt = cv(dt);
+  pr.dt_bias = dt_bias;
+  pr.softplus = dt_softplus ? 1 : 0;
+  pr.A = A;
+  pr.D = D;
+  pr.z = cv(z);
+  pr.h0 = h0;
+  ssd::BwdIn in{};
+  in.dout = cv(dout);
+  in.dh_final = dh_final;
+  in.dcs_out = K > 0 ? cv(dconv_state_out) : ssd::View{nullptr, 0, 0};
+  ssd::BwdOut o{};
+  o.dxbc = mv(dxbc);
+  o.ddt = mv(ddt);
+  o.dz = z.ptr ? mv(dz) : ssd::MView{nullptr, 0, 0};
+  o.dA = dA;
+  o.dD = dD;
+  o.ddt_bias = ddt_bias;
+  o.dconv_w = K > 0 ? dconv_w : nullptr;
+  o.dconv_b = K > 0 ? dconv_b : nullptr;
+  o.dh0 = dh0;
+  o.dcs_in = K > 0 ? mv(dconv_state_in) : ssd::MView{nullptr, 0, 0};
+  o.accumulate = accumulate ? 1 : 0;
+  const hipError_t e = ssd::launch_bwd(pr, in, o, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ssd_bwd launch");
+  return SSD_OK;
 }
 
 namespace {
@@ -258,7 +313,10 @@ ssd_status conv1d_fwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
 
 ssd_status conv1d_bwd_workspace(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
                                 size_t* bytes) {
-  return fail(SSD_ERR_UNSUPPORTED, "conv1d_bwd not built yet");
+  TRY(check_conv(batch, seqlen, channels, width, SSD_F32));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes: NULL");
+  *bytes = ssd::conv_bwd_workspace_bytes(batch, seqlen, channels);
+  return SSD_OK;
 }
 
 ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
@@ -267,7 +325,24 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
                       float* dw, float* db, ssd_view dstate_in, int accumulate, void* ws,
                       size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  return fail(SSD_ERR_UNSUPPORTED, "conv1d_bwd not built yet");
+  TRY(check_conv(batch, seqlen, channels, width, io));
+  TRY(check_view(x, "x", io, true, true, seqlen, channels));
+  TRY(check_view(dout, "dout", io, true, true, seqlen, channels));
+  TRY(check_view(dx, "dx", io, true, true, seqlen, channels));
+  TRY(check_view(state_in, "state_in", io, false, true, width - 1, channels));
+  TRY(check_view(dstate_out, "dstate_out", io, false, true, width - 1, channels));
+  TRY(check_view(dstate_in, "dstate_in", io, false, true, width - 1, channels));
+  if (!w) return fail(SSD_ERR_NULL, "w: NULL");
+  if (!dw) return fail(SSD_ERR_NULL, "dw: NULL");
+  const size_t need = ssd::conv_bwd_workspace_bytes(batch, seqlen, channels);
+  if (!ws || ws_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  const ssd::ConvProblem cp = make_conv(batch, seqlen, channels, width, io, x, w, b, silu, state_in);
+  const hipError_t e = ssd::launch_conv_bwd(cp, cv(dout), cv(dstate_out), mv(dx), dw, db,
+                                            mv(dstate_in), accumulate ? 1 : 0, ws,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "conv1d_bwd launch");
+  return SSD_OK;
 }
 
 }  // extern "C"

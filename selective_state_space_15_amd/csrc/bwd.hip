@@ -1,0 +1,717 @@
+// Backward pass of the mixer hot path on gfx950: gradients of
+//   out_t = y_t * silu(z_t),   y_t = h_t C_t + D x_t,
+//   h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t^T          (Eq. (1) of the Video-Ma2mba
+//   review, pith.science verdict for arXiv 2411.19460, in its selective form)
+// with respect to x, B, C, dt (raw), z, A, D, dt_bias and h0, recomputing the
+// forward from (h0, conv state) -- one segment of sequence-axis checkpointing.
+//
+// Chunked form (chunks of Q = 64, cs_t the chunk-local cumsum of l = dt A,
+// H_{c-1} the state entering chunk c, dH_c the gradient of the state leaving it):
+//   dy    = dout silu(z),   dz = dout y silu'(z)
+//   dH_{c-1} = exp(cs_Q) dH_c + sum_t exp(cs_t) dy_t C_t^T            (reverse scan)
+//   Mt[t,s] = (C_t . B_s) exp(cs_t - cs_s) dt_s          (s <= t)
+//   W[t,s]  = (dy_t . x_s) exp(cs_t - cs_s) dt_s          (s <= t)
+//   dx_s  = sum_t Mt[t,s] dy_t + exp(cs_Q - cs_s) dt_s dH_c B_s + D dy_s
+//   dB_s  = sum_t W[t,s] C_t + exp(cs_Q - cs_s) dt_s x_s dH_c          (summed over heads)
+//   dC_t  = sum_s W[t,s] B_s + exp(cs_t) dy_t H_{c-1}                 (summed over heads)
+//   d cs_t (as independent variables):
+//       + sum_s (C_t.B_s) e^{cs_t-cs_s} dt_s (dy_t.x_s)   - [same, summed over t] at s
+//       + dy_t . exp(cs_t) H_{c-1} C_t                     (carried-state term)
+//       - exp(cs_Q - cs_s) dt_s x_s^T dH_c B_s             (chunk-state term)
+//       + [at the last row] <dH_c, H_c> = exp(cs_Q) <dH_c, H_{c-1}> + sum_s (previous term)
+//   dl_r  = sum_{t >= r} dcs_t,   ddt_s = (direct terms) + A dl_s,   dA = sum dt dl,
+//   dD = sum dy . x,   ddt_raw = ddt sigmoid(dt_raw + dt_bias),  ddt_bias = sum ddt_raw.
+//
+// Kernels: chunk states H_{c-1} (forward walk in state mode + scan, shared with
+// the forward pass); dstate_kernel (per chunk and head, the dy C^T term);
+// scan_rev_kernel (reverse scan, dh0); bwd_main_kernel (per chunk and block of
+// heads of one group: every gradient above, dB / dC summed over the block's
+// heads in registers and written as one fp32 partial per block); then the conv
+// backward (or the dB / dC finalize without conv) and ordered parameter reductions.
+#include "chunk_io.hpp"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+
+hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_part,
+                                 int nhb, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
+                                 MView dcs_in, int accumulate, void* ws, hipStream_t s);
+size_t conv_bwd_partials_bytes(int64_t B, int64_t L, int64_t C);
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct BwdArgs {
+  Problem pr;
+  int64_t nch;
+  int hb_heads;            // heads per block (all in one group)
+  int nhb;                 // blocks of heads
+  const float* Hs;         // [B][nch][H][P][N] state entering each chunk
+  const float* lsum;       // [B][nch][H] chunk log-decay
+  float* dHs;              // [B][nch][H][P][N] dS_c, then dH_c (leaving chunk c)
+  View dout;
+  MView dx;                // x-channel gradients [B][L][H*P] (dxbc itself, or scratch)
+  MView dz;
+  MView ddt;
+  float* dbc_part;         // [nhb][B][L][2N] fp32
+  float* par_part;         // [B][nch][H][3]: dA, dD, ddt_bias partials
+};
+
+// ------------------------------------------------------------------ dstate
+// dS_c[p][n] = sum_t exp(cs_t) dy_t[p] C_t[n] for one (batch, chunk, head).
+template <typename IO, int P, int N>
+__global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  using Lt = typename T::lds;
+  constexpr int PADK = 16 / sizeof(Lt);
+  constexpr int ldN = N + PADK, ldQ = kQ + PADK;
+  __shared__ __align__(16) Lt sC[kQ * ldN];
+  __shared__ __align__(16) Lt sDyT[P * ldQ];
+  // bf16 I/O: low parts of C and dy (the state gradient feeds the log-decay gradient)
+  constexpr bool SPLIT = sizeof(Lt) == 2;
+  __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
+  __shared__ __align__(16) Lt sDyTlo[SPLIT ? P * ldQ : 8];
+  __shared__ float s_ecs[kQ];
+
+  const Problem& pr = a.pr;
+  const int64_t total = static_cast<int64_t>(pr.B) * a.nch * pr.H;
+  const int64_t lid = xcd_remap(blockIdx.x, total);
+  const int h = static_cast<int>(lid % pr.H);
+  const int64_t c = (lid / pr.H) % a.nch;
+  const int b = static_cast<int>(lid / (static_cast<int64_t>(pr.H) * a.nch));
+  const int g = h / (pr.H / pr.G);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t t0 = c * kQ;
+
+  if (wave == 0) {
+    const int64_t t = t0 + lane;
+    float dtv = 0.f;
+    if (t < pr.L) {
+      const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h]) +
+                      (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+      dtv = pr.softplus ? softplusf_(u) : u;
+    }
+    const float cs = wave_incl_scan(dtv * pr.A[h]);
+    s_ecs[lane] = __expf(cs);
+  }
+  conv_rows<IO, P, N, false, false, true>(pr, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+    lds_put_row<IO>(sC + s * ldN + cl, o);
+  });
+  const bool clo = SPLIT && pr.bc_lo.p != nullptr;
+  if (clo) {
+    Problem prl = pr;
+    prl.bc = pr.bc_lo;
+    conv_rows<IO, P, N, false, false, true>(prl, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+      lds_put_row<IO>(sClo + s * ldN + cl, o);
+    });
+  }
+  __syncthreads();
+  // dy * exp(cs_t), transposed into sDyT[p][t]
+  {
+    constexpr int V = T::vec;
+    const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
+    const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+    for (int task = threadIdx.x; task < (P / V) * kQ; task += kThreads) {
+      const int cl = (task % (P / V)) * V, r = task / (P / V);
+      const int64_t t = t0 + r;
+      vec16<IO> dv, zv;
+      zero_vec16<IO>(dv);
+      zero_vec16<IO>(zv);
+      if (t < pr.L) {
+        load_vec16<IO>(dv, dp + t * a.dout.st + cl);
+        if (zp) load_vec16<IO>(zv, zp + t * pr.z.st + cl);
+      }
+      const float ecs = s_ecs[r];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float dy = (zp ? dv.v[v] * siluf_(zv.v[v]) : dv.v[v]) * ecs;
+        const Lt hi = T::to_lds(dy);
+        sDyT[(cl + v) * ldQ + r] = hi;
+        if constexpr (SPLIT) sDyTlo[(cl + v) * ldQ + r] = T::to_lds(dy - T::lds_to_f(hi));
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int PT = P / 16, NT = N / 16, WPP = 4 / PT, NJS = (NT + WPP - 1) / WPP;
+  const int s_pi = wave / WPP, s_nj0 = (wave % WPP) * NJS;
+  if (s_nj0 < NT) {
+    f32x4 acc[NJS];
+#pragma unroll
+    for (int j = 0; j < NJS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_strip<Lt, true, false, NJS>(acc, sDyT, ldQ, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
+    if constexpr (SPLIT) {
+      mma_strip<Lt, true, false, NJS>(acc, sDyTlo, ldQ, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
+      if (clo) mma_strip<Lt, true, false, NJS>(acc, sDyT, ldQ, s_pi * 16, sClo, ldN, s_nj0 * 16, kQ);
+    }
+    const int64_t PN = static_cast<int64_t>(P) * N;
+    float* dst = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
+#pragma unroll
+    for (int j = 0; j < NJS; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[j][e];
+  }
+}
+
+// ------------------------------------------------------------------ reverse scan
+// dHs[c] <- gradient leaving chunk c; g runs dH_{c-1} = exp(lsum_c) dH_c + dS_c.
+__global__ void __launch_bounds__(256) scan_rev_kernel(const float* dh_final, float* dHs,
+                                                       const float* lsum, float* dh0, int64_t B,
+                                                       int H, int64_t PN, int64_t nch) {
+  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t per_b = H * PN;
+  if (e >= B * per_b) return;
+  const int64_t b = e / per_b, rem = e % per_b;
+  const int h = static_cast<int>(rem / PN);
+  float gcur = dh_final ? dh_final[e] : 0.f;
+  float* base = dHs + b * nch * per_b + rem;
+  const float* lb = lsum + b * nch * H + h;
+  int64_t c = nch - 1;
+  for (; c >= 7; c -= 8) {
+    float s[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[i] = base[(c - i) * per_b];
+      l[i] = lb[(c - i) * H];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      base[(c - i) * per_b] = gcur;
+      gcur = __expf(l[i]) * gcur + s[i];
+    }
+  }
+  for (; c >= 0; --c) {
+    const float s = base[c * per_b];
+    base[c * per_b] = gcur;
+    gcur = __expf(lb[c * H]) * gcur + s;
+  }
+  if (dh0) dh0[e] = gcur;
+}
+
+// ------------------------------------------------------------------ main
+template <typename IO, int P, int N>
+__global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  using Lt = typename T::lds;
+  constexpr int PADK = 16 / sizeof(Lt);
+  constexpr int ldN = N + PADK, ldQ = kQ + PADK, ldP = P + PADK;
+  constexpr int NTn = N / 16, PJ = P / 16;
+  __shared__ __align__(16) Lt sC[kQ * ldN];   // C rows [t][n]
+  __shared__ __align__(16) Lt sB[kQ * ldN];   // B rows [s][n]
+  __shared__ __align__(16) Lt sXT[P * ldQ];   // x^T [p][s]
+  __shared__ __align__(16) Lt sM[kQ * ldQ];   // Mt [t][s]
+  __shared__ __align__(16) Lt sW[kQ * ldQ];   // W  [t][s]
+  __shared__ __align__(16) Lt sDY[kQ * ldP];  // dy [t][p]
+  __shared__ __align__(16) Lt sH[P * ldN];    // H_{c-1} [p][n]
+  __shared__ __align__(16) Lt sdH[P * ldN];   // dH_c [p][n]
+  // bf16 I/O: dy and C also as low parts (v - bf16(v)), so the products that feed
+  // the log-decay gradient most (dy x^T, C B^T, C H^T) run at about 16 bits
+  constexpr bool SPLIT = sizeof(Lt) == 2;
+  __shared__ __align__(16) Lt sDYlo[SPLIT ? kQ * ldP : 8];
+  __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
+  __shared__ float s_dt[kQ], s_cs[kQ], s_sig[kQ], s_dq[kQ];
+  __shared__ float s_row[kQ], s_yo[kQ], s_v[kQ], s_col[4][kQ];
+  __shared__ float s_red[2][4];
+
+  const Problem& pr = a.pr;
+  const int64_t total = static_cast<int64_t>(pr.B) * a.nch * a.nhb;
+  const int64_t lid = xcd_remap(blockIdx.x, total);
+  const int hb = static_cast<int>(lid % a.nhb);
+  const int64_t c = (lid / a.nhb) % a.nch;
+  const int b = static_cast<int>(lid / (static_cast<int64_t>(a.nhb) * a.nch));
+  const int h_first = hb * a.hb_heads;
+  const int g = h_first / (pr.H / pr.G);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int m0 = wave * 16;
+  const int64_t t0 = c * kQ;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+
+  // B and C rows of the group (post-conv), shared by every head of the block
+  conv_rows<IO, P, N, false, true, true>(pr, b, 0, g, t0, [&](int seg, int s, int cl, const float* o) {
+    lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
+  });
+  const bool clo = SPLIT && pr.bc_lo.p != nullptr;
+  if (clo) {
+    Problem prl = pr;
+    prl.bc = pr.bc_lo;
+    conv_rows<IO, P, N, false, false, true>(prl, b, 0, g, t0, [&](int, int s, int cl, const float* o) {
+      lds_put_row<IO>(sClo + s * ldN + cl, o);
+    });
+  }
+  __syncthreads();
+  f32x4 cb[4];  // (C B^T)[t in rows m0.., s], all 64 columns
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mma_strip<Lt, true, true, 4>(cb, sC, ldN, m0, sB, ldN, 0, N);
+  if (clo) mma_strip<Lt, true, true, 4>(cb, sClo, ldN, m0, sB, ldN, 0, N);
+
+  f32x4 accdB[NTn], accdC[NTn];
+#pragma unroll
+  for (int j = 0; j < NTn; ++j) {
+    accdB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accdC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int hh = 0; hh < a.hb_heads; ++hh) {
+    const int h = h_first + hh;
+    const float Ah = pr.A[h];
+    const float Dh = pr.D ? pr.D[h] : 0.f;
+    // (1) dt, cs, softplus slope, chunk-state decays (wave 0)
+    if (wave == 0) {
+      const int64_t t = t0 + lane;
+      float dtv = 0.f, sig = 1.f;
+      if (t < pr.L) {
+        const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h]) +
+                        (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+        dtv = pr.softplus ? softplusf_(u) : u;
+        sig = pr.softplus ? sigmoidf_(u) : 1.f;
+      }
+      const float cs = wave_incl_scan(dtv * Ah);
+      const float csl = __shfl(cs, kWave - 1, kWave);
+      s_dt[lane] = dtv;
+      s_cs[lane] = cs;
+      s_sig[lane] = sig;
+      s_dq[lane] = __expf(csl - cs);
+    }
+    // (2) x of head h (post-conv, transposed)
+    conv_rows<IO, P, N, true, false, false>(pr, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+#pragma unroll
+      for (int v = 0; v < T::vec; ++v) sXT[(cl + v) * ldQ + s] = T::to_lds(o[v]);
+    });
+    // dout, z at this lane's accumulator positions (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
+    float dyr[PJ][4], g2r[PJ][4];
+    {
+      const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
+      const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+#pragma unroll
+      for (int j = 0; j < PJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = t0 + m0 + acc_row(e);
+          const int p = 16 * j + acc_col();
+          float dv = 0.f, zv = 0.f;
+          if (t < pr.L) {
+            dv = T::to_f(dp[t * a.dout.st + p]);
+            if (zp) zv = T::to_f(zp[t * pr.z.st + p]);
+          }
+          dyr[j][e] = zp ? dv * siluf_(zv) : dv;
+          g2r[j][e] = zp ? dv * dsiluf_(zv) : 0.f;
+          const Lt hi = T::to_lds(dyr[j][e]);
+          sDY[(m0 + acc_row(e)) * ldP + p] = hi;
+          if constexpr (SPLIT) sDYlo[(m0 + acc_row(e)) * ldP + p] = T::to_lds(dyr[j][e] - T::lds_to_f(hi));
+        }
+    }
+    // H_{c-1}, dH_c of head h; <dH, H> on the way
+    {
+      const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
+      const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
+      float dot = 0.f;
+      for (int i = threadIdx.x * 4; i < P * N; i += kThreads * 4) {
+        const float4 hv = *reinterpret_cast<const float4*>(Hg + i);
+        const float4 dv = *reinterpret_cast<const float4*>(dHg + i);
+        const int p = i / N, n = i % N;
+        const float hf[4] = {hv.x, hv.y, hv.z, hv.w};
+        const float df[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sH[p * ldN + n + q] = T::to_lds(hf[q]);
+          sdH[p * ldN + n + q] = T::to_lds(df[q]);
+        }
+        dot += hv.x * dv.x + hv.y * dv.y + hv.z * dv.z + hv.w * dv.w;
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) s_red[0][wave] = dot;
+    }
+    __syncthreads();
+
+    // (a) Mt, y, dz, carried-state dcs term, dD
+    float lt[4][4];  // exp(cs_t - cs_s) masked, at the cb positions
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = m0 + acc_row(e), s = 16 * j + acc_col();
+        lt[j][e] = s <= t ? __expf(s_cs[t] - s_cs[s]) : 0.f;
+        sM[t * ldQ + s] = T::to_lds(cb[j][e] * lt[j][e] * s_dt[s]);
+      }
+    f32x4 yacc[PJ];
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_strip<Lt, true, true, PJ>(yacc, sC, ldN, m0, sH, ldN, 0, N);
+    if (clo) mma_strip<Lt, true, true, PJ>(yacc, sClo, ldN, m0, sH, ldN, 0, N);
+    float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ecs = __expf(s_cs[m0 + acc_row(e)]);
+#pragma unroll
+      for (int j = 0; j < PJ; ++j) {
+        yacc[j][e] *= ecs;
+        yo_part[e] += dyr[j][e] * yacc[j][e];
+      }
+    }
+    __syncthreads();
+    mma_strip<Lt, true, true, PJ>(yacc, sM, ldQ, m0, sXT, ldQ, 0, kQ);
+    float dD_part = 0.f;
+    {
+      E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + h * P : nullptr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = m0 + acc_row(e);
+        const int64_t tg = t0 + t;
+#pragma unroll
+        for (int j = 0; j < PJ; ++j) {
+          const int p = 16 * j + acc_col();
+          const float xv = T::lds_to_f(sXT[p * ldQ + t]);
+          const float y = yacc[j][e] + Dh * xv;
+          dD_part += dyr[j][e] * xv;
+          if (dzp && tg < pr.L) dzp[tg * a.dz.st + p] = T::from_f(g2r[j][e] * y);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) yo_part[e] += __shfl_xor(yo_part[e], off, kWave);
+    if (acc_col() == 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_yo[m0 + acc_row(e)] = yo_part[e];
+    dD_part = wave_sum(dD_part);
+    if (lane == 0) s_red[1][wave] = dD_part;
+
+    // (b) dYX = dY X^T, W, row / column sums of (C.B)(dy.x) e^{..} (dt)
+    {
+      f32x4 dyx[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, false, 4>(dyx, sDY, ldP, m0, sXT, ldQ, 0, P);
+      if constexpr (SPLIT) mma_strip<Lt, true, false, 4>(dyx, sDYlo, ldP, m0, sXT, ldQ, 0, P);
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float csum = 0.f;
+        const int s = 16 * j + acc_col();
+        const float dts = s_dt[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = m0 + acc_row(e);
+          const float wp = dyx[j][e] * lt[j][e];  // (dy_t.x_s) e^{cs_t-cs_s}, masked
+          const float m2 = wp * cb[j][e];
+          rs[e] += m2 * dts;
+          csum += m2;
+          sW[t * ldQ + s] = T::to_lds(wp * dts);
+        }
+        csum += __shfl_xor(csum, 16, kWave);
+        csum += __shfl_xor(csum, 32, kWave);
+        if (lane < 16) s_col[wave][s] = csum;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) rs[e] += __shfl_xor(rs[e], off, kWave);
+      }
+      if (acc_col() == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_row[m0 + acc_row(e)] = rs[e];
+    }
+    __syncthreads();
+
+    // (c) dx rows s = m0..: Mt^T dY + exp(cs_Q - cs_s) dt_s B dH^T + D dy
+    {
+      f32x4 dxd[PJ], dxs[PJ];
+#pragma unroll
+      for (int j = 0; j < PJ; ++j) {
+        dxd[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dxs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      mma_strip<Lt, false, false, PJ>(dxd, sM, ldQ, m0, sDY, ldP, 0, kQ);
+      mma_strip<Lt, true, true, PJ>(dxs, sB, ldN, m0, sdH, ldN, 0, N);
+      E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + h * P;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = m0 + acc_row(e);
+        const int64_t sg = t0 + s;
+        const float sc = s_dq[s] * s_dt[s];
+#pragma unroll
+        for (int j = 0; j < PJ; ++j) {
+          const int p = 16 * j + acc_col();
+          const float dxv = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
+          if (sg < pr.L) dxp[sg * a.dx.st + p] = T::from_f(dxv);
+        }
+      }
+    }
+    // (d) dB rows s: W^T C + exp(cs_Q - cs_s) dt_s (X dH); chunk-state dcs term
+    {
+      f32x4 U[NTn];
+#pragma unroll
+      for (int j = 0; j < NTn; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, false, false, NTn>(U, sXT, ldQ, m0, sdH, ldN, 0, P);
+      float vp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = m0 + acc_row(e);
+        const float sc = s_dq[s] * s_dt[s];
+#pragma unroll
+        for (int j = 0; j < NTn; ++j) {
+          vp[e] += U[j][e] * T::lds_to_f(sB[s * ldN + 16 * j + acc_col()]);
+          accdB[j][e] += sc * U[j][e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) vp[e] += __shfl_xor(vp[e], off, kWave);
+      if (acc_col() == 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_v[m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
+      mma_strip<Lt, false, false, NTn>(accdB, sW, ldQ, m0, sC, ldN, 0, kQ);
+    }
+    // (e) dC rows t: W B + exp(cs_t) dY H
+    {
+      mma_strip<Lt, true, false, NTn>(accdC, sW, ldQ, m0, sB, ldN, 0, kQ);
+      f32x4 tmp[NTn];
+#pragma unroll
+      for (int j = 0; j < NTn; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, false, NTn>(tmp, sDY, ldP, m0, sH, ldN, 0, P);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ecs = __expf(s_cs[m0 + acc_row(e)]);
+#pragma unroll
+        for (int j = 0; j < NTn; ++j) accdC[j][e] += ecs * tmp[j][e];
+      }
+    }
+    __syncthreads();
+
+    // (f) dcs -> dl (reverse cumsum) -> ddt, dA, ddt_bias (wave 0, one token per lane)
+    if (wave == 0) {
+      const int s = lane;
+      const float dts = s_dt[s];
+      const float colsum = s_col[0][s] + s_col[1][s] + s_col[2][s] + s_col[3][s];
+      const float vs = s_v[s];
+      float dcs = s_row[s] + s_yo[s] - dts * colsum - dts * vs;
+      const float hdh = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+      const float sum_dtv = wave_sum(dts * vs);
+      if (s == kQ - 1) dcs += __expf(s_cs[kQ - 1]) * hdh + sum_dtv;
+      // dl_s = sum_{t >= s} dcs_t: inclusive scan over reversed lanes
+      const float rev = __shfl(dcs, kWave - 1 - lane, kWave);
+      const float rscan = wave_incl_scan(rev);
+      const float dl = __shfl(rscan, kWave - 1 - lane, kWave);
+      const float ddt = colsum + vs + Ah * dl;
+      const bool valid = t0 + s < pr.L;
+      const float ddt_raw = valid ? ddt * s_sig[s] : 0.f;
+      if (valid)
+        static_cast<E*>(a.ddt.p)[b * a.ddt.sb + (t0 + s) * a.ddt.st + h] = T::from_f(ddt_raw);
+      const float dA_part = wave_sum(dts * dl);
+      const float db_part = wave_sum(ddt_raw);
+      if (lane == 0) {
+        float* pp = a.par_part + ((b * a.nch + c) * pr.H + h) * 3;
+        pp[0] = dA_part;
+        pp[1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+        pp[2] = db_part;
+      }
+    }
+    __syncthreads();
+  }
+
+  // dB (rows s) and dC (rows t) of the block's heads -> fp32 partial
+  float* part = a.dbc_part + ((static_cast<int64_t>(hb) * pr.B + b) * pr.L) * (2 * N);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t t = t0 + m0 + acc_row(e);
+    if (t < pr.L)
+#pragma unroll
+      for (int j = 0; j < NTn; ++j) {
+        part[t * (2 * N) + 16 * j + acc_col()] = accdB[j][e];
+        part[t * (2 * N) + N + 16 * j + acc_col()] = accdC[j][e];
+      }
+  }
+}
+
+// dB / dC of each group = sum of its head-block partials -> the B / C channels of dxbc
+template <typename IO>
+__global__ void __launch_bounds__(256) dbc_finalize_kernel(Problem pr, const float* part, int nhb,
+                                                           MView dxbc) {
+  using E = typename io_traits<IO>::elem;
+  const int N = pr.N, G = pr.G;
+  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t per_t = 2LL * G * N;
+  if (e >= pr.B * pr.L * per_t) return;
+  const int64_t ch = e % per_t, t = (e / per_t) % pr.L, b = e / (per_t * pr.L);
+  const bool isC = ch >= static_cast<int64_t>(G) * N;
+  const int g = static_cast<int>((isC ? ch - G * N : ch) / N);
+  const int n = static_cast<int>((isC ? ch - G * N : ch) % N);
+  const int per_g = nhb / G;
+  float acc = 0.f;
+  for (int q = 0; q < per_g; ++q) {
+    const int hb = g * per_g + q;
+    acc += part[((static_cast<int64_t>(hb) * pr.B + b) * pr.L + t) * (2 * N) + (isC ? N : 0) + n];
+  }
+  const int64_t col = static_cast<int64_t>(pr.H) * pr.P + ch;
+  static_cast<E*>(dxbc.p)[b * dxbc.sb + t * dxbc.st + col] = io_traits<IO>::from_f(acc);
+}
+
+// dA, dD, ddt_bias: ordered sums of the per-(batch, chunk) partials
+__global__ void __launch_bounds__(256) head_params_kernel(const float* par, int64_t B, int64_t nch,
+                                                          int H, float* dA, float* dD,
+                                                          float* ddt_bias, int accumulate) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 3 * H) return;
+  const int h = i / 3, k = i % 3;
+  float* dst = k == 0 ? dA : (k == 1 ? dD : ddt_bias);
+  if (!dst) return;
+  float acc = 0.f;
+  for (int64_t bc = 0; bc < B * nch; ++bc) acc += par[(bc * H + h) * 3 + k];
+  dst[h] = accumulate ? dst[h] + acc : acc;
+}
+
+struct BwdLayout {
+  size_t bc, bc_lo, H, lsum, dH, dbc, par, dx, conv, total;
+  int64_t nch;
+  int hb_heads, nhb;
+};
+
+BwdLayout bwd_layout(const Problem& pr) {
+  BwdLayout l{};
+  l.nch = (pr.L + kQ - 1) / kQ;
+  const int hpg = pr.H / pr.G;
+  int hb = 1;
+  for (int d = 1; d <= 8; ++d)
+    if (hpg % d == 0) hb = d;
+  l.hb_heads = hb;
+  l.nhb = pr.H / hb;
+  const size_t es = pr.bf16 ? 2 : 4;
+  const size_t PN = static_cast<size_t>(pr.P) * pr.N;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.bc = take(bc_prepass_bytes(pr));
+  l.bc_lo = take(pr.bf16 ? bc_prepass_bytes(pr) : 0);
+  l.H = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
+  l.lsum = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 4);
+  l.dH = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
+  l.dbc = take(static_cast<size_t>(l.nhb) * pr.B * pr.L * 2 * pr.N * 4);
+  l.par = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 3 * 4);
+  l.dx = take(pr.K > 0 ? static_cast<size_t>(pr.B) * pr.L * pr.H * pr.P * es : 0);
+  const int64_t cd = static_cast<int64_t>(pr.H) * pr.P + 2LL * pr.G * pr.N;
+  l.conv = take(pr.K > 0 ? conv_bwd_partials_bytes(pr.B, pr.L, cd) : 0);
+  l.total = off;
+  return l;
+}
+
+template <typename IO, int P, int N>
+hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws,
+                   const BwdLayout& l, hipStream_t s) {
+  BwdArgs a{};
+  a.pr = pr;
+  a.nch = l.nch;
+  a.hb_heads = l.hb_heads;
+  a.nhb = l.nhb;
+  a.Hs = reinterpret_cast<float*>(ws + l.H);
+  a.lsum = reinterpret_cast<float*>(ws + l.lsum);
+  a.dHs = reinterpret_cast<float*>(ws + l.dH);
+  a.dout = in.dout;
+  a.dz = o.dz;
+  a.ddt = o.ddt;
+  a.dbc_part = reinterpret_cast<float*>(ws + l.dbc);
+  a.par_part = reinterpret_cast<float*>(ws + l.par);
+  if (pr.K > 0) {
+    const int64_t hp = static_cast<int64_t>(pr.H) * pr.P;
+    a.dx = MView{ws + l.dx, pr.L * hp, hp};
+  } else {
+    a.dx = o.dxbc;  // x channels come first in dxbc rows
+  }
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  const int64_t ne = pr.B * pr.H * PN;
+  // 1. forward states entering each chunk
+  hipError_t e = launch_chunk_states(pr, l.nch, reinterpret_cast<float*>(ws + l.H),
+                                     reinterpret_cast<float*>(ws + l.lsum), s);
+  if (e != hipSuccess) return e;
+  // 2. per-chunk dy C^T terms, 3. reverse scan -> dH_c, dh0
+  {
+    TimingScope ts(kKDstate, s);
+    hipLaunchKernelGGL((dstate_kernel<IO, P, N>), dim3(static_cast<unsigned>(pr.B * l.nch * pr.H)),
+                       dim3(kThreads), 0, s, a);
+  }
+  {
+    TimingScope ts(kKScanRev, s);
+    hipLaunchKernelGGL(scan_rev_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0,
+                       s, in.dh_final, a.dHs, a.lsum, o.dh0, pr.B, pr.H, PN, l.nch);
+  }
+  // 4. main
+  {
+    TimingScope ts(kKBwdMain, s);
+    hipLaunchKernelGGL((bwd_main_kernel<IO, P, N>), dim3(static_cast<unsigned>(pr.B * l.nch * l.nhb)),
+                       dim3(kThreads), 0, s, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 5. dB / dC (and the conv backward)
+  if (pr.K > 0) {
+    e = launch_conv_bwd_fused(pr, ws + l.dx, a.dbc_part, l.nhb, in.dcs_out, o.dxbc, o.dconv_w,
+                              o.dconv_b, o.dcs_in, o.accumulate, ws + l.conv, s);
+    if (e != hipSuccess) return e;
+  } else {
+    const int64_t n = pr.B * pr.L * 2LL * pr.G * pr.N;
+    TimingScope ts(kKDbcFinalize, s);
+    hipLaunchKernelGGL(dbc_finalize_kernel<IO>, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, s, pr, a.dbc_part, l.nhb, o.dxbc);
+  }
+  // 6. parameter reductions
+  TimingScope ts(kKParams, s);
+  hipLaunchKernelGGL(head_params_kernel, dim3(static_cast<unsigned>((3 * pr.H + 255) / 256)),
+                     dim3(256), 0, s, a.par_part, pr.B, l.nch, pr.H, o.dA, o.dD, o.ddt_bias,
+                     o.accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const Problem& pr) { return bwd_layout(pr).total; }
+
+bool bwd_supported(const Problem& pr) {
+  // fp32 operands of the P x N state tiles do not fit the LDS budget at N = 128
+  return pr.bf16 || pr.N <= 64;
+}
+
+hipError_t launch_bwd(const Problem& pr_in, const BwdIn& in, const BwdOut& o, void* ws_v,
+                      hipStream_t s) {
+  Problem pr = pr_in;
+  char* ws = static_cast<char*>(ws_v);
+  const BwdLayout l = bwd_layout(pr);
+  if (pr.K > 0) {
+    const hipError_t e = launch_bc_prepass(pr, ws + l.bc, ws + l.bc_lo, s);
+    if (e != hipSuccess) return e;
+    const int64_t gn2 = 2LL * pr.G * pr.N;
+    pr.bc = View{ws + l.bc, pr.L * gn2, gn2};
+    if (pr.bf16) pr.bc_lo = View{ws + l.bc_lo, pr.L * gn2, gn2};
+  }
+#define SSD_CASE(IO, PP, NN) \
+  if (pr.P == PP && pr.N == NN) return run_bwd<IO, PP, NN>(pr, in, o, ws, l, s);
+  if (pr.bf16) {
+    SSD_CASE(bf16_t, 64, 128)
+    SSD_CASE(bf16_t, 64, 64)
+    SSD_CASE(bf16_t, 64, 32)
+    SSD_CASE(bf16_t, 64, 16)
+    SSD_CASE(bf16_t, 32, 128)
+    SSD_CASE(bf16_t, 32, 64)
+    SSD_CASE(bf16_t, 32, 32)
+    SSD_CASE(bf16_t, 32, 16)
+  } else {
+    SSD_CASE(float, 64, 64)
+    SSD_CASE(float, 64, 32)
+    SSD_CASE(float, 64, 16)
+    SSD_CASE(float, 32, 64)
+    SSD_CASE(float, 32, 32)
+    SSD_CASE(float, 32, 16)
+  }
+#undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssd

@@ -41,6 +41,7 @@ struct ConvFwdArgs {
   void* out;
   int64_t o_sb, o_st;
   int o_c0;
+  void* out_lo;  // optional: out value minus its rounding to the I/O dtype (same layout)
 };
 
 template <typename IO>
@@ -97,18 +98,334 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
         o[v] = a.silu ? siluf_(pre) : pre;
       }
       store_vec16<IO>(ob + t * a.o_st, o);
+      if (a.out_lo) {
+        float lo[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
+        store_vec16<IO>(static_cast<E*>(a.out_lo) + b * a.o_sb + a.o_c0 + c + t * a.o_st, lo);
+      }
     }
   }
 }
 
+// ------------------------------------------------------------------ backward
+constexpr int kBatch = 4;  // output rows per register batch in the backward walk
+
+struct ConvBwdArgs {
+  int64_t B, L;
+  int C, K, silu;
+  const void* x;  // raw rows
+  int64_t x_sb, x_st;
+  const void* st;  // carried state rows (null = zeros)
+  int64_t st_sb, st_st;
+  const float* w;
+  const float* bias;
+  // gradient of the conv output: a view (standalone) or the fused SSD sources
+  const void* g;
+  int64_t g_sb, g_st;
+  const float* dbc_part;  // [nhb][B][L][2N] fp32 (fused)
+  int nhb, hp, G, N;
+  const void* dso;  // gradient of the returned state rows (null = zero)
+  int64_t dso_sb, dso_st;
+  void* dx;
+  int64_t dx_sb, dx_st;
+  void* dsi;  // gradient of the carried-in state rows (null = skip)
+  int64_t dsi_sb, dsi_st;
+  float* part;  // [B][ntile][C][5]: dw taps 0..K-1, db at 4
+};
+
+template <typename IO, bool FUSED>
+__device__ __forceinline__ void conv_grad_row(const ConvBwdArgs& a, int64_t b, int64_t t, int c,
+                                              float (&gv)[io_traits<IO>::vec]) {
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  constexpr int V = T::vec;
+  if (t < 0 || t >= a.L) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) gv[v] = 0.f;
+    return;
+  }
+  if (!FUSED || c < a.hp) {
+    const int64_t sb = FUSED ? static_cast<int64_t>(a.L) * a.hp : a.g_sb;
+    const int64_t st = FUSED ? a.hp : a.g_st;
+    vec16<IO> r;
+    load_vec16<IO>(r, static_cast<const E*>(a.g) + b * sb + t * st + c);
+#pragma unroll
+    for (int v = 0; v < V; ++v) gv[v] = r.v[v];
+    return;
+  }
+  const int gn = a.G * a.N;
+  const int rel = c - a.hp;
+  const bool isC = rel >= gn;
+  const int g = (isC ? rel - gn : rel) / a.N;
+  const int n0 = (isC ? rel - gn : rel) % a.N;
+  const int per_g = a.nhb / a.G;
+#pragma unroll
+  for (int v = 0; v < V; ++v) gv[v] = 0.f;
+  for (int q = 0; q < per_g; ++q) {
+    const float* p = a.dbc_part +
+                     ((static_cast<int64_t>(g * per_g + q) * a.B + b) * a.L + t) * (2 * a.N) +
+                     (isC ? a.N : 0) + n0;
+#pragma unroll
+    for (int v4 = 0; v4 < V; v4 += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p + v4);
+      gv[v4] += f.x;
+      gv[v4 + 1] += f.y;
+      gv[v4 + 2] += f.z;
+      gv[v4 + 3] += f.w;
+    }
+  }
+}
+
+// One thread per (batch, 64-row tile, channel vector); rows are processed in
+// batches of kBatch outputs, each batch loading its raw rows and gradient rows
+// up front (independent loads in flight).
+template <typename IO, bool FUSED>
+__global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  constexpr int V = T::vec;
+  const int ncv = a.C / V;
+  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
+  const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (gid >= a.B * ntile * ncv) return;
+  const int cv = static_cast<int>(gid % ncv);
+  const int64_t tile = (gid / ncv) % ntile;
+  const int64_t b = gid / (static_cast<int64_t>(ncv) * ntile);
+  const int c = cv * V;
+  const int K = a.K;
+  const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + c;
+  const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + c : nullptr;
+
+  float w4[4][V], bias[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    bias[v] = a.bias ? a.bias[c + v] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = j - (4 - K);  // taps right-aligned on 4: tap j reads row t - 3 + j
+      w4[j][v] = kk >= 0 ? a.w[(c + v) * K + kk] : 0.f;
+    }
+  }
+  auto raw_row = [&](int64_t t) -> uint4 {
+    if (t >= a.L || t < -(K - 1)) return make_uint4(0u, 0u, 0u, 0u);
+    if (t >= 0) return *reinterpret_cast<const uint4*>(xb + t * a.x_st);
+    if (sb) return *reinterpret_cast<const uint4*>(sb + (t + K - 1) * a.st_st);
+    return make_uint4(0u, 0u, 0u, 0u);
+  };
+  float dw[4][V], db[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    db[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
+  }
+  E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + c;
+  const E* dsob = a.dso ? static_cast<const E*>(a.dso) + b * a.dso_sb + c : nullptr;
+  E* dsib = a.dsi ? static_cast<E*>(a.dsi) + b * a.dsi_sb + c : nullptr;
+  const int64_t t_lo = tile * kRowsB;
+  // tile 0 also produces the gradient of the carried-in state rows (tau < 0)
+  const int64_t tau_begin = tile == 0 ? -(K - 1) : t_lo;
+  const int64_t tau_end = t_lo + kRowsB < a.L ? t_lo + kRowsB : a.L;
+  for (int64_t tau0 = tau_begin; tau0 < tau_end; tau0 += kBatch) {
+    // dpre rows tau0 .. tau0 + kBatch + 2 need raw rows tau0 - 3 .. tau0 + kBatch + 2
+    uint4 raw[kBatch + 6];
+#pragma unroll
+    for (int i = 0; i < kBatch + 6; ++i) raw[i] = raw_row(tau0 - 3 + i);
+    float gr[kBatch + 3][V];
+#pragma unroll
+    for (int i = 0; i < kBatch + 3; ++i) conv_grad_row<IO, FUSED>(a, b, tau0 + i, c, gr[i]);
+    float dpre[kBatch + 3][V];
+#pragma unroll
+    for (int i = 0; i < kBatch + 3; ++i) {
+      const int64_t t = tau0 + i;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float d = 0.f;
+        if (t >= 0 && t < a.L) {
+          if (a.silu) {
+            float pre = bias[v];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[i + j], v), pre);
+            d = gr[i][v] * dsiluf_(pre);
+          } else {
+            d = gr[i][v];
+          }
+        }
+        dpre[i][v] = d;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const int64_t tau = tau0 + r;
+      if (tau >= tau_end) break;
+      float o[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = fmaf(w4[j][v], dpre[r + 3 - j][v], acc);
+        o[v] = acc;
+      }
+      const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
+      if (dsob && js >= 0) {
+        vec16<IO> d;
+        load_vec16<IO>(d, dsob + js * a.dso_st);
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] += d.v[v];
+      }
+      if (tau >= 0) {
+        store_vec16<IO>(dxb + tau * a.dx_st, o);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          db[v] += dpre[r][v];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dpre[r][v], raw_elem<IO>(raw[r + j], v), dw[j][v]);
+        }
+      } else if (dsib) {
+        store_vec16<IO>(dsib + (tau + K - 1) * a.dsi_st, o);
+      }
+    }
+  }
+  float* pp = a.part + ((b * ntile + tile) * a.C + c) * 5;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = j - (4 - K);
+      if (kk >= 0) pp[v * 5 + kk] = dw[j][v];
+    }
+    pp[v * 5 + 4] = db[v];
+  }
+}
+
+// dw[c][k], db[c]: ordered sums of the per-(batch, tile) partials
+__global__ void __launch_bounds__(256) conv_params_kernel(const float* part, int64_t n_bt, int C,
+                                                          int K, float* dw, float* db,
+                                                          int accumulate) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= C * 5) return;
+  const int c = i / 5, k = i % 5;
+  if (k < 4 && k >= K) return;
+  float* dst = k == 4 ? (db ? db + c : nullptr) : (dw ? dw + c * K + k : nullptr);
+  if (!dst) return;
+  float acc = 0.f;
+  for (int64_t q = 0; q < n_bt; ++q) acc += part[(q * C + c) * 5 + k];
+  *dst = accumulate ? *dst + acc : acc;
+}
+
+hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* db, int accumulate,
+                        hipStream_t s) {
+  const int V = bf16 ? 8 : 4;
+  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
+  const int64_t n = a.B * ntile * (a.C / V);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  TimingScope ts(kKConvBwd, s);
+  if (bf16) {
+    if (fused)
+      hipLaunchKernelGGL((conv_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((conv_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((conv_bwd_kernel<float, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((conv_bwd_kernel<float, false>), grid, dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(conv_params_kernel, dim3(static_cast<unsigned>((a.C * 5 + 255) / 256)),
+                     dim3(256), 0, s, a.part, a.B * ntile, a.C, a.K, dw, db, accumulate);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t conv_bwd_partials_bytes(int64_t B, int64_t L, int64_t C) {
+  const int64_t ntile = (L + kRowsB - 1) / kRowsB;
+  return static_cast<size_t>(B) * ntile * C * 5 * sizeof(float);
+}
+
+size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C) {
+  return conv_bwd_partials_bytes(B, L, C);
+}
+
+hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,
+                           float* db, MView dstate_in, int accumulate, void* ws, hipStream_t s) {
+  ConvBwdArgs a{};
+  a.B = cp.B;
+  a.L = cp.L;
+  a.C = static_cast<int>(cp.C);
+  a.K = cp.K;
+  a.silu = cp.silu;
+  a.x = cp.x.p;
+  a.x_sb = cp.x.sb;
+  a.x_st = cp.x.st;
+  a.st = cp.state_in.p;
+  a.st_sb = cp.state_in.sb;
+  a.st_st = cp.state_in.st;
+  a.w = cp.w;
+  a.bias = cp.b;
+  a.g = dout.p;
+  a.g_sb = dout.sb;
+  a.g_st = dout.st;
+  a.dso = dstate_out.p;
+  a.dso_sb = dstate_out.sb;
+  a.dso_st = dstate_out.st;
+  a.dx = dx.p;
+  a.dx_sb = dx.sb;
+  a.dx_st = dx.st;
+  a.dsi = dstate_in.p;
+  a.dsi_sb = dstate_in.sb;
+  a.dsi_st = dstate_in.st;
+  a.part = static_cast<float*>(ws);
+  return run_conv_bwd(a, cp.bf16, false, dw, db, accumulate, s);
+}
+
+// Conv backward of the SSD entry point: the post-conv gradient of the x channels
+// comes from `dx_ws` ([B][L][H*P], I/O dtype), that of the B and C channels from
+// the per-head-block fp32 partials.
+hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_part,
+                                 int nhb, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
+                                 MView dcs_in, int accumulate, void* ws, hipStream_t s) {
+  ConvBwdArgs a{};
+  a.B = pr.B;
+  a.L = pr.L;
+  a.C = pr.H * pr.P + 2 * pr.G * pr.N;
+  a.K = pr.K;
+  a.silu = 1;
+  a.x = pr.xbc.p;
+  a.x_sb = pr.xbc.sb;
+  a.x_st = pr.xbc.st;
+  a.st = pr.cs_in.p;
+  a.st_sb = pr.cs_in.sb;
+  a.st_st = pr.cs_in.st;
+  a.w = pr.conv_w;
+  a.bias = pr.conv_b;
+  a.g = dx_ws;
+  a.dbc_part = dbc_part;
+  a.nhb = nhb;
+  a.hp = pr.H * pr.P;
+  a.G = pr.G;
+  a.N = pr.N;
+  a.dso = dcs_out.p;
+  a.dso_sb = dcs_out.sb;
+  a.dso_st = dcs_out.st;
+  a.dx = dxbc.p;
+  a.dx_sb = dxbc.sb;
+  a.dx_st = dxbc.st;
+  a.dsi = dcs_in.p;
+  a.dsi_sb = dcs_in.sb;
+  a.dsi_st = dcs_in.st;
+  a.part = static_cast<float*>(ws);
+  return run_conv_bwd(a, pr.bf16, true, dconv_w, dconv_b, accumulate, s);
+}
 
 // Conv forward over channels [c0, c0 + C) of the rows of `x`, writing channels
 // [o_c0, o_c0 + C) of `out`.  Weights / bias pointers refer to channel c0.
 hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, int silu, View x,
                                  int x_c0, View st, int st_c0, const float* w, const float* bias,
-                                 MView out, int o_c0, hipStream_t s) {
+                                 MView out, int o_c0, hipStream_t s, void* out_lo) {
   ConvFwdArgs a{};
+  a.out_lo = out_lo;
   a.B = B;
   a.L = L;
   a.C = C;
@@ -131,6 +448,7 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
   const int V = bf16 ? 8 : 4;
   const int64_t n = B * ((L + kRowsF - 1) / kRowsF) * (C / V);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  TimingScope ts(kKConvFwd, s);
   if (bf16)
     hipLaunchKernelGGL(conv_fwd_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else
@@ -144,17 +462,19 @@ size_t bc_prepass_bytes(const Problem& pr) {
   return (n + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_bc_prepass(const Problem& pr, void* dst, hipStream_t s) {
+hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s) {
+  TimingScope ts(kKBcPrepass, s);
   const int hp = pr.H * pr.P, gn2 = 2 * pr.G * pr.N;
   const MView out{dst, pr.L * gn2, gn2};
   return launch_conv_fwd_range(pr.bf16, pr.B, pr.L, gn2, pr.K, 1, pr.xbc, hp, pr.cs_in, hp,
                                pr.conv_w + static_cast<int64_t>(hp) * pr.K,
-                               pr.conv_b ? pr.conv_b + hp : nullptr, out, 0, s);
+                               pr.conv_b ? pr.conv_b + hp : nullptr, out, 0, s,
+                               pr.bf16 ? dst_lo : nullptr);
 }
 
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s) {
   hipError_t e = launch_conv_fwd_range(cp.bf16, cp.B, cp.L, static_cast<int>(cp.C), cp.K, cp.silu,
-                                       cp.x, 0, cp.state_in, 0, cp.w, cp.b, out, 0, s);
+                                       cp.x, 0, cp.state_in, 0, cp.w, cp.b, out, 0, s, nullptr);
   if (e != hipSuccess || !state_out.p) return e;
   // returned state: the last K-1 inputs (reuse the SSD conv-state copy with Cd = C)
   Problem pr{};

@@ -387,10 +387,17 @@ hipError_t run_walks(const Problem& pr, const FwdOut& o, const Plan& pl, float* 
   const int64_t PN = static_cast<int64_t>(P) * N;
   const dim3 grid(static_cast<unsigned>(pr.B * pl.n_sub * pr.H));
   if (pl.n_sub > 1) {
-    hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeState>), grid, dim3(WalkShape<kModeState>::waves * 64), 0, s, a);
+    {
+      TimingScope ts(kKWalkState, s);
+      hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeState>), grid,
+                         dim3(WalkShape<kModeState>::waves * 64), 0, s, a);
+    }
     const int64_t ne = pr.B * pr.H * PN;
-    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
-                       pr.h0, ws_state, ws_lsum, pr.B, pr.H, PN, pl.n_sub);
+    {
+      TimingScope ts(kKScan, s);
+      hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+                         pr.h0, ws_state, ws_lsum, pr.B, pr.H, PN, pl.n_sub);
+    }
     a.init = ws_state;
     a.init_sb = pl.n_sub * pr.H * PN;
     a.init_sk = pr.H * PN;
@@ -399,7 +406,11 @@ hipError_t run_walks(const Problem& pr, const FwdOut& o, const Plan& pl, float* 
     a.init_sb = pr.H * PN;
     a.init_sk = 0;
   }
-  hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeOut>), grid, dim3(WalkShape<kModeOut>::waves * 64), 0, s, a);
+  {
+    TimingScope ts(kKWalkOut, s);
+    hipLaunchKernelGGL((walk_kernel<IO, P, N, kModeOut>), grid, dim3(WalkShape<kModeOut>::waves * 64),
+                       0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -455,7 +466,7 @@ hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, voi
   char* w = static_cast<char*>(ws);
   hipError_t err = hipSuccess;
   if (pr.K > 0) {
-    err = launch_bc_prepass(pr, w, s);
+    err = launch_bc_prepass(pr, w, nullptr, s);
     if (err != hipSuccess) return err;
     const int64_t gn2 = 2LL * pr.G * pr.N;
     pr.bc = View{w, pr.L * gn2, gn2};
@@ -487,10 +498,12 @@ hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, floa
   a.ckpt_every = 1;
   const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
   const dim3 grid(static_cast<unsigned>(pr.B * nch * pr.H));
-#define SSD_CASE(IO, PP, NN)                                                                    \
-  if (pr.P == PP && pr.N == NN) {                                                               \
-    hipLaunchKernelGGL((walk_kernel<IO, PP, NN, kModeState>), grid, dim3(WalkShape<kModeState>::waves * 64), 0, s, a); \
-    launched = true;                                                                            \
+#define SSD_CASE(IO, PP, NN)                                                              \
+  if (pr.P == PP && pr.N == NN) {                                                         \
+    TimingScope ts(kKChunkStates, s);                                                     \
+    hipLaunchKernelGGL((walk_kernel<IO, PP, NN, kModeState>), grid,                       \
+                       dim3(WalkShape<kModeState>::waves * 64), 0, s, a);                 \
+    launched = true;                                                                      \
   }
   bool launched = false;
   if (pr.bf16) {
@@ -505,8 +518,11 @@ hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, floa
 #undef SSD_CASE
   if (!launched) return hipErrorInvalidValue;
   const int64_t ne = pr.B * pr.H * PN;
-  hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
-                     pr.h0, ws_H, ws_lsum, pr.B, pr.H, PN, nch);
+  {
+    TimingScope ts(kKScan, s);
+    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+                       pr.h0, ws_H, ws_lsum, pr.B, pr.H, PN, nch);
+  }
   return hipGetLastError();
 }
 
@@ -515,6 +531,7 @@ hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s) {
   const int64_t ne = pr.B * (pr.K - 1) * cd;
   if (ne <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((ne + 255) / 256));
+  TimingScope ts(kKConvStateOut, s);
   if (pr.bf16)
     hipLaunchKernelGGL(conv_state_out_kernel<bf16_t>, grid, dim3(256), 0, s, pr, dst);
   else

@@ -11,6 +11,28 @@ namespace ssd {
 constexpr int kQ = 64;         // chunk length of the chunked evaluation
 constexpr int kThreads = 256;  // threads per workgroup of the chunk kernels
 
+// Kernel kinds of the timing instrumentation (ssd_timing_* in ssd.h).
+enum KernelKind {
+  kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
+  kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcFinalize, kKParams, kKernelKinds
+};
+
+// Brackets the launches made during its lifetime with HIP events on stream `s`
+// when timing is enabled (no-op otherwise).
+class TimingScope {
+ public:
+  TimingScope(int kind, hipStream_t s);
+  ~TimingScope();
+  TimingScope(const TimingScope&) = delete;
+  TimingScope& operator=(const TimingScope&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t s_;
+  void* a_ = nullptr;
+  void* b_ = nullptr;
+};
+
 struct View {
   const void* p;
   int64_t sb, st;  // element strides (batch, time)
@@ -43,7 +65,8 @@ struct Problem {
   const float* D;
   View z;  // p may be null
   const float* h0;
-  View bc;  // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
+  View bc;     // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
+  View bc_lo;  // bf16 I/O backward: post-conv B|C minus its bf16 rounding (p null: none)
 };
 
 struct FwdOut {
@@ -81,6 +104,7 @@ struct BwdOut {
   int accumulate;
 };
 size_t bwd_workspace_bytes(const Problem& pr);
+bool bwd_supported(const Problem& pr);
 hipError_t launch_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, void* ws,
                       hipStream_t s);
 
@@ -97,9 +121,10 @@ struct ConvProblem {
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s);
 hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, int silu, View x,
                                  int x_c0, View st, int st_c0, const float* w, const float* bias,
-                                 MView out, int o_c0, hipStream_t s);
-// B|C post-conv pre-pass of the SSD entry points: channels [H*P, Cd) of xbc -> dst
-hipError_t launch_bc_prepass(const Problem& pr, void* dst, hipStream_t s);
+                                 MView out, int o_c0, hipStream_t s, void* out_lo);
+// B|C post-conv pre-pass of the SSD entry points: channels [H*P, Cd) of xbc -> dst,
+// and (dst_lo != null, bf16 I/O) the rounding residual v - bf16(v) -> dst_lo
+hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s);
 size_t bc_prepass_bytes(const Problem& pr);
 size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);
 hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,

@@ -134,3 +134,104 @@ class Case:
             r = dict(out=out, y=y, h_final=hf, conv_state_out=None)
         r["out"] = r["out"].reshape(B, L, d.hp)
         return r
+
+
+# ---------------------------------------------------------------------- backward
+
+GRAD_KEYS = ("dxbc", "ddt", "dz", "dA", "dD", "ddt_bias", "dconv_w", "dconv_b", "dh0", "dconv_state")
+
+
+def _bwd_outputs(d: synth.Dims, L: int, io):
+    B = d.B
+    o = dict(dxbc=torch.empty(B, L, d.cd, dtype=io, device="cuda"),
+             ddt=torch.empty(B, L, d.H, dtype=io, device="cuda"),
+             dz=torch.empty(B, L, d.hp, dtype=io, device="cuda") if d.gate else None,
+             dA=torch.zeros(d.H, device="cuda"), dD=torch.zeros(d.H, device="cuda"),
+             ddt_bias=torch.zeros(d.H, device="cuda"),
+             dh0=torch.empty(B, d.H, d.P, d.N, device="cuda"))
+    if d.K:
+        o["dconv_w"] = torch.zeros(d.cd, d.K, device="cuda")
+        o["dconv_b"] = torch.zeros(d.cd, device="cuda")
+        o["dconv_state"] = torch.empty(B, d.K - 1, d.cd, dtype=io, device="cuda")
+    return o
+
+
+def _dout(case, t0, t1):
+    d = case.d
+    if not hasattr(case, "_dout"):
+        case._dout = synth.dout(d, case.seed + 7)
+    return case._dout[:, t0:t1]
+
+
+def gpu_bwd(case, t0=0, t1=None, h0=None, conv_state=None, dh_final=None, dconv_state=None):
+    d = case.d
+    t1 = d.L if t1 is None else t1
+    L = t1 - t0
+    io = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    zx, z, xbc, dt = case.dev_inputs()
+    sl = slice(t0, t1)
+    z = z[:, sl] if z is not None else None
+    xbc, dt = xbc[:, sl], dt[:, sl]
+    dout = to_dev(_dout(case, t0, t1), d.dtype)
+    dims = case.dims(L)
+    o = _bwd_outputs(d, L, io)
+    nb = bd.ssd_bwd_workspace(dims, bd.SSD_BF16 if d.dtype == "bf16" else bd.SSD_F32)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    p = case.p
+    bd.ssd_bwd(dims, xbc, fdev(p["A"]), dt, dout, o["dxbc"], o["ddt"], o["dA"],
+               conv_w=fdev(p.get("conv_w")) if d.K else None,
+               conv_b=fdev(p.get("conv_b")) if d.K else None,
+               conv_state_in=None if conv_state is None else to_dev(conv_state, d.dtype),
+               dt_bias=fdev(p["dt_bias"]), dt_softplus=True, D=fdev(p["D"]), z=z,
+               h0=fdev(h0), dh_final=fdev(dh_final),
+               dconv_state_out=None if dconv_state is None else to_dev(dconv_state, d.dtype),
+               dz=o["dz"], dD=o["dD"], ddt_bias=o["ddt_bias"], dconv_w=o.get("dconv_w"),
+               dconv_b=o.get("dconv_b"), dh0=o["dh0"], dconv_state_in=o.get("dconv_state"), ws=ws)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_bwd(case, t0=0, t1=None, h0=None, conv_state=None, dh_final=None, dconv_state=None):
+    d = case.d
+    t1 = d.L if t1 is None else t1
+    z, xbc, dt = case.host_split(t0, t1)
+    B, L = xbc.shape[:2]
+    p = {k: v.astype(np.float64) for k, v in case.p.items()}
+    dout = f64(_dout(case, t0, t1)).reshape(B, L, d.H, d.P)
+    zz = z.reshape(B, L, d.H, d.P) if z is not None else None
+    f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)
+    if d.K:
+        r = orc.mixer_bwd(xbc, p["conv_w"], p["conv_b"], dt, p["A"], d.H, d.P, d.G, d.N, dout,
+                          dt_bias=p["dt_bias"], D=p["D"], z=zz, h0=f(h0), conv_state=f(conv_state),
+                          dh_final=f(dh_final), dconv_state_out=f(dconv_state))
+        r["dxbc"] = r["dxbc_raw"]
+    else:
+        x, Bm, Cm = orc.split_xbc(xbc, d.H, d.P, d.G, d.N)
+        r = orc.ssd_bwd(x, dt, p["A"], Bm, Cm, dout, p["dt_bias"], True, p["D"], zz, f(h0), f(dh_final))
+        r["dxbc"] = np.concatenate([r["dx"].reshape(B, L, d.hp), r["dB"].reshape(B, L, d.G * d.N),
+                                    r["dC"].reshape(B, L, d.G * d.N)], axis=-1)
+    if r.get("dz") is not None:
+        r["dz"] = r["dz"].reshape(B, L, d.hp)
+    return r
+
+
+def compare_grads(g, r, tol, tag=""):
+    errs = {}
+    for k in GRAD_KEYS:
+        if g.get(k) is None or r.get(k) is None:
+            continue
+        errs[k] = rel_l2(to_host(g[k]), r[k])
+    print(f"[bwd] {tag} " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+    return errs
+
+
+def bwd_check(case) -> dict:
+    """Gradients of one case (with its carried states, if any) vs the oracle."""
+    st = case.st
+    kw = dict(h0=st.get("h0"), conv_state=st.get("conv_state"), dh_final=st.get("dh_final"),
+              dconv_state=st.get("dconv_state"))
+    g = gpu_bwd(case, **kw)
+    r = oracle_bwd(case, **kw)
+    return compare_grads(g, r, TOL[case.d.dtype], str(case.d.L))

@@ -1,0 +1,157 @@
+"""GPU parity of ssd_bwd / conv1d_bwd and of the segmented (checkpointed) backward
+against the fp64 oracle's full-storage backprop.
+
+Every gradient is compared: dxbc (raw conv input: x, B, C paths), ddt (w.r.t. the
+raw dt), dz, dA, dD, ddt_bias, the conv weight and bias, dh0 and the gradient of
+the carried conv state.  Bar: relative L2 <= 1e-4 (fp32 I/O) / 1e-2 (bf16 I/O).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from selective_state_space_15_amd import binding as bd
+from selective_state_space_15_amd import segmented, synth
+from tests.gpu_cases import (TOL, Case, _bwd_outputs, _dout, bwd_check, compare_grads, fdev,
+                             gpu_bwd, oracle_bwd, rel_l2, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_c0_scan_fp32_bwd():
+    bwd_check(Case(synth.CONFIGS["c0"], seed=0))
+
+
+def test_c0_ragged_fp32_bwd_with_states():
+    bwd_check(Case(synth.CONFIGS["c0"].with_(L=500), seed=1, states=True))
+
+
+@pytest.mark.parametrize("L", [1, 3, 64, 65, 300, 1000])
+def test_c1_shapes_bwd(L):
+    bwd_check(Case(synth.CONFIGS["c1"].with_(L=L), seed=10 + L))
+
+
+@pytest.mark.parametrize("L", [2, 700])
+def test_c1_bwd_carried_states(L):
+    bwd_check(Case(synth.CONFIGS["c1"].with_(L=L), seed=20 + L, states=True))
+
+
+def test_c1_full_length_bwd():
+    bwd_check(Case(synth.CONFIGS["c1"], seed=30))
+
+
+def test_grouped_batched_bwd():
+    d = synth.Dims(B=2, L=333, H=8, P=64, N=64, G=2, K=4, d_model=256)
+    bwd_check(Case(d, seed=31, states=True))
+
+
+@pytest.mark.parametrize("P,N", [(32, 16), (32, 128), (64, 16), (64, 32)])
+def test_other_head_shapes_bwd(P, N):
+    d = synth.Dims(B=1, L=257, H=3, P=P, N=N, G=1, K=4, d_model=128)
+    bwd_check(Case(d, seed=32, states=True))
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_narrow_conv_bwd(K):
+    d = synth.Dims(B=1, L=200, H=2, P=64, N=64, G=1, K=K, d_model=128)
+    bwd_check(Case(d, seed=33, states=True))
+
+
+def test_fp32_mixer_bwd():
+    d = synth.Dims(B=1, L=300, H=2, P=64, N=64, G=1, K=4, d_model=64, dtype="f32")
+    bwd_check(Case(d, seed=34, states=True))
+
+
+def test_fp32_dstate128_is_unsupported():
+    d = bd.make_dims(1, 64, 2, 64, 128, 1, 0, 4)
+    with pytest.raises(bd.SsdError) as e:
+        bd.ssd_bwd_workspace(d, bd.SSD_F32)
+    assert e.value.status == bd.SSD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,K,silu,L", [("bf16", 4, True, 333), ("bf16", 3, False, 70),
+                                            ("bf16", 2, True, 2), ("f32", 4, True, 200)])
+def test_conv1d_bwd_standalone(dtype, K, silu, L):
+    r = np.random.default_rng(K * 100 + L)
+    B, C = 2, 64
+    x = synth.round_io(r.standard_normal((B, L, C)), dtype)
+    st = synth.round_io(r.standard_normal((B, K - 1, C)), dtype)
+    go = synth.round_io(r.standard_normal((B, L, C)), dtype)
+    dso = synth.round_io(r.standard_normal((B, K - 1, C)), dtype)
+    w = r.uniform(-0.5, 0.5, (C, K)).astype(np.float32)
+    bias = r.uniform(-0.5, 0.5, C).astype(np.float32)
+    io = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dx = torch.empty(B, L, C, dtype=io, device="cuda")
+    dsi = torch.empty(B, K - 1, C, dtype=io, device="cuda")
+    dw = torch.zeros(C, K, device="cuda")
+    db = torch.zeros(C, device="cuda")
+    ws = torch.empty(bd.conv1d_bwd_workspace(B, L, C, K), dtype=torch.uint8, device="cuda")
+    bd.conv1d_bwd(to_dev(x, dtype), fdev(w), to_dev(go, dtype), dx, dw, b=fdev(bias), silu=silu,
+                  state_in=to_dev(st, dtype), dstate_out=to_dev(dso, dtype), db=db, dstate_in=dsi, ws=ws)
+    torch.cuda.synchronize()
+    rdx, rdw, rdb, rdsi = orc.conv1d_bwd(x, w, bias, st, silu, go, dso)
+    errs = dict(dx=rel_l2(to_host(dx), rdx), dw=rel_l2(to_host(dw), rdw), db=rel_l2(to_host(db), rdb),
+                dsi=rel_l2(to_host(dsi), rdsi))
+    print(f"[conv_bwd] {dtype} K={K} L={L}", errs)
+    assert all(v <= TOL[dtype] for v in errs.values()), errs
+
+
+def _segmented_case(d, seed, seg):
+    """Forward with checkpoints every `seg` tokens, then the reverse per-segment
+    backward; returns the GPU gradients."""
+    c = Case(d, seed=seed, states=True)
+    io = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    zx, z, xbc, dt = c.dev_inputs()
+    dims = c.dims()
+    p = {k: fdev(v) for k, v in c.p.items()}
+    st = c.st
+    cs_in = to_dev(st["conv_state"], d.dtype)
+    h0 = fdev(st["h0"])
+    out = torch.empty(d.B, d.L, d.hp, dtype=io, device="cuda")
+    fws = torch.empty(max(bd.ssd_fwd_workspace(dims, bd.io_dtype(xbc)), 1), dtype=torch.uint8, device="cuda")
+    h_ckpt = segmented.forward_segmented(dims, seg, xbc, p["A"], dt, out, conv_w=p["conv_w"],
+                                         conv_b=p["conv_b"], conv_state_in=cs_in, dt_bias=p["dt_bias"],
+                                         D=p["D"], z=z, h0=h0, ws=fws)
+    o = _bwd_outputs(d, d.L, io)
+    seg_dims = c.dims(seg)
+    bws = torch.empty(max(bd.ssd_bwd_workspace(seg_dims, bd.io_dtype(xbc)), 1), dtype=torch.uint8,
+                      device="cuda")
+    dout = to_dev(_dout(c, 0, d.L), d.dtype)
+    segmented.backward_segmented(dims, seg, h_ckpt, xbc, p["A"], dt, dout, o["dxbc"], o["ddt"], o["dA"],
+                                 conv_w=p["conv_w"], conv_b=p["conv_b"], conv_state_in=cs_in,
+                                 dt_bias=p["dt_bias"], D=p["D"], z=z, dz=o["dz"], dD=o["dD"],
+                                 ddt_bias=o["ddt_bias"], dconv_w=o["dconv_w"], dconv_b=o["dconv_b"],
+                                 dh_final=fdev(st["dh_final"]),
+                                 dconv_state_out=to_dev(st["dconv_state"], d.dtype), dh0=o["dh0"],
+                                 dconv_state_in=o["dconv_state"], ws=bws)
+    torch.cuda.synchronize()
+    return c, o
+
+
+@pytest.mark.parametrize("seg", [1024, 320])
+def test_segmented_backward_equals_full_storage(seg):
+    """Checkpoint only (h, conv buffer) every `seg` tokens; the per-segment
+    recompute-and-backprop matches the oracle's full-storage gradients."""
+    d = synth.CONFIGS["c3"].with_(L=4096)
+    c, g = _segmented_case(d, 40, seg)
+    st = c.st
+    r = oracle_bwd(c, h0=st["h0"], conv_state=st["conv_state"], dh_final=st["dh_final"],
+                   dconv_state=st["dconv_state"])
+    compare_grads(g, r, TOL["bf16"], f"segmented seg={seg}")
+
+
+def test_reviewer_spec_fp32_segmented():
+    """1 block, d_model 64 (2 heads x 64), conv width 4, S=1024, s=128, fp32 I/O:
+    segmented gradients vs full-storage backprop (oracle) and vs the unsegmented
+    GPU backward."""
+    d = synth.Dims(B=1, L=1024, H=2, P=64, N=64, G=1, K=4, d_model=64, dtype="f32")
+    c, g = _segmented_case(d, 41, 128)
+    st = c.st
+    kw = dict(h0=st["h0"], conv_state=st["conv_state"], dh_final=st["dh_final"],
+              dconv_state=st["dconv_state"])
+    r = oracle_bwd(c, **kw)
+    compare_grads(g, r, TOL["f32"], "reviewer-spec segmented vs oracle")
+    full = gpu_bwd(c, **kw)
+    for k in ("dxbc", "ddt", "dz", "dA", "dD", "ddt_bias", "dconv_w", "dconv_b", "dh0", "dconv_state"):
+        e = rel_l2(to_host(g[k]), to_host(full[k]))
+        assert e <= 1e-5, (k, e)
