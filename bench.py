@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--L", type=int, default=1 << 20)
     ap.add_argument("--seg", type=int, default=16384)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=4096, help="oracle prefix tokens (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=49152, help="oracle prefix tokens (0 = skip)")
     return ap.parse_args()
 
 
