@@ -34,8 +34,8 @@
 
 namespace ssd {
 
-hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_part,
-                                 int nhb, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
+hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_sum,
+                                 int per_g, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
                                  MView dcs_in, int accumulate, void* ws, hipStream_t s);
 size_t conv_bwd_partials_bytes(int64_t B, int64_t L, int64_t C);
 
@@ -86,52 +86,65 @@ __global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t t0 = c * kQ;
 
+  // issue every global load (dt, C rows, their low parts, dout, z) before any is used
+  E dt_e{};
+  if (wave == 0 && t0 + lane < pr.L)
+    dt_e = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h];
+  ChunkLoader<IO, P, N, false, false, true> cl_hi, cl_lo;
+  cl_hi.issue(pr, b, h, g, t0);
+  const bool clo = SPLIT && pr.bc_lo.p != nullptr;
+  Problem prl = pr;
+  prl.bc = pr.bc_lo;
+  if (clo) cl_lo.issue(prl, b, h, g, t0);
+  constexpr int V = T::vec;
+  constexpr int NDT = (P / V) * kQ / kThreads;  // dout / z vectors per thread
+  static_assert((P / V) * kQ % kThreads == 0, "dout tasks must tile the block");
+  uint4 dvr[NDT], zvr[NDT];
+  {
+    const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
+    const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) {
+      const int task = threadIdx.x + q * kThreads;
+      const int col = (task % (P / V)) * V, r = task / (P / V);
+      const int64_t t = t0 + r;
+      dvr[q] = zvr[q] = make_uint4(0u, 0u, 0u, 0u);
+      if (t < pr.L) {
+        dvr[q] = *reinterpret_cast<const uint4*>(dp + t * a.dout.st + col);
+        if (zp) zvr[q] = *reinterpret_cast<const uint4*>(zp + t * pr.z.st + col);
+      }
+    }
+  }
   if (wave == 0) {
-    const int64_t t = t0 + lane;
     float dtv = 0.f;
-    if (t < pr.L) {
-      const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h]) +
-                      (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+    if (t0 + lane < pr.L) {
+      const float u = T::to_f(dt_e) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
       dtv = pr.softplus ? softplusf_(u) : u;
     }
     const float cs = wave_incl_scan(dtv * pr.A[h]);
     s_ecs[lane] = __expf(cs);
   }
-  conv_rows<IO, P, N, false, false, true>(pr, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+  cl_hi.consume(pr, h, t0, [&](int, int s, int cl, const float* o) {
     lds_put_row<IO>(sC + s * ldN + cl, o);
   });
-  const bool clo = SPLIT && pr.bc_lo.p != nullptr;
-  if (clo) {
-    Problem prl = pr;
-    prl.bc = pr.bc_lo;
-    conv_rows<IO, P, N, false, false, true>(prl, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+  if (clo)
+    cl_lo.consume(prl, h, t0, [&](int, int s, int cl, const float* o) {
       lds_put_row<IO>(sClo + s * ldN + cl, o);
     });
-  }
   __syncthreads();
   // dy * exp(cs_t), transposed into sDyT[p][t]
-  {
-    constexpr int V = T::vec;
-    const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-    const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
-    for (int task = threadIdx.x; task < (P / V) * kQ; task += kThreads) {
-      const int cl = (task % (P / V)) * V, r = task / (P / V);
-      const int64_t t = t0 + r;
-      vec16<IO> dv, zv;
-      zero_vec16<IO>(dv);
-      zero_vec16<IO>(zv);
-      if (t < pr.L) {
-        load_vec16<IO>(dv, dp + t * a.dout.st + cl);
-        if (zp) load_vec16<IO>(zv, zp + t * pr.z.st + cl);
-      }
-      const float ecs = s_ecs[r];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const float dy = (zp ? dv.v[v] * siluf_(zv.v[v]) : dv.v[v]) * ecs;
-        const Lt hi = T::to_lds(dy);
-        sDyT[(cl + v) * ldQ + r] = hi;
-        if constexpr (SPLIT) sDyTlo[(cl + v) * ldQ + r] = T::to_lds(dy - T::lds_to_f(hi));
-      }
+  for (int q = 0; q < NDT; ++q) {
+    const int task = threadIdx.x + q * kThreads;
+    const int col = (task % (P / V)) * V, r = task / (P / V);
+    const float ecs = s_ecs[r];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float dv = raw_elem<IO>(dvr[q], v);
+      const float dy = (pr.z.p ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * ecs;
+      const Lt hi = T::to_lds(dy);
+      sDyT[(col + v) * ldQ + r] = hi;
+      if constexpr (SPLIT) sDyTlo[(col + v) * ldQ + r] = T::to_lds(dy - T::lds_to_f(hi));
     }
   }
   __syncthreads();
@@ -260,13 +273,54 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     const int h = h_first + hh;
     const float Ah = pr.A[h];
     const float Dh = pr.D ? pr.D[h] : 0.f;
+    // Every global load of head h is issued before any is consumed, so the head
+    // waits for memory once: dt (wave 0), the raw x rows, dout / z at this lane's
+    // accumulator positions (rows m0 + 4*(lane/16)+e, cols 16j + lane%16), H_{c-1}
+    // and dH_c.
+    E dt_e{};
+    if (wave == 0 && t0 + lane < pr.L)
+      dt_e = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h];
+    ChunkLoader<IO, P, N, true, false, false> xl;
+    xl.issue(pr, b, h, g, t0);
+    E dv_e[PJ][4], zv_e[PJ][4];
+    {
+      const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
+      const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+#pragma unroll
+      for (int j = 0; j < PJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t t = t0 + m0 + acc_row(e);
+          const int p = 16 * j + acc_col();
+          dv_e[j][e] = E{};
+          zv_e[j][e] = E{};
+          if (t < pr.L) {
+            dv_e[j][e] = dp[t * a.dout.st + p];
+            if (zp) zv_e[j][e] = zp[t * pr.z.st + p];
+          }
+        }
+    }
+    constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
+    float4 hv[NH4], gv[NH4];
+    {
+      const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
+      const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
+#pragma unroll
+      for (int q = 0; q < NH4; ++q) {
+        const int i = (threadIdx.x + q * kThreads) * 4;
+        hv[q] = gv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (i < P * N) {
+          hv[q] = *reinterpret_cast<const float4*>(Hg + i);
+          gv[q] = *reinterpret_cast<const float4*>(dHg + i);
+        }
+      }
+    }
     // (1) dt, cs, softplus slope, chunk-state decays (wave 0)
     if (wave == 0) {
       const int64_t t = t0 + lane;
       float dtv = 0.f, sig = 1.f;
       if (t < pr.L) {
-        const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h]) +
-                        (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+        const float u = T::to_f(dt_e) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
         dtv = pr.softplus ? softplusf_(u) : u;
         sig = pr.softplus ? sigmoidf_(u) : 1.f;
       }
@@ -278,50 +332,41 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       s_dq[lane] = __expf(csl - cs);
     }
     // (2) x of head h (post-conv, transposed)
-    conv_rows<IO, P, N, true, false, false>(pr, b, h, g, t0, [&](int, int s, int cl, const float* o) {
+    xl.consume(pr, h, t0, [&](int, int s, int cl, const float* o) {
 #pragma unroll
       for (int v = 0; v < T::vec; ++v) sXT[(cl + v) * ldQ + s] = T::to_lds(o[v]);
     });
-    // dout, z at this lane's accumulator positions (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
+    // dy = dout silu(z) and dout silu'(z) in registers, dy (and its low part) in LDS
     float dyr[PJ][4], g2r[PJ][4];
-    {
-      const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-      const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
 #pragma unroll
-      for (int j = 0; j < PJ; ++j)
+    for (int j = 0; j < PJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t t = t0 + m0 + acc_row(e);
-          const int p = 16 * j + acc_col();
-          float dv = 0.f, zv = 0.f;
-          if (t < pr.L) {
-            dv = T::to_f(dp[t * a.dout.st + p]);
-            if (zp) zv = T::to_f(zp[t * pr.z.st + p]);
-          }
-          dyr[j][e] = zp ? dv * siluf_(zv) : dv;
-          g2r[j][e] = zp ? dv * dsiluf_(zv) : 0.f;
-          const Lt hi = T::to_lds(dyr[j][e]);
-          sDY[(m0 + acc_row(e)) * ldP + p] = hi;
-          if constexpr (SPLIT) sDYlo[(m0 + acc_row(e)) * ldP + p] = T::to_lds(dyr[j][e] - T::lds_to_f(hi));
-        }
-    }
-    // H_{c-1}, dH_c of head h; <dH, H> on the way
+      for (int e = 0; e < 4; ++e) {
+        const int p = 16 * j + acc_col();
+        const float dv = T::to_f(dv_e[j][e]), zv = T::to_f(zv_e[j][e]);
+        dyr[j][e] = pr.z.p ? dv * siluf_(zv) : dv;
+        g2r[j][e] = pr.z.p ? dv * dsiluf_(zv) : 0.f;
+        const Lt hi = T::to_lds(dyr[j][e]);
+        sDY[(m0 + acc_row(e)) * ldP + p] = hi;
+        if constexpr (SPLIT) sDYlo[(m0 + acc_row(e)) * ldP + p] = T::to_lds(dyr[j][e] - T::lds_to_f(hi));
+      }
+    // H_{c-1}, dH_c of head h into LDS; <dH, H> on the way
     {
-      const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
-      const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
       float dot = 0.f;
-      for (int i = threadIdx.x * 4; i < P * N; i += kThreads * 4) {
-        const float4 hv = *reinterpret_cast<const float4*>(Hg + i);
-        const float4 dv = *reinterpret_cast<const float4*>(dHg + i);
-        const int p = i / N, n = i % N;
-        const float hf[4] = {hv.x, hv.y, hv.z, hv.w};
-        const float df[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          sH[p * ldN + n + q] = T::to_lds(hf[q]);
-          sdH[p * ldN + n + q] = T::to_lds(df[q]);
+      for (int q = 0; q < NH4; ++q) {
+        const int i = (threadIdx.x + q * kThreads) * 4;
+        if (i < P * N) {
+          const int p = i / N, n = i % N;
+          const float hf[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
+          const float df[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            sH[p * ldN + n + k] = T::to_lds(hf[k]);
+            sdH[p * ldN + n + k] = T::to_lds(df[k]);
+            dot += hf[k] * df[k];
+          }
         }
-        dot += hv.x * dv.x + hv.y * dv.y + hv.z * dv.z + hv.w * dv.w;
       }
       dot = wave_sum(dot);
       if (lane == 0) s_red[0][wave] = dot;
@@ -530,40 +575,55 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   }
 }
 
-// dB / dC of each group = sum of its head-block partials -> the B / C channels of dxbc
-template <typename IO>
-__global__ void __launch_bounds__(256) dbc_finalize_kernel(Problem pr, const float* part, int nhb,
-                                                           MView dxbc) {
+// dB / dC of each group = the sum of its head-block partials, in block order.
+// Without conv the sums are the B / C channels of dxbc; with conv they are the
+// post-conv gradient the conv backward reads, stored in place in the group's
+// first slot.  One thread per 4 consecutive values.
+template <typename IO, bool TO_DXBC>
+__global__ void __launch_bounds__(256) dbc_reduce_kernel(Problem pr, float* part, int nhb,
+                                                          MView dxbc) {
   using E = typename io_traits<IO>::elem;
   const int N = pr.N, G = pr.G;
-  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-  const int64_t per_t = 2LL * G * N;
-  if (e >= pr.B * pr.L * per_t) return;
+  const int64_t q4 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t per_t = 2LL * G * N;  // B | C channels of one row
+  if (q4 * 4 >= pr.B * pr.L * per_t) return;
+  const int64_t e = q4 * 4;
   const int64_t ch = e % per_t, t = (e / per_t) % pr.L, b = e / (per_t * pr.L);
   const bool isC = ch >= static_cast<int64_t>(G) * N;
   const int g = static_cast<int>((isC ? ch - G * N : ch) / N);
   const int n = static_cast<int>((isC ? ch - G * N : ch) % N);
   const int per_g = nhb / G;
-  float acc = 0.f;
-  for (int q = 0; q < per_g; ++q) {
-    const int hb = g * per_g + q;
-    acc += part[((static_cast<int64_t>(hb) * pr.B + b) * pr.L + t) * (2 * N) + (isC ? N : 0) + n];
+  const int64_t slot = static_cast<int64_t>(pr.B) * pr.L * (2 * N);
+  float* p0 = part + (static_cast<int64_t>(g) * per_g) * slot + (b * pr.L + t) * (2 * N) +
+              (isC ? N : 0) + n;
+  float4 acc = *reinterpret_cast<const float4*>(p0);
+  for (int q = 1; q < per_g; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(p0 + q * slot);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
   }
-  const int64_t col = static_cast<int64_t>(pr.H) * pr.P + ch;
-  static_cast<E*>(dxbc.p)[b * dxbc.sb + t * dxbc.st + col] = io_traits<IO>::from_f(acc);
+  if constexpr (TO_DXBC) {
+    const float f[4] = {acc.x, acc.y, acc.z, acc.w};
+    E* dst = static_cast<E*>(dxbc.p) + b * dxbc.sb + t * dxbc.st + static_cast<int64_t>(pr.H) * pr.P + ch;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dst[v] = io_traits<IO>::from_f(f[v]);
+  } else {
+    *reinterpret_cast<float4*>(p0) = acc;
+  }
 }
 
-// dA, dD, ddt_bias: ordered sums of the per-(batch, chunk) partials
+// dA, dD, ddt_bias: ordered sums of the per-(batch, chunk) partials ([B*nch][H][3])
 __global__ void __launch_bounds__(256) head_params_kernel(const float* par, int64_t B, int64_t nch,
                                                           int H, float* dA, float* dD,
                                                           float* ddt_bias, int accumulate) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= 3 * H) return;
+  const float acc = block_colsum(par, B * nch, 3LL * H);
+  const int i = blockIdx.x * kWave + threadIdx.x;
+  if (threadIdx.x >= kWave || i >= 3 * H) return;
   const int h = i / 3, k = i % 3;
   float* dst = k == 0 ? dA : (k == 1 ? dD : ddt_bias);
   if (!dst) return;
-  float acc = 0.f;
-  for (int64_t bc = 0; bc < B * nch; ++bc) acc += par[(bc * H + h) * 3 + k];
   dst[h] = accumulate ? dst[h] + acc : acc;
 }
 
@@ -651,20 +711,26 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 5. dB / dC (and the conv backward)
+  // 5. dB / dC: head-block sums (and the conv backward)
+  {
+    const int64_t n4 = pr.B * pr.L * 2LL * pr.G * pr.N / 4;
+    const dim3 grid(static_cast<unsigned>((n4 + 255) / 256));
+    TimingScope ts(kKDbcReduce, s);
+    if (pr.K > 0)
+      hipLaunchKernelGGL((dbc_reduce_kernel<IO, false>), grid, dim3(256), 0, s, pr, a.dbc_part,
+                         l.nhb, o.dxbc);
+    else
+      hipLaunchKernelGGL((dbc_reduce_kernel<IO, true>), grid, dim3(256), 0, s, pr, a.dbc_part,
+                         l.nhb, o.dxbc);
+  }
   if (pr.K > 0) {
-    e = launch_conv_bwd_fused(pr, ws + l.dx, a.dbc_part, l.nhb, in.dcs_out, o.dxbc, o.dconv_w,
-                              o.dconv_b, o.dcs_in, o.accumulate, ws + l.conv, s);
+    e = launch_conv_bwd_fused(pr, ws + l.dx, a.dbc_part, l.nhb / pr.G, in.dcs_out, o.dxbc,
+                              o.dconv_w, o.dconv_b, o.dcs_in, o.accumulate, ws + l.conv, s);
     if (e != hipSuccess) return e;
-  } else {
-    const int64_t n = pr.B * pr.L * 2LL * pr.G * pr.N;
-    TimingScope ts(kKDbcFinalize, s);
-    hipLaunchKernelGGL(dbc_finalize_kernel<IO>, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, s, pr, a.dbc_part, l.nhb, o.dxbc);
   }
   // 6. parameter reductions
   TimingScope ts(kKParams, s);
-  hipLaunchKernelGGL(head_params_kernel, dim3(static_cast<unsigned>((3 * pr.H + 255) / 256)),
+  hipLaunchKernelGGL(head_params_kernel, dim3(static_cast<unsigned>((3 * pr.H + kWave - 1) / kWave)),
                      dim3(256), 0, s, a.par_part, pr.B, l.nch, pr.H, o.dA, o.dD, o.ddt_bias,
                      o.accumulate);
   return hipGetLastError();

@@ -235,6 +235,31 @@ __device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda,
   }
 }
 
+// Ordered column sums of a row-major [rows][cols] fp32 matrix, 64 columns per
+// 256-thread block (column blockIdx.x * 64 + lane).  Wave w adds rows w, w + 4,
+// w + 8, ... with 16 loads in flight; the four wave partials are then added in
+// wave order, so the result is the same on every run.  Valid on wave 0.
+__device__ __forceinline__ float block_colsum(const float* m, int64_t rows, int64_t cols) {
+  __shared__ float s_part[4][kWave];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t col = blockIdx.x * static_cast<int64_t>(kWave) + lane;
+  float acc = 0.f;
+  if (col < cols) {
+    int64_t q = wave;
+    for (; q + 4 * 15 < rows; q += 4 * 16) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = m[(q + 4 * i) * cols + col];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc += v[i];
+    }
+    for (; q < rows; q += 4) acc += m[q * cols + col];
+  }
+  s_part[wave][lane] = acc;
+  __syncthreads();
+  return s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
+}
+
 // Row / column of accumulator element e (0..3) of this lane inside a 16x16 tile.
 __device__ __forceinline__ int acc_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }

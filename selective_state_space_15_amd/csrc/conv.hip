@@ -12,8 +12,8 @@
 // registers and the 16 output rows are stored as 16-byte vectors.  Adjacent threads
 // take adjacent channel vectors, so every row access is coalesced.
 //
-// Backward: one thread per (batch, 64-row tile, channel vector) walks its rows with
-// a sliding register window; dpre = dout * silu'(pre) is recomputed from the raw
+// Backward: one thread per (batch, 32-row tile, 4 channels) walks its rows with a
+// sliding register window; dpre = dout * silu'(pre) is recomputed from the raw
 // rows, dx[tau] = sum_k dpre[tau + K-1-k] w[k] (plus the gradient of the returned
 // conv state for the last K-1 rows), and per-tile partial sums of dw and db go to
 // scratch for an ordered reduction (deterministic, no atomics).
@@ -25,7 +25,7 @@ namespace ssd {
 namespace {
 
 constexpr int kRowsF = 16;  // rows per thread, forward
-constexpr int kRowsB = 64;  // rows per thread, backward
+constexpr int kRowsB = 32;  // rows per thread, backward
 
 struct ConvFwdArgs {
   int64_t B, L;
@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
 }
 
 // ------------------------------------------------------------------ backward
-constexpr int kBatch = 4;  // output rows per register batch in the backward walk
+constexpr int kBatch = 4;  // output rows per step of the backward register window
 
 struct ConvBwdArgs {
   int64_t B, L;
@@ -123,8 +123,8 @@ struct ConvBwdArgs {
   // gradient of the conv output: a view (standalone) or the fused SSD sources
   const void* g;
   int64_t g_sb, g_st;
-  const float* dbc_part;  // [nhb][B][L][2N] fp32 (fused)
-  int nhb, hp, G, N;
+  const float* dbc;  // fused: dB | dC of group g at [(g * per_g * B + b) * L + t][2N] (fp32)
+  int per_g, hp, G, N;
   const void* dso;  // gradient of the returned state rows (null = zero)
   int64_t dso_sb, dso_st;
   void* dx;
@@ -134,72 +134,63 @@ struct ConvBwdArgs {
   float* part;  // [B][ntile][C][5]: dw taps 0..K-1, db at 4
 };
 
-template <typename IO, bool FUSED>
-__device__ __forceinline__ void conv_grad_row(const ConvBwdArgs& a, int64_t b, int64_t t, int c,
-                                              float (&gv)[io_traits<IO>::vec]) {
-  using T = io_traits<IO>;
-  using E = typename T::elem;
-  constexpr int V = T::vec;
-  if (t < 0 || t >= a.L) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) gv[v] = 0.f;
-    return;
+// Four channels of I/O elements: 8 bytes of bf16 or 16 bytes of fp32, held in a uint4.
+template <typename IO>
+struct quad;
+template <>
+struct quad<bf16_t> {
+  __device__ static __forceinline__ uint4 load(const uint16_t* p) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(r.x, r.y, 0u, 0u);
   }
-  if (!FUSED || c < a.hp) {
-    const int64_t sb = FUSED ? static_cast<int64_t>(a.L) * a.hp : a.g_sb;
-    const int64_t st = FUSED ? a.hp : a.g_st;
-    vec16<IO> r;
-    load_vec16<IO>(r, static_cast<const E*>(a.g) + b * sb + t * st + c);
-#pragma unroll
-    for (int v = 0; v < V; ++v) gv[v] = r.v[v];
-    return;
+  __device__ static __forceinline__ float get(const uint4& r, int v) {
+    const uint32_t w = v < 2 ? r.x : r.y;
+    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
   }
-  const int gn = a.G * a.N;
-  const int rel = c - a.hp;
-  const bool isC = rel >= gn;
-  const int g = (isC ? rel - gn : rel) / a.N;
-  const int n0 = (isC ? rel - gn : rel) % a.N;
-  const int per_g = a.nhb / a.G;
-#pragma unroll
-  for (int v = 0; v < V; ++v) gv[v] = 0.f;
-  for (int q = 0; q < per_g; ++q) {
-    const float* p = a.dbc_part +
-                     ((static_cast<int64_t>(g * per_g + q) * a.B + b) * a.L + t) * (2 * a.N) +
-                     (isC ? a.N : 0) + n0;
-#pragma unroll
-    for (int v4 = 0; v4 < V; v4 += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(p + v4);
-      gv[v4] += f.x;
-      gv[v4 + 1] += f.y;
-      gv[v4 + 2] += f.z;
-      gv[v4 + 3] += f.w;
-    }
+  __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(f2bf2(f[0], f[1]), f2bf2(f[2], f[3]));
   }
+};
+template <>
+struct quad<float> {
+  __device__ static __forceinline__ uint4 load(const float* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ static __forceinline__ float get(const uint4& r, int v) {
+    return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
+  }
+  __device__ static __forceinline__ void store(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+__device__ __forceinline__ float word_f(const uint4& r, int v) {
+  return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
 }
 
-// One thread per (batch, 64-row tile, channel vector); rows are processed in
-// batches of kBatch outputs, each batch loading its raw rows and gradient rows
-// up front (independent loads in flight).
+// One thread per (batch, kRowsB-row tile, 4 channels).  The thread walks its rows
+// kBatch at a time with a register window: raw[i] holds raw row tau0 - 3 + i and
+// dp[i] holds dpre of row tau0 + i, so each step loads only kBatch new raw rows
+// and kBatch new gradient rows, and those of the next step are in flight while
+// this one computes.  Every load is unconditional (rows outside the sequence read
+// row 0 and are masked to zero), so the loads of a step issue back to back.
 template <typename IO, bool FUSED>
 __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   using T = io_traits<IO>;
   using E = typename T::elem;
-  constexpr int V = T::vec;
-  const int ncv = a.C / V;
+  using Qd = quad<IO>;
+  const int ncq = a.C / 4;
   const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
   const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-  if (gid >= a.B * ntile * ncv) return;
-  const int cv = static_cast<int>(gid % ncv);
-  const int64_t tile = (gid / ncv) % ntile;
-  const int64_t b = gid / (static_cast<int64_t>(ncv) * ntile);
-  const int c = cv * V;
+  if (gid >= a.B * ntile * ncq) return;
+  const int c = static_cast<int>(gid % ncq) * 4;
+  const int64_t tile = (gid / ncq) % ntile;
+  const int64_t b = gid / (static_cast<int64_t>(ncq) * ntile);
   const int K = a.K;
-  const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + c;
-  const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + c : nullptr;
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 
-  float w4[4][V], bias[V];
+  float w4[4][4], bias[4];
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
+  for (int v = 0; v < 4; ++v) {
     bias[v] = a.bias ? a.bias[c + v] : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -207,15 +198,67 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
       w4[j][v] = kk >= 0 ? a.w[(c + v) * K + kk] : 0.f;
     }
   }
+  const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + c;
+  const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + c : nullptr;
   auto raw_row = [&](int64_t t) -> uint4 {
-    if (t >= a.L || t < -(K - 1)) return make_uint4(0u, 0u, 0u, 0u);
-    if (t >= 0) return *reinterpret_cast<const uint4*>(xb + t * a.x_st);
-    if (sb) return *reinterpret_cast<const uint4*>(sb + (t + K - 1) * a.st_st);
-    return make_uint4(0u, 0u, 0u, 0u);
+    const E* p = xb;
+    bool ok = false;
+    if (t >= 0 && t < a.L) {
+      p = xb + t * a.x_st;
+      ok = true;
+    } else if (sb && t < 0 && t >= -(K - 1)) {
+      p = sb + (t + K - 1) * a.st_st;
+      ok = true;
+    }
+    const uint4 v = Qd::load(p);
+    return ok ? v : zero4;
   };
-  float dw[4][V], db[V];
+  // gradient rows: I/O-typed view, or (fused, B / C channels) the fp32 group sums
+  const bool from_f32 = FUSED && c >= a.hp;
+  const E* gb = nullptr;
+  int64_t g_st = 0;
+  const float* fb = nullptr;
+  const int64_t f_st = 2LL * a.N;
+  if (FUSED) {
+    if (from_f32) {
+      const int gn = a.G * a.N, rel = c - a.hp;
+      const bool isC = rel >= gn;
+      const int g = (isC ? rel - gn : rel) / a.N, n0 = (isC ? rel - gn : rel) % a.N;
+      fb = a.dbc + ((static_cast<int64_t>(g) * a.per_g * a.B + b) * a.L) * f_st + (isC ? a.N : 0) + n0;
+    } else {
+      gb = static_cast<const E*>(a.g) + b * a.L * a.hp + c;
+      g_st = a.hp;
+    }
+  } else {
+    gb = static_cast<const E*>(a.g) + b * a.g_sb + c;
+    g_st = a.g_st;
+  }
+  auto grad_row = [&](int64_t t) -> uint4 {
+    const bool ok = t >= 0 && t < a.L;
+    const int64_t tt = ok ? t : 0;
+    const uint4 v = from_f32 ? *reinterpret_cast<const uint4*>(fb + tt * f_st) : Qd::load(gb + tt * g_st);
+    return ok ? v : zero4;
+  };
+  // dpre of row t from its four raw rows r[0..3] (rows t-3 .. t) and gradient gr
+  auto dpre_row = [&](int64_t t, const uint4* r, const uint4& gr, float* d) {
+    const bool ok = t >= 0 && t < a.L;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
+    for (int v = 0; v < 4; ++v) {
+      const float gv = from_f32 ? word_f(gr, v) : Qd::get(gr, v);
+      float dv = gv;
+      if (a.silu) {
+        float pre = bias[v];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], Qd::get(r[j], v), pre);
+        dv = gv * dsiluf_(pre);
+      }
+      d[v] = ok ? dv : 0.f;
+    }
+  };
+
+  float dw[4][4], db[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
     db[v] = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
@@ -227,69 +270,81 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   // tile 0 also produces the gradient of the carried-in state rows (tau < 0)
   const int64_t tau_begin = tile == 0 ? -(K - 1) : t_lo;
   const int64_t tau_end = t_lo + kRowsB < a.L ? t_lo + kRowsB : a.L;
-  for (int64_t tau0 = tau_begin; tau0 < tau_end; tau0 += kBatch) {
-    // dpre rows tau0 .. tau0 + kBatch + 2 need raw rows tau0 - 3 .. tau0 + kBatch + 2
-    uint4 raw[kBatch + 6];
+
+  uint4 raw[kBatch + 6];
+  float dp[kBatch + 3][4];
+  int64_t tau0 = tau_begin;
+  {
+    uint4 g0[3];
 #pragma unroll
-    for (int i = 0; i < kBatch + 6; ++i) raw[i] = raw_row(tau0 - 3 + i);
-    float gr[kBatch + 3][V];
+    for (int i = 0; i < 6; ++i) raw[i] = raw_row(tau0 - 3 + i);
 #pragma unroll
-    for (int i = 0; i < kBatch + 3; ++i) conv_grad_row<IO, FUSED>(a, b, tau0 + i, c, gr[i]);
-    float dpre[kBatch + 3][V];
+    for (int i = 0; i < 3; ++i) g0[i] = grad_row(tau0 + i);
 #pragma unroll
-    for (int i = 0; i < kBatch + 3; ++i) {
-      const int64_t t = tau0 + i;
+    for (int i = 0; i < 3; ++i) dpre_row(tau0 + i, raw + i, g0[i], dp[i]);
+  }
+  uint4 nraw[kBatch], ngr[kBatch];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        float d = 0.f;
-        if (t >= 0 && t < a.L) {
-          if (a.silu) {
-            float pre = bias[v];
+  for (int i = 0; i < kBatch; ++i) {
+    nraw[i] = raw_row(tau0 + 3 + i);
+    ngr[i] = grad_row(tau0 + 3 + i);
+  }
+  for (; tau0 < tau_end; tau0 += kBatch) {
+    uint4 cgr[kBatch];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[i + j], v), pre);
-            d = gr[i][v] * dsiluf_(pre);
-          } else {
-            d = gr[i][v];
-          }
-        }
-        dpre[i][v] = d;
-      }
+    for (int i = 0; i < kBatch; ++i) {
+      raw[6 + i] = nraw[i];
+      cgr[i] = ngr[i];
     }
+    // next step's rows (harmless past the tile: masked or simply unused)
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      nraw[i] = raw_row(tau0 + kBatch + 3 + i);
+      ngr[i] = grad_row(tau0 + kBatch + 3 + i);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) dpre_row(tau0 + 3 + i, raw + 3 + i, cgr[i], dp[3 + i]);
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int64_t tau = tau0 + r;
-      if (tau >= tau_end) break;
-      float o[V];
+      if (tau < tau_end) {
+        float o[4];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        float acc = 0.f;
+        for (int v = 0; v < 4; ++v) {
+          float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = fmaf(w4[j][v], dpre[r + 3 - j][v], acc);
-        o[v] = acc;
-      }
-      const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
-      if (dsob && js >= 0) {
-        vec16<IO> d;
-        load_vec16<IO>(d, dsob + js * a.dso_st);
-#pragma unroll
-        for (int v = 0; v < V; ++v) o[v] += d.v[v];
-      }
-      if (tau >= 0) {
-        store_vec16<IO>(dxb + tau * a.dx_st, o);
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          db[v] += dpre[r][v];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dpre[r][v], raw_elem<IO>(raw[r + j], v), dw[j][v]);
+          for (int j = 0; j < 4; ++j) acc = fmaf(w4[j][v], dp[r + 3 - j][v], acc);
+          o[v] = acc;
         }
-      } else if (dsib) {
-        store_vec16<IO>(dsib + (tau + K - 1) * a.dsi_st, o);
+        const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
+        if (dsob && js >= 0) {
+          const uint4 d = Qd::load(dsob + js * a.dso_st);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] += Qd::get(d, v);
+        }
+        if (tau >= 0) {
+          Qd::store(dxb + tau * a.dx_st, o);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            db[v] += dp[r][v];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dp[r][v], Qd::get(raw[r + j], v), dw[j][v]);
+          }
+        } else if (dsib) {
+          Qd::store(dsib + (tau + K - 1) * a.dsi_st, o);
+        }
       }
     }
+#pragma unroll
+    for (int i = 0; i < 6; ++i) raw[i] = raw[i + kBatch];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dp[i][v] = dp[i + kBatch][v];
   }
   float* pp = a.part + ((b * ntile + tile) * a.C + c) * 5;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
+  for (int v = 0; v < 4; ++v) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kk = j - (4 - K);
@@ -299,26 +354,24 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   }
 }
 
-// dw[c][k], db[c]: ordered sums of the per-(batch, tile) partials
+// dw[c][k], db[c]: ordered sums of the per-(batch, tile) partials ([n_bt][C][5])
 __global__ void __launch_bounds__(256) conv_params_kernel(const float* part, int64_t n_bt, int C,
                                                           int K, float* dw, float* db,
                                                           int accumulate) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= C * 5) return;
+  const float acc = block_colsum(part, n_bt, static_cast<int64_t>(C) * 5);
+  const int i = blockIdx.x * kWave + threadIdx.x;
+  if (threadIdx.x >= kWave || i >= C * 5) return;
   const int c = i / 5, k = i % 5;
   if (k < 4 && k >= K) return;
   float* dst = k == 4 ? (db ? db + c : nullptr) : (dw ? dw + c * K + k : nullptr);
   if (!dst) return;
-  float acc = 0.f;
-  for (int64_t q = 0; q < n_bt; ++q) acc += part[(q * C + c) * 5 + k];
   *dst = accumulate ? *dst + acc : acc;
 }
 
 hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* db, int accumulate,
                         hipStream_t s) {
-  const int V = bf16 ? 8 : 4;
   const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int64_t n = a.B * ntile * (a.C / V);
+  const int64_t n = a.B * ntile * (a.C / 4);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   TimingScope ts(kKConvBwd, s);
   if (bf16) {
@@ -332,7 +385,7 @@ hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* d
     else
       hipLaunchKernelGGL((conv_bwd_kernel<float, false>), grid, dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL(conv_params_kernel, dim3(static_cast<unsigned>((a.C * 5 + 255) / 256)),
+  hipLaunchKernelGGL(conv_params_kernel, dim3(static_cast<unsigned>((a.C * 5 + kWave - 1) / kWave)),
                      dim3(256), 0, s, a.part, a.B * ntile, a.C, a.K, dw, db, accumulate);
   return hipGetLastError();
 }
@@ -382,9 +435,10 @@ hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MV
 
 // Conv backward of the SSD entry point: the post-conv gradient of the x channels
 // comes from `dx_ws` ([B][L][H*P], I/O dtype), that of the B and C channels from
-// the per-head-block fp32 partials.
-hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_part,
-                                 int nhb, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
+// the fp32 sums over each group's head blocks, held in the partial slot of the
+// group's first block (slot g * per_g of a [slots][B][L][2N] array).
+hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_sum,
+                                 int per_g, View dcs_out, MView dxbc, float* dconv_w, float* dconv_b,
                                  MView dcs_in, int accumulate, void* ws, hipStream_t s) {
   ConvBwdArgs a{};
   a.B = pr.B;
@@ -401,8 +455,8 @@ hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const flo
   a.w = pr.conv_w;
   a.bias = pr.conv_b;
   a.g = dx_ws;
-  a.dbc_part = dbc_part;
-  a.nhb = nhb;
+  a.dbc = dbc_sum;
+  a.per_g = per_g;
   a.hp = pr.H * pr.P;
   a.G = pr.G;
   a.N = pr.N;

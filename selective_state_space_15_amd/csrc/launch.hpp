@@ -14,7 +14,7 @@ constexpr int kThreads = 256;  // threads per workgroup of the chunk kernels
 // Kernel kinds of the timing instrumentation (ssd_timing_* in ssd.h).
 enum KernelKind {
   kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
-  kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcFinalize, kKParams, kKernelKinds
+  kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKernelKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events on stream `s`
