@@ -188,9 +188,22 @@ struct frag<uint16_t, kc> {
       const uint4 raw = *reinterpret_cast<const uint4*>(base + row * ld + k);
       return __builtin_bit_cast(bf16x8, raw);
     } else {
-      u16x8 u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = base[(k + e) * ld + row];
+      // Two gfx950 LDS transpose reads (ds_read_b64_tr_b16).  Inside each group of 16
+      // lanes, lane i receives element i % 4 of the 8-byte chunks that lanes i / 4,
+      // i / 4 + 4, i / 4 + 8 and i / 4 + 12 address.  So lane s of the group points at
+      // row k + s / 4, columns row0 + 4 (s % 4) .. + 3 (row0 = row - s, the tile's
+      // first column) and gets back column `row` at k .. k + 3; the second read adds 4
+      // to k.  Needs ld and row0 to be multiples of 4 elements (8-byte chunks).
+      const int s = threadIdx.x & 15;
+      const uint16_t* p = base + (k + (s >> 2)) * ld + (row - s) + 4 * (s & 3);
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 4 * ld));
+      const u16x8 u = {static_cast<uint16_t>(lo[0]), static_cast<uint16_t>(lo[1]),
+                       static_cast<uint16_t>(lo[2]), static_cast<uint16_t>(lo[3]),
+                       static_cast<uint16_t>(hi[0]), static_cast<uint16_t>(hi[1]),
+                       static_cast<uint16_t>(hi[2]), static_cast<uint16_t>(hi[3])};
       return __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -224,12 +237,15 @@ __device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda,
   // than two waves per SIMD have
 #pragma unroll 1
   for (int k0 = 0; k0 < K; k0 += kstep) {
-    const int k = k0 + kpl * kg;
-    const bool kin = k < K;
-    const auto a = kin ? frag<L, akc>::get(A, lda, m0 + r, k) : frag<L, akc>::zero();
+    const int kr = k0 + kpl * kg;
+    const bool kin = kr < K;
+    const int k = kin ? kr : 0;  // every lane reads (transpose reads are cooperative)
+    const auto av = frag<L, akc>::get(A, lda, m0 + r, k);
+    const auto a = kin ? av : frag<L, akc>::zero();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const auto b = kin ? frag<L, bkc>::get(B, ldb, n0 + 16 * j + r, k) : frag<L, bkc>::zero();
+      const auto bv = frag<L, bkc>::get(B, ldb, n0 + 16 * j + r, k);
+      const auto b = kin ? bv : frag<L, bkc>::zero();
       acc[j] = mfma_step(a, b, acc[j]);
     }
   }
