@@ -35,7 +35,31 @@ def parse():
     ap.add_argument("--seg", type=int, default=16384)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=49152, help="oracle prefix tokens (0 = skip)")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for counter runs: one 256 MiB device copy (byte-counter calibration), "
+                         "then two fwd+bwd passes over a single segment; prints no JSON")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+# HBM bytes of the dominant kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of
+# `bench.py --pmc-probe` (see the report for the commands and the copy calibration)
+TRAFFIC_REPORT = os.path.join(ROOT, "profiles", "bwd_main_seg16k_hbm_bytes.md")
+KERNEL_SYMBOL = {"bwd_main": "bwd_main_kernel", "walk_out": "walk_kernel", "walk_state": "walk_kernel",
+                 "conv_bwd": "conv_bwd_kernel"}
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch of kernel `kind` from the committed counter report, or None
+    when there is none for it or its sources changed since the counters were taken."""
+    from selective_state_space_15_amd import profiling
+    rec = profiling.read_bytes_report(TRAFFIC_REPORT)
+    sym = KERNEL_SYMBOL.get(kind)
+    if not rec or rec.get("kernel") != sym:
+        return None
+    if rec.get("source_fingerprint") != profiling.source_fingerprint(sym):
+        return None
+    return rec["hbm_bytes_per_launch"]
 
 
 def main():
@@ -51,6 +75,8 @@ def main():
     from selective_state_space_15_amd import binding as bd
     from selective_state_space_15_amd import segmented, synth
 
+    if args.pmc_probe:
+        args.L = args.seg
     d = synth.CONFIGS["c2"].with_(L=args.L, seg=args.seg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -92,6 +118,16 @@ def main():
 
     def step():
         bwd(fwd())
+
+    if args.pmc_probe:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        print("pmc probe done", flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -144,6 +180,7 @@ def main():
     else:
         per_tok, tok_per_launch = bwd_bytes, B * args.seg
     achieved = per_tok * tok_per_launch / (dom_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
 
     res = {
         "metric": "SSD mixer fwd+bwd tokens/sec at d=1024, L=1M (segmented 64 x 16384)",
@@ -164,7 +201,7 @@ def main():
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "ms_fwd": ms_fwd,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
                      "kernel_avg_ms": dom_avg_ms, "kernel_launches_per_step": dom_n / args.steps,
                      "alg_bytes_per_launch": per_tok * tok_per_launch},
         "path_roofline": {"alg_bytes_per_token": step_bytes, "roofline_tokens_per_s": roof_tok_s,
