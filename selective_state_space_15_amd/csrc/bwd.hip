@@ -67,13 +67,13 @@ __global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
   using E = typename T::elem;
   using Lt = typename T::lds;
   constexpr int PADK = 16 / sizeof(Lt);
-  constexpr int ldN = N + PADK, ldQ = kQ + PADK;
+  constexpr int ldN = N + PADK, ldP = P + PADK;
   __shared__ __align__(16) Lt sC[kQ * ldN];
-  __shared__ __align__(16) Lt sDyT[P * ldQ];
+  __shared__ __align__(16) Lt sDy[kQ * ldP];  // dy exp(cs_t), rows t (read transposed)
   // bf16 I/O: low parts of C and dy (the state gradient feeds the log-decay gradient)
   constexpr bool SPLIT = sizeof(Lt) == 2;
   __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
-  __shared__ __align__(16) Lt sDyTlo[SPLIT ? P * ldQ : 8];
+  __shared__ __align__(16) Lt sDylo[SPLIT ? kQ * ldP : 8];
   __shared__ float s_ecs[kQ];
 
   const Problem& pr = a.pr;
@@ -132,20 +132,21 @@ __global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
       lds_put_row<IO>(sClo + s * ldN + cl, o);
     });
   __syncthreads();
-  // dy * exp(cs_t), transposed into sDyT[p][t]
+  // dy * exp(cs_t) (and its low part) as row-major 16-byte stores
 #pragma unroll
   for (int q = 0; q < NDT; ++q) {
     const int task = threadIdx.x + q * kThreads;
     const int col = (task % (P / V)) * V, r = task / (P / V);
     const float ecs = s_ecs[r];
+    float dy[V], lo[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const float dv = raw_elem<IO>(dvr[q], v);
-      const float dy = (pr.z.p ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * ecs;
-      const Lt hi = T::to_lds(dy);
-      sDyT[(col + v) * ldQ + r] = hi;
-      if constexpr (SPLIT) sDyTlo[(col + v) * ldQ + r] = T::to_lds(dy - T::lds_to_f(hi));
+      dy[v] = (pr.z.p ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * ecs;
+      lo[v] = dy[v] - T::to_f(T::from_f(dy[v]));
     }
+    lds_put_row<IO>(sDy + r * ldP + col, dy);
+    if constexpr (SPLIT) lds_put_row<IO>(sDylo + r * ldP + col, lo);
   }
   __syncthreads();
   constexpr int PT = P / 16, NT = N / 16, WPP = 4 / PT, NJS = (NT + WPP - 1) / WPP;
@@ -154,10 +155,10 @@ __global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
     f32x4 acc[NJS];
 #pragma unroll
     for (int j = 0; j < NJS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_strip<Lt, true, false, NJS>(acc, sDyT, ldQ, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
+    mma_strip<Lt, false, false, NJS>(acc, sDy, ldP, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
     if constexpr (SPLIT) {
-      mma_strip<Lt, true, false, NJS>(acc, sDyTlo, ldQ, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
-      if (clo) mma_strip<Lt, true, false, NJS>(acc, sDyT, ldQ, s_pi * 16, sClo, ldN, s_nj0 * 16, kQ);
+      mma_strip<Lt, false, false, NJS>(acc, sDylo, ldP, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
+      if (clo) mma_strip<Lt, false, false, NJS>(acc, sDy, ldP, s_pi * 16, sClo, ldN, s_nj0 * 16, kQ);
     }
     const int64_t PN = static_cast<int64_t>(P) * N;
     float* dst = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
@@ -215,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   constexpr int NTn = N / 16, PJ = P / 16;
   __shared__ __align__(16) Lt sC[kQ * ldN];   // C rows [t][n]
   __shared__ __align__(16) Lt sB[kQ * ldN];   // B rows [s][n]
-  __shared__ __align__(16) Lt sXT[P * ldQ];   // x^T [p][s]
+  __shared__ __align__(16) Lt sX[kQ * ldP];   // x [s][p]
   __shared__ __align__(16) Lt sM[kQ * ldQ];   // Mt [t][s]
   __shared__ __align__(16) Lt sW[kQ * ldQ];   // W  [t][s]
   __shared__ __align__(16) Lt sDY[kQ * ldP];  // dy [t][p]
@@ -331,10 +332,9 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       s_sig[lane] = sig;
       s_dq[lane] = __expf(csl - cs);
     }
-    // (2) x of head h (post-conv, transposed)
+    // (2) x of head h (post-conv, row-major)
     xl.consume(pr, h, t0, [&](int, int s, int cl, const float* o) {
-#pragma unroll
-      for (int v = 0; v < T::vec; ++v) sXT[(cl + v) * ldQ + s] = T::to_lds(o[v]);
+      lds_put_row<IO>(sX + s * ldP + cl, o);
     });
     // dy = dout silu(z) and dout silu'(z) in registers, dy (and its low part) in LDS
     float dyr[PJ][4], g2r[PJ][4];
@@ -399,7 +399,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    mma_strip<Lt, true, true, PJ>(yacc, sM, ldQ, m0, sXT, ldQ, 0, kQ);
+    mma_strip<Lt, true, false, PJ>(yacc, sM, ldQ, m0, sX, ldP, 0, kQ);
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + h * P : nullptr;
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < PJ; ++j) {
           const int p = 16 * j + acc_col();
-          const float xv = T::lds_to_f(sXT[p * ldQ + t]);
+          const float xv = T::lds_to_f(sX[t * ldP + p]);
           const float y = yacc[j][e] + Dh * xv;
           dD_part += dyr[j][e] * xv;
           if (dzp && tg < pr.L) dzp[tg * a.dz.st + p] = T::from_f(g2r[j][e] * y);
@@ -432,8 +432,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       f32x4 dyx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, false, 4>(dyx, sDY, ldP, m0, sXT, ldQ, 0, P);
-      if constexpr (SPLIT) mma_strip<Lt, true, false, 4>(dyx, sDYlo, ldP, m0, sXT, ldQ, 0, P);
+      mma_strip<Lt, true, true, 4>(dyx, sDY, ldP, m0, sX, ldP, 0, P);
+      if constexpr (SPLIT) mma_strip<Lt, true, true, 4>(dyx, sDYlo, ldP, m0, sX, ldP, 0, P);
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -493,7 +493,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       f32x4 U[NTn];
 #pragma unroll
       for (int j = 0; j < NTn; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, false, false, NTn>(U, sXT, ldQ, m0, sdH, ldN, 0, P);
+      mma_strip<Lt, true, false, NTn>(U, sX, ldP, m0, sdH, ldN, 0, P);
       float vp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

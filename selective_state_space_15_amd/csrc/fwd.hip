@@ -74,11 +74,13 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   constexpr bool OUT = MODE == kModeOut;
   constexpr int V = T::vec;
   constexpr int PADK = 16 / sizeof(Lt);
-  constexpr int ldN = N + PADK, ldQ = kQ + PADK;
+  constexpr int ldN = N + PADK, ldQ = kQ + PADK, ldP = P + PADK;
+  // x and w o x are kept row-major ([s][p], 16-byte row stores); the products that
+  // need them transposed read them with LDS transpose loads
   __shared__ __align__(16) Lt sB[kQ * ldN];
-  __shared__ __align__(16) Lt sXwT[P * ldQ];
+  __shared__ __align__(16) Lt sXw[kQ * ldP];
   __shared__ __align__(16) Lt sC[OUT ? kQ * ldN : 8];
-  __shared__ __align__(16) Lt sXT[OUT ? P * ldQ : 8];
+  __shared__ __align__(16) Lt sX[OUT ? kQ * ldP : 8];
   __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
   __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
   __shared__ float s_dt[kQ], s_cs[kQ], s_w[kQ];
@@ -213,17 +215,17 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     const float cs_last = s_cs[kQ - 1];
     lsum += cs_last;
     // (2) conv + stores into LDS
-    //   sXT[p][s] = x (OUT only), sXwT[p][s] = x * w_s, sB[s][n], sC[s][n] (OUT only)
+    //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
     prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
     ld.issue(pr, b, h, g, t0);
     ld.consume(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
       if (seg == 0) {
         const float ws = s_w[s];
+        float ow[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          if constexpr (OUT) sXT[(cl + v) * ldQ + s] = T::to_lds(o[v]);
-          sXwT[(cl + v) * ldQ + s] = T::to_lds(o[v] * ws);
-        }
+        for (int v = 0; v < V; ++v) ow[v] = o[v] * ws;
+        if constexpr (OUT) lds_put_row<IO>(sX + s * ldP + cl, o);
+        lds_put_row<IO>(sXw + s * ldP + cl, ow);
       } else {
         lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
       }
@@ -262,7 +264,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
       }
       __syncthreads();
-      mma_strip<Lt, true, true, YJ>(yacc, sM, ldQ, m0, sXT, ldQ, 16 * YJ * half, kQ);
+      mma_strip<Lt, true, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
       // y = Ydiag + exp(cs_t) Yoff + D x;  out = y * silu(z)
       const float Dh = pr.D ? pr.D[h] : 0.f;
       E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
@@ -273,7 +275,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
 #pragma unroll
         for (int j = 0; j < YJ; ++j) {
           const int p = 16 * (YJ * half + j) + acc_col();
-          float y = yacc[j][e] + Dh * T::lds_to_f(sXT[p * ldQ + t]);
+          float y = yacc[j][e] + Dh * T::lds_to_f(sX[t * ldP + p]);
           if (gate) y *= siluf_(zval(j, e));
           if (tg < pr.L) op[tg * a.out.st + p] = T::from_f(y);
         }
@@ -284,7 +286,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       const float decay = __expf(cs_last);
 #pragma unroll
       for (int j = 0; j < NJS; ++j) accH[j] *= decay;
-      mma_strip<Lt, true, false, NJS>(accH, sXwT, ldQ, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+      mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
     }
     __syncthreads();
     if constexpr (OUT) {
