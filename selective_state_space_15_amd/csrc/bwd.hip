@@ -227,6 +227,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   constexpr bool SPLIT = sizeof(Lt) == 2;
   __shared__ __align__(16) Lt sDYlo[SPLIT ? kQ * ldP : 8];
   __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
+  constexpr int ldG = P + 4;
+  __shared__ __align__(16) float sG2[kQ * ldG];  // dout silu'(z) [t][p] (fp32)
   __shared__ float s_dt[kQ], s_cs[kQ], s_sig[kQ], s_dq[kQ];
   __shared__ float s_row[kQ], s_yo[kQ], s_v[kQ], s_col[4][kQ];
   __shared__ float s_red[2][4];
@@ -243,6 +245,56 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   const int m0 = wave * 16;
   const int64_t t0 = c * kQ;
   const int64_t PN = static_cast<int64_t>(P) * N;
+
+  // Every global input of a head (dt, post-conv x rows, dout, z, H_{c-1}, dH_c) is
+  // loaded into registers by prefetch(), issued for head h+1 while head h runs its
+  // last MFMA phase, and moved into LDS by stage() at the start of head h+1, so the
+  // memory latency of a head hides behind the previous head's compute.
+  constexpr int V = T::vec;
+  constexpr int NXV = P * kQ / (V * kThreads);  // 16-byte row vectors per thread
+  static_assert(P * kQ % (V * kThreads) == 0, "the x / dout tiles must tile the block");
+  constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
+  E pf_dt{};
+  uint4 pf_x[NXV], pf_do[NXV], pf_z[NXV];
+  float4 hv[NH4], gv[NH4];
+  // without conv, x is the raw xbc channels (fields selected one by one: a selected
+  // struct copy of the kernel argument would go through scratch memory)
+  const bool xpre = pr.xp.p != nullptr;
+  const E* xs_p = static_cast<const E*>(xpre ? pr.xp.p : pr.xbc.p);
+  const int64_t xs_sb = xpre ? pr.xp.sb : pr.xbc.sb, xs_st = xpre ? pr.xp.st : pr.xbc.st;
+  auto prefetch = [&](int h) {
+    if (wave == 0)
+      pf_dt = t0 + lane < pr.L ? static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h]
+                               : E{};
+    const E* xq = xs_p + b * xs_sb + h * P;
+    const E* dq = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
+    const E* zq = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+#pragma unroll
+    for (int q = 0; q < NXV; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      const int r = i / (P / V), cl = (i % (P / V)) * V;
+      // rows past the end load row t0 (always valid) and are zeroed after the load,
+      // so every load is unconditional
+      const bool ok = t0 + r < pr.L;
+      const int64_t t = ok ? t0 + r : t0;
+      pf_x[q] = keep_if(ok, *reinterpret_cast<const uint4*>(xq + t * xs_st + cl));
+      pf_do[q] = keep_if(ok, *reinterpret_cast<const uint4*>(dq + t * a.dout.st + cl));
+      pf_z[q] = make_uint4(0u, 0u, 0u, 0u);
+      if (zq) pf_z[q] = keep_if(ok, *reinterpret_cast<const uint4*>(zq + t * pr.z.st + cl));
+    }
+    const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
+    const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
+#pragma unroll
+    for (int q = 0; q < NH4; ++q) {
+      const int i = (threadIdx.x + q * kThreads) * 4;
+      hv[q] = gv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < P * N) {
+        hv[q] = *reinterpret_cast<const float4*>(Hg + i);
+        gv[q] = *reinterpret_cast<const float4*>(dHg + i);
+      }
+    }
+  };
+  prefetch(h_first);
 
   // B and C rows of the group (post-conv), shared by every head of the block
   conv_rows<IO, P, N, false, true, true>(pr, b, 0, g, t0, [&](int seg, int s, int cl, const float* o) {
@@ -274,54 +326,13 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     const int h = h_first + hh;
     const float Ah = pr.A[h];
     const float Dh = pr.D ? pr.D[h] : 0.f;
-    // Every global load of head h is issued before any is consumed, so the head
-    // waits for memory once: dt (wave 0), the raw x rows, dout / z at this lane's
-    // accumulator positions (rows m0 + 4*(lane/16)+e, cols 16j + lane%16), H_{c-1}
-    // and dH_c.
-    E dt_e{};
-    if (wave == 0 && t0 + lane < pr.L)
-      dt_e = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h];
-    ChunkLoader<IO, P, N, true, false, false> xl;
-    xl.issue(pr, b, h, g, t0);
-    E dv_e[PJ][4], zv_e[PJ][4];
-    {
-      const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-      const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
-#pragma unroll
-      for (int j = 0; j < PJ; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t t = t0 + m0 + acc_row(e);
-          const int p = 16 * j + acc_col();
-          dv_e[j][e] = E{};
-          zv_e[j][e] = E{};
-          if (t < pr.L) {
-            dv_e[j][e] = dp[t * a.dout.st + p];
-            if (zp) zv_e[j][e] = zp[t * pr.z.st + p];
-          }
-        }
-    }
-    constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
-    float4 hv[NH4], gv[NH4];
-    {
-      const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
-      const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
-#pragma unroll
-      for (int q = 0; q < NH4; ++q) {
-        const int i = (threadIdx.x + q * kThreads) * 4;
-        hv[q] = gv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < P * N) {
-          hv[q] = *reinterpret_cast<const float4*>(Hg + i);
-          gv[q] = *reinterpret_cast<const float4*>(dHg + i);
-        }
-      }
-    }
+    // ---- stage head h from the prefetch registers into LDS
     // (1) dt, cs, softplus slope, chunk-state decays (wave 0)
     if (wave == 0) {
       const int64_t t = t0 + lane;
       float dtv = 0.f, sig = 1.f;
       if (t < pr.L) {
-        const float u = T::to_f(dt_e) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+        const float u = T::to_f(pf_dt) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
         dtv = pr.softplus ? softplusf_(u) : u;
         sig = pr.softplus ? sigmoidf_(u) : 1.f;
       }
@@ -332,25 +343,27 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       s_sig[lane] = sig;
       s_dq[lane] = __expf(csl - cs);
     }
-    // (2) x of head h (post-conv, row-major)
-    xl.consume(pr, h, t0, [&](int, int s, int cl, const float* o) {
-      lds_put_row<IO>(sX + s * ldP + cl, o);
-    });
-    // dy = dout silu(z) and dout silu'(z) in registers, dy (and its low part) in LDS
-    float dyr[PJ][4], g2r[PJ][4];
+    // (2) x rows; dy = dout silu(z) (and its low part); dout silu'(z)
 #pragma unroll
-    for (int j = 0; j < PJ; ++j)
+    for (int q = 0; q < NXV; ++q) {
+      const int i = threadIdx.x + q * kThreads;
+      const int r = i / (P / V), cl = (i % (P / V)) * V;
+      *reinterpret_cast<uint4*>(sX + r * ldP + cl) = pf_x[q];
+      float dy[V], lo[V], g2[V];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = 16 * j + acc_col();
-        const float dv = T::to_f(dv_e[j][e]), zv = T::to_f(zv_e[j][e]);
-        dyr[j][e] = pr.z.p ? dv * siluf_(zv) : dv;
-        g2r[j][e] = pr.z.p ? dv * dsiluf_(zv) : 0.f;
-        const Lt hi = T::to_lds(dyr[j][e]);
-        sDY[(m0 + acc_row(e)) * ldP + p] = hi;
-        if constexpr (SPLIT) sDYlo[(m0 + acc_row(e)) * ldP + p] = T::to_lds(dyr[j][e] - T::lds_to_f(hi));
+      for (int v = 0; v < V; ++v) {
+        const float dv = raw_elem<IO>(pf_do[q], v), zv = raw_elem<IO>(pf_z[q], v);
+        dy[v] = pr.z.p ? dv * siluf_(zv) : dv;
+        g2[v] = pr.z.p ? dv * dsiluf_(zv) : 0.f;
+        lo[v] = dy[v] - T::to_f(T::from_f(dy[v]));
       }
-    // H_{c-1}, dH_c of head h into LDS; <dH, H> on the way
+      lds_put_row<IO>(sDY + r * ldP + cl, dy);
+      if constexpr (SPLIT) lds_put_row<IO>(sDYlo + r * ldP + cl, lo);
+#pragma unroll
+      for (int v = 0; v < V; v += 4)
+        *reinterpret_cast<float4*>(sG2 + r * ldG + cl + v) = make_float4(g2[v], g2[v + 1], g2[v + 2], g2[v + 3]);
+    }
+    // (3) H_{c-1}, dH_c into LDS; <dH, H> on the way
     {
       float dot = 0.f;
 #pragma unroll
@@ -372,6 +385,18 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       if (lane == 0) s_red[0][wave] = dot;
     }
     __syncthreads();
+    // dy (hi + lo) and dout silu'(z) at this lane's accumulator positions
+    // (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
+    float dyr[PJ][4], g2r[PJ][4];
+#pragma unroll
+    for (int j = 0; j < PJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = m0 + acc_row(e), p = 16 * j + acc_col();
+        dyr[j][e] = T::lds_to_f(sDY[t * ldP + p]);
+        if constexpr (SPLIT) dyr[j][e] += T::lds_to_f(sDYlo[t * ldP + p]);
+        g2r[j][e] = sG2[t * ldG + p];
+      }
 
     // (a) Mt, y, dz, carried-state dcs term, dD
     float lt[4][4];  // exp(cs_t - cs_s) masked, at the cb positions
@@ -464,6 +489,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     }
     __syncthreads();
 
+    // the next head's inputs go in flight now, behind the remaining MFMA work
+    if (hh + 1 < a.hb_heads) prefetch(h + 1);
     // (c) dx rows s = m0..: Mt^T dY + exp(cs_Q - cs_s) dt_s B dH^T + D dy
     {
       f32x4 dxd[PJ], dxs[PJ];
@@ -628,7 +655,7 @@ __global__ void __launch_bounds__(256) head_params_kernel(const float* par, int6
 }
 
 struct BwdLayout {
-  size_t bc, bc_lo, H, lsum, dH, dbc, par, dx, conv, total;
+  size_t bc, bc_lo, xp, H, lsum, dH, dbc, par, dx, conv, total;
   int64_t nch;
   int hb_heads, nhb;
 };
@@ -652,6 +679,7 @@ BwdLayout bwd_layout(const Problem& pr) {
   };
   l.bc = take(bc_prepass_bytes(pr));
   l.bc_lo = take(pr.bf16 ? bc_prepass_bytes(pr) : 0);
+  l.xp = take(x_prepass_bytes(pr));
   l.H = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
   l.lsum = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 4);
   l.dH = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
@@ -756,6 +784,10 @@ hipError_t launch_bwd(const Problem& pr_in, const BwdIn& in, const BwdOut& o, vo
     const int64_t gn2 = 2LL * pr.G * pr.N;
     pr.bc = View{ws + l.bc, pr.L * gn2, gn2};
     if (pr.bf16) pr.bc_lo = View{ws + l.bc_lo, pr.L * gn2, gn2};
+    const hipError_t e2 = launch_x_prepass(pr, ws + l.xp, s);
+    if (e2 != hipSuccess) return e2;
+    const int64_t hp = static_cast<int64_t>(pr.H) * pr.P;
+    pr.xp = View{ws + l.xp, pr.L * hp, hp};
   }
 #define SSD_CASE(IO, PP, NN) \
   if (pr.P == PP && pr.N == NN) return run_bwd<IO, PP, NN>(pr, in, o, ws, l, s);

@@ -7,8 +7,10 @@
 //   is evaluated in registers (the causal depthwise conv of the Video-Ma2mba
 //   review's Conv1d critique, skeptic critique of the pith.science verdict).
 //   B and C are shared by every head of a group, so their conv runs once in a
-//   pre-pass (Problem::bc); here they are only loaded.  Without conv all rows are
-//   passed through.  Rows >= L are delivered as zero.
+//   pre-pass (Problem::bc); here they are only loaded.  The backward, which reads
+//   the x rows of a chunk in two kernels, also takes x from a pre-pass
+//   (Problem::xp), computed with the same arithmetic, so the values are identical.
+//   Without conv all rows are passed through.  Rows >= L are delivered as zero.
 //   Each delivered row vector (16 bytes of I/O elements, as floats) goes to
 //   put(seg, row, local_channel, const float* v) with seg 0 = x, 1 = B, 2 = C.
 //
@@ -25,7 +27,7 @@ namespace ssd {
 // registers (so they can be in flight while the previous chunk computes);
 // consume() turns them into post-conv rows and hands them to put().
 template <typename IO, int P, int N, bool DX, bool DB, bool DC, int NTHR = kThreads, int RX = 2,
-          int RB = 8>
+          int RB = 8, bool XPRE = true>  // XPRE: may take x from Problem::xp
 struct ChunkLoader {
   using T = io_traits<IO>;
   using E = typename T::elem;
@@ -43,6 +45,22 @@ struct ChunkLoader {
     if constexpr (DX) {
       const E* xbc = static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
       const E* csi = pr.cs_in.p ? static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb : nullptr;
+      if (XPRE && pr.xp.p) {
+        // post-conv rows from the pre-pass: rows t0 + r0 .. + RX - 1 into slots 3 ..
+        const E* xp = static_cast<const E*>(pr.xp.p) + b * pr.xp.sb;
+#pragma unroll
+        for (int q = 0; q < XT; ++q) {
+          const int task = threadIdx.x + q * NTHR;
+          const int cl = (task % (P / V)) * V;
+          const int r0 = (task / (P / V)) * RX;
+#pragma unroll
+          for (int i = 0; i < RX; ++i) {
+            const bool ok = task < NTX && t0 + r0 + i < pr.L;
+            const int64_t t = ok ? t0 + r0 + i : t0;  // masked rows read a valid row
+            xin[q][3 + i] = keep_if(ok, *reinterpret_cast<const uint4*>(xp + t * pr.xp.st + h * P + cl));
+          }
+        }
+      } else
 #pragma unroll
       for (int q = 0; q < XT; ++q) {
         const int task = threadIdx.x + q * NTHR;
@@ -51,14 +69,14 @@ struct ChunkLoader {
         const int c = h * P + cl;
 #pragma unroll
         for (int i = 0; i < RX + 3; ++i) {
+          // every load is unconditional: masked rows read row t0 of xbc (always valid)
           const int64_t t = t0 + r0 - 3 + i;
-          xin[q][i] = make_uint4(0u, 0u, 0u, 0u);
-          if (task >= NTX || (K == 0 && i < 3) || t >= pr.L) {
-          } else if (t >= 0) {
-            xin[q][i] = *reinterpret_cast<const uint4*>(xbc + t * pr.xbc.st + c);
-          } else if (csi && t >= -(K - 1)) {
-            xin[q][i] = *reinterpret_cast<const uint4*>(csi + (t + K - 1) * pr.cs_in.st + c);
-          }
+          const bool live = task < NTX && !(K == 0 && i < 3) && t < pr.L;
+          const bool from_state = t < 0;
+          const bool ok = live && (!from_state || (csi && t >= -(K - 1)));
+          const E* src = xbc + t0 * pr.xbc.st + c;
+          if (ok) src = from_state ? csi + (t + K - 1) * pr.cs_in.st + c : xbc + t * pr.xbc.st + c;
+          xin[q][i] = keep_if(ok, *reinterpret_cast<const uint4*>(src));
         }
       }
     }
@@ -78,9 +96,9 @@ struct ChunkLoader {
         const E* col = src + (isB ? cB + grp * V : cC + (grp - GB) * V);
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-          const int64_t t = t0 + r0 + r;
-          bin[q][r] = (task < NTB && t < pr.L) ? *reinterpret_cast<const uint4*>(col + t * sst)
-                                               : make_uint4(0u, 0u, 0u, 0u);
+          const bool ok = task < NTB && t0 + r0 + r < pr.L;
+          const int64_t t = ok ? t0 + r0 + r : t0;  // masked rows read a valid row
+          bin[q][r] = keep_if(ok, *reinterpret_cast<const uint4*>(col + t * sst));
         }
       }
     }
@@ -98,7 +116,7 @@ struct ChunkLoader {
         const int r0 = (task / (P / V)) * RX;
         const int c = h * P + cl;
         float w4[4][V], bias[V];
-        if (K > 0) {
+        if (K > 0 && !(XPRE && pr.xp.p)) {
 #pragma unroll
           for (int v = 0; v < V; ++v) {
             bias[v] = pr.conv_b ? pr.conv_b[c + v] : 0.f;
@@ -112,7 +130,7 @@ struct ChunkLoader {
 #pragma unroll
         for (int r = 0; r < RX; ++r) {
           float o[V];
-          if (K > 0) {
+          if (K > 0 && !(XPRE && pr.xp.p)) {
 #pragma unroll
             for (int v = 0; v < V; ++v) {
               float pre = bias[v];

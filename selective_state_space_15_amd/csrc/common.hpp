@@ -113,6 +113,12 @@ __device__ __forceinline__ float raw_elem(const uint4& raw, int v) {
     return __uint_as_float(w);
 }
 
+// v if keep, else zeros.  Selects the four words separately: a select between two
+// uint4 structs is lowered through scratch memory.
+__device__ __forceinline__ uint4 keep_if(bool keep, const uint4& v) {
+  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+
 template <typename IO>
 __device__ __forceinline__ void zero_vec16(vec16<IO>& out) {
 #pragma unroll

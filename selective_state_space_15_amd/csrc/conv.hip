@@ -186,7 +186,6 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   const int64_t tile = (gid / ncq) % ntile;
   const int64_t b = gid / (static_cast<int64_t>(ncq) * ntile);
   const int K = a.K;
-  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
 
   float w4[4][4], bias[4];
 #pragma unroll
@@ -210,8 +209,7 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
       p = sb + (t + K - 1) * a.st_st;
       ok = true;
     }
-    const uint4 v = Qd::load(p);
-    return ok ? v : zero4;
+    return keep_if(ok, Qd::load(p));
   };
   // gradient rows: I/O-typed view, or (fused, B / C channels) the fp32 group sums
   const bool from_f32 = FUSED && c >= a.hp;
@@ -236,8 +234,12 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   auto grad_row = [&](int64_t t) -> uint4 {
     const bool ok = t >= 0 && t < a.L;
     const int64_t tt = ok ? t : 0;
-    const uint4 v = from_f32 ? *reinterpret_cast<const uint4*>(fb + tt * f_st) : Qd::load(gb + tt * g_st);
-    return ok ? v : zero4;
+    uint4 v;
+    if (from_f32)
+      v = *reinterpret_cast<const uint4*>(fb + tt * f_st);
+    else
+      v = Qd::load(gb + tt * g_st);
+    return keep_if(ok, v);
   };
   // dpre of row t from its four raw rows r[0..3] (rows t-3 .. t) and gradient gr
   auto dpre_row = [&](int64_t t, const uint4* r, const uint4& gr, float* d) {
@@ -524,6 +526,20 @@ hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStre
                                pr.conv_w + static_cast<int64_t>(hp) * pr.K,
                                pr.conv_b ? pr.conv_b + hp : nullptr, out, 0, s,
                                pr.bf16 ? dst_lo : nullptr);
+}
+
+size_t x_prepass_bytes(const Problem& pr) {
+  if (pr.K == 0) return 0;
+  const size_t n = static_cast<size_t>(pr.B) * pr.L * pr.H * pr.P * (pr.bf16 ? 2 : 4);
+  return (n + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s) {
+  TimingScope ts(kKBcPrepass, s);
+  const int hp = pr.H * pr.P;
+  const MView out{dst, pr.L * hp, hp};
+  return launch_conv_fwd_range(pr.bf16, pr.B, pr.L, hp, pr.K, 1, pr.xbc, 0, pr.cs_in, 0, pr.conv_w,
+                               pr.conv_b, out, 0, s, nullptr);
 }
 
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s) {

@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   const int64_t tbeg = k * a.cps * kQ;
   constexpr int RXL = HALVES == 1 ? 2 : 1;  // x rows per loader task: all threads busy
   constexpr int RBL = 8 / HALVES;           // B/C rows per loader task
-  ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL> ld;
+  ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL, !OUT> ld;
   float dt_raw = 0.f;
   // gate inputs of this lane's output elements (rows m0 + 4*(lane/16) + e,
   // columns 16*(YJ*half + j) + lane%16), kept as raw I/O bits (bf16: two per register)

@@ -67,6 +67,7 @@ struct Problem {
   const float* h0;
   View bc;     // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
   View bc_lo;  // bf16 I/O backward: post-conv B|C minus its bf16 rounding (p null: none)
+  View xp;     // post-conv x rows [B][L][H*P] from a pre-pass (p null: conv in the loaders)
 };
 
 struct FwdOut {
@@ -126,6 +127,9 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
 // and (dst_lo != null, bf16 I/O) the rounding residual v - bf16(v) -> dst_lo
 hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s);
 size_t bc_prepass_bytes(const Problem& pr);
+// Post-conv x channels [B][L][H*P] (I/O dtype) for the backward's chunk loaders.
+hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s);
+size_t x_prepass_bytes(const Problem& pr);
 size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);
 hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,
                            float* db, MView dstate_in, int accumulate, void* ws, hipStream_t s);

@@ -47,7 +47,7 @@ hipEvent_t take_event(TimingState& s) {
 }
 
 const char* const kNames[kKernelKinds] = {
-    "bc_prepass", "walk_state", "scan", "walk_out", "conv_state_out", "conv_fwd",
+    "prepass", "walk_state", "scan", "walk_out", "conv_state_out", "conv_fwd",
     "chunk_states", "dstate", "scan_rev", "bwd_main", "conv_bwd", "dbc_reduce", "params"};
 
 }  // namespace
