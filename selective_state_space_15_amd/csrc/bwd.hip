@@ -206,6 +206,10 @@ __global__ void __launch_bounds__(256) scan_rev_kernel(const float* dh_final, fl
 }
 
 // ------------------------------------------------------------------ main
+// One wave per SIMD has registers to spare: unroll the MFMA K loops so operand
+// reads overlap the MFMAs.
+constexpr int kMainUnroll = 2;
+
 template <typename IO, int P, int N>
 __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   using T = io_traits<IO>;
@@ -312,8 +316,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   f32x4 cb[4];  // (C B^T)[t in rows m0.., s], all 64 columns
 #pragma unroll
   for (int j = 0; j < 4; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mma_strip<Lt, true, true, 4>(cb, sC, ldN, m0, sB, ldN, 0, N);
-  if (clo) mma_strip<Lt, true, true, 4>(cb, sClo, ldN, m0, sB, ldN, 0, N);
+  mma_strip<Lt, true, true, 4, kMainUnroll>(cb, sC, ldN, m0, sB, ldN, 0, N);
+  if (clo) mma_strip<Lt, true, true, 4, kMainUnroll>(cb, sClo, ldN, m0, sB, ldN, 0, N);
 
   f32x4 accdB[NTn], accdC[NTn];
 #pragma unroll
@@ -411,8 +415,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     f32x4 yacc[PJ];
 #pragma unroll
     for (int j = 0; j < PJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_strip<Lt, true, true, PJ>(yacc, sC, ldN, m0, sH, ldN, 0, N);
-    if (clo) mma_strip<Lt, true, true, PJ>(yacc, sClo, ldN, m0, sH, ldN, 0, N);
+    mma_strip<Lt, true, true, PJ, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, 0, N);
+    if (clo) mma_strip<Lt, true, true, PJ, kMainUnroll>(yacc, sClo, ldN, m0, sH, ldN, 0, N);
     float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -424,7 +428,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    mma_strip<Lt, true, false, PJ>(yacc, sM, ldQ, m0, sX, ldP, 0, kQ);
+    mma_strip<Lt, true, false, PJ, kMainUnroll>(yacc, sM, ldQ, m0, sX, ldP, 0, kQ);
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + h * P : nullptr;
@@ -457,8 +461,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       f32x4 dyx[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, true, 4>(dyx, sDY, ldP, m0, sX, ldP, 0, P);
-      if constexpr (SPLIT) mma_strip<Lt, true, true, 4>(dyx, sDYlo, ldP, m0, sX, ldP, 0, P);
+      mma_strip<Lt, true, true, 4, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, 0, P);
+      if constexpr (SPLIT) mma_strip<Lt, true, true, 4, kMainUnroll>(dyx, sDYlo, ldP, m0, sX, ldP, 0, P);
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -499,8 +503,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         dxd[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         dxs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      mma_strip<Lt, false, false, PJ>(dxd, sM, ldQ, m0, sDY, ldP, 0, kQ);
-      mma_strip<Lt, true, true, PJ>(dxs, sB, ldN, m0, sdH, ldN, 0, N);
+      mma_strip<Lt, false, false, PJ, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, 0, kQ);
+      mma_strip<Lt, true, true, PJ, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, 0, N);
       E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + h * P;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -520,7 +524,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       f32x4 U[NTn];
 #pragma unroll
       for (int j = 0; j < NTn; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, false, NTn>(U, sX, ldP, m0, sdH, ldN, 0, P);
+      mma_strip<Lt, true, false, NTn, kMainUnroll>(U, sX, ldP, m0, sdH, ldN, 0, P);
       float vp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -539,15 +543,15 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       if (acc_col() == 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s_v[m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
-      mma_strip<Lt, false, false, NTn>(accdB, sW, ldQ, m0, sC, ldN, 0, kQ);
+      mma_strip<Lt, false, false, NTn, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, 0, kQ);
     }
     // (e) dC rows t: W B + exp(cs_t) dY H
     {
-      mma_strip<Lt, true, false, NTn>(accdC, sW, ldQ, m0, sB, ldN, 0, kQ);
+      mma_strip<Lt, true, false, NTn, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, 0, kQ);
       f32x4 tmp[NTn];
 #pragma unroll
       for (int j = 0; j < NTn; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, false, NTn>(tmp, sDY, ldP, m0, sH, ldN, 0, P);
+      mma_strip<Lt, true, false, NTn, kMainUnroll>(tmp, sDY, ldP, m0, sH, ldN, 0, P);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float ecs = __expf(s_cs[m0 + acc_row(e)]);

@@ -229,8 +229,9 @@ struct frag<float, kc> {
 //   B tile j: columns n0 + 16*j .. +15, stored per `bkc`.
 // K must be a multiple of the per-lane K-slice (8 for bf16); when it is not a
 // multiple of the MFMA K-step, lanes whose slice lies at or past K feed zeros.
-// Executed by one full wave.
-template <typename L, bool akc, bool bkc, int NJ>
+// Executed by one full wave.  UNROLL > 1 unrolls the K loop so the operand reads of
+// later K-steps issue ahead of the MFMAs (for kernels with registers to spare).
+template <typename L, bool akc, bool bkc, int NJ, int UNROLL = 1>
 __device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda, int m0, const L* B,
                                           int ldb, int n0, int K) {
   constexpr int kstep = sizeof(L) == 2 ? 32 : 4;
@@ -238,10 +239,10 @@ __device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda,
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15;
   const int kg = lane >> 4;
-  // one K-step at a time: a fully unrolled K loop lets the scheduler hoist every
-  // fragment read of every tile ahead of the MFMAs, which costs more registers
-  // than two waves per SIMD have
-#pragma unroll 1
+  // one K-step at a time by default: a fully unrolled K loop lets the scheduler
+  // hoist every fragment read of every tile ahead of the MFMAs, which costs more
+  // registers than two waves per SIMD have
+#pragma unroll UNROLL
   for (int k0 = 0; k0 < K; k0 += kstep) {
     const int kr = k0 + kpl * kg;
     const bool kin = kr < K;

@@ -504,7 +504,6 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
   const int V = bf16 ? 8 : 4;
   const int64_t n = B * ((L + kRowsF - 1) / kRowsF) * (C / V);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  TimingScope ts(kKConvFwd, s);
   if (bf16)
     hipLaunchKernelGGL(conv_fwd_kernel<bf16_t>, grid, dim3(256), 0, s, a);
   else
@@ -543,6 +542,7 @@ hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s) {
 }
 
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s) {
+  TimingScope ts(kKConvFwd, s);
   hipError_t e = launch_conv_fwd_range(cp.bf16, cp.B, cp.L, static_cast<int>(cp.C), cp.K, cp.silu,
                                        cp.x, 0, cp.state_in, 0, cp.w, cp.b, out, 0, s, nullptr);
   if (e != hipSuccess || !state_out.p) return e;
