@@ -40,6 +40,11 @@ def test_c1_full_length_bwd():
     bwd_check(Case(synth.CONFIGS["c1"], seed=30))
 
 
+def test_c4_shapes_batch16_80_heads_bwd():
+    # d_model 2560 mixer shapes (80 heads: head blocks of 8, conv channels 5376) at batch 16
+    bwd_check(Case(synth.CONFIGS["c4"].with_(L=333), seed=41, states=True))
+
+
 def test_grouped_batched_bwd():
     d = synth.Dims(B=2, L=333, H=8, P=64, N=64, G=2, K=4, d_model=256)
     bwd_check(Case(d, seed=31, states=True))

@@ -1,0 +1,121 @@
+"""Parity at the benchmark's full size, in the benchmark's launch configuration.
+
+Workload: the d_model 1024 hot path (32 heads x 64, d_state 128, conv 4, bf16 I/O)
+over L = 1,048,576 tokens, run as bench.py runs it: one ssd_fwd over the whole
+sequence keeping the state every 16,384 tokens, then ssd_bwd segment by segment
+in reverse, carrying (dh, dconv) between segments.
+
+The fp64 oracle cannot replay a million tokens for all 32 heads within a test, so
+it checks outputs it can compute one by one:
+
+* forward, one sampled head over the whole sequence: its gated output at every
+  token, its state at every one of the 64 checkpoints and at the end (the oracle
+  runs the head's own recurrence segment by segment, which is the unsplit
+  recurrence exactly);
+* backward, every per-token gradient of that head in the last segment (the
+  pre-conv gradient of its x channels, the dt gradient, the z gradient), from the
+  oracle's backward of that segment started at the oracle's own state.  Nothing
+  after the last segment feeds these, so they are exact targets; the B / C
+  gradients (sums over all heads) and the sequence-wide parameter sums are covered
+  by the smaller cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from selective_state_space_15_amd import binding as bd
+from selective_state_space_15_amd import segmented, synth
+from tests.gpu_cases import TOL, f64, rel_l2, to_host
+
+pytestmark = pytest.mark.gpu
+
+SEG = 16384
+HEAD = 11  # the sampled head
+
+
+def test_full_length_segmented_fwd_bwd_sampled_head():
+    d = synth.CONFIGS["c2"].with_(seg=SEG)
+    L, H, P, N, K = d.L, d.H, d.P, d.N, d.K
+    hp, cd = d.hp, d.cd
+    dev = torch.device("cuda:0")
+    zx_bits = synth.zxbcdt(d, 0)                       # [1, L, d_in_proj] bf16 bits
+    do_bits = synth.dout(d, 7)                         # [1, L, H*P]
+    prm = synth.params(d, 0)
+    print(f"[full] inputs ready L={L}", flush=True)
+
+    # ---------------------------------------------------------------- GPU, as bench.py
+    zx = torch.from_numpy(zx_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    dout = torch.from_numpy(do_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    p = {k: torch.from_numpy(v).to(dev) for k, v in prm.items()}
+    z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+    dims = bd.make_dims(1, L, H, P, N, 1, 0, K)
+    seg_dims = bd.make_dims(1, SEG, H, P, N, 1, 0, K)
+    out = torch.empty(1, L, hp, dtype=torch.bfloat16, device=dev)
+    h_final = torch.empty(1, H, P, N, device=dev)
+    fws = torch.empty(bd.ssd_fwd_workspace(dims, bd.SSD_BF16), dtype=torch.uint8, device=dev)
+    bws = torch.empty(bd.ssd_bwd_workspace(seg_dims, bd.SSD_BF16), dtype=torch.uint8, device=dev)
+    h_ckpt = segmented.forward_segmented(dims, SEG, xbc, p["A"], dt, out, conv_w=p["conv_w"],
+                                         conv_b=p["conv_b"], dt_bias=p["dt_bias"], D=p["D"], z=z,
+                                         h_final=h_final, ws=fws)
+    dxbc = torch.empty(1, L, cd, dtype=torch.bfloat16, device=dev)
+    ddt = torch.empty(1, L, H, dtype=torch.bfloat16, device=dev)
+    dzg = torch.empty(1, L, hp, dtype=torch.bfloat16, device=dev)
+    dA, dD, ddtb = (torch.empty(H, device=dev) for _ in range(3))
+    dcw, dcb = torch.empty(cd, K, device=dev), torch.empty(cd, device=dev)
+    segmented.backward_segmented(dims, SEG, h_ckpt, xbc, p["A"], dt, dout, dxbc, ddt, dA,
+                                 conv_w=p["conv_w"], conv_b=p["conv_b"], dt_bias=p["dt_bias"],
+                                 D=p["D"], z=z, dz=dzg, dD=dD, ddt_bias=ddtb, dconv_w=dcw,
+                                 dconv_b=dcb, ws=bws)
+    torch.cuda.synchronize()
+    cols = slice(HEAD * P, (HEAD + 1) * P)
+    g_out = to_host(out[0, :, cols])
+    g_ck = h_ckpt[:, 0, HEAD].cpu().numpy().astype(np.float64)
+    g_hf = h_final[0, HEAD].cpu().numpy().astype(np.float64)
+    t0 = L - SEG
+    g_dx = to_host(dxbc[0, t0:, cols])
+    g_ddt = to_host(ddt[0, t0:, HEAD])
+    g_dz = to_host(dzg[0, t0:, cols])
+    assert np.isfinite(to_host(dA)).all() and np.isfinite(g_dx).all()
+    del zx, dout, out, dxbc, dzg, fws, bws
+    torch.cuda.empty_cache()
+    print("[full] GPU done", flush=True)
+
+    # ---------------------------------------------------------------- oracle, one head
+    # the head's channels of the conv input: its 64 x channels, then B and C
+    ch = np.r_[hp + HEAD * P: hp + (HEAD + 1) * P, 2 * hp: 2 * hp + 2 * N]
+    wch = np.r_[HEAD * P:(HEAD + 1) * P, hp:hp + 2 * N]
+    conv_w = prm["conv_w"][wch].astype(np.float64)
+    conv_b = prm["conv_b"][wch].astype(np.float64)
+    A, D = prm["A"][[HEAD]].astype(np.float64), prm["D"][[HEAD]].astype(np.float64)
+    dtb = prm["dt_bias"][[HEAD]].astype(np.float64)
+    xraw = f64(zx_bits[:, :, ch])                                   # [1, L, 64 + 2N]
+    post, _ = orc.conv1d_fwd(xraw, conv_w, conv_b, None, silu=True)
+    x, Bm, Cm = orc.split_xbc(post, 1, P, 1, N)
+    dtr = f64(zx_bits[:, :, hp + cd + HEAD:hp + cd + HEAD + 1])
+    zh = f64(zx_bits[:, :, HEAD * P:(HEAD + 1) * P]).reshape(1, L, 1, P)
+    h = np.zeros((1, 1, P, N))
+    outs, ck = [], []
+    for k in range(L // SEG):
+        s = slice(k * SEG, (k + 1) * SEG)
+        ck.append(h[0, 0].copy())
+        o, _, h = orc.ssd_fwd(x[:, s], dtr[:, s], A, Bm[:, s], Cm[:, s], dtb, True, D, zh[:, s], h)
+        outs.append(o.reshape(SEG, P))
+    r_out = np.concatenate(outs)
+    e_out = rel_l2(g_out, r_out)
+    e_ck = rel_l2(g_ck, np.stack(ck))
+    e_hf = rel_l2(g_hf, h[0, 0])
+    # the last segment's backward from the oracle's own state at its start
+    s = slice(t0, L)
+    dout_h = f64(do_bits[:, s, HEAD * P:(HEAD + 1) * P]).reshape(1, SEG, 1, P)
+    r = orc.mixer_bwd(xraw[:, s], conv_w, conv_b, dtr[:, s], A, 1, P, 1, N, dout_h, dt_bias=dtb,
+                      D=D, z=zh[:, s], h0=np.asarray(ck[-1])[None, None], conv_state=xraw[:, t0 - (K - 1):t0])
+    e_dx = rel_l2(g_dx, r["dxbc_raw"][0, :, :P])
+    e_ddt = rel_l2(g_ddt, r["ddt"][0, :, 0])
+    e_dz = rel_l2(g_dz, r["dz"].reshape(SEG, P))
+    print(f"[full] head {HEAD}: out={e_out:.2e} ckpt={e_ck:.2e} h_final={e_hf:.2e} "
+          f"last-seg dx={e_dx:.2e} ddt={e_ddt:.2e} dz={e_dz:.2e}", flush=True)
+    tol = TOL["bf16"]
+    for name, e in [("out", e_out), ("ckpt", e_ck), ("h_final", e_hf), ("dx", e_dx), ("ddt", e_ddt),
+                    ("dz", e_dz)]:
+        assert e <= tol, (name, e)

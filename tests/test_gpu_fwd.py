@@ -57,6 +57,11 @@ def test_c1_carried_state(L):
     check_fwd(c, h0=c.st["h0"], conv_state=c.st["conv_state"])
 
 
+def test_c4_shapes_batch16_80_heads():
+    # d_model 2560 mixer shapes (80 heads, conv channels 5376) at batch 16, ragged length
+    check_fwd(Case(synth.CONFIGS["c4"].with_(L=333), seed=40))
+
+
 def test_grouped_bc_batch():
     d = synth.Dims(B=2, L=333, H=4, P=64, N=64, G=2, K=4, d_model=256)
     c = Case(d, seed=4, states=True)
