@@ -167,24 +167,21 @@ __device__ __forceinline__ float word_f(const uint4& r, int v) {
   return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
 }
 
-// One thread per (batch, kRowsB-row tile, 4 channels).  The thread walks its rows
-// kBatch at a time with a register window: raw[i] holds raw row tau0 - 3 + i and
-// dp[i] holds dpre of row tau0 + i, so each step loads only kBatch new raw rows
+// One work item = (batch, kRowsB-row tile, 4 channels).  The thread walks the tile's
+// rows kBatch at a time with a register window: raw[i] holds raw row tau0 - 3 + i
+// and dp[i] holds dpre of row tau0 + i, so each step loads only kBatch new raw rows
 // and kBatch new gradient rows, and those of the next step are in flight while
-// this one computes.  Every load is unconditional (rows outside the sequence read
-// row 0 and are masked to zero), so the loads of a step issue back to back.
-template <typename IO, bool FUSED>
-__global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
+// this one computes.  Row pointers advance by a stride per step (no 64-bit
+// multiplies per row).  INTERIOR tiles (all rows they touch inside the sequence,
+// no carried-state rows, no returned-state rows) run without any masking; the
+// first and last tiles take the general path, where rows outside the sequence
+// read a valid row and are masked to zero after the load.
+template <typename IO, bool FUSED, bool INTERIOR>
+__device__ __forceinline__ void conv_bwd_tile(const ConvBwdArgs& a, int64_t b, int64_t tile, int c) {
   using T = io_traits<IO>;
   using E = typename T::elem;
   using Qd = quad<IO>;
-  const int ncq = a.C / 4;
   const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-  if (gid >= a.B * ntile * ncq) return;
-  const int c = static_cast<int>(gid % ncq) * 4;
-  const int64_t tile = (gid / ncq) % ntile;
-  const int64_t b = gid / (static_cast<int64_t>(ncq) * ntile);
   const int K = a.K;
 
   float w4[4][4], bias[4];
@@ -199,17 +196,22 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   }
   const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + c;
   const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + c : nullptr;
+  const int64_t xst = a.x_st;
   auto raw_row = [&](int64_t t) -> uint4 {
-    const E* p = xb;
-    bool ok = false;
-    if (t >= 0 && t < a.L) {
-      p = xb + t * a.x_st;
-      ok = true;
-    } else if (sb && t < 0 && t >= -(K - 1)) {
-      p = sb + (t + K - 1) * a.st_st;
-      ok = true;
+    if constexpr (INTERIOR) {
+      return Qd::load(xb + t * xst);
+    } else {
+      const E* p = xb;
+      bool ok = false;
+      if (t >= 0 && t < a.L) {
+        p = xb + t * xst;
+        ok = true;
+      } else if (sb && t < 0 && t >= -(K - 1)) {
+        p = sb + (t + K - 1) * a.st_st;
+        ok = true;
+      }
+      return keep_if(ok, Qd::load(p));
     }
-    return keep_if(ok, Qd::load(p));
   };
   // gradient rows: I/O-typed view, or (fused, B / C channels) the fp32 group sums
   const bool from_f32 = FUSED && c >= a.hp;
@@ -232,28 +234,33 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
     g_st = a.g_st;
   }
   auto grad_row = [&](int64_t t) -> uint4 {
-    const bool ok = t >= 0 && t < a.L;
+    const bool ok = INTERIOR || (t >= 0 && t < a.L);
     const int64_t tt = ok ? t : 0;
     uint4 v;
     if (from_f32)
       v = *reinterpret_cast<const uint4*>(fb + tt * f_st);
     else
       v = Qd::load(gb + tt * g_st);
-    return keep_if(ok, v);
+    return INTERIOR ? v : keep_if(ok, v);
   };
-  // dpre of row t from its four raw rows r[0..3] (rows t-3 .. t) and gradient gr
-  auto dpre_row = [&](int64_t t, const uint4* r, const uint4& gr, float* d) {
-    const bool ok = t >= 0 && t < a.L;
+  auto unpack = [&](const uint4& r, float* f) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) f[v] = Qd::get(r, v);
+  };
+  auto unpack_grad = [&](const uint4& r, float* f) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) f[v] = from_f32 ? word_f(r, v) : Qd::get(r, v);
+  };
+  // dpre of row t from its four raw rows (rows t-3 .. t) and its gradient g
+  const bool silu = a.silu != 0;
+  auto dpre_row = [&](int64_t t, const float (*rw)[4], const float* gv, float* d) {
+    const bool ok = INTERIOR || (t >= 0 && t < a.L);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float gv = from_f32 ? word_f(gr, v) : Qd::get(gr, v);
-      float dv = gv;
-      if (a.silu) {
-        float pre = bias[v];
+      float pre = bias[v];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], Qd::get(r[j], v), pre);
-        dv = gv * dsiluf_(pre);
-      }
+      for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], rw[j][v], pre);
+      const float dv = silu ? gv[v] * dsiluf_(pre) : gv[v];
       d[v] = ok ? dv : 0.f;
     }
   };
@@ -273,17 +280,23 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   const int64_t tau_begin = tile == 0 ? -(K - 1) : t_lo;
   const int64_t tau_end = t_lo + kRowsB < a.L ? t_lo + kRowsB : a.L;
 
-  uint4 raw[kBatch + 6];
-  float dp[kBatch + 3][4];
+  float raw[kBatch + 6][4];   // raw row tau0 - 3 + i
+  float dp[kBatch + 3][4];    // dpre of row tau0 + i
   int64_t tau0 = tau_begin;
   {
-    uint4 g0[3];
+    uint4 r0[6], g0[3];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) raw[i] = raw_row(tau0 - 3 + i);
+    for (int i = 0; i < 6; ++i) r0[i] = raw_row(tau0 - 3 + i);
 #pragma unroll
     for (int i = 0; i < 3; ++i) g0[i] = grad_row(tau0 + i);
 #pragma unroll
-    for (int i = 0; i < 3; ++i) dpre_row(tau0 + i, raw + i, g0[i], dp[i]);
+    for (int i = 0; i < 6; ++i) unpack(r0[i], raw[i]);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      float gv[4];
+      unpack_grad(g0[i], gv);
+      dpre_row(tau0 + i, raw + i, gv, dp[i]);
+    }
   }
   uint4 nraw[kBatch], ngr[kBatch];
 #pragma unroll
@@ -291,12 +304,14 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
     nraw[i] = raw_row(tau0 + 3 + i);
     ngr[i] = grad_row(tau0 + 3 + i);
   }
-  for (; tau0 < tau_end; tau0 += kBatch) {
-    uint4 cgr[kBatch];
+  E* dxrow = dxb + tau0 * a.dx_st;  // advanced by kBatch rows per step
+  const int64_t dx_step = kBatch * a.dx_st;
+  for (; tau0 < tau_end; tau0 += kBatch, dxrow += dx_step) {
+    float cgr[kBatch][4];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      raw[6 + i] = nraw[i];
-      cgr[i] = ngr[i];
+      unpack(nraw[i], raw[6 + i]);
+      unpack_grad(ngr[i], cgr[i]);
     }
     // next step's rows (harmless past the tile: masked or simply unused)
 #pragma unroll
@@ -309,7 +324,7 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
       const int64_t tau = tau0 + r;
-      if (tau < tau_end) {
+      if (INTERIOR || tau < tau_end) {
         float o[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -318,19 +333,21 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
           for (int j = 0; j < 4; ++j) acc = fmaf(w4[j][v], dp[r + 3 - j][v], acc);
           o[v] = acc;
         }
-        const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
-        if (dsob && js >= 0) {
-          const uint4 d = Qd::load(dsob + js * a.dso_st);
+        if constexpr (!INTERIOR) {
+          const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
+          if (dsob && js >= 0) {
+            const uint4 d = Qd::load(dsob + js * a.dso_st);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] += Qd::get(d, v);
+            for (int v = 0; v < 4; ++v) o[v] += Qd::get(d, v);
+          }
         }
-        if (tau >= 0) {
-          Qd::store(dxb + tau * a.dx_st, o);
+        if (INTERIOR || tau >= 0) {
+          Qd::store(dxrow + r * a.dx_st, o);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             db[v] += dp[r][v];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dp[r][v], Qd::get(raw[r + j], v), dw[j][v]);
+            for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dp[r][v], raw[r + j][v], dw[j][v]);
           }
         } else if (dsib) {
           Qd::store(dsib + (tau + K - 1) * a.dsi_st, o);
@@ -338,7 +355,9 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < 6; ++i) raw[i] = raw[i + kBatch];
+    for (int i = 0; i < 6; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) raw[i][v] = raw[i + kBatch][v];
 #pragma unroll
     for (int i = 0; i < 3; ++i)
 #pragma unroll
@@ -356,6 +375,35 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   }
 }
 
+template <typename IO, bool FUSED>
+__device__ __forceinline__ void conv_bwd_item(const ConvBwdArgs& a, int64_t gid) {
+  const int ncq = a.C / 4;
+  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
+  const int c = static_cast<int>(gid % ncq) * 4;
+  const int64_t tile = (gid / ncq) % ntile;
+  const int64_t b = gid / (static_cast<int64_t>(ncq) * ntile);
+  // interior: rows t_lo - 3 .. t_lo + kRowsB + 2 * kBatch + 2 (prefetch reach) inside
+  // the sequence, and none of the last K - 1 rows (gradient of the returned state)
+  const int64_t t_lo = tile * kRowsB;
+  const bool interior = tile > 0 && t_lo + kRowsB + 2 * kBatch + 3 <= a.L - (a.K - 1);
+  if (interior)
+    conv_bwd_tile<IO, FUSED, true>(a, b, tile, c);
+  else
+    conv_bwd_tile<IO, FUSED, false>(a, b, tile, c);
+}
+
+// Grid-stride over the (batch, tile, 4-channel) items: the grid is sized to what
+// the device holds at once, so no partial last round of workgroups.
+template <typename IO, bool FUSED>
+__global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
+  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
+  const int64_t total = a.B * ntile * (a.C / 4);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; gid < total;
+       gid += stride)
+    conv_bwd_item<IO, FUSED>(a, gid);
+}
+
 // dw[c][k], db[c]: ordered sums of the per-(batch, tile) partials ([n_bt][C][5])
 __global__ void __launch_bounds__(256) conv_params_kernel(const float* part, int64_t n_bt, int C,
                                                           int K, float* dw, float* db,
@@ -370,22 +418,30 @@ __global__ void __launch_bounds__(256) conv_params_kernel(const float* part, int
   *dst = accumulate ? *dst + acc : acc;
 }
 
+template <typename IO, bool FUSED>
+void launch_conv_bwd_kernel(const ConvBwdArgs& a, int64_t n, hipStream_t s) {
+  const int64_t cap = resident_blocks(reinterpret_cast<const void*>(conv_bwd_kernel<IO, FUSED>), 256);
+  int64_t blocks = (n + 255) / 256;
+  if (cap > 0 && blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((conv_bwd_kernel<IO, FUSED>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     s, a);
+}
+
 hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* db, int accumulate,
                         hipStream_t s) {
   const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
   const int64_t n = a.B * ntile * (a.C / 4);
-  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   TimingScope ts(kKConvBwd, s);
   if (bf16) {
     if (fused)
-      hipLaunchKernelGGL((conv_bwd_kernel<bf16_t, true>), grid, dim3(256), 0, s, a);
+      launch_conv_bwd_kernel<bf16_t, true>(a, n, s);
     else
-      hipLaunchKernelGGL((conv_bwd_kernel<bf16_t, false>), grid, dim3(256), 0, s, a);
+      launch_conv_bwd_kernel<bf16_t, false>(a, n, s);
   } else {
     if (fused)
-      hipLaunchKernelGGL((conv_bwd_kernel<float, true>), grid, dim3(256), 0, s, a);
+      launch_conv_bwd_kernel<float, true>(a, n, s);
     else
-      hipLaunchKernelGGL((conv_bwd_kernel<float, false>), grid, dim3(256), 0, s, a);
+      launch_conv_bwd_kernel<float, false>(a, n, s);
   }
   hipLaunchKernelGGL(conv_params_kernel, dim3(static_cast<unsigned>((a.C * 5 + kWave - 1) / kWave)),
                      dim3(256), 0, s, a.part, a.B * ntile, a.C, a.K, dw, db, accumulate);

@@ -127,6 +127,9 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
 // and (dst_lo != null, bf16 I/O) the rounding residual v - bf16(v) -> dst_lo
 hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s);
 size_t bc_prepass_bytes(const Problem& pr);
+// Workgroups of `threads` threads of `kernel` resident on the current device at once
+// (all CUs; cached per device and kernel); 0 if the runtime cannot tell.
+int64_t resident_blocks(const void* kernel, int threads);
 // Post-conv x channels [B][L][H*P] (I/O dtype) for the backward's chunk loaders.
 hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s);
 size_t x_prepass_bytes(const Problem& pr);

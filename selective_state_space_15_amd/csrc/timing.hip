@@ -69,6 +69,30 @@ TimingScope::~TimingScope() {
   t.pending.push_back(Pending{kind_, static_cast<hipEvent_t>(a_), static_cast<hipEvent_t>(b_)});
 }
 
+int64_t resident_blocks(const void* kernel, int threads) {
+  struct Entry {
+    const void* kernel;
+    int threads, device;
+    int64_t blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& e : cache)
+      if (e.kernel == kernel && e.threads == threads && e.device == dev) return e.blocks;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  const int64_t blocks = static_cast<int64_t>(cus) * per_cu;
+  std::lock_guard<std::mutex> lk(mu);
+  cache.push_back(Entry{kernel, threads, dev, blocks});
+  return blocks;
+}
+
 }  // namespace ssd
 
 extern "C" {
