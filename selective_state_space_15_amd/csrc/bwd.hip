@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         sig = pr.softplus ? sigmoidf_(u) : 1.f;
       }
       const float cs = wave_incl_scan(dtv * Ah);
-      const float csl = __shfl(cs, kWave - 1, kWave);
+      const float csl = lane_value(cs, kWave - 1);
       s_dt[lane] = dtv;
       s_cs[lane] = cs;
       s_sig[lane] = sig;
@@ -448,8 +448,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) yo_part[e] += __shfl_xor(yo_part[e], off, kWave);
+      yo_part[e] = row_sum16(yo_part[e]);
     if (acc_col() == 0)
 #pragma unroll
       for (int e = 0; e < 4; ++e) s_yo[m0 + acc_row(e)] = yo_part[e];
@@ -484,8 +483,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) rs[e] += __shfl_xor(rs[e], off, kWave);
+        rs[e] = row_sum16(rs[e]);
       }
       if (acc_col() == 0)
 #pragma unroll
@@ -538,8 +536,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) vp[e] += __shfl_xor(vp[e], off, kWave);
+        vp[e] = row_sum16(vp[e]);
       if (acc_col() == 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s_v[m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];

@@ -155,21 +155,57 @@ __device__ __forceinline__ float dsiluf_(float u) {
   return s * (1.f + u * (1.f - s));
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ float wave_incl_scan(float v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+// ---------------------------------------------------------------- cross-lane (DPP)
+// Cross-lane moves within the VALU (data-parallel primitives of the gfx9 family),
+// instead of LDS-routed permutes.  update_dpp(old, src, ctrl, row_mask, bank_mask,
+// bound_ctrl): each lane takes src from the lane the control selects; lanes whose
+// source is outside its 16-lane row get 0 when bound_ctrl is set, and lanes of rows
+// masked off keep `old`.
+template <int CTRL, int ROW_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xf, BOUND_CTRL));
+}
+constexpr int kDppQuad1032 = 0xB1;     // quad_perm: lane i ^ 1
+constexpr int kDppQuad2301 = 0x4E;     // quad_perm: lane i ^ 2
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowShr = 0x110;      // + shift (1 .. 15)
+constexpr int kDppRowBcast15 = 0x142;  // lane 15 of each row -> the next row
+constexpr int kDppRowBcast31 = 0x143;  // lane 31 -> rows 2 and 3
+
+// Sum over the 16 lanes of each row (lanes 16r .. 16r+15); every lane of the row
+// receives it.  Pairs, quads, half rows, rows.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuad1032>(0.f, v);
+  v += dpp_f<kDppQuad2301>(0.f, v);
+  v += dpp_f<kDppRowHalfMirror>(0.f, v);
+  v += dpp_f<kDppRowMirror>(0.f, v);
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+// Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele inside each
+// row (shifts 1, 2, 4, 8), then the totals of the rows before are added.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp_f<kDppRowShr + 1, 0xf, true>(0.f, v);
+  v += dpp_f<kDppRowShr + 2, 0xf, true>(0.f, v);
+  v += dpp_f<kDppRowShr + 4, 0xf, true>(0.f, v);
+  v += dpp_f<kDppRowShr + 8, 0xf, true>(0.f, v);
+  v += dpp_f<kDppRowBcast15, 0xa>(0.f, v);  // rows 1, 3 += totals of rows 0, 2
+  v += dpp_f<kDppRowBcast31, 0xc>(0.f, v);  // rows 2, 3 += total of rows 0..1
   return v;
+}
+
+// Value of lane `src` (a wave-uniform lane index), in every lane.
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
+// Sum over the 64 lanes of a wave, in every lane: row sums, then the four rows in order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  return ((lane_value(v, 0) + lane_value(v, 16)) + lane_value(v, 32)) + lane_value(v, 48);
 }
 
 // ---------------------------------------------------------------- MFMA tiles

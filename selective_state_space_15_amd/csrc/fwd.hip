@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         dtv = pr.softplus ? softplusf_(u) : u;
       }
       const float cs = wave_incl_scan(dtv * Ah);
-      const float csl = __shfl(cs, kWave - 1, kWave);
+      const float csl = lane_value(cs, kWave - 1);
       s_dt[lane] = dtv;
       s_cs[lane] = cs;
       s_w[lane] = dtv * __expf(csl - cs);
