@@ -47,7 +47,8 @@
  *              h_final, checkpoints, dh) and parameter gradients: fp32.  All
  *              arithmetic accumulates in fp32; bf16 results are rounded to nearest
  *              even.
- *   Layouts    h0 / h_final / dh: [B][H][P][N] (n contiguous) fp32.
+ *   Layouts    h0 / h_final / dh: [B][H][P][N] (n contiguous) fp32, base pointer
+ *                                 16-byte aligned (SSD_ERR_ALIGN otherwise).
  *              conv state:        [B][K-1][Cd] rows, oldest first -- the same layout
  *                                 as xbc rows, so the previous segment's last K-1
  *                                 input rows can be passed as a view.

@@ -36,6 +36,12 @@ int esize(ssd_dtype io) { return io == SSD_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// fp32 state arrays are read and written as 16-byte vectors
+ssd_status check_state(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "%s: state pointer not 16-byte aligned", name);
+  return SSD_OK;
+}
+
 // A [B, T, C] activation view.  vec: 16-byte rule (vector loads); else element rule.
 ssd_status check_view(const ssd_view& v, const char* name, ssd_dtype io, bool required, bool vec,
                       int64_t T, int64_t C) {
@@ -157,6 +163,9 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
     TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));
     TRY(check_view(conv_state_out, "conv_state_out", io, false, true, K - 1, Cd));
   }
+  TRY(check_state(h0, "h0"));
+  TRY(check_state(h_final, "h_final"));
+  TRY(check_state(h_ckpt, "h_ckpt"));
   if (h_ckpt && (ckpt_every <= 0 || ckpt_every % ssd::kQ))
     return fail(SSD_ERR_SHAPE, "ckpt_every %lld must be a positive multiple of %d",
                 (long long)ckpt_every, ssd::kQ);
@@ -217,6 +226,9 @@ ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
   TRY(check_view(dz, "dz", io, z.ptr != nullptr, true, L, HP));
   if (!A) return fail(SSD_ERR_NULL, "A: NULL");
   if (!dA) return fail(SSD_ERR_NULL, "dA: NULL");
+  TRY(check_state(h0, "h0"));
+  TRY(check_state(dh_final, "dh_final"));
+  TRY(check_state(dh0, "dh0"));
   if (K > 0) {
     if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
     TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));

@@ -321,36 +321,44 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   }
 }
 
-// Exclusive scan of the affine sub-segment maps: ws_state[k] <- H_in(k).
+// Exclusive scan of the affine sub-segment maps: ws_state[k] <- H_in(k).  Each
+// thread owns 4 consecutive state elements (one head: P*N is a multiple of 4) and
+// keeps 8 steps of loads in flight.
+__device__ __forceinline__ float4 axpy4(float a, const float4& x, const float4& y) {
+  return make_float4(fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w));
+}
+
 __global__ void __launch_bounds__(256) scan_kernel(const float* h0, float* ws_state,
                                                    const float* ws_lsum, int64_t B, int H,
                                                    int64_t PN, int64_t n_sub) {
-  const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int64_t e4 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   const int64_t per_b = H * PN;
-  if (e >= B * per_b) return;
+  if (e4 * 4 >= B * per_b) return;
+  const int64_t e = e4 * 4;
   const int64_t b = e / per_b, rem = e % per_b;
   const int h = static_cast<int>(rem / PN);
-  float hc = h0 ? h0[e] : 0.f;
+  float4 hc = h0 ? *reinterpret_cast<const float4*>(h0 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
   float* base = ws_state + b * n_sub * per_b + rem;
   const float* lb = ws_lsum + b * n_sub * H + h;
   int64_t k = 0;
   for (; k + 8 <= n_sub; k += 8) {
-    float s[8], l[8];
+    float4 sv[8];
+    float l[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      s[i] = base[(k + i) * per_b];
+      sv[i] = *reinterpret_cast<const float4*>(base + (k + i) * per_b);
       l[i] = lb[(k + i) * H];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      base[(k + i) * per_b] = hc;
-      hc = __expf(l[i]) * hc + s[i];
+      *reinterpret_cast<float4*>(base + (k + i) * per_b) = hc;
+      hc = axpy4(__expf(l[i]), hc, sv[i]);
     }
   }
   for (; k < n_sub; ++k) {
-    const float s = base[k * per_b];
-    base[k * per_b] = hc;
-    hc = __expf(lb[k * H]) * hc + s;
+    const float4 sv = *reinterpret_cast<const float4*>(base + k * per_b);
+    *reinterpret_cast<float4*>(base + k * per_b) = hc;
+    hc = axpy4(__expf(lb[k * H]), hc, sv);
   }
 }
 
@@ -397,7 +405,7 @@ hipError_t run_walks(const Problem& pr, const FwdOut& o, const Plan& pl, float* 
     const int64_t ne = pr.B * pr.H * PN;
     {
       TimingScope ts(kKScan, s);
-      hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+      hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0, s,
                          pr.h0, ws_state, ws_lsum, pr.B, pr.H, PN, pl.n_sub);
     }
     a.init = ws_state;
@@ -522,7 +530,7 @@ hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, floa
   const int64_t ne = pr.B * pr.H * PN;
   {
     TimingScope ts(kKScan, s);
-    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0, s,
                        pr.h0, ws_H, ws_lsum, pr.B, pr.H, PN, nch);
   }
   return hipGetLastError();

@@ -87,6 +87,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     st = lib.ssd_fwd(ctypes.byref(d), bd.SSD_BF16, bad, None, None, nullv, nullv, nullv, None, 1,
                      None, None, nullv, None, nullv, None, None, 0, None, 0, None)
     assert st == bd.SSD_ERR_ALIGN
+    # fp32 state pointers must be 16-byte aligned
+    st = lib.ssd_fwd(ctypes.byref(d), bd.SSD_BF16, bd.ssd_view(0x1000, 100 * cd, cd), 0x8000, None,
+                     nullv, nullv, bd.ssd_view(0x2000, 400, 4), None, 1, 0x9000, None, nullv, 0x9004,
+                     bd.ssd_view(0x4000, 100 * 256, 256), None, None, 0, None, 0, None)
+    assert st == bd.SSD_ERR_ALIGN and b"h0" in lib.ssd_last_error()
     # checkpoint spacing must be a multiple of 64
     good = bd.ssd_view(0x1000, 100 * cd, cd)
     dtv = bd.ssd_view(0x2000, 400, 4)
