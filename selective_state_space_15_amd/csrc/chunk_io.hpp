@@ -104,8 +104,11 @@ struct ChunkLoader {
     }
   }
 
+  // wl: optional LDS copy of the head's conv taps and bias, [P][5] (taps right-aligned
+  // on 4, bias last), so the chunk loop does not re-read them from global memory.
   template <typename F>
-  __device__ __forceinline__ void consume(const Problem& pr, int h, int64_t t0, F&& put) const {
+  __device__ __forceinline__ void consume(const Problem& pr, int h, int64_t t0, F&& put,
+                                          const float* wl = nullptr) const {
     const int K = pr.K;
     if constexpr (DX) {
 #pragma unroll
@@ -117,13 +120,23 @@ struct ChunkLoader {
         const int c = h * P + cl;
         float w4[4][V], bias[V];
         if (K > 0 && !(XPRE && pr.xp.p)) {
+          if (wl) {
 #pragma unroll
-          for (int v = 0; v < V; ++v) {
-            bias[v] = pr.conv_b ? pr.conv_b[c + v] : 0.f;
+            for (int v = 0; v < V; ++v) {
+              const float* wv = wl + (cl + v) * 5;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int kk = j - (4 - K);  // taps right-aligned on 4
-              w4[j][v] = kk >= 0 ? pr.conv_w[(c + v) * K + kk] : 0.f;
+              for (int j = 0; j < 4; ++j) w4[j][v] = wv[j];
+              bias[v] = wv[4];
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+              bias[v] = pr.conv_b ? pr.conv_b[c + v] : 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int kk = j - (4 - K);  // taps right-aligned on 4
+                w4[j][v] = kk >= 0 ? pr.conv_w[(c + v) * K + kk] : 0.f;
+              }
             }
           }
         }

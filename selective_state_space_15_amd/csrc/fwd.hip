@@ -84,6 +84,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
   __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
   __shared__ float s_dt[kQ], s_cs[kQ], s_w[kQ];
+  __shared__ float s_conv[P * 5];  // head h's conv taps (right-aligned on 4) and bias
 
   const Problem& pr = a.pr;
   const int64_t total = static_cast<int64_t>(pr.B) * a.n_sub * pr.H;
@@ -112,6 +113,14 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   const int s_nj0 = (wave / PT) * NJS;
   const bool s_owns = s_nj0 < NT;
   const int64_t PN = static_cast<int64_t>(P) * N;
+
+  // the head's conv taps and bias, once per workgroup (read by every chunk's loads)
+  if (pr.K > 0 && !(pr.xp.p && !OUT))
+    for (int i = threadIdx.x; i < P * 5; i += NTHR) {
+      const int cl = i / 5, j = i % 5, c = h * P + cl;
+      const int kk = j - (4 - pr.K);
+      s_conv[i] = j == 4 ? (pr.conv_b ? pr.conv_b[c] : 0.f) : (kk >= 0 ? pr.conv_w[c * pr.K + kk] : 0.f);
+    }
 
   f32x4 accH[NJS];
   {
@@ -229,7 +238,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       } else {
         lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
       }
-    });
+    }, s_conv);
     // next chunk's loads go in flight now
     if (c + 1 < a.cps && t0 + kQ < pr.L) prefetch(t0 + kQ);
     __syncthreads();
