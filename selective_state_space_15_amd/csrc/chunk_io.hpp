@@ -104,11 +104,21 @@ struct ChunkLoader {
     }
   }
 
-  // wl: optional LDS copy of the head's conv taps and bias, [P][5] (taps right-aligned
-  // on 4, bias last), so the chunk loop does not re-read them from global memory.
   template <typename F>
-  __device__ __forceinline__ void consume(const Problem& pr, int h, int64_t t0, F&& put,
-                                          const float* wl = nullptr) const {
+  __device__ __forceinline__ void consume(const Problem& pr, int h, int64_t t0, F&& put) const {
+    consume_impl<false>(pr, h, t0, put, nullptr);
+  }
+  // wl: LDS copy of the head's conv taps and bias, [P][5] (taps right-aligned on 4,
+  // bias last), so a chunk loop does not re-read them from global memory.
+  template <typename F>
+  __device__ __forceinline__ void consume_lds_taps(const Problem& pr, int h, int64_t t0, F&& put,
+                                                   const float* wl) const {
+    consume_impl<true>(pr, h, t0, put, wl);
+  }
+
+  template <bool WLDS, typename F>
+  __device__ __forceinline__ void consume_impl(const Problem& pr, int h, int64_t t0, F&& put,
+                                               const float* wl) const {
     const int K = pr.K;
     if constexpr (DX) {
 #pragma unroll
@@ -120,7 +130,7 @@ struct ChunkLoader {
         const int c = h * P + cl;
         float w4[4][V], bias[V];
         if (K > 0 && !(XPRE && pr.xp.p)) {
-          if (wl) {
+          if constexpr (WLDS) {
 #pragma unroll
             for (int v = 0; v < V; ++v) {
               const float* wv = wl + (cl + v) * 5;

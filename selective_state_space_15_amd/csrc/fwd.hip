@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
     prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
     ld.issue(pr, b, h, g, t0);
-    ld.consume(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
+    ld.consume_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
       if (seg == 0) {
         const float ws = s_w[s];
         float ow[V];
