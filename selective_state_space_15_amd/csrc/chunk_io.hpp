@@ -41,6 +41,49 @@ struct ChunkLoader {
   uint4 bin[BT > 0 ? BT : 1][RB];
 
   __device__ __forceinline__ void issue(const Problem& pr, int b, int h, int g, int64_t t0) {
+    // interior chunk: every row it touches (conv halo included) is inside the
+    // sequence, so the loads need no masks and the rows are plain stride steps
+    constexpr bool XFULL = NTX % NTHR == 0, BFULL = NTB % NTHR == 0;
+    if (t0 >= 3 && t0 + kQ <= pr.L) {
+      if constexpr (DX) {
+        const bool pre = XPRE && pr.xp.p != nullptr;
+        const E* base = pre ? static_cast<const E*>(pr.xp.p) + b * pr.xp.sb
+                            : static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
+        const int64_t st = pre ? pr.xp.st : pr.xbc.st;
+        const int first = pre ? 3 : 0;  // post-conv rows skip the halo slots
+#pragma unroll
+        for (int q = 0; q < XT; ++q) {
+          const int task = threadIdx.x + q * NTHR;
+          if (!XFULL && task >= NTX) continue;
+          const int cl = (task % (P / V)) * V;
+          const int r0 = (task / (P / V)) * RX;
+          const E* rowp = base + (t0 + r0 - 3) * st + h * P + cl;
+#pragma unroll
+          for (int i = 0; i < RX + 3; ++i)
+            if (i >= first) xin[q][i] = *reinterpret_cast<const uint4*>(rowp + i * st);
+        }
+      }
+      if constexpr (DB || DC) {
+        const bool pre = pr.bc.p != nullptr;
+        const E* src = pre ? static_cast<const E*>(pr.bc.p) + b * pr.bc.sb
+                           : static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
+        const int64_t sst = pre ? pr.bc.st : pr.xbc.st;
+        const int cB = (pre ? 0 : pr.H * P) + g * N;
+        const int cC = (pre ? 0 : pr.H * P) + pr.G * N + g * N;
+#pragma unroll
+        for (int q = 0; q < BT; ++q) {
+          const int task = threadIdx.x + q * NTHR;
+          if (!BFULL && task >= NTB) continue;
+          const int grp = task % (GB + GC);
+          const int r0 = (task / (GB + GC)) * RB;
+          const bool isB = grp < GB;
+          const E* rowp = src + (isB ? cB + grp * V : cC + (grp - GB) * V) + (t0 + r0) * sst;
+#pragma unroll
+          for (int r = 0; r < RB; ++r) bin[q][r] = *reinterpret_cast<const uint4*>(rowp + r * sst);
+        }
+      }
+      return;
+    }
     const int K = pr.K;
     if constexpr (DX) {
       const E* xbc = static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
