@@ -22,9 +22,8 @@
 //   dl_r  = sum_{t >= r} dcs_t,   ddt_s = (direct terms) + A dl_s,   dA = sum dt dl,
 //   dD = sum dy . x,   ddt_raw = ddt sigmoid(dt_raw + dt_bias),  ddt_bias = sum ddt_raw.
 //
-// Kernels: chunk states H_{c-1} (forward walk in state mode + scan, shared with
-// the forward pass); dstate_kernel (per chunk and head, the dy C^T term);
-// scan_rev_kernel (reverse scan, dh0); bwd_main_kernel (per chunk and block of
+// Kernels: chunk states H_{c-1} (each chunk's own state, then a scan); the
+// per-chunk dy C^T terms (both in chunk_states.hip); scan_rev_kernel (reverse scan, dh0); bwd_main_kernel (per chunk and block of
 // heads of one group: every gradient above, dB / dC summed over the block's
 // heads in registers and written as one fp32 partial per block); then the conv
 // backward (or the dB / dC finalize without conv) and ordered parameter reductions.
@@ -58,117 +57,6 @@ struct BwdArgs {
   float* dbc_part;         // [nhb][B][L][2N] fp32
   float* par_part;         // [B][nch][H][3]: dA, dD, ddt_bias partials
 };
-
-// ------------------------------------------------------------------ dstate
-// dS_c[p][n] = sum_t exp(cs_t) dy_t[p] C_t[n] for one (batch, chunk, head).
-template <typename IO, int P, int N>
-__global__ void __launch_bounds__(kThreads) dstate_kernel(BwdArgs a) {
-  using T = io_traits<IO>;
-  using E = typename T::elem;
-  using Lt = typename T::lds;
-  constexpr int PADK = 16 / sizeof(Lt);
-  constexpr int ldN = N + PADK, ldP = P + PADK;
-  __shared__ __align__(16) Lt sC[kQ * ldN];
-  __shared__ __align__(16) Lt sDy[kQ * ldP];  // dy exp(cs_t), rows t (read transposed)
-  // bf16 I/O: low parts of C and dy (the state gradient feeds the log-decay gradient)
-  constexpr bool SPLIT = sizeof(Lt) == 2;
-  __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
-  __shared__ __align__(16) Lt sDylo[SPLIT ? kQ * ldP : 8];
-  __shared__ float s_ecs[kQ];
-
-  const Problem& pr = a.pr;
-  const int64_t total = static_cast<int64_t>(pr.B) * a.nch * pr.H;
-  const int64_t lid = xcd_remap(blockIdx.x, total);
-  const int h = static_cast<int>(lid % pr.H);
-  const int64_t c = (lid / pr.H) % a.nch;
-  const int b = static_cast<int>(lid / (static_cast<int64_t>(pr.H) * a.nch));
-  const int g = h / (pr.H / pr.G);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t t0 = c * kQ;
-
-  // issue every global load (dt, C rows, their low parts, dout, z) before any is used
-  E dt_e{};
-  if (wave == 0 && t0 + lane < pr.L)
-    dt_e = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h];
-  ChunkLoader<IO, P, N, false, false, true> cl_hi, cl_lo;
-  cl_hi.issue(pr, b, h, g, t0);
-  const bool clo = SPLIT && pr.bc_lo.p != nullptr;
-  Problem prl = pr;
-  prl.bc = pr.bc_lo;
-  if (clo) cl_lo.issue(prl, b, h, g, t0);
-  constexpr int V = T::vec;
-  constexpr int NDT = (P / V) * kQ / kThreads;  // dout / z vectors per thread
-  static_assert((P / V) * kQ % kThreads == 0, "dout tasks must tile the block");
-  uint4 dvr[NDT], zvr[NDT];
-  {
-    const E* dp = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-    const E* zp = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
-#pragma unroll
-    for (int q = 0; q < NDT; ++q) {
-      const int task = threadIdx.x + q * kThreads;
-      const int col = (task % (P / V)) * V, r = task / (P / V);
-      const int64_t t = t0 + r;
-      dvr[q] = zvr[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (t < pr.L) {
-        dvr[q] = *reinterpret_cast<const uint4*>(dp + t * a.dout.st + col);
-        if (zp) zvr[q] = *reinterpret_cast<const uint4*>(zp + t * pr.z.st + col);
-      }
-    }
-  }
-  if (wave == 0) {
-    float dtv = 0.f;
-    if (t0 + lane < pr.L) {
-      const float u = T::to_f(dt_e) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
-      dtv = pr.softplus ? softplusf_(u) : u;
-    }
-    const float cs = wave_incl_scan(dtv * pr.A[h]);
-    s_ecs[lane] = __expf(cs);
-  }
-  cl_hi.consume(pr, h, t0, [&](int, int s, int cl, const float* o) {
-    lds_put_row<IO>(sC + s * ldN + cl, o);
-  });
-  if (clo)
-    cl_lo.consume(prl, h, t0, [&](int, int s, int cl, const float* o) {
-      lds_put_row<IO>(sClo + s * ldN + cl, o);
-    });
-  __syncthreads();
-  // dy * exp(cs_t) (and its low part) as row-major 16-byte stores
-#pragma unroll
-  for (int q = 0; q < NDT; ++q) {
-    const int task = threadIdx.x + q * kThreads;
-    const int col = (task % (P / V)) * V, r = task / (P / V);
-    const float ecs = s_ecs[r];
-    float dy[V], lo[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const float dv = raw_elem<IO>(dvr[q], v);
-      dy[v] = (pr.z.p ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * ecs;
-      lo[v] = dy[v] - T::to_f(T::from_f(dy[v]));
-    }
-    lds_put_row<IO>(sDy + r * ldP + col, dy);
-    if constexpr (SPLIT) lds_put_row<IO>(sDylo + r * ldP + col, lo);
-  }
-  __syncthreads();
-  constexpr int PT = P / 16, NT = N / 16, WPP = 4 / PT, NJS = (NT + WPP - 1) / WPP;
-  const int s_pi = wave / WPP, s_nj0 = (wave % WPP) * NJS;
-  if (s_nj0 < NT) {
-    f32x4 acc[NJS];
-#pragma unroll
-    for (int j = 0; j < NJS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_strip<Lt, false, false, NJS>(acc, sDy, ldP, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
-    if constexpr (SPLIT) {
-      mma_strip<Lt, false, false, NJS>(acc, sDylo, ldP, s_pi * 16, sC, ldN, s_nj0 * 16, kQ);
-      if (clo) mma_strip<Lt, false, false, NJS>(acc, sDy, ldP, s_pi * 16, sClo, ldN, s_nj0 * 16, kQ);
-    }
-    const int64_t PN = static_cast<int64_t>(P) * N;
-    float* dst = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
-#pragma unroll
-    for (int j = 0; j < NJS; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[j][e];
-  }
-}
 
 // ------------------------------------------------------------------ reverse scan
 // dHs[c] <- gradient leaving chunk c; g runs dH_{c-1} = exp(lsum_c) dH_c + dS_c.
@@ -729,11 +617,8 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
                                      reinterpret_cast<float*>(ws + l.lsum), s);
   if (e != hipSuccess) return e;
   // 2. per-chunk dy C^T terms, 3. reverse scan -> dH_c, dh0
-  {
-    TimingScope ts(kKDstate, s);
-    hipLaunchKernelGGL((dstate_kernel<IO, P, N>), dim3(static_cast<unsigned>(pr.B * l.nch * pr.H)),
-                       dim3(kThreads), 0, s, a);
-  }
+  e = launch_chunk_dstates(pr, l.nch, in.dout, a.dHs, s);
+  if (e != hipSuccess) return e;
   {
     TimingScope ts(kKScanRev, s);
     hipLaunchKernelGGL(scan_rev_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0,

@@ -503,39 +503,14 @@ hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, voi
   return err;
 }
 
-// Chunk-start states for the backward pass: the walk in state mode with one
-// chunk per sub-segment gives each chunk's local end state and log-decay; the
-// exclusive scan (from h0) turns them into H_{c-1}, the state entering chunk c.
+// Chunk-start states for the backward pass: each chunk's own end state and
+// log-decay (computed independently per chunk), then the exclusive scan from h0
+// turns them into H_{c-1}, the state entering chunk c.
 hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
                                hipStream_t s) {
-  WalkArgs a{};
-  a.pr = pr;
-  a.cps = 1;
-  a.n_sub = nch;
-  a.ws_state = ws_H;
-  a.ws_lsum = ws_lsum;
-  a.ckpt_every = 1;
   const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
-  const dim3 grid(static_cast<unsigned>(pr.B * nch * pr.H));
-#define SSD_CASE(IO, PP, NN)                                                              \
-  if (pr.P == PP && pr.N == NN) {                                                         \
-    TimingScope ts(kKChunkStates, s);                                                     \
-    hipLaunchKernelGGL((walk_kernel<IO, PP, NN, kModeState>), grid,                       \
-                       dim3(WalkShape<kModeState>::waves * 64), 0, s, a);                 \
-    launched = true;                                                                      \
-  }
-  bool launched = false;
-  if (pr.bf16) {
-    SSD_CASE(bf16_t, 64, 128) else SSD_CASE(bf16_t, 64, 64) else SSD_CASE(bf16_t, 64, 32)
-    else SSD_CASE(bf16_t, 64, 16) else SSD_CASE(bf16_t, 32, 128) else SSD_CASE(bf16_t, 32, 64)
-    else SSD_CASE(bf16_t, 32, 32) else SSD_CASE(bf16_t, 32, 16)
-  } else {
-    SSD_CASE(float, 64, 128) else SSD_CASE(float, 64, 64) else SSD_CASE(float, 64, 32)
-    else SSD_CASE(float, 64, 16) else SSD_CASE(float, 32, 128) else SSD_CASE(float, 32, 64)
-    else SSD_CASE(float, 32, 32) else SSD_CASE(float, 32, 16)
-  }
-#undef SSD_CASE
-  if (!launched) return hipErrorInvalidValue;
+  hipError_t err = launch_chunk_local_states(pr, nch, ws_H, ws_lsum, s);
+  if (err != hipSuccess) return err;
   const int64_t ne = pr.B * pr.H * PN;
   {
     TimingScope ts(kKScan, s);
