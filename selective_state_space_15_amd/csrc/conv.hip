@@ -12,11 +12,12 @@
 // registers and the 16 output rows are stored as 16-byte vectors.  Adjacent threads
 // take adjacent channel vectors, so every row access is coalesced.
 //
-// Backward: one thread per (batch, 32-row tile, 4 channels) walks its rows with a
-// sliding register window; dpre = dout * silu'(pre) is recomputed from the raw
-// rows, dx[tau] = sum_k dpre[tau + K-1-k] w[k] (plus the gradient of the returned
-// conv state for the last K-1 rows), and per-tile partial sums of dw and db go to
-// scratch for an ordered reduction (deterministic, no atomics).
+// Backward: one workgroup per (batch, 128-row tile, 64 channels) stages the tile's raw
+// and gradient rows in LDS (all loads in flight at once), then each thread walks 32
+// rows of one channel with a sliding register window; dpre = dout * silu'(pre) is
+// recomputed from the raw rows, dx[tau] = sum_k dpre[tau + K-1-k] w[k] (plus the
+// gradient of the returned conv state for the last K-1 rows), and per-tile partial
+// sums of dw and db go to scratch for an ordered reduction (deterministic, no atomics).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,8 +25,10 @@ namespace ssd {
 
 namespace {
 
-constexpr int kRowsF = 16;  // rows per thread, forward
-constexpr int kRowsB = 32;  // rows per thread, backward
+constexpr int kRowsF = 16;     // rows per thread, forward
+constexpr int kTileRows = 128; // rows per workgroup, backward
+constexpr int kTileCh = 64;    // channels per workgroup, backward
+constexpr int kSegRows = 32;   // rows per thread, backward (four segments per tile)
 
 struct ConvFwdArgs {
   int64_t B, L;
@@ -109,7 +112,6 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
 }
 
 // ------------------------------------------------------------------ backward
-constexpr int kBatch = 4;  // output rows per step of the backward register window
 
 struct ConvBwdArgs {
   int64_t B, L;
@@ -134,274 +136,202 @@ struct ConvBwdArgs {
   float* part;  // [B][ntile][C][5]: dw taps 0..K-1, db at 4
 };
 
-// Four channels of I/O elements: 8 bytes of bf16 or 16 bytes of fp32, held in a uint4.
-template <typename IO>
-struct quad;
-template <>
-struct quad<bf16_t> {
-  __device__ static __forceinline__ uint4 load(const uint16_t* p) {
-    const uint2 r = *reinterpret_cast<const uint2*>(p);
-    return make_uint4(r.x, r.y, 0u, 0u);
-  }
-  __device__ static __forceinline__ float get(const uint4& r, int v) {
-    const uint32_t w = v < 2 ? r.x : r.y;
-    return __uint_as_float((v & 1) ? (w & 0xffff0000u) : (w << 16));
-  }
-  __device__ static __forceinline__ void store(uint16_t* p, const float* f) {
-    *reinterpret_cast<uint2*>(p) = make_uint2(f2bf2(f[0], f[1]), f2bf2(f[2], f[3]));
-  }
-};
-template <>
-struct quad<float> {
-  __device__ static __forceinline__ uint4 load(const float* p) {
-    return *reinterpret_cast<const uint4*>(p);
-  }
-  __device__ static __forceinline__ float get(const uint4& r, int v) {
-    return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
-  }
-  __device__ static __forceinline__ void store(float* p, const float* f) {
-    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
-  }
-};
-__device__ __forceinline__ float word_f(const uint4& r, int v) {
-  return __uint_as_float(v == 0 ? r.x : v == 1 ? r.y : v == 2 ? r.z : r.w);
-}
-
-// One work item = (batch, kRowsB-row tile, 4 channels).  The thread walks the tile's
-// rows kBatch at a time with a register window: raw[i] holds raw row tau0 - 3 + i
-// and dp[i] holds dpre of row tau0 + i, so each step loads only kBatch new raw rows
-// and kBatch new gradient rows, and those of the next step are in flight while
-// this one computes.  Row pointers advance by a stride per step (no 64-bit
-// multiplies per row).  INTERIOR tiles (all rows they touch inside the sequence,
-// no carried-state rows, no returned-state rows) run without any masking; the
-// first and last tiles take the general path, where rows outside the sequence
-// read a valid row and are masked to zero after the load.
-template <typename IO, bool FUSED, bool INTERIOR>
-__device__ __forceinline__ void conv_bwd_tile(const ConvBwdArgs& a, int64_t b, int64_t tile, int c) {
-  using T = io_traits<IO>;
-  using E = typename T::elem;
-  using Qd = quad<IO>;
-  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int K = a.K;
-
-  float w4[4][4], bias[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    bias[v] = a.bias ? a.bias[c + v] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = j - (4 - K);  // taps right-aligned on 4: tap j reads row t - 3 + j
-      w4[j][v] = kk >= 0 ? a.w[(c + v) * K + kk] : 0.f;
-    }
-  }
-  const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + c;
-  const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + c : nullptr;
-  const int64_t xst = a.x_st;
-  auto raw_row = [&](int64_t t) -> uint4 {
-    if constexpr (INTERIOR) {
-      return Qd::load(xb + t * xst);
-    } else {
-      const E* p = xb;
-      bool ok = false;
-      if (t >= 0 && t < a.L) {
-        p = xb + t * xst;
-        ok = true;
-      } else if (sb && t < 0 && t >= -(K - 1)) {
-        p = sb + (t + K - 1) * a.st_st;
-        ok = true;
-      }
-      return keep_if(ok, Qd::load(p));
-    }
-  };
-  // gradient rows: I/O-typed view, or (fused, B / C channels) the fp32 group sums
-  const bool from_f32 = FUSED && c >= a.hp;
-  const E* gb = nullptr;
-  int64_t g_st = 0;
-  const float* fb = nullptr;
-  const int64_t f_st = 2LL * a.N;
-  if (FUSED) {
-    if (from_f32) {
-      const int gn = a.G * a.N, rel = c - a.hp;
-      const bool isC = rel >= gn;
-      const int g = (isC ? rel - gn : rel) / a.N, n0 = (isC ? rel - gn : rel) % a.N;
-      fb = a.dbc + ((static_cast<int64_t>(g) * a.per_g * a.B + b) * a.L) * f_st + (isC ? a.N : 0) + n0;
-    } else {
-      gb = static_cast<const E*>(a.g) + b * a.L * a.hp + c;
-      g_st = a.hp;
-    }
-  } else {
-    gb = static_cast<const E*>(a.g) + b * a.g_sb + c;
-    g_st = a.g_st;
-  }
-  auto grad_row = [&](int64_t t) -> uint4 {
-    const bool ok = INTERIOR || (t >= 0 && t < a.L);
-    const int64_t tt = ok ? t : 0;
-    uint4 v;
-    if (from_f32)
-      v = *reinterpret_cast<const uint4*>(fb + tt * f_st);
-    else
-      v = Qd::load(gb + tt * g_st);
-    return INTERIOR ? v : keep_if(ok, v);
-  };
-  auto unpack = [&](const uint4& r, float* f) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) f[v] = Qd::get(r, v);
-  };
-  auto unpack_grad = [&](const uint4& r, float* f) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) f[v] = from_f32 ? word_f(r, v) : Qd::get(r, v);
-  };
-  // dpre of row t from its four raw rows (rows t-3 .. t) and its gradient g
-  const bool silu = a.silu != 0;
-  auto dpre_row = [&](int64_t t, const float (*rw)[4], const float* gv, float* d) {
-    const bool ok = INTERIOR || (t >= 0 && t < a.L);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float pre = bias[v];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], rw[j][v], pre);
-      const float dv = silu ? gv[v] * dsiluf_(pre) : gv[v];
-      d[v] = ok ? dv : 0.f;
-    }
-  };
-
-  float dw[4][4], db[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    db[v] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dw[j][v] = 0.f;
-  }
-  E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + c;
-  const E* dsob = a.dso ? static_cast<const E*>(a.dso) + b * a.dso_sb + c : nullptr;
-  E* dsib = a.dsi ? static_cast<E*>(a.dsi) + b * a.dsi_sb + c : nullptr;
-  const int64_t t_lo = tile * kRowsB;
-  // tile 0 also produces the gradient of the carried-in state rows (tau < 0)
-  const int64_t tau_begin = tile == 0 ? -(K - 1) : t_lo;
-  const int64_t tau_end = t_lo + kRowsB < a.L ? t_lo + kRowsB : a.L;
-
-  float raw[kBatch + 6][4];   // raw row tau0 - 3 + i
-  float dp[kBatch + 3][4];    // dpre of row tau0 + i
-  int64_t tau0 = tau_begin;
-  {
-    uint4 r0[6], g0[3];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) r0[i] = raw_row(tau0 - 3 + i);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) g0[i] = grad_row(tau0 + i);
-#pragma unroll
-    for (int i = 0; i < 6; ++i) unpack(r0[i], raw[i]);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      float gv[4];
-      unpack_grad(g0[i], gv);
-      dpre_row(tau0 + i, raw + i, gv, dp[i]);
-    }
-  }
-  uint4 nraw[kBatch], ngr[kBatch];
-#pragma unroll
-  for (int i = 0; i < kBatch; ++i) {
-    nraw[i] = raw_row(tau0 + 3 + i);
-    ngr[i] = grad_row(tau0 + 3 + i);
-  }
-  E* dxrow = dxb + tau0 * a.dx_st;  // advanced by kBatch rows per step
-  const int64_t dx_step = kBatch * a.dx_st;
-  for (; tau0 < tau_end; tau0 += kBatch, dxrow += dx_step) {
-    float cgr[kBatch][4];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      unpack(nraw[i], raw[6 + i]);
-      unpack_grad(ngr[i], cgr[i]);
-    }
-    // next step's rows (harmless past the tile: masked or simply unused)
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      nraw[i] = raw_row(tau0 + kBatch + 3 + i);
-      ngr[i] = grad_row(tau0 + kBatch + 3 + i);
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) dpre_row(tau0 + 3 + i, raw + 3 + i, cgr[i], dp[3 + i]);
-#pragma unroll
-    for (int r = 0; r < kBatch; ++r) {
-      const int64_t tau = tau0 + r;
-      if (INTERIOR || tau < tau_end) {
-        float o[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float acc = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc = fmaf(w4[j][v], dp[r + 3 - j][v], acc);
-          o[v] = acc;
-        }
-        if constexpr (!INTERIOR) {
-          const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
-          if (dsob && js >= 0) {
-            const uint4 d = Qd::load(dsob + js * a.dso_st);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] += Qd::get(d, v);
-          }
-        }
-        if (INTERIOR || tau >= 0) {
-          Qd::store(dxrow + r * a.dx_st, o);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            db[v] += dp[r][v];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dw[j][v] = fmaf(dp[r][v], raw[r + j][v], dw[j][v]);
-          }
-        } else if (dsib) {
-          Qd::store(dsib + (tau + K - 1) * a.dsi_st, o);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 6; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) raw[i][v] = raw[i + kBatch][v];
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dp[i][v] = dp[i + kBatch][v];
-  }
-  float* pp = a.part + ((b * ntile + tile) * a.C + c) * 5;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = j - (4 - K);
-      if (kk >= 0) pp[v * 5 + kk] = dw[j][v];
-    }
-    pp[v * 5 + 4] = db[v];
-  }
-}
-
-template <typename IO, bool FUSED>
-__device__ __forceinline__ void conv_bwd_item(const ConvBwdArgs& a, int64_t gid) {
-  const int ncq = a.C / 4;
-  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int c = static_cast<int>(gid % ncq) * 4;
-  const int64_t tile = (gid / ncq) % ntile;
-  const int64_t b = gid / (static_cast<int64_t>(ncq) * ntile);
-  // interior: rows t_lo - 3 .. t_lo + kRowsB + 2 * kBatch + 2 (prefetch reach) inside
-  // the sequence, and none of the last K - 1 rows (gradient of the returned state)
-  const int64_t t_lo = tile * kRowsB;
-  const bool interior = tile > 0 && t_lo + kRowsB + 2 * kBatch + 3 <= a.L - (a.K - 1);
-  if (interior)
-    conv_bwd_tile<IO, FUSED, true>(a, b, tile, c);
-  else
-    conv_bwd_tile<IO, FUSED, false>(a, b, tile, c);
-}
-
-// Grid-stride over the (batch, tile, 4-channel) items: the grid is sized to what
-// the device holds at once, so no partial last round of workgroups.
+// One workgroup = (batch, kTileRows-row tile, kTileCh channels).  The tile's raw rows
+// (with the 3-row halo on each side) and its gradient rows (with 3 rows below) are
+// first loaded as 16-byte vectors, every load in flight at once, into LDS (the
+// gradient as fp32).  Then thread (channel cl, segment s) walks rows
+// [t_lo + 32 s, t_lo + 32 s + 32) with a register window: dpre of rows tau .. tau + 3
+// and raw rows tau - 3 .. tau + 3, so each row reads one raw and one gradient value
+// from LDS.  Rows outside the sequence are zero; tile 0 also produces the gradient of
+// the carried-in state rows (tau < 0), and the last K-1 rows add the gradient of the
+// returned state.  The dw / db sums of the four segments are added in segment order
+// and written as one partial per (batch, tile, channel).
 template <typename IO, bool FUSED>
 __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
-  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int64_t total = a.B * ntile * (a.C / 4);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; gid < total;
-       gid += stride)
-    conv_bwd_item<IO, FUSED>(a, gid);
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  constexpr int V = T::vec;                  // channels per 16-byte I/O vector
+  constexpr int RROWS = kTileRows + 6;       // raw rows t_lo - 3 .. t_lo + kTileRows + 2
+  constexpr int GROWS = kTileRows + 3;       // gradient rows t_lo .. t_lo + kTileRows + 2
+  constexpr int RVPR = kTileCh / V;          // raw vectors per row
+  constexpr int NRV = (RROWS * RVPR + 255) / 256;
+  constexpr int GVPR_F = kTileCh / 4;        // fp32 gradient vectors per row
+  constexpr int NGV = (GROWS * GVPR_F + 255) / 256;  // slots for the widest gradient case
+  static_assert(kTileRows == 4 * kSegRows, "four row segments per tile");
+  __shared__ __align__(16) E sR[RROWS * kTileCh];
+  __shared__ __align__(16) float sG[GROWS * kTileCh];
+
+  // channel blocks: the I/O-gradient channels [0, xlim) in blocks of kTileCh, then (fused)
+  // the fp32-gradient B / C channels [hp, C); a block never mixes the two
+  const int xlim = FUSED ? a.hp : a.C;
+  const int nxb = (xlim + kTileCh - 1) / kTileCh;
+  const int ncb = nxb + (FUSED ? (a.C - a.hp + kTileCh - 1) / kTileCh : 0);
+  const int64_t ntile = (a.L + kTileRows - 1) / kTileRows;
+  const int64_t wg = blockIdx.x;
+  const int cb = static_cast<int>(wg % ncb);
+  const int64_t tile = (wg / ncb) % ntile;
+  const int64_t b = wg / (static_cast<int64_t>(ncb) * ntile);
+  const bool from_f32 = FUSED && cb >= nxb;
+  const int c0 = from_f32 ? a.hp + (cb - nxb) * kTileCh : cb * kTileCh;
+  const int climit = from_f32 ? a.C : xlim;  // channels of this block: [c0, min(c0 + kTileCh, climit))
+  const int64_t t_lo = tile * kTileRows;
+  const int K = a.K;
+  const int tid = threadIdx.x;
+
+  // ---- raw rows -> sR (rows before the sequence from the carried state, after it zero)
+  {
+    const E* xb = static_cast<const E*>(a.x) + b * a.x_sb;
+    const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb : nullptr;
+    uint4 rr[NRV];
+#pragma unroll
+    for (int q = 0; q < NRV; ++q) {
+      const int k = min(tid + 256 * q, RROWS * RVPR - 1);
+      const int row = k / RVPR, cv = (k % RVPR) * V;
+      const int c = c0 + cv;
+      const int64_t t = t_lo - 3 + row;
+      const bool in_seq = t >= 0 && t < a.L;
+      const bool in_st = sb && t < 0 && t >= -(K - 1);
+      const bool ok = c < climit && (in_seq || in_st);
+      const int cc = c < climit ? c : c0;  // masked vectors read a valid address
+      const E* src = in_st ? sb + (t + K - 1) * a.st_st + cc : xb + (in_seq ? t : 0) * a.x_st + cc;
+      rr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(src));
+    }
+#pragma unroll
+    for (int q = 0; q < NRV; ++q) {
+      const int k = tid + 256 * q;
+      if (k < RROWS * RVPR) *reinterpret_cast<uint4*>(sR + (k / RVPR) * kTileCh + (k % RVPR) * V) = rr[q];
+    }
+  }
+  // ---- gradient rows -> sG (fp32): the I/O-typed view, or (fused, B / C channels)
+  // the fp32 group sums; rows outside the sequence zero
+  {
+    const int gvpr = from_f32 ? GVPR_F : kTileCh / V;
+    const int cw = from_f32 ? 4 : V;  // channels per vector
+    uint4 gr[NGV];
+#pragma unroll
+    for (int q = 0; q < NGV; ++q) {
+      const int k = min(tid + 256 * q, GROWS * gvpr - 1);
+      const int row = k / gvpr, cv = (k % gvpr) * cw;
+      const int c = c0 + cv;
+      const int64_t t = t_lo + row;
+      const bool ok = c < climit && t < a.L;
+      const int cc = c < climit ? c : c0;
+      const int64_t tt = t < a.L ? t : 0;
+      const void* src;
+      if (from_f32) {
+        const int gn = a.G * a.N, rel = cc - a.hp;
+        const bool isC = rel >= gn;
+        const int g = (isC ? rel - gn : rel) / a.N, n0 = (isC ? rel - gn : rel) % a.N;
+        src = a.dbc + ((static_cast<int64_t>(g) * a.per_g * a.B + b) * a.L + tt) * (2LL * a.N) + (isC ? a.N : 0) + n0;
+      } else if (FUSED) {
+        src = static_cast<const E*>(a.g) + (b * a.L + tt) * a.hp + cc;
+      } else {
+        src = static_cast<const E*>(a.g) + b * a.g_sb + tt * a.g_st + cc;
+      }
+      gr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(src));
+    }
+#pragma unroll
+    for (int q = 0; q < NGV; ++q) {
+      const int k = tid + 256 * q;
+      if (k < GROWS * gvpr) {
+        float* dst = sG + (k / gvpr) * kTileCh + (k % gvpr) * cw;
+        if (from_f32) {
+          *reinterpret_cast<uint4*>(dst) = gr[q];
+        } else {
+          float f[V];
+#pragma unroll
+          for (int v = 0; v < V; ++v) f[v] = raw_elem<IO>(gr[q], v);
+#pragma unroll
+          for (int v = 0; v < V; v += 4) *reinterpret_cast<float4*>(dst + v) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the thread's channel and row segment
+  const int cl = tid % kTileCh, seg = tid / kTileCh;
+  const int c = c0 + cl;
+  const bool cvalid = c < climit;
+  float w4[4], bias = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kk = j - (4 - K);  // taps right-aligned on 4: tap j reads row t - 3 + j
+    w4[j] = cvalid && kk >= 0 ? a.w[c * K + kk] : 0.f;
+  }
+  if (cvalid && a.bias) bias = a.bias[c];
+  const bool silu = a.silu != 0;
+  const int64_t r0 = t_lo + seg * kSegRows;
+  // output rows: the segment's rows inside the sequence; tile 0's first segment also
+  // the carried-state rows -(K-1) .. -1
+  const int64_t tau_b = (tile == 0 && seg == 0) ? -(K - 1) : r0;
+  const int64_t tau_e = r0 + kSegRows < a.L ? r0 + kSegRows : a.L;
+  auto raw_at = [&](int64_t t) -> float {
+    return t >= t_lo - 3 ? T::lds_to_f(sR[(t - t_lo + 3) * kTileCh + cl]) : 0.f;
+  };
+  auto dp_of = [&](int64_t t, const float* rw4) -> float {  // rw4: raw rows t-3 .. t
+    if (t < 0 || t >= a.L) return 0.f;
+    float pre = bias;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pre = fmaf(w4[j], rw4[j], pre);
+    const float gv = sG[(t - t_lo) * kTileCh + cl];
+    return silu ? gv * dsiluf_(pre) : gv;
+  };
+  float dw[4] = {0.f, 0.f, 0.f, 0.f}, db = 0.f;
+  if (cvalid && tau_b < tau_e) {
+    E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + c;
+    const E* dsob = a.dso ? static_cast<const E*>(a.dso) + b * a.dso_sb + c : nullptr;
+    E* dsib = a.dsi ? static_cast<E*>(a.dsi) + b * a.dsi_sb + c : nullptr;
+    // window: rw[i] = raw row tau - 3 + i (i < 7), d[i] = dpre of row tau + i (i < 4)
+    float rw[7], d[4];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) rw[i] = raw_at(tau_b - 3 + i);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) d[i] = dp_of(tau_b + i, rw + i);
+    for (int64_t tau = tau_b; tau < tau_e; ++tau) {
+      rw[6] = raw_at(tau + 3);
+      d[3] = dp_of(tau + 3, rw + 3);
+      float o = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o = fmaf(w4[j], d[3 - j], o);
+      const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
+      if (dsob && js >= 0) o += T::to_f(dsob[js * a.dso_st]);
+      if (tau >= 0) {
+        dxb[tau * a.dx_st] = T::from_f(o);
+        db += d[0];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dw[j] = fmaf(d[0], rw[j], dw[j]);
+      } else if (dsib) {
+        dsib[(tau + K - 1) * a.dsi_st] = T::from_f(o);
+      }
+#pragma unroll
+      for (int i = 0; i < 6; ++i) rw[i] = rw[i + 1];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) d[i] = d[i + 1];
+    }
+  }
+  // ---- dw / db: the four segments in order, one partial per (batch, tile, channel);
+  // the sums go through the raw tile's LDS once every thread is done with it
+  __syncthreads();
+  float* sPart = reinterpret_cast<float*>(sR);  // [4 segments][5][kTileCh]
+  static_assert(4 * 5 * kTileCh * sizeof(float) <= sizeof(sR), "partials fit the raw tile");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sPart[(seg * 5 + j) * kTileCh + cl] = dw[j];
+  sPart[(seg * 5 + 4) * kTileCh + cl] = db;
+  __syncthreads();
+  if (seg == 0 && cvalid) {
+    float* pp = a.part + ((b * ntile + tile) * a.C + c) * 5;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const float v = ((sPart[j * kTileCh + cl] + sPart[(5 + j) * kTileCh + cl]) + sPart[(10 + j) * kTileCh + cl]) +
+                      sPart[(15 + j) * kTileCh + cl];
+      const int kk = j - (4 - K);
+      if (j == 4)
+        pp[4] = v;
+      else if (kk >= 0)
+        pp[kk] = v;
+    }
+  }
 }
 
 // dw[c][k], db[c]: ordered sums of the per-(batch, tile) partials ([n_bt][C][5])
@@ -419,29 +349,28 @@ __global__ void __launch_bounds__(256) conv_params_kernel(const float* part, int
 }
 
 template <typename IO, bool FUSED>
-void launch_conv_bwd_kernel(const ConvBwdArgs& a, int64_t n, hipStream_t s) {
-  const int64_t cap = resident_blocks(reinterpret_cast<const void*>(conv_bwd_kernel<IO, FUSED>), 256);
-  int64_t blocks = (n + 255) / 256;
-  if (cap > 0 && blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((conv_bwd_kernel<IO, FUSED>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     s, a);
+void launch_conv_bwd_kernel(const ConvBwdArgs& a, hipStream_t s) {
+  const int64_t ntile = (a.L + kTileRows - 1) / kTileRows;
+  const int xlim = FUSED ? a.hp : a.C;
+  const int64_t ncb = (xlim + kTileCh - 1) / kTileCh + (FUSED ? (a.C - a.hp + kTileCh - 1) / kTileCh : 0);
+  const int64_t blocks = a.B * ntile * ncb;
+  hipLaunchKernelGGL((conv_bwd_kernel<IO, FUSED>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
 }
 
 hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* db, int accumulate,
                         hipStream_t s) {
-  const int64_t ntile = (a.L + kRowsB - 1) / kRowsB;
-  const int64_t n = a.B * ntile * (a.C / 4);
+  const int64_t ntile = (a.L + kTileRows - 1) / kTileRows;
   TimingScope ts(kKConvBwd, s);
   if (bf16) {
     if (fused)
-      launch_conv_bwd_kernel<bf16_t, true>(a, n, s);
+      launch_conv_bwd_kernel<bf16_t, true>(a, s);
     else
-      launch_conv_bwd_kernel<bf16_t, false>(a, n, s);
+      launch_conv_bwd_kernel<bf16_t, false>(a, s);
   } else {
     if (fused)
-      launch_conv_bwd_kernel<float, true>(a, n, s);
+      launch_conv_bwd_kernel<float, true>(a, s);
     else
-      launch_conv_bwd_kernel<float, false>(a, n, s);
+      launch_conv_bwd_kernel<float, false>(a, s);
   }
   hipLaunchKernelGGL(conv_params_kernel, dim3(static_cast<unsigned>((a.C * 5 + kWave - 1) / kWave)),
                      dim3(256), 0, s, a.part, a.B * ntile, a.C, a.K, dw, db, accumulate);
@@ -451,7 +380,7 @@ hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* d
 }  // namespace
 
 size_t conv_bwd_partials_bytes(int64_t B, int64_t L, int64_t C) {
-  const int64_t ntile = (L + kRowsB - 1) / kRowsB;
+  const int64_t ntile = (L + kTileRows - 1) / kTileRows;
   return static_cast<size_t>(B) * ntile * C * 5 * sizeof(float);
 }
 
