@@ -12,8 +12,8 @@
 // registers and the 16 output rows are stored as 16-byte vectors.  Adjacent threads
 // take adjacent channel vectors, so every row access is coalesced.
 //
-// Backward: one workgroup per (batch, 128-row tile, 64 channels) stages the tile's raw
-// and gradient rows in LDS (all loads in flight at once), then each thread walks 32
+// Backward: one workgroup per (batch, 64-row tile, 64 channels) stages the tile's raw
+// and gradient rows in LDS (all loads in flight at once), then each thread walks 16
 // rows of one channel with a sliding register window; dpre = dout * silu'(pre) is
 // recomputed from the raw rows, dx[tau] = sum_k dpre[tau + K-1-k] w[k] (plus the
 // gradient of the returned conv state for the last K-1 rows), and per-tile partial
@@ -26,9 +26,9 @@ namespace ssd {
 namespace {
 
 constexpr int kRowsF = 16;     // rows per thread, forward
-constexpr int kTileRows = 128; // rows per workgroup, backward
+constexpr int kTileRows = 64;  // rows per workgroup, backward
 constexpr int kTileCh = 64;    // channels per workgroup, backward
-constexpr int kSegRows = 32;   // rows per thread, backward (four segments per tile)
+constexpr int kSegRows = 16;   // rows per thread, backward (four segments per tile)
 
 struct ConvFwdArgs {
   int64_t B, L;
@@ -140,7 +140,7 @@ struct ConvBwdArgs {
 // (with the 3-row halo on each side) and its gradient rows (with 3 rows below) are
 // first loaded as 16-byte vectors, every load in flight at once, into LDS (the
 // gradient as fp32).  Then thread (channel cl, segment s) walks rows
-// [t_lo + 32 s, t_lo + 32 s + 32) with a register window: dpre of rows tau .. tau + 3
+// [t_lo + kSegRows s, t_lo + kSegRows (s + 1)) with a register window: dpre of rows tau .. tau + 3
 // and raw rows tau - 3 .. tau + 3, so each row reads one raw and one gradient value
 // from LDS.  Rows outside the sequence are zero; tile 0 also produces the gradient of
 // the carried-in state rows (tau < 0), and the last K-1 rows add the gradient of the
