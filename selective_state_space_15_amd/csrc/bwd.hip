@@ -672,13 +672,11 @@ hipError_t launch_bwd(const Problem& pr_in, const BwdIn& in, const BwdOut& o, vo
   char* ws = static_cast<char*>(ws_v);
   const BwdLayout l = bwd_layout(pr);
   if (pr.K > 0) {
-    const hipError_t e = launch_bc_prepass(pr, ws + l.bc, ws + l.bc_lo, s);
+    const hipError_t e = launch_xbc_prepass(pr, ws + l.xp, ws + l.bc, ws + l.bc_lo, s);
     if (e != hipSuccess) return e;
     const int64_t gn2 = 2LL * pr.G * pr.N;
     pr.bc = View{ws + l.bc, pr.L * gn2, gn2};
     if (pr.bf16) pr.bc_lo = View{ws + l.bc_lo, pr.L * gn2, gn2};
-    const hipError_t e2 = launch_x_prepass(pr, ws + l.xp, s);
-    if (e2 != hipSuccess) return e2;
     const int64_t hp = static_cast<int64_t>(pr.H) * pr.P;
     pr.xp = View{ws + l.xp, pr.L * hp, hp};
   }

@@ -45,6 +45,12 @@ struct ConvFwdArgs {
   int64_t o_sb, o_st;
   int o_c0;
   void* out_lo;  // optional: out value minus its rounding to the I/O dtype (same layout)
+  // channels c >= split (relative to x_c0) go to out2 at channel c - split instead
+  // (with out2_lo as out_lo); split >= C: everything goes to out
+  int split;
+  void* out2;
+  int64_t o2_sb, o2_st;
+  void* out2_lo;
 };
 
 template <typename IO>
@@ -87,7 +93,12 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
       w4[j][v] = kk >= 0 ? a.w[(c + v) * K + kk] : 0.f;
     }
   }
-  E* ob = static_cast<E*>(a.out) + b * a.o_sb + a.o_c0 + c;
+  const bool second = c >= a.split;  // a vector never straddles the split (split % V == 0)
+  E* ob = second ? static_cast<E*>(a.out2) + b * a.o2_sb + (c - a.split)
+                 : static_cast<E*>(a.out) + b * a.o_sb + a.o_c0 + c;
+  E* olb = second ? (a.out2_lo ? static_cast<E*>(a.out2_lo) + b * a.o2_sb + (c - a.split) : nullptr)
+                  : (a.out_lo ? static_cast<E*>(a.out_lo) + b * a.o_sb + a.o_c0 + c : nullptr);
+  const int64_t ost = second ? a.o2_st : a.o_st;
 #pragma unroll
   for (int r = 0; r < kRowsF; ++r) {
     const int64_t t = t0 + r;
@@ -100,12 +111,12 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
         for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(in[r + j], v), pre);
         o[v] = a.silu ? siluf_(pre) : pre;
       }
-      store_vec16<IO>(ob + t * a.o_st, o);
-      if (a.out_lo) {
+      store_vec16<IO>(ob + t * ost, o);
+      if (olb) {
         float lo[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
-        store_vec16<IO>(static_cast<E*>(a.out_lo) + b * a.o_sb + a.o_c0 + c + t * a.o_st, lo);
+        store_vec16<IO>(olb + t * ost, lo);
       }
     }
   }
@@ -467,6 +478,7 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
                                  MView out, int o_c0, hipStream_t s, void* out_lo) {
   ConvFwdArgs a{};
   a.out_lo = out_lo;
+  a.split = C;  // one output
   a.B = B;
   a.L = L;
   a.C = C;
@@ -518,12 +530,43 @@ size_t x_prepass_bytes(const Problem& pr) {
   return (n + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s) {
+hipError_t launch_xbc_prepass(const Problem& pr, void* xp, void* bc, void* bc_lo, hipStream_t s) {
   TimingScope ts(kKBcPrepass, s);
-  const int hp = pr.H * pr.P;
-  const MView out{dst, pr.L * hp, hp};
-  return launch_conv_fwd_range(pr.bf16, pr.B, pr.L, hp, pr.K, 1, pr.xbc, 0, pr.cs_in, 0, pr.conv_w,
-                               pr.conv_b, out, 0, s, nullptr);
+  const int hp = pr.H * pr.P, gn2 = 2 * pr.G * pr.N, C = hp + gn2;
+  ConvFwdArgs a{};
+  a.B = pr.B;
+  a.L = pr.L;
+  a.C = C;
+  a.K = pr.K;
+  a.silu = 1;
+  a.x = pr.xbc.p;
+  a.x_sb = pr.xbc.sb;
+  a.x_st = pr.xbc.st;
+  a.x_c0 = 0;
+  a.st = pr.cs_in.p;
+  a.st_sb = pr.cs_in.sb;
+  a.st_st = pr.cs_in.st;
+  a.st_c0 = 0;
+  a.w = pr.conv_w;
+  a.bias = pr.conv_b;
+  a.out = xp;
+  a.o_sb = pr.L * hp;
+  a.o_st = hp;
+  a.o_c0 = 0;
+  a.out_lo = nullptr;
+  a.split = hp;
+  a.out2 = bc;
+  a.o2_sb = pr.L * gn2;
+  a.o2_st = gn2;
+  a.out2_lo = pr.bf16 ? bc_lo : nullptr;
+  const int V = pr.bf16 ? 8 : 4;
+  const int64_t n = pr.B * ((pr.L + kRowsF - 1) / kRowsF) * (C / V);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (pr.bf16)
+    hipLaunchKernelGGL(conv_fwd_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(conv_fwd_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s) {

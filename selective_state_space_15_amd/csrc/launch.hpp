@@ -135,8 +135,10 @@ size_t bc_prepass_bytes(const Problem& pr);
 // Workgroups of `threads` threads of `kernel` resident on the current device at once
 // (all CUs; cached per device and kernel); 0 if the runtime cannot tell.
 int64_t resident_blocks(const void* kernel, int threads);
-// Post-conv x channels [B][L][H*P] (I/O dtype) for the backward's chunk loaders.
-hipError_t launch_x_prepass(const Problem& pr, void* dst, hipStream_t s);
+// Both pre-passes of the backward in one launch: post-conv x channels -> xp
+// ([B][L][H*P]), post-conv B|C -> bc ([B][L][2GN]) and (bf16 I/O) its rounding
+// residual -> bc_lo.
+hipError_t launch_xbc_prepass(const Problem& pr, void* xp, void* bc, void* bc_lo, hipStream_t s);
 size_t x_prepass_bytes(const Problem& pr);
 size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);
 hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,
