@@ -79,7 +79,13 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   // need them transposed read them with LDS transpose loads
   __shared__ __align__(16) Lt sB[kQ * ldN];
   __shared__ __align__(16) Lt sXw[kQ * ldP];
-  __shared__ __align__(16) Lt sC[OUT ? kQ * ldN : 8];
+  // the C tile; in the output epilogue (C is dead by then) it holds y + D x as fp32
+  constexpr int ldY = P + 4;
+  constexpr size_t kCBytes = OUT ? kQ * ldN * sizeof(Lt) : 16;
+  constexpr size_t kYBytes = OUT ? kQ * ldY * sizeof(float) : 16;
+  __shared__ __align__(16) char sCY[kCBytes > kYBytes ? kCBytes : kYBytes];
+  Lt* sC = reinterpret_cast<Lt*>(sCY);
+  float* sY = reinterpret_cast<float*>(sCY);
   __shared__ __align__(16) Lt sX[OUT ? kQ * ldP : 8];
   __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
   __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
@@ -155,36 +161,24 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   constexpr int RBL = 8 / HALVES;           // B/C rows per loader task
   ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL, !OUT> ld;
   float dt_raw = 0.f;
-  // gate inputs of this lane's output elements (rows m0 + 4*(lane/16) + e,
-  // columns 16*(YJ*half + j) + lane%16), kept as raw I/O bits (bf16: two per register)
-  constexpr int ZPR = sizeof(E) == 2 ? 2 : 1;
-  uint32_t zv[OUT ? YJ : 1][4 / ZPR];
+  // gate inputs of this thread's output vectors (row k / (P / V), columns
+  // V (k % (P / V)) for k = tid + NTHR q), loaded one chunk phase ahead as 16-byte rows
+  constexpr int NYV = (kQ * P / V + NTHR - 1) / NTHR;
+  uint4 zr[OUT ? NYV : 1];
+  // without a gate the (unused) loads read x rows, which are always valid
+  const E* zsrc = zp ? zp : static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
+  const int64_t zst = zp ? pr.z.st : pr.xbc.st;
   auto prefetch_z = [&](int64_t tn) {
     if constexpr (OUT) {
 #pragma unroll
-      for (int j = 0; j < YJ; ++j)
-#pragma unroll
-        for (int e2 = 0; e2 < 4 / ZPR; ++e2) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int q = 0; q < ZPR; ++q) {
-            const int64_t tg = tn + m0 + acc_row(e2 * ZPR + q);
-            const E v = (zp && tg < pr.L) ? zp[tg * pr.z.st + 16 * (YJ * half + j) + acc_col()] : E(0);
-            if constexpr (ZPR == 2)
-              word |= static_cast<uint32_t>(v) << (16 * q);
-            else
-              word = __float_as_uint(v);
-          }
-          zv[j][e2] = word;
-        }
+      for (int q = 0; q < NYV; ++q) {
+        const int k = min(static_cast<int>(threadIdx.x) + NTHR * q, kQ * P / V - 1);
+        const int r = k / (P / V), col = (k % (P / V)) * V;
+        const bool ok = zp && tn + r < pr.L;
+        const int64_t t = ok ? tn + r : 0;  // masked rows read a valid row
+        zr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(zsrc + t * zst + col));
+      }
     }
-  };
-  auto zval = [&](int j, int e) -> float {
-    const uint32_t w = zv[j][e / ZPR];
-    if constexpr (ZPR == 2)
-      return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-    else
-      return __uint_as_float(w);
   };
   // dt is prefetched one chunk ahead; the row loads are issued right before use
   // (holding them across the MFMA phase costs more registers than 2 waves/SIMD allow)
@@ -274,19 +268,32 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       }
       __syncthreads();
       mma_strip<Lt, true, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
-      // y = Ydiag + exp(cs_t) Yoff + D x;  out = y * silu(z)
+      // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
+      // out = y * silu(z) on 16-byte rows
       const float Dh = pr.D ? pr.D[h] : 0.f;
-      E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
-        const int64_t tg = t0 + t;
 #pragma unroll
         for (int j = 0; j < YJ; ++j) {
           const int p = 16 * (YJ * half + j) + acc_col();
-          float y = yacc[j][e] + Dh * T::lds_to_f(sX[t * ldP + p]);
-          if (gate) y *= siluf_(zval(j, e));
-          if (tg < pr.L) op[tg * a.out.st + p] = T::from_f(y);
+          sY[t * ldY + p] = yacc[j][e] + Dh * T::lds_to_f(sX[t * ldP + p]);
+        }
+      }
+      __syncthreads();
+      E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
+#pragma unroll
+      for (int q = 0; q < NYV; ++q) {
+        const int k = static_cast<int>(threadIdx.x) + NTHR * q;
+        const int r = k / (P / V), col = (k % (P / V)) * V;
+        if ((kQ * P / V) % NTHR == 0 || k < kQ * P / V) {
+          float y[V];
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            y[v] = sY[r * ldY + col + v];
+            if (gate) y[v] *= siluf_(raw_elem<IO>(zr[q], v));
+          }
+          if (t0 + r < pr.L) store_vec16<IO>(op + (t0 + r) * a.out.st + col, y);
         }
       }
     }
