@@ -42,6 +42,8 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+constexpr int kMaxHeadBlock = 8;  // heads per bwd_main workgroup, at most
+
 struct BwdArgs {
   Problem pr;
   int64_t nch;
@@ -131,6 +133,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   __shared__ float s_dt[kQ], s_cs[kQ], s_sig[kQ], s_dq[kQ];
   __shared__ float s_row[kQ], s_yo[kQ], s_v[kQ], s_col[4][kQ];
   __shared__ float s_red[2][4];
+  __shared__ float s_par[3][kMaxHeadBlock];  // A, D, dt_bias of the block's heads
 
   const Problem& pr = a.pr;
   const int64_t total = static_cast<int64_t>(pr.B) * a.nch * a.nhb;
@@ -161,39 +164,47 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   const bool xpre = pr.xp.p != nullptr;
   const E* xs_p = static_cast<const E*>(xpre ? pr.xp.p : pr.xbc.p);
   const int64_t xs_sb = xpre ? pr.xp.sb : pr.xbc.sb, xs_st = xpre ? pr.xp.st : pr.xbc.st;
+  // Every load is unconditional, from a clamped (valid) address, and nothing uses the
+  // loaded values before stage(): rows past the end are zeroed there.  A select right
+  // after a load would make the wave wait for it at the point of issue.
+  const bool gate = pr.z.p != nullptr;
   auto prefetch = [&](int h) {
-    if (wave == 0)
-      pf_dt = t0 + lane < pr.L ? static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h]
-                               : E{};
+    if (wave == 0) {
+      const int64_t t = t0 + lane < pr.L ? t0 + lane : pr.L - 1;
+      pf_dt = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h];
+    }
     const E* xq = xs_p + b * xs_sb + h * P;
     const E* dq = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-    const E* zq = pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
+    // without a gate the z loads repeat the dout loads (and are not used)
+    const E* zq = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : dq;
+    const int64_t zst = gate ? pr.z.st : a.dout.st;
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
       const int i = threadIdx.x + q * kThreads;
       const int r = i / (P / V), cl = (i % (P / V)) * V;
-      // rows past the end load row t0 (always valid) and are zeroed after the load,
-      // so every load is unconditional
-      const bool ok = t0 + r < pr.L;
-      const int64_t t = ok ? t0 + r : t0;
-      pf_x[q] = keep_if(ok, *reinterpret_cast<const uint4*>(xq + t * xs_st + cl));
-      pf_do[q] = keep_if(ok, *reinterpret_cast<const uint4*>(dq + t * a.dout.st + cl));
-      pf_z[q] = make_uint4(0u, 0u, 0u, 0u);
-      if (zq) pf_z[q] = keep_if(ok, *reinterpret_cast<const uint4*>(zq + t * pr.z.st + cl));
+      const int64_t t = t0 + r < pr.L ? t0 + r : t0;
+      pf_x[q] = *reinterpret_cast<const uint4*>(xq + t * xs_st + cl);
+      pf_do[q] = *reinterpret_cast<const uint4*>(dq + t * a.dout.st + cl);
+      pf_z[q] = *reinterpret_cast<const uint4*>(zq + t * zst + cl);
     }
     const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
     const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
-      const int i = (threadIdx.x + q * kThreads) * 4;
-      hv[q] = gv[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < P * N) {
-        hv[q] = *reinterpret_cast<const float4*>(Hg + i);
-        gv[q] = *reinterpret_cast<const float4*>(dHg + i);
-      }
+      const int i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
+      hv[q] = *reinterpret_cast<const float4*>(Hg + i);
+      gv[q] = *reinterpret_cast<const float4*>(dHg + i);
     }
   };
   prefetch(h_first);
+  // the block's per-head parameters, read once (a load right where a head needs them
+  // would stall that head on its latency)
+  if (threadIdx.x < a.hb_heads) {
+    const int h = h_first + threadIdx.x;
+    s_par[0][threadIdx.x] = pr.A[h];
+    s_par[1][threadIdx.x] = pr.D ? pr.D[h] : 0.f;
+    s_par[2][threadIdx.x] = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+  }
 
   // B and C rows of the group (post-conv), shared by every head of the block
   conv_rows<IO, P, N, false, true, true>(pr, b, 0, g, t0, [&](int seg, int s, int cl, const float* o) {
@@ -223,15 +234,15 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
 
   for (int hh = 0; hh < a.hb_heads; ++hh) {
     const int h = h_first + hh;
-    const float Ah = pr.A[h];
-    const float Dh = pr.D ? pr.D[h] : 0.f;
+    const float Ah = s_par[0][hh];
+    const float Dh = s_par[1][hh];
     // ---- stage head h from the prefetch registers into LDS
     // (1) dt, cs, softplus slope, chunk-state decays (wave 0)
     if (wave == 0) {
       const int64_t t = t0 + lane;
       float dtv = 0.f, sig = 1.f;
       if (t < pr.L) {
-        const float u = T::to_f(pf_dt) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+        const float u = T::to_f(pf_dt) + s_par[2][hh];
         dtv = pr.softplus ? softplusf_(u) : u;
         sig = pr.softplus ? sigmoidf_(u) : 1.f;
       }
@@ -247,13 +258,14 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     for (int q = 0; q < NXV; ++q) {
       const int i = threadIdx.x + q * kThreads;
       const int r = i / (P / V), cl = (i % (P / V)) * V;
-      *reinterpret_cast<uint4*>(sX + r * ldP + cl) = pf_x[q];
+      const bool ok = t0 + r < pr.L;  // rows past the end are zero
+      *reinterpret_cast<uint4*>(sX + r * ldP + cl) = keep_if(ok, pf_x[q]);
       float dy[V], lo[V], g2[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const float dv = raw_elem<IO>(pf_do[q], v), zv = raw_elem<IO>(pf_z[q], v);
-        dy[v] = pr.z.p ? dv * siluf_(zv) : dv;
-        g2[v] = pr.z.p ? dv * dsiluf_(zv) : 0.f;
+        dy[v] = ok ? (gate ? dv * siluf_(zv) : dv) : 0.f;
+        g2[v] = ok && gate ? dv * dsiluf_(zv) : 0.f;
         lo[v] = dy[v] - T::to_f(T::from_f(dy[v]));
       }
       lds_put_row<IO>(sDY + r * ldP + cl, dy);
@@ -561,7 +573,7 @@ BwdLayout bwd_layout(const Problem& pr) {
   l.nch = (pr.L + kQ - 1) / kQ;
   const int hpg = pr.H / pr.G;
   int hb = 1;
-  for (int d = 1; d <= 8; ++d)
+  for (int d = 1; d <= kMaxHeadBlock; ++d)
     if (hpg % d == 0) hb = d;
   l.hb_heads = hb;
   l.nhb = pr.H / hb;
