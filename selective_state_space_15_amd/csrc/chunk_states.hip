@@ -97,17 +97,21 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
   uint4 dvr[NDT], zvr[DS ? NDT : 1];
   const View rows = DS ? a.dout : (pr.K > 0 ? pr.xp : pr.xbc);  // x channels lead xbc rows
   const E* dbase = static_cast<const E*>(rows.p) + b * rows.sb;
-  const E* zbase = DS && pr.z.p ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : nullptr;
+  const bool gate = DS && pr.z.p != nullptr;
+  // without a gate the z loads repeat the dout loads (and are not used)
+  const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
+  const int64_t zst = gate ? pr.z.st : rows.st;
+  // The loads are unconditional, from clamped (valid) rows, and their values are first
+  // used when the head is staged, where rows past the end are zeroed: a select right
+  // after a load would make the wave wait for it at the point of issue.
   auto issue_head = [&](int h) {
 #pragma unroll
     for (int q = 0; q < NDT; ++q) {
-      const int task = threadIdx.x + q * NTHR;
+      const int task = min(static_cast<int>(threadIdx.x) + q * NTHR, (P / V) * kQ - 1);
       const int col = (task % (P / V)) * V, r = task / (P / V);
-      const bool ok = task < (P / V) * kQ && (interior || t0 + r < pr.L);
-      const int64_t t = ok ? t0 + r : t0;  // masked vectors read a valid row
-      dvr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col));
-      if constexpr (DS)
-        if (zbase) zvr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(zbase + t * pr.z.st + h * P + col));
+      const int64_t t = interior || t0 + r < pr.L ? t0 + r : t0;
+      dvr[q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col);
+      if constexpr (DS) zvr[q] = *reinterpret_cast<const uint4*>(zbase + t * zst + h * P + col);
     }
   };
   issue_head(hfirst);
@@ -157,16 +161,17 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
       const int task = threadIdx.x + q * NTHR;
       if (task >= (P / V) * kQ) continue;
       const int col = (task % (P / V)) * V, r = task / (P / V);
+      const bool ok = interior || t0 + r < pr.L;  // rows past the end are zero
       const float sc = s_w[hh][r];
       float o[V], lo[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const float dv = raw_elem<IO>(dvr[q], v);
         if constexpr (DS) {
-          o[v] = (zbase ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * sc;
+          o[v] = ok ? (gate ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * sc : 0.f;
           lo[v] = o[v] - T::to_f(T::from_f(o[v]));
         } else {
-          o[v] = dv * sc;
+          o[v] = ok ? dv * sc : 0.f;
         }
       }
       lds_put_row<IO>(A + r * ldP + col, o);

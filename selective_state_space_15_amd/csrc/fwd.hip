@@ -174,9 +174,10 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       for (int q = 0; q < NYV; ++q) {
         const int k = min(static_cast<int>(threadIdx.x) + NTHR * q, kQ * P / V - 1);
         const int r = k / (P / V), col = (k % (P / V)) * V;
-        const bool ok = zp && tn + r < pr.L;
-        const int64_t t = ok ? tn + r : 0;  // masked rows read a valid row
-        zr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(zsrc + t * zst + col));
+        // rows past the end read row 0 and are never stored; no select after the
+        // load, so it stays in flight until the epilogue
+        const int64_t t = tn + r < pr.L ? tn + r : 0;
+        zr[q] = *reinterpret_cast<const uint4*>(zsrc + t * zst + col);
       }
     }
   };
