@@ -149,9 +149,11 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   const int64_t PN = static_cast<int64_t>(P) * N;
 
   // Every global input of a head (dt, post-conv x rows, dout, z, H_{c-1}, dH_c) is
-  // loaded into registers by prefetch(), issued for head h+1 while head h runs its
-  // last MFMA phase, and moved into LDS by stage() at the start of head h+1, so the
-  // memory latency of a head hides behind the previous head's compute.
+  // loaded into registers by prefetch(), issued for head h+1 in three parts while
+  // head h runs its last three MFMA phases (dt / x / dout / z, then H, then dH: one
+  // burst of all 23 loads per thread stalls the wave on the memory pipeline), and
+  // moved into LDS at the start of head h+1, so the memory latency of a head hides
+  // behind the previous head's compute.
   constexpr int V = T::vec;
   constexpr int NXV = P * kQ / (V * kThreads);  // 16-byte row vectors per thread
   static_assert(P * kQ % (V * kThreads) == 0, "the x / dout tiles must tile the block");
@@ -168,8 +170,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   // loaded values before stage(): rows past the end are zeroed there.  A select right
   // after a load would make the wave wait for it at the point of issue.
   const bool gate = pr.z.p != nullptr;
-  auto prefetch = [&](int h) {
-    if (wave == 0) {
+  auto prefetch = [&](int h, int part) {
+    if (part == 0 && wave == 0) {
       const int64_t t = t0 + lane < pr.L ? t0 + lane : pr.L - 1;
       pf_dt = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h];
     }
@@ -178,6 +180,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     // without a gate the z loads repeat the dout loads (and are not used)
     const E* zq = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : dq;
     const int64_t zst = gate ? pr.z.st : a.dout.st;
+    if (part == 0)
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
       const int i = threadIdx.x + q * kThreads;
@@ -192,11 +195,13 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
       const int i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
-      hv[q] = *reinterpret_cast<const float4*>(Hg + i);
-      gv[q] = *reinterpret_cast<const float4*>(dHg + i);
+      if (part == 1) hv[q] = *reinterpret_cast<const float4*>(Hg + i);
+      if (part == 2) gv[q] = *reinterpret_cast<const float4*>(dHg + i);
     }
   };
-  prefetch(h_first);
+  prefetch(h_first, 0);
+  prefetch(h_first, 1);
+  prefetch(h_first, 2);
   // the block's per-head parameters, read once (a load right where a head needs them
   // would stall that head on its latency)
   if (threadIdx.x < a.hb_heads) {
@@ -399,7 +404,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     __syncthreads();
 
     // the next head's inputs go in flight now, behind the remaining MFMA work
-    if (hh + 1 < a.hb_heads) prefetch(h + 1);
+    if (hh + 1 < a.hb_heads) prefetch(h + 1, 0);
     // (c) dx rows s = m0..: Mt^T dY + exp(cs_Q - cs_s) dt_s B dH^T + D dy
     {
       f32x4 dxd[PJ], dxs[PJ];
@@ -424,6 +429,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         }
       }
     }
+    if (hh + 1 < a.hb_heads) prefetch(h + 1, 1);
     // (d) dB rows s: W^T C + exp(cs_Q - cs_s) dt_s (X dH); chunk-state dcs term
     {
       f32x4 U[NTn];
@@ -449,6 +455,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) s_v[m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
       mma_strip<Lt, false, false, NTn, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, 0, kQ);
     }
+    if (hh + 1 < a.hb_heads) prefetch(h + 1, 2);
     // (e) dC rows t: W B + exp(cs_t) dY H
     {
       mma_strip<Lt, true, false, NTn, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, 0, kQ);
