@@ -53,6 +53,8 @@
  *                                 as xbc rows, so the previous segment's last K-1
  *                                 input rows can be passed as a view.
  *              conv weight:       [Cd][K]; w[c][K-1] multiplies the current token.
+ *                                 Weight and bias base pointers 16-byte aligned
+ *                                 (SSD_ERR_ALIGN otherwise).
  *   Errors     Every call returns ssd_status.  All validation happens before any
  *              launch; nothing is enqueued on error.  Launch failures return
  *              SSD_ERR_HIP with detail in ssd_last_error() (thread-local).

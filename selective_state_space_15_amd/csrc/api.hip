@@ -42,6 +42,12 @@ ssd_status check_state(const void* p, const char* name) {
   return SSD_OK;
 }
 
+// conv weights and bias are read as 16-byte vectors
+ssd_status check_param16(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(SSD_ERR_ALIGN, "%s: pointer not 16-byte aligned", name);
+  return SSD_OK;
+}
+
 // A [B, T, C] activation view.  vec: 16-byte rule (vector loads); else element rule.
 ssd_status check_view(const ssd_view& v, const char* name, ssd_dtype io, bool required, bool vec,
                       int64_t T, int64_t C) {
@@ -160,6 +166,8 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
   if (!A) return fail(SSD_ERR_NULL, "A: NULL");
   if (K > 0) {
     if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+    TRY(check_param16(conv_w, "conv_w"));
+    TRY(check_param16(conv_b, "conv_b"));
     TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));
     TRY(check_view(conv_state_out, "conv_state_out", io, false, true, K - 1, Cd));
   }
@@ -231,6 +239,8 @@ ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
   TRY(check_state(dh0, "dh0"));
   if (K > 0) {
     if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+    TRY(check_param16(conv_w, "conv_w"));
+    TRY(check_param16(conv_b, "conv_b"));
     TRY(check_view(conv_state_in, "conv_state_in", io, false, true, K - 1, Cd));
     TRY(check_view(dconv_state_out, "dconv_state_out", io, false, true, K - 1, Cd));
     TRY(check_view(dconv_state_in, "dconv_state_in", io, false, true, K - 1, Cd));
@@ -317,6 +327,8 @@ ssd_status conv1d_fwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
   TRY(check_view(state_in, "state_in", io, false, true, width - 1, channels));
   TRY(check_view(state_out, "state_out", io, false, true, width - 1, channels));
   if (!w) return fail(SSD_ERR_NULL, "w: NULL");
+  TRY(check_param16(w, "w"));
+  TRY(check_param16(b, "b"));
   const ssd::ConvProblem cp = make_conv(batch, seqlen, channels, width, io, x, w, b, silu, state_in);
   const hipError_t e = ssd::launch_conv_fwd(cp, mv(out), mv(state_out), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "conv1d_fwd launch");
@@ -346,6 +358,8 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
   TRY(check_view(dstate_in, "dstate_in", io, false, true, width - 1, channels));
   if (!w) return fail(SSD_ERR_NULL, "w: NULL");
   if (!dw) return fail(SSD_ERR_NULL, "dw: NULL");
+  TRY(check_param16(w, "w"));
+  TRY(check_param16(b, "b"));
   const size_t need = ssd::conv_bwd_workspace_bytes(batch, seqlen, channels);
   if (!ws || ws_bytes < need)
     return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);

@@ -53,11 +53,16 @@ struct ConvFwdArgs {
   void* out2_lo;
 };
 
-template <typename IO>
+// K is a template parameter so that every load is straight-line code: a load under a
+// branch, a select right after a load, or control flow that merges registers with
+// loads in flight makes the compiler wait for every outstanding memory operation
+// (the previous rows' stores included) inside each output row.
+template <typename IO, int K>
 __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
   using T = io_traits<IO>;
   using E = typename T::elem;
   constexpr int V = T::vec;
+  static_assert(K >= 1 && K <= 4, "taps are right-aligned on 4");
   const int ncv = a.C / V;
   const int64_t ntile = (a.L + kRowsF - 1) / kRowsF;
   const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
@@ -66,58 +71,100 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
   const int64_t tile = (gid / ncv) % ntile;
   const int64_t b = gid / (static_cast<int64_t>(ncv) * ntile);
   const int c = cv * V;
-  const int K = a.K;
   const int64_t t0 = tile * kRowsF;
   const E* xb = static_cast<const E*>(a.x) + b * a.x_sb + a.x_c0 + c;
-  const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb + a.st_c0 + c : nullptr;
+  const bool has_st = a.st != nullptr;
+  const E* sb = has_st ? static_cast<const E*>(a.st) + b * a.st_sb + a.st_c0 + c : xb;
+  const int64_t sst = has_st ? a.st_st : 0;
 
-  uint4 in[kRowsF + 3];  // raw rows t0-3 .. t0+15
+  // weights of the V channels: [C][K] rows of consecutive channels are contiguous, V*K
+  // floats from a 16-byte aligned offset (the pointer is checked 16-byte aligned)
+  constexpr int NWV = V * K / 4;
+  float wf[V * K];
+  {
+    const float4* wv = reinterpret_cast<const float4*>(a.w + static_cast<int64_t>(c) * K);
+#pragma unroll
+    for (int q = 0; q < NWV; ++q) {
+      const float4 v4 = wv[q];
+      wf[4 * q] = v4.x;
+      wf[4 * q + 1] = v4.y;
+      wf[4 * q + 2] = v4.z;
+      wf[4 * q + 3] = v4.w;
+    }
+  }
+  const bool has_bias = a.bias != nullptr;
+  const float* bp = has_bias ? a.bias + c : a.w;  // any valid address without a bias
+  float bias_raw[V];
+#pragma unroll
+  for (int v = 0; v < V; v += 4) {
+    const float4 v4 = *reinterpret_cast<const float4*>(bp + v);
+    bias_raw[v] = v4.x;
+    bias_raw[v + 1] = v4.y;
+    bias_raw[v + 2] = v4.z;
+    bias_raw[v + 3] = v4.w;
+  }
+  // raw rows t0-3 .. t0+15 from rows clamped into [0, L), and the carried-state rows
+  // for the three rows before the tile (used on the first tile only)
+  uint4 in[kRowsF + 3], sin[3];
 #pragma unroll
   for (int i = 0; i < kRowsF + 3; ++i) {
     const int64_t t = t0 - 3 + i;
-    in[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (t >= a.L) {
-    } else if (t >= 0) {
-      in[i] = *reinterpret_cast<const uint4*>(xb + t * a.x_st);
-    } else if (sb && t >= -(K - 1)) {
-      in[i] = *reinterpret_cast<const uint4*>(sb + (t + K - 1) * a.st_st);
-    }
+    const int64_t tc = t < 0 ? 0 : (t >= a.L ? a.L - 1 : t);
+    in[i] = *reinterpret_cast<const uint4*>(xb + tc * a.x_st);
   }
-  float w4[4][V], bias[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    bias[v] = a.bias ? a.bias[c + v] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = j - (4 - K);  // taps right-aligned on 4
-      w4[j][v] = kk >= 0 ? a.w[(c + v) * K + kk] : 0.f;
-    }
+  for (int i = 0; i < 3; ++i) {
+    const int j = i + K - 4;  // state row of t = -3 + i (valid for j >= 0)
+    sin[i] = *reinterpret_cast<const uint4*>(sb + (j < 0 ? 0 : j) * sst);
   }
+
   const bool second = c >= a.split;  // a vector never straddles the split (split % V == 0)
   E* ob = second ? static_cast<E*>(a.out2) + b * a.o2_sb + (c - a.split)
                  : static_cast<E*>(a.out) + b * a.o_sb + a.o_c0 + c;
   E* olb = second ? (a.out2_lo ? static_cast<E*>(a.out2_lo) + b * a.o2_sb + (c - a.split) : nullptr)
                   : (a.out_lo ? static_cast<E*>(a.out_lo) + b * a.o_sb + a.o_c0 + c : nullptr);
   const int64_t ost = second ? a.o2_st : a.o_st;
+
+  // input value of row index i (t = t0 - 3 + i), channel v; zero outside the sequence
+  // and before the carried state
+  auto raw = [&](int i, int v) __attribute__((always_inline)) {
+    const int64_t t = t0 - 3 + i;
+    float x = raw_elem<IO>(in[i], v);
+    if (i < 3) x = t < 0 ? raw_elem<IO>(sin[i], v) : x;
+    const bool ok = t < a.L && t >= -(K - 1) && (t >= 0 || has_st);
+    return ok ? x : 0.f;
+  };
+  auto row = [&](int r, float* o) __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < kRowsF; ++r) {
-    const int64_t t = t0 + r;
-    if (t < a.L) {
+    for (int v = 0; v < V; ++v) {
+      float pre = has_bias ? bias_raw[v] : 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) pre = fmaf(wf[v * K + k], raw(r + 4 - K + k, v), pre);
+      o[v] = a.silu ? siluf_(pre) : pre;
+    }
+  };
+  auto put = [&](int r, const float* o) __attribute__((always_inline)) {
+    store_vec16<IO>(ob + (t0 + r) * ost, o);
+    if (olb) {
+      float lo[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
+      store_vec16<IO>(olb + (t0 + r) * ost, lo);
+    }
+  };
+  if (t0 + kRowsF <= a.L) {
+#pragma unroll
+    for (int r = 0; r < kRowsF; ++r) {
       float o[V];
+      row(r, o);
+      put(r, o);
+    }
+  } else {
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        float pre = bias[v];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(in[r + j], v), pre);
-        o[v] = a.silu ? siluf_(pre) : pre;
-      }
-      store_vec16<IO>(ob + t * ost, o);
-      if (olb) {
-        float lo[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
-        store_vec16<IO>(olb + t * ost, lo);
-      }
+    for (int r = 0; r < kRowsF; ++r) {
+      float o[V];
+      row(r, o);
+      if (t0 + r < a.L) put(r, o);
     }
   }
 }
@@ -368,6 +415,25 @@ void launch_conv_bwd_kernel(const ConvBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((conv_bwd_kernel<IO, FUSED>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
 }
 
+hipError_t launch_conv_fwd_kernel(int bf16, const ConvFwdArgs& a, dim3 grid, hipStream_t s) {
+#define SSD_CONV_FWD(IO, KK)                                                          \
+  if (a.K == KK) {                                                                    \
+    hipLaunchKernelGGL((conv_fwd_kernel<IO, KK>), grid, dim3(256), 0, s, a);          \
+    return hipGetLastError();                                                         \
+  }
+  if (bf16) {
+    SSD_CONV_FWD(bf16_t, 4)
+    SSD_CONV_FWD(bf16_t, 3)
+    SSD_CONV_FWD(bf16_t, 2)
+  } else {
+    SSD_CONV_FWD(float, 4)
+    SSD_CONV_FWD(float, 3)
+    SSD_CONV_FWD(float, 2)
+  }
+#undef SSD_CONV_FWD
+  return hipErrorInvalidValue;
+}
+
 hipError_t run_conv_bwd(ConvBwdArgs a, int bf16, bool fused, float* dw, float* db, int accumulate,
                         hipStream_t s) {
   const int64_t ntile = (a.L + kTileRows - 1) / kTileRows;
@@ -501,11 +567,7 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
   const int V = bf16 ? 8 : 4;
   const int64_t n = B * ((L + kRowsF - 1) / kRowsF) * (C / V);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(conv_fwd_kernel<bf16_t>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(conv_fwd_kernel<float>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_conv_fwd_kernel(bf16, a, grid, s);
 }
 
 size_t bc_prepass_bytes(const Problem& pr) {
@@ -562,11 +624,7 @@ hipError_t launch_xbc_prepass(const Problem& pr, void* xp, void* bc, void* bc_lo
   const int V = pr.bf16 ? 8 : 4;
   const int64_t n = pr.B * ((pr.L + kRowsF - 1) / kRowsF) * (C / V);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
-  if (pr.bf16)
-    hipLaunchKernelGGL(conv_fwd_kernel<bf16_t>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(conv_fwd_kernel<float>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_conv_fwd_kernel(pr.bf16, a, grid, s);
 }
 
 hipError_t launch_conv_fwd(const ConvProblem& cp, MView out, MView state_out, hipStream_t s) {

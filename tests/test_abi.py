@@ -115,6 +115,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
         == bd.SSD_ERR_UNSUPPORTED
     assert lib.conv1d_fwd(1, 10, 60, 4, bd.SSD_BF16, good, 0x8000, None, 1, nullv, good, nullv, None) \
         == bd.SSD_ERR_UNSUPPORTED
+    # conv weights and bias are read as 16-byte vectors
+    assert lib.conv1d_fwd(1, 10, 64, 4, bd.SSD_BF16, good, 0x8004, None, 1, nullv, good, nullv, None) \
+        == bd.SSD_ERR_ALIGN
+    assert lib.conv1d_fwd(1, 10, 64, 4, bd.SSD_BF16, good, 0x8000, 0x9008, 1, nullv, good, nullv, None) \
+        == bd.SSD_ERR_ALIGN
+    st = lib.ssd_fwd(ctypes.byref(d), bd.SSD_BF16, good, 0x8004, None, nullv, nullv, dtv, None, 1,
+                     0x9000, None, nullv, None, outv, None, None, 0, None, 0, None)
+    assert st == bd.SSD_ERR_ALIGN and b"conv_w" in lib.ssd_last_error()
 
 
 def test_workspace_scaling_is_linear_and_modest():
