@@ -103,18 +103,34 @@ __global__ void __launch_bounds__(256) scan_rev_kernel(const float* dh_final, fl
 }
 
 // ------------------------------------------------------------------ main
-// One wave per SIMD has registers to spare: unroll the MFMA K loops so operand
-// reads overlap the MFMAs.
-constexpr int kMainUnroll = 2;
+// Launch shape: NW = 4 waves (one per SIMD; every wave computes a 16-row strip of
+// each product across all of its columns) or NW = 8 (two per SIMD; waves w and w+4
+// share strip w % 4 and take one half of the columns each, so each SIMD has a
+// second instruction stream to issue while the other waits on LDS, MFMA or memory
+// latency).  Row sums over columns are then kept per half and added in (f).
+template <int NW>
+struct MainShape {
+  static constexpr int threads = NW * kWave;
+  static constexpr int halves = NW / 4;
+  // with one wave per SIMD there are registers to spare: unroll the MFMA K loops so
+  // operand reads overlap the MFMAs
+  static constexpr int unroll = NW == 4 ? 2 : 1;
+};
 
-template <typename IO, int P, int N>
-__global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
+template <typename IO, int P, int N, int NW>
+__global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   using T = io_traits<IO>;
   using E = typename T::elem;
   using Lt = typename T::lds;
+  constexpr int kThreads = MainShape<NW>::threads;
+  constexpr int NHALF = MainShape<NW>::halves;
+  constexpr int kMainUnroll = MainShape<NW>::unroll;
   constexpr int PADK = 16 / sizeof(Lt);
   constexpr int ldN = N + PADK, ldQ = kQ + PADK, ldP = P + PADK;
   constexpr int NTn = N / 16, PJ = P / 16;
+  // 16-column tiles per wave: P columns, Q (= 64) columns, N columns
+  constexpr int PJw = PJ / NHALF, QJw = 4 / NHALF, NTw = NTn / NHALF;
+  static_assert(PJ % NHALF == 0 && NTn % NHALF == 0, "column halves must be whole tiles");
   __shared__ __align__(16) Lt sC[kQ * ldN];   // C rows [t][n]
   __shared__ __align__(16) Lt sB[kQ * ldN];   // B rows [s][n]
   __shared__ __align__(16) Lt sX[kQ * ldP];   // x [s][p]
@@ -131,8 +147,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   constexpr int ldG = P + 4;
   __shared__ __align__(16) float sG2[kQ * ldG];  // dout silu'(z) [t][p] (fp32)
   __shared__ float s_dt[kQ], s_cs[kQ], s_sig[kQ], s_dq[kQ];
-  __shared__ float s_row[kQ], s_yo[kQ], s_v[kQ], s_col[4][kQ];
-  __shared__ float s_red[2][4];
+  __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
+  __shared__ float s_red[2][NW];
   __shared__ float s_par[3][kMaxHeadBlock];  // A, D, dt_bias of the block's heads
 
   const Problem& pr = a.pr;
@@ -144,7 +160,10 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   const int h_first = hb * a.hb_heads;
   const int g = h_first / (pr.H / pr.G);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int m0 = wave * 16;
+  const int strip = wave % 4, hf = wave / 4;
+  const int m0 = strip * 16;
+  // first column of this wave's half: P, Q and N columns
+  const int p0 = hf * PJw * 16, s0 = hf * QJw * 16, n0 = hf * NTw * 16;
   const int64_t t0 = c * kQ;
   const int64_t PN = static_cast<int64_t>(P) * N;
 
@@ -212,27 +231,27 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
   }
 
   // B and C rows of the group (post-conv), shared by every head of the block
-  conv_rows<IO, P, N, false, true, true>(pr, b, 0, g, t0, [&](int seg, int s, int cl, const float* o) {
+  conv_rows<IO, P, N, false, true, true, kThreads>(pr, b, 0, g, t0, [&](int seg, int s, int cl, const float* o) {
     lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
   });
   const bool clo = SPLIT && pr.bc_lo.p != nullptr;
   if (clo) {
     Problem prl = pr;
     prl.bc = pr.bc_lo;
-    conv_rows<IO, P, N, false, false, true>(prl, b, 0, g, t0, [&](int, int s, int cl, const float* o) {
+    conv_rows<IO, P, N, false, false, true, kThreads>(prl, b, 0, g, t0, [&](int, int s, int cl, const float* o) {
       lds_put_row<IO>(sClo + s * ldN + cl, o);
     });
   }
   __syncthreads();
-  f32x4 cb[4];  // (C B^T)[t in rows m0.., s], all 64 columns
+  f32x4 cb[QJw];  // (C B^T)[t in rows m0.., s in this wave's half]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mma_strip<Lt, true, true, 4, kMainUnroll>(cb, sC, ldN, m0, sB, ldN, 0, N);
-  if (clo) mma_strip<Lt, true, true, 4, kMainUnroll>(cb, sClo, ldN, m0, sB, ldN, 0, N);
+  for (int j = 0; j < QJw; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sC, ldN, m0, sB, ldN, s0, N);
+  if (clo) mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sClo, ldN, m0, sB, ldN, s0, N);
 
-  f32x4 accdB[NTn], accdC[NTn];
+  f32x4 accdB[NTw], accdC[NTw];
 #pragma unroll
-  for (int j = 0; j < NTn; ++j) {
+  for (int j = 0; j < NTw; ++j) {
     accdB[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     accdC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -303,44 +322,44 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     __syncthreads();
     // dy (hi + lo) and dout silu'(z) at this lane's accumulator positions
     // (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
-    float dyr[PJ][4], g2r[PJ][4];
+    float dyr[PJw][4], g2r[PJw][4];
 #pragma unroll
-    for (int j = 0; j < PJ; ++j)
+    for (int j = 0; j < PJw; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = m0 + acc_row(e), p = 16 * j + acc_col();
+        const int t = m0 + acc_row(e), p = p0 + 16 * j + acc_col();
         dyr[j][e] = T::lds_to_f(sDY[t * ldP + p]);
         if constexpr (SPLIT) dyr[j][e] += T::lds_to_f(sDYlo[t * ldP + p]);
         g2r[j][e] = sG2[t * ldG + p];
       }
 
     // (a) Mt, y, dz, carried-state dcs term, dD
-    float lt[4][4];  // exp(cs_t - cs_s) masked, at the cb positions
+    float lt[QJw][4];  // exp(cs_t - cs_s) masked, at the cb positions
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < QJw; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = m0 + acc_row(e), s = 16 * j + acc_col();
+        const int t = m0 + acc_row(e), s = s0 + 16 * j + acc_col();
         lt[j][e] = s <= t ? __expf(s_cs[t] - s_cs[s]) : 0.f;
         sM[t * ldQ + s] = T::to_lds(cb[j][e] * lt[j][e] * s_dt[s]);
       }
-    f32x4 yacc[PJ];
+    f32x4 yacc[PJw];
 #pragma unroll
-    for (int j = 0; j < PJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_strip<Lt, true, true, PJ, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, 0, N);
-    if (clo) mma_strip<Lt, true, true, PJ, kMainUnroll>(yacc, sClo, ldN, m0, sH, ldN, 0, N);
+    for (int j = 0; j < PJw; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, p0, N);
+    if (clo) mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sClo, ldN, m0, sH, ldN, p0, N);
     float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float ecs = __expf(s_cs[m0 + acc_row(e)]);
 #pragma unroll
-      for (int j = 0; j < PJ; ++j) {
+      for (int j = 0; j < PJw; ++j) {
         yacc[j][e] *= ecs;
         yo_part[e] += dyr[j][e] * yacc[j][e];
       }
     }
     __syncthreads();
-    mma_strip<Lt, true, false, PJ, kMainUnroll>(yacc, sM, ldQ, m0, sX, ldP, 0, kQ);
+    mma_strip<Lt, true, false, PJw, kMainUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + h * P : nullptr;
@@ -349,8 +368,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         const int t = m0 + acc_row(e);
         const int64_t tg = t0 + t;
 #pragma unroll
-        for (int j = 0; j < PJ; ++j) {
-          const int p = 16 * j + acc_col();
+        for (int j = 0; j < PJw; ++j) {
+          const int p = p0 + 16 * j + acc_col();
           const float xv = T::lds_to_f(sX[t * ldP + p]);
           const float y = yacc[j][e] + Dh * xv;
           dD_part += dyr[j][e] * xv;
@@ -363,22 +382,22 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       yo_part[e] = row_sum16(yo_part[e]);
     if (acc_col() == 0)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_yo[m0 + acc_row(e)] = yo_part[e];
+      for (int e = 0; e < 4; ++e) s_yo[hf][m0 + acc_row(e)] = yo_part[e];
     dD_part = wave_sum(dD_part);
     if (lane == 0) s_red[1][wave] = dD_part;
 
     // (b) dYX = dY X^T, W, row / column sums of (C.B)(dy.x) e^{..} (dt)
     {
-      f32x4 dyx[4];
+      f32x4 dyx[QJw];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, true, 4, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, 0, P);
-      if constexpr (SPLIT) mma_strip<Lt, true, true, 4, kMainUnroll>(dyx, sDYlo, ldP, m0, sX, ldP, 0, P);
+      for (int j = 0; j < QJw; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, s0, P);
+      if constexpr (SPLIT) mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDYlo, ldP, m0, sX, ldP, s0, P);
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < QJw; ++j) {
         float csum = 0.f;
-        const int s = 16 * j + acc_col();
+        const int s = s0 + 16 * j + acc_col();
         const float dts = s_dt[s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -391,7 +410,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         }
         csum += __shfl_xor(csum, 16, kWave);
         csum += __shfl_xor(csum, 32, kWave);
-        if (lane < 16) s_col[wave][s] = csum;
+        if (lane < 16) s_col[strip][s] = csum;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -399,7 +418,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       }
       if (acc_col() == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_row[m0 + acc_row(e)] = rs[e];
+        for (int e = 0; e < 4; ++e) s_row[hf][m0 + acc_row(e)] = rs[e];
     }
     __syncthreads();
 
@@ -407,14 +426,14 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     if (hh + 1 < a.hb_heads) prefetch(h + 1, 0);
     // (c) dx rows s = m0..: Mt^T dY + exp(cs_Q - cs_s) dt_s B dH^T + D dy
     {
-      f32x4 dxd[PJ], dxs[PJ];
+      f32x4 dxd[PJw], dxs[PJw];
 #pragma unroll
-      for (int j = 0; j < PJ; ++j) {
+      for (int j = 0; j < PJw; ++j) {
         dxd[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         dxs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      mma_strip<Lt, false, false, PJ, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, 0, kQ);
-      mma_strip<Lt, true, true, PJ, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, 0, N);
+      mma_strip<Lt, false, false, PJw, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, p0, kQ);
+      mma_strip<Lt, true, true, PJw, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, p0, N);
       E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + h * P;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -422,8 +441,8 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         const int64_t sg = t0 + s;
         const float sc = s_dq[s] * s_dt[s];
 #pragma unroll
-        for (int j = 0; j < PJ; ++j) {
-          const int p = 16 * j + acc_col();
+        for (int j = 0; j < PJw; ++j) {
+          const int p = p0 + 16 * j + acc_col();
           const float dxv = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
           if (sg < pr.L) dxp[sg * a.dx.st + p] = T::from_f(dxv);
         }
@@ -432,18 +451,18 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     if (hh + 1 < a.hb_heads) prefetch(h + 1, 1);
     // (d) dB rows s: W^T C + exp(cs_Q - cs_s) dt_s (X dH); chunk-state dcs term
     {
-      f32x4 U[NTn];
+      f32x4 U[NTw];
 #pragma unroll
-      for (int j = 0; j < NTn; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, false, NTn, kMainUnroll>(U, sX, ldP, m0, sdH, ldN, 0, P);
+      for (int j = 0; j < NTw; ++j) U[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, false, NTw, kMainUnroll>(U, sX, ldP, m0, sdH, ldN, n0, P);
       float vp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
         const float sc = s_dq[s] * s_dt[s];
 #pragma unroll
-        for (int j = 0; j < NTn; ++j) {
-          vp[e] += U[j][e] * T::lds_to_f(sB[s * ldN + 16 * j + acc_col()]);
+        for (int j = 0; j < NTw; ++j) {
+          vp[e] += U[j][e] * T::lds_to_f(sB[s * ldN + n0 + 16 * j + acc_col()]);
           accdB[j][e] += sc * U[j][e];
         }
       }
@@ -452,22 +471,22 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
         vp[e] = row_sum16(vp[e]);
       if (acc_col() == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_v[m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
-      mma_strip<Lt, false, false, NTn, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, 0, kQ);
+        for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
+      mma_strip<Lt, false, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
     }
     if (hh + 1 < a.hb_heads) prefetch(h + 1, 2);
     // (e) dC rows t: W B + exp(cs_t) dY H
     {
-      mma_strip<Lt, true, false, NTn, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, 0, kQ);
-      f32x4 tmp[NTn];
+      mma_strip<Lt, true, false, NTw, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, n0, kQ);
+      f32x4 tmp[NTw];
 #pragma unroll
-      for (int j = 0; j < NTn; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, false, NTn, kMainUnroll>(tmp, sDY, ldP, m0, sH, ldN, 0, P);
+      for (int j = 0; j < NTw; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_strip<Lt, true, false, NTw, kMainUnroll>(tmp, sDY, ldP, m0, sH, ldN, n0, P);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float ecs = __expf(s_cs[m0 + acc_row(e)]);
 #pragma unroll
-        for (int j = 0; j < NTn; ++j) accdC[j][e] += ecs * tmp[j][e];
+        for (int j = 0; j < NTw; ++j) accdC[j][e] += ecs * tmp[j][e];
       }
     }
     __syncthreads();
@@ -477,9 +496,20 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       const int s = lane;
       const float dts = s_dt[s];
       const float colsum = s_col[0][s] + s_col[1][s] + s_col[2][s] + s_col[3][s];
-      const float vs = s_v[s];
-      float dcs = s_row[s] + s_yo[s] - dts * colsum - dts * vs;
-      const float hdh = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+      float vs = s_v[0][s], rsum = s_row[0][s], yo = s_yo[0][s];
+#pragma unroll
+      for (int k = 1; k < NHALF; ++k) {
+        vs += s_v[k][s];
+        rsum += s_row[k][s];
+        yo += s_yo[k][s];
+      }
+      float dcs = rsum + yo - dts * colsum - dts * vs;
+      float hdh = 0.f, dD_sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        hdh += s_red[0][w];
+        dD_sum += s_red[1][w];
+      }
       const float sum_dtv = wave_sum(dts * vs);
       if (s == kQ - 1) dcs += __expf(s_cs[kQ - 1]) * hdh + sum_dtv;
       // dl_s = sum_{t >= s} dcs_t: inclusive scan over reversed lanes
@@ -496,7 +526,7 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
       if (lane == 0) {
         float* pp = a.par_part + ((b * a.nch + c) * pr.H + h) * 3;
         pp[0] = dA_part;
-        pp[1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+        pp[1] = dD_sum;
         pp[2] = db_part;
       }
     }
@@ -510,9 +540,9 @@ __global__ void __launch_bounds__(kThreads) bwd_main_kernel(BwdArgs a) {
     const int64_t t = t0 + m0 + acc_row(e);
     if (t < pr.L)
 #pragma unroll
-      for (int j = 0; j < NTn; ++j) {
-        part[t * (2 * N) + 16 * j + acc_col()] = accdB[j][e];
-        part[t * (2 * N) + N + 16 * j + acc_col()] = accdC[j][e];
+      for (int j = 0; j < NTw; ++j) {
+        part[t * (2 * N) + n0 + 16 * j + acc_col()] = accdB[j][e];
+        part[t * (2 * N) + N + n0 + 16 * j + acc_col()] = accdC[j][e];
       }
   }
 }
@@ -646,8 +676,11 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   // 4. main
   {
     TimingScope ts(kKBwdMain, s);
-    hipLaunchKernelGGL((bwd_main_kernel<IO, P, N>), dim3(static_cast<unsigned>(pr.B * l.nch * l.nhb)),
-                       dim3(kThreads), 0, s, a);
+    // two waves per SIMD where the column halves are whole tiles and the x / dout
+    // tiles split evenly over 512 threads (bf16, P = 64, N >= 32)
+    constexpr int NW = (sizeof(IO) == 2 && P == 64 && N >= 32) ? 8 : 4;
+    hipLaunchKernelGGL((bwd_main_kernel<IO, P, N, NW>), dim3(static_cast<unsigned>(pr.B * l.nch * l.nhb)),
+                       dim3(MainShape<NW>::threads), 0, s, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

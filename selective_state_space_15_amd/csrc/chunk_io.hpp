@@ -237,10 +237,10 @@ struct ChunkLoader {
 };
 
 // One-shot form of ChunkLoader (issue then consume).
-template <typename IO, int P, int N, bool DX, bool DB, bool DC, typename F>
+template <typename IO, int P, int N, bool DX, bool DB, bool DC, int NTHR = kThreads, typename F>
 __device__ __forceinline__ void conv_rows(const Problem& pr, int b, int h, int g, int64_t t0,
                                           F&& put) {
-  ChunkLoader<IO, P, N, DX, DB, DC> ld;
+  ChunkLoader<IO, P, N, DX, DB, DC, NTHR> ld;
   ld.issue(pr, b, h, g, t0);
   ld.consume(pr, h, t0, put);
 }
