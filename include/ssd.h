@@ -41,7 +41,8 @@
  *              A view with ptr == NULL means "absent" where the argument is optional.
  *              Activations use the I/O dtype `io`; base pointers must be 16-byte
  *              aligned and stride_b, stride_t multiples of 16 bytes, except the dt /
- *              ddt views, which need only element alignment.
+ *              ddt views, which need only element alignment.  stride_t is at most
+ *              2^24 elements (SSD_ERR_SHAPE otherwise).
  *   Dtypes     Activations, conv states and activation gradients: `io` (bf16 or
  *              fp32).  Parameters (A, D, dt_bias, conv w and b), SSD states (h0,
  *              h_final, checkpoints, dh) and parameter gradients: fp32.  All

@@ -59,6 +59,10 @@ ssd_status check_view(const ssd_view& v, const char* name, ssd_dtype io, bool re
   if (v.stride_t < C && T > 1) return fail(SSD_ERR_SHAPE, "%s: stride_t %lld < channels %lld", name,
                                            (long long)v.stride_t, (long long)C);
   if (v.stride_b < 0 || v.stride_t < 0) return fail(SSD_ERR_SHAPE, "%s: negative stride", name);
+  // kernels address a chunk's rows as a uniform base plus a 32-bit in-chunk offset
+  if (v.stride_t > ssd::kMaxRowStride)
+    return fail(SSD_ERR_SHAPE, "%s: stride_t %lld elements exceeds %lld", name, (long long)v.stride_t,
+                (long long)ssd::kMaxRowStride);
   if (vec) {
     if (!aligned16(v.ptr)) return fail(SSD_ERR_ALIGN, "%s: base pointer not 16-byte aligned", name);
     if ((v.stride_b * es) % 16 || (v.stride_t * es) % 16)

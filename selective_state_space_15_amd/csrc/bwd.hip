@@ -189,31 +189,38 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   // loaded values before stage(): rows past the end are zeroed there.  A select right
   // after a load would make the wave wait for it at the point of issue.
   const bool gate = pr.z.p != nullptr;
+  // Global addresses are a uniform base (the chunk's first row; scalar registers)
+  // plus a 32-bit per-thread offset (row strides are at most kMaxRowStride), which
+  // keeps each address in one vector register.
+  const E* xs_c = xs_p + b * xs_sb + t0 * xs_st;
+  const E* dq_c = static_cast<const E*>(a.dout.p) + b * a.dout.sb + t0 * a.dout.st;
+  // without a gate the z loads repeat the dout loads (and are not used)
+  const E* zq_c = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + t0 * pr.z.st : dq_c;
+  const int64_t zst = gate ? pr.z.st : a.dout.st;
   auto prefetch = [&](int h, int part) {
     if (part == 0 && wave == 0) {
-      const int64_t t = t0 + lane < pr.L ? t0 + lane : pr.L - 1;
-      pf_dt = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h];
+      const uint32_t r = t0 + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
+      pf_dt = *byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
+                        r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
     }
-    const E* xq = xs_p + b * xs_sb + h * P;
-    const E* dq = static_cast<const E*>(a.dout.p) + b * a.dout.sb + h * P;
-    // without a gate the z loads repeat the dout loads (and are not used)
-    const E* zq = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : dq;
-    const int64_t zst = gate ? pr.z.st : a.dout.st;
     if (part == 0)
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
       const int i = threadIdx.x + q * kThreads;
-      const int r = i / (P / V), cl = (i % (P / V)) * V;
-      const int64_t t = t0 + r < pr.L ? t0 + r : t0;
-      pf_x[q] = *reinterpret_cast<const uint4*>(xq + t * xs_st + cl);
-      pf_do[q] = *reinterpret_cast<const uint4*>(dq + t * a.dout.st + cl);
-      pf_z[q] = *reinterpret_cast<const uint4*>(zq + t * zst + cl);
+      const uint32_t r = t0 + i / (P / V) < pr.L ? i / (P / V) : 0;
+      const uint32_t cl = (i % (P / V)) * V;
+      pf_x[q] = *byte_off(reinterpret_cast<const uint4*>(xs_c + h * P),
+                          (r * static_cast<uint32_t>(xs_st) + cl) * sizeof(E));
+      pf_do[q] = *byte_off(reinterpret_cast<const uint4*>(dq_c + h * P),
+                           (r * static_cast<uint32_t>(a.dout.st) + cl) * sizeof(E));
+      pf_z[q] = *byte_off(reinterpret_cast<const uint4*>(zq_c + h * P),
+                          (r * static_cast<uint32_t>(zst) + cl) * sizeof(E));
     }
     const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
     const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
-      const int i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
+      const uint32_t i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
       if (part == 1) hv[q] = *reinterpret_cast<const float4*>(Hg + i);
       if (part == 2) gv[q] = *reinterpret_cast<const float4*>(dHg + i);
     }
@@ -362,18 +369,18 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     mma_strip<Lt, true, false, PJw, kMainUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
     float dD_part = 0.f;
     {
-      E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + h * P : nullptr;
+      E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + t0 * a.dz.st + h * P : nullptr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
-        const int64_t tg = t0 + t;
+        E* dzr = dzp ? byte_off(dzp, (t * static_cast<uint32_t>(a.dz.st) + p0 + acc_col()) * sizeof(E)) : nullptr;
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
           const int p = p0 + 16 * j + acc_col();
           const float xv = T::lds_to_f(sX[t * ldP + p]);
           const float y = yacc[j][e] + Dh * xv;
           dD_part += dyr[j][e] * xv;
-          if (dzp && tg < pr.L) dzp[tg * a.dz.st + p] = T::from_f(g2r[j][e] * y);
+          if (dzp && t0 + t < pr.L) dzr[16 * j] = T::from_f(g2r[j][e] * y);
         }
       }
     }
@@ -434,17 +441,16 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       }
       mma_strip<Lt, false, false, PJw, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, p0, kQ);
       mma_strip<Lt, true, true, PJw, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, p0, N);
-      E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + h * P;
+      E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + t0 * a.dx.st + h * P;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
-        const int64_t sg = t0 + s;
         const float sc = s_dq[s] * s_dt[s];
+        E* dxr = byte_off(dxp, (s * static_cast<uint32_t>(a.dx.st) + p0 + acc_col()) * sizeof(E));
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
-          const int p = p0 + 16 * j + acc_col();
           const float dxv = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
-          if (sg < pr.L) dxp[sg * a.dx.st + p] = T::from_f(dxv);
+          if (t0 + s < pr.L) dxr[16 * j] = T::from_f(dxv);
         }
       }
     }
@@ -520,7 +526,8 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       const bool valid = t0 + s < pr.L;
       const float ddt_raw = valid ? ddt * s_sig[s] : 0.f;
       if (valid)
-        static_cast<E*>(a.ddt.p)[b * a.ddt.sb + (t0 + s) * a.ddt.st + h] = T::from_f(ddt_raw);
+        *byte_off(static_cast<E*>(a.ddt.p) + b * a.ddt.sb + t0 * a.ddt.st + h,
+                  s * static_cast<uint32_t>(a.ddt.st) * sizeof(E)) = T::from_f(ddt_raw);
       const float dA_part = wave_sum(dts * dl);
       const float db_part = wave_sum(ddt_raw);
       if (lane == 0) {
@@ -534,11 +541,11 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   }
 
   // dB (rows s) and dC (rows t) of the block's heads -> fp32 partial
-  float* part = a.dbc_part + ((static_cast<int64_t>(hb) * pr.B + b) * pr.L) * (2 * N);
+  float* part = a.dbc_part + ((static_cast<int64_t>(hb) * pr.B + b) * pr.L + t0) * (2 * N);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int64_t t = t0 + m0 + acc_row(e);
-    if (t < pr.L)
+    const uint32_t t = m0 + acc_row(e);
+    if (t0 + t < pr.L)
 #pragma unroll
       for (int j = 0; j < NTw; ++j) {
         part[t * (2 * N) + n0 + 16 * j + acc_col()] = accdB[j][e];

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ssd {
 
 constexpr int kWave = 64;
@@ -320,6 +322,17 @@ __device__ __forceinline__ float block_colsum(const float* m, int64_t rows, int6
 }
 
 // Row / column of accumulator element e (0..3) of this lane inside a 16x16 tile.
+// base + `bytes`, with the byte offset held as an opaque 32-bit vector value: the
+// address is then formed at the access as a scalar base plus a 32-bit offset (one
+// vector register), instead of a 64-bit per-thread pointer that the compiler would
+// hoist out of a loop (two registers each, spilled under register pressure).
+template <typename Ptr>
+__device__ __forceinline__ Ptr byte_off(Ptr base, uint32_t bytes) {
+  asm volatile("" : "+v"(bytes));
+  using C = std::conditional_t<std::is_const_v<std::remove_pointer_t<Ptr>>, const char*, char*>;
+  return reinterpret_cast<Ptr>(reinterpret_cast<C>(base) + bytes);
+}
+
 __device__ __forceinline__ int acc_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
 

@@ -10,6 +10,9 @@ namespace ssd {
 
 constexpr int kQ = 64;         // chunk length of the chunked evaluation
 constexpr int kThreads = 256;  // threads per workgroup of the chunk kernels
+// Largest row stride (elements) of an activation view: 64 rows of a chunk plus a
+// row's channels then stay within a 32-bit element offset from the chunk's first row.
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 
 // Kernel kinds of the timing instrumentation (ssd_timing_* in ssd.h).
 enum KernelKind {
