@@ -146,10 +146,11 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   __shared__ __align__(16) Lt sClo[SPLIT ? kQ * ldN : 8];
   constexpr int ldG = P + 4;
   __shared__ __align__(16) float sG2[kQ * ldG];  // dout silu'(z) [t][p] (fp32)
-  __shared__ float s_dt[kQ], s_cs[kQ], s_sig[kQ], s_dq[kQ];
+  // per head of the block: dt and the chunk-local cumsum cs of dt A
+  __shared__ float s_dtH[kMaxHeadBlock][kQ], s_csH[kMaxHeadBlock][kQ];
   __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
   __shared__ float s_red[2][NW];
-  __shared__ float s_par[3][kMaxHeadBlock];  // A, D, dt_bias of the block's heads
+  __shared__ float s_par[2][kMaxHeadBlock];  // A, D of the block's heads
 
   const Problem& pr = a.pr;
   const int64_t total = static_cast<int64_t>(pr.B) * a.nch * a.nhb;
@@ -177,7 +178,6 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   constexpr int NXV = P * kQ / (V * kThreads);  // 16-byte row vectors per thread
   static_assert(P * kQ % (V * kThreads) == 0, "the x / dout tiles must tile the block");
   constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
-  E pf_dt{};
   uint4 pf_x[NXV], pf_do[NXV], pf_z[NXV];
   float4 hv[NH4], gv[NH4];
   // without conv, x is the raw xbc channels (fields selected one by one: a selected
@@ -198,11 +198,6 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   const E* zq_c = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + t0 * pr.z.st : dq_c;
   const int64_t zst = gate ? pr.z.st : a.dout.st;
   auto prefetch = [&](int h, int part) {
-    if (part == 0 && wave == 0) {
-      const uint32_t r = t0 + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
-      pf_dt = *byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
-                        r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
-    }
     if (part == 0)
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
@@ -228,13 +223,25 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   prefetch(h_first, 0);
   prefetch(h_first, 1);
   prefetch(h_first, 2);
+  // dt and cs of every head of the block, once:
+  // one wave per head, one token per lane (a barrier follows before any use)
+  for (int hh = wave; hh < a.hb_heads; hh += NW) {
+    const int h = h_first + hh;
+    const bool live = t0 + lane < pr.L;
+    const uint32_t r = live ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
+    const float u = T::to_f(*byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
+                                      r * static_cast<uint32_t>(pr.dt.st) * sizeof(E))) +
+                    (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+    const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
+    s_dtH[hh][lane] = dtv;
+    s_csH[hh][lane] = wave_incl_scan(dtv * pr.A[h]);
+  }
   // the block's per-head parameters, read once (a load right where a head needs them
   // would stall that head on its latency)
   if (threadIdx.x < a.hb_heads) {
     const int h = h_first + threadIdx.x;
     s_par[0][threadIdx.x] = pr.A[h];
     s_par[1][threadIdx.x] = pr.D ? pr.D[h] : 0.f;
-    s_par[2][threadIdx.x] = pr.dt_bias ? pr.dt_bias[h] : 0.f;
   }
 
   // B and C rows of the group (post-conv), shared by every head of the block
@@ -267,23 +274,12 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     const int h = h_first + hh;
     const float Ah = s_par[0][hh];
     const float Dh = s_par[1][hh];
+    const float* s_dt = s_dtH[hh];
+    const float* s_cs = s_csH[hh];
+    // chunk-state decay exp(cs_Q - cs_s)
+    const float cs_last = s_cs[kQ - 1];
+    auto dq = [&](int s) __attribute__((always_inline)) { return __expf(cs_last - s_cs[s]); };
     // ---- stage head h from the prefetch registers into LDS
-    // (1) dt, cs, softplus slope, chunk-state decays (wave 0)
-    if (wave == 0) {
-      const int64_t t = t0 + lane;
-      float dtv = 0.f, sig = 1.f;
-      if (t < pr.L) {
-        const float u = T::to_f(pf_dt) + s_par[2][hh];
-        dtv = pr.softplus ? softplusf_(u) : u;
-        sig = pr.softplus ? sigmoidf_(u) : 1.f;
-      }
-      const float cs = wave_incl_scan(dtv * Ah);
-      const float csl = lane_value(cs, kWave - 1);
-      s_dt[lane] = dtv;
-      s_cs[lane] = cs;
-      s_sig[lane] = sig;
-      s_dq[lane] = __expf(csl - cs);
-    }
     // (2) x rows; dy = dout silu(z) (and its low part); dout silu'(z)
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
@@ -445,7 +441,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
-        const float sc = s_dq[s] * s_dt[s];
+        const float sc = dq(s) * s_dt[s];
         E* dxr = byte_off(dxp, (s * static_cast<uint32_t>(a.dx.st) + p0 + acc_col()) * sizeof(E));
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
@@ -465,7 +461,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
-        const float sc = s_dq[s] * s_dt[s];
+        const float sc = dq(s) * s_dt[s];
 #pragma unroll
         for (int j = 0; j < NTw; ++j) {
           vp[e] += U[j][e] * T::lds_to_f(sB[s * ldN + n0 + 16 * j + acc_col()]);
@@ -477,7 +473,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         vp[e] = row_sum16(vp[e]);
       if (acc_col() == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = s_dq[m0 + acc_row(e)] * vp[e];
+        for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = dq(m0 + acc_row(e)) * vp[e];
       mma_strip<Lt, false, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
     }
     if (hh + 1 < a.hb_heads) prefetch(h + 1, 2);
@@ -524,7 +520,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       const float dl = __shfl(rscan, kWave - 1 - lane, kWave);
       const float ddt = colsum + vs + Ah * dl;
       const bool valid = t0 + s < pr.L;
-      const float ddt_raw = valid ? ddt * s_sig[s] : 0.f;
+      // d softplus(u)/du = sigmoid(u) = 1 - exp(-softplus(u))
+      const float sig = pr.softplus ? -expm1f(-dts) : 1.f;
+      const float ddt_raw = valid ? ddt * sig : 0.f;
       if (valid)
         *byte_off(static_cast<E*>(a.ddt.p) + b * a.ddt.sb + t0 * a.ddt.st + h,
                   s * static_cast<uint32_t>(a.ddt.st) * sizeof(E)) = T::from_f(ddt_raw);
