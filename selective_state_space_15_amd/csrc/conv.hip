@@ -236,138 +236,197 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   const int K = a.K;
   const int tid = threadIdx.x;
 
-  // ---- raw rows -> sR (rows before the sequence from the carried state, after it zero)
-  {
-    const E* xb = static_cast<const E*>(a.x) + b * a.x_sb;
-    const E* sb = a.st ? static_cast<const E*>(a.st) + b * a.st_sb : nullptr;
-    uint4 rr[NRV];
+  // ---- tile loads.  Every load is unconditional, from a clamped (valid) address,
+  // and all of them are in flight together; the masks (rows outside the sequence,
+  // channels past the block) are applied where the values go to LDS.  A load under a
+  // branch, or a select right after it, would make the wave wait for it at once.
+  const bool has_st = a.st != nullptr;
+  const E* xb = static_cast<const E*>(a.x) + b * a.x_sb;
+  const E* sbp = has_st ? static_cast<const E*>(a.st) + b * a.st_sb : xb;
+  const int64_t sst = has_st ? a.st_st : 0;
+  uint4 rr[NRV];
 #pragma unroll
-    for (int q = 0; q < NRV; ++q) {
-      const int k = min(tid + 256 * q, RROWS * RVPR - 1);
-      const int row = k / RVPR, cv = (k % RVPR) * V;
-      const int c = c0 + cv;
-      const int64_t t = t_lo - 3 + row;
-      const bool in_seq = t >= 0 && t < a.L;
-      const bool in_st = sb && t < 0 && t >= -(K - 1);
-      const bool ok = c < climit && (in_seq || in_st);
-      const int cc = c < climit ? c : c0;  // masked vectors read a valid address
-      const E* src = in_st ? sb + (t + K - 1) * a.st_st + cc : xb + (in_seq ? t : 0) * a.x_st + cc;
-      rr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(src));
-    }
-#pragma unroll
-    for (int q = 0; q < NRV; ++q) {
-      const int k = tid + 256 * q;
-      if (k < RROWS * RVPR) *reinterpret_cast<uint4*>(sR + (k / RVPR) * kTileCh + (k % RVPR) * V) = rr[q];
-    }
+  for (int q = 0; q < NRV; ++q) {
+    const int k = min(tid + 256 * q, RROWS * RVPR - 1);
+    const int row = k / RVPR, cv = (k % RVPR) * V;
+    const int cc = c0 + cv < climit ? c0 + cv : c0;
+    const int64_t t = t_lo - 3 + row;
+    const bool in_st = has_st && t < 0 && t >= -(K - 1);
+    const int64_t tc = t < 0 ? 0 : (t >= a.L ? a.L - 1 : t);
+    const E* src = in_st ? sbp + (t + K - 1) * sst + cc : xb + tc * a.x_st + cc;
+    rr[q] = *reinterpret_cast<const uint4*>(src);
   }
-  // ---- gradient rows -> sG (fp32): the I/O-typed view, or (fused, B / C channels)
-  // the fp32 group sums; rows outside the sequence zero
+  // gradient rows: 16-byte vectors of cw channels (the I/O view, or the fp32 group
+  // sums for the fused B / C channels); gvpr = vectors per row (a power of two)
+  const int gsh = from_f32 ? 4 : (V == 8 ? 3 : 4);
+  const int cw = from_f32 ? 4 : V;
+  uint4 gr[NGV];
   {
-    const int gvpr = from_f32 ? GVPR_F : kTileCh / V;
-    const int cw = from_f32 ? 4 : V;  // channels per vector
-    uint4 gr[NGV];
+    const int gn = FUSED ? a.G * a.N : 0;
 #pragma unroll
     for (int q = 0; q < NGV; ++q) {
-      const int k = min(tid + 256 * q, GROWS * gvpr - 1);
-      const int row = k / gvpr, cv = (k % gvpr) * cw;
-      const int c = c0 + cv;
+      const int k = min(tid + 256 * q, (GROWS << gsh) - 1);
+      const int row = k >> gsh, cv = (k & ((1 << gsh) - 1)) * cw;
+      const int cc = c0 + cv < climit ? c0 + cv : c0;
       const int64_t t = t_lo + row;
-      const bool ok = c < climit && t < a.L;
-      const int cc = c < climit ? c : c0;
-      const int64_t tt = t < a.L ? t : 0;
-      const void* src;
-      if (from_f32) {
-        const int gn = a.G * a.N, rel = cc - a.hp;
+      const int64_t tt = t < a.L ? t : a.L - 1;
+      const char* src;
+      if constexpr (FUSED) {
+        const int rel = cc > a.hp ? cc - a.hp : 0;
         const bool isC = rel >= gn;
-        const int g = (isC ? rel - gn : rel) / a.N, n0 = (isC ? rel - gn : rel) % a.N;
-        src = a.dbc + ((static_cast<int64_t>(g) * a.per_g * a.B + b) * a.L + tt) * (2LL * a.N) + (isC ? a.N : 0) + n0;
-      } else if (FUSED) {
-        src = static_cast<const E*>(a.g) + (b * a.L + tt) * a.hp + cc;
+        const int rc = isC ? rel - gn : rel;
+        const float* pf = a.dbc + ((static_cast<int64_t>(rc / a.N) * a.per_g * a.B + b) * a.L + tt) * (2LL * a.N) +
+                          (isC ? a.N : 0) + rc % a.N;
+        const E* pe = static_cast<const E*>(a.g) + (b * a.L + tt) * a.hp + cc;
+        src = from_f32 ? reinterpret_cast<const char*>(pf) : reinterpret_cast<const char*>(pe);
       } else {
-        src = static_cast<const E*>(a.g) + b * a.g_sb + tt * a.g_st + cc;
+        src = reinterpret_cast<const char*>(static_cast<const E*>(a.g) + b * a.g_sb + tt * a.g_st + cc);
       }
-      gr[q] = keep_if(ok, *reinterpret_cast<const uint4*>(src));
-    }
-#pragma unroll
-    for (int q = 0; q < NGV; ++q) {
-      const int k = tid + 256 * q;
-      if (k < GROWS * gvpr) {
-        float* dst = sG + (k / gvpr) * kTileCh + (k % gvpr) * cw;
-        if (from_f32) {
-          *reinterpret_cast<uint4*>(dst) = gr[q];
-        } else {
-          float f[V];
-#pragma unroll
-          for (int v = 0; v < V; ++v) f[v] = raw_elem<IO>(gr[q], v);
-#pragma unroll
-          for (int v = 0; v < V; v += 4) *reinterpret_cast<float4*>(dst + v) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
-        }
-      }
+      gr[q] = *reinterpret_cast<const uint4*>(src);
     }
   }
-  __syncthreads();
-
-  // ---- the thread's channel and row segment
+  // gradient of the returned state rows L-(K-1) .. L-1 (zero without one), fp32 in LDS
+  __shared__ float sDso[3][kTileCh];
+  uint4 dso_v;
+  constexpr int DVPR = kTileCh / V;
+  const bool has_dso = a.dso != nullptr;
+  {
+    const int k = min(tid, 3 * DVPR - 1);
+    const int js = k / DVPR, cv = (k % DVPR) * V;
+    const int cc = c0 + cv < climit ? c0 + cv : c0;
+    const E* src = has_dso ? static_cast<const E*>(a.dso) + b * a.dso_sb + (js < K - 1 ? js : 0) * a.dso_st + cc
+                           : xb + cc;
+    dso_v = *reinterpret_cast<const uint4*>(src);
+  }
+  // this thread's channel: taps (right-aligned on 4: tap j reads row t - 3 + j) and bias
   const int cl = tid % kTileCh, seg = tid / kTileCh;
   const int c = c0 + cl;
   const bool cvalid = c < climit;
-  float w4[4], bias = 0.f;
+  const int cwc = cvalid ? c : c0;
+  float w4[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kk = j - (4 - K);  // taps right-aligned on 4: tap j reads row t - 3 + j
-    w4[j] = cvalid && kk >= 0 ? a.w[c * K + kk] : 0.f;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int kk = jj - (4 - K);
+    w4[jj] = a.w[cwc * K + (kk >= 0 ? kk : 0)];
   }
-  if (cvalid && a.bias) bias = a.bias[c];
+  const float bias_raw = a.bias ? a.bias[cwc] : 0.f;
+
+  // ---- masks, then LDS
+#pragma unroll
+  for (int q = 0; q < NRV; ++q) {
+    const int k = tid + 256 * q;
+    const int row = k / RVPR, cv = (k % RVPR) * V;
+    const int64_t t = t_lo - 3 + row;
+    const bool in_seq = t >= 0 && t < a.L;
+    const bool in_st = has_st && t < 0 && t >= -(K - 1);
+    const bool ok = c0 + cv < climit && (in_seq || in_st);
+    if (k < RROWS * RVPR) *reinterpret_cast<uint4*>(sR + row * kTileCh + cv) = keep_if(ok, rr[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < NGV; ++q) {
+    const int k = tid + 256 * q;
+    const int row = k >> gsh, cv = (k & ((1 << gsh) - 1)) * cw;
+    const bool ok = c0 + cv < climit && t_lo + row < a.L;
+    if (k < (GROWS << gsh)) {
+      float* dst = sG + row * kTileCh + cv;
+      if (from_f32) {
+        *reinterpret_cast<uint4*>(dst) = keep_if(ok, gr[q]);
+      } else {
+        float f[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) f[v] = ok ? raw_elem<IO>(gr[q], v) : 0.f;
+#pragma unroll
+        for (int v = 0; v < V; v += 4) *reinterpret_cast<float4*>(dst + v) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
+      }
+    }
+  }
+  if (tid < 3 * DVPR) {
+    const int js = tid / DVPR, cv = (tid % DVPR) * V;
+    const bool ok = has_dso && js < K - 1;
+#pragma unroll
+    for (int v = 0; v < V; ++v) sDso[js][cv + v] = ok ? raw_elem<IO>(dso_v, v) : 0.f;
+  }
+  for (int jj = 0; jj < 4; ++jj)
+    if (jj < 4 - K || !cvalid) w4[jj] = 0.f;
+  const float bias = cvalid ? bias_raw : 0.f;
+  __syncthreads();
+
+  // ---- the row walk: thread (channel cl, segment seg) produces dx of rows
+  // r0 .. r0 + kSegRows - 1 with a register window (raw rows tau-3 .. tau+3, dpre of
+  // rows tau .. tau+3); tile 0's first segment also the carried-state rows -(K-1)..-1
   const bool silu = a.silu != 0;
   const int64_t r0 = t_lo + seg * kSegRows;
-  // output rows: the segment's rows inside the sequence; tile 0's first segment also
-  // the carried-state rows -(K-1) .. -1
-  const int64_t tau_b = (tile == 0 && seg == 0) ? -(K - 1) : r0;
-  const int64_t tau_e = r0 + kSegRows < a.L ? r0 + kSegRows : a.L;
-  auto raw_at = [&](int64_t t) -> float {
-    return t >= t_lo - 3 ? T::lds_to_f(sR[(t - t_lo + 3) * kTileCh + cl]) : 0.f;
+  const int lr0 = seg * kSegRows;  // r0 - t_lo
+  auto raw_l = [&](int lr) __attribute__((always_inline)) {  // raw row t_lo + lr (lr >= -3)
+    return T::lds_to_f(sR[(lr + 3) * kTileCh + cl]);
   };
-  auto dp_of = [&](int64_t t, const float* rw4) -> float {  // rw4: raw rows t-3 .. t
-    if (t < 0 || t >= a.L) return 0.f;
+  auto dpre_l = [&](int lr, const float* rw4) __attribute__((always_inline)) {  // row t_lo + lr >= t_lo
     float pre = bias;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pre = fmaf(w4[j], rw4[j], pre);
-    const float gv = sG[(t - t_lo) * kTileCh + cl];
+    for (int jj = 0; jj < 4; ++jj) pre = fmaf(w4[jj], rw4[jj], pre);
+    const float gv = sG[lr * kTileCh + cl];  // zero outside the sequence
     return silu ? gv * dsiluf_(pre) : gv;
   };
   float dw[4] = {0.f, 0.f, 0.f, 0.f}, db = 0.f;
-  if (cvalid && tau_b < tau_e) {
-    E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + c;
-    const E* dsob = a.dso ? static_cast<const E*>(a.dso) + b * a.dso_sb + c : nullptr;
-    E* dsib = a.dsi ? static_cast<E*>(a.dsi) + b * a.dsi_sb + c : nullptr;
-    // window: rw[i] = raw row tau - 3 + i (i < 7), d[i] = dpre of row tau + i (i < 4)
-    float rw[7], d[4];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) rw[i] = raw_at(tau_b - 3 + i);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) d[i] = dp_of(tau_b + i, rw + i);
-    for (int64_t tau = tau_b; tau < tau_e; ++tau) {
-      rw[6] = raw_at(tau + 3);
-      d[3] = dp_of(tau + 3, rw + 3);
+  E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + t_lo * a.dx_st + cwc;
+  // carried-state rows (tile 0, segment 0: one whole wave)
+  if (tile == 0 && seg == 0 && a.dsi != nullptr) {
+    E* dsib = static_cast<E*>(a.dsi) + b * a.dsi_sb + cwc;
+    for (int tau = -(K - 1); tau < 0; ++tau) {
+      // o = sum_j w[j] dpre(tau + 3 - j); dpre of rows outside [0, L) is zero
       float o = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o = fmaf(w4[j], d[3 - j], o);
-      const int64_t js = tau - (a.L - (K - 1));  // row of the returned state
-      if (dsob && js >= 0) o += T::to_f(dsob[js * a.dso_st]);
-      if (tau >= 0) {
-        dxb[tau * a.dx_st] = T::from_f(o);
-        db += d[0];
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = tau + 3 - jj;
+        if (t >= 0 && t < a.L) {
+          float rw4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dw[j] = fmaf(d[0], rw[j], dw[j]);
-      } else if (dsib) {
-        dsib[(tau + K - 1) * a.dsi_st] = T::from_f(o);
+          for (int i = 0; i < 4; ++i) rw4[i] = raw_l(t - 3 + i);
+          o = fmaf(w4[jj], dpre_l(t, rw4), o);
+        }
+      }
+      const int64_t js = tau - (a.L - (K - 1));
+      if (js >= 0) o += sDso[js][cl];
+      if (cvalid) dsib[(tau + K - 1) * a.dsi_st] = T::from_f(o);
+    }
+  }
+  auto walk = [&](auto edge_tag) __attribute__((always_inline)) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    float rw[7], d[4];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) rw[i] = raw_l(lr0 - 3 + i);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) d[i] = dpre_l(lr0 + i, rw + i);
+#pragma unroll
+    for (int r = 0; r < kSegRows; ++r) {
+      const int lr = lr0 + r;
+      rw[6] = raw_l(lr + 3);
+      d[3] = dpre_l(lr + 3, rw + 3);
+      float o = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) o = fmaf(w4[jj], d[3 - jj], o);
+      db += d[0];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dw[jj] = fmaf(d[0], rw[jj], dw[jj]);
+      if constexpr (EDGE) {
+        const int64_t tau = t_lo + lr;
+        const int64_t js = tau - (a.L - (K - 1));
+        if (js >= 0 && js < K - 1) o += sDso[js][cl];
+        if (cvalid && tau < a.L) dxb[lr * a.dx_st] = T::from_f(o);
+      } else {
+        if (cvalid) dxb[lr * a.dx_st] = T::from_f(o);
       }
 #pragma unroll
       for (int i = 0; i < 6; ++i) rw[i] = rw[i + 1];
 #pragma unroll
       for (int i = 0; i < 3; ++i) d[i] = d[i + 1];
     }
-  }
+  };
+  // interior tiles: every row is inside the sequence and none is a returned-state row
+  if (t_lo + kTileRows <= a.L - (K - 1))
+    walk(std::false_type{});
+  else if (r0 < a.L)
+    walk(std::true_type{});
   // ---- dw / db: the four segments in order, one partial per (batch, tile, channel);
   // the sums go through the raw tile's LDS once every thread is done with it
   __syncthreads();
