@@ -103,6 +103,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   const int lane = threadIdx.x % kWave;
   const float Ah = pr.A[h];
   const float bias_h = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+  const float Dh = OUT && pr.D ? pr.D[h] : 0.f;
   const bool gate = OUT && pr.z.p != nullptr;
 
   // Output tiles (16x16) of the 64-row chunk products: row tile rt = wave % 4; with
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   constexpr int RXL = HALVES == 1 ? 2 : 1;  // x rows per loader task: all threads busy
   constexpr int RBL = 8 / HALVES;           // B/C rows per loader task
   ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL, !OUT> ld;
-  float dt_raw = 0.f;
+  E dt_raw{};
   // gate inputs of this thread's output vectors (row k / (P / V), columns
   // V (k % (P / V)) for k = tid + NTHR q), loaded one chunk phase ahead as 16-byte rows
   constexpr int NYV = (kQ * P / V + NTHR - 1) / NTHR;
@@ -183,8 +184,14 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   };
   // dt is prefetched one chunk ahead; the row loads are issued right before use
   // (holding them across the MFMA phase costs more registers than 2 waves/SIMD allow)
+  // (unconditional, from a clamped row: a load under a branch would be waited for at
+  // once, and with it every load still in flight; rows past the end are masked in (1))
+  // The raw element is kept as loaded and converted in (1): converting it here would
+  // make the wave wait for the load at once.  Every wave loads it (no branch); wave 0
+  // uses it.
   auto prefetch = [&](int64_t tn) {
-    if (wave == 0 && tn + lane < pr.L) dt_raw = T::to_f(dtp[(tn + lane) * pr.dt.st]);
+    const uint32_t r = tn + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - tn);
+    dt_raw = *byte_off(dtp + tn * pr.dt.st, r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
   };
   prefetch(tbeg);
 
@@ -206,7 +213,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     if (wave == 0) {
       float dtv = 0.f;
       if (t0 + lane < pr.L) {
-        const float u = dt_raw + bias_h;
+        const float u = T::to_f(dt_raw) + bias_h;
         dtv = pr.softplus ? softplusf_(u) : u;
       }
       const float cs = wave_incl_scan(dtv * Ah);
@@ -220,8 +227,9 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     lsum += cs_last;
     // (2) conv + stores into LDS
     //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
-    prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
     ld.issue(pr, b, h, g, t0);
+    // issued after the row loads, so waiting for those does not wait for these
+    prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
     ld.consume_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
       if (seg == 0) {
         const float ws = s_w[s];
@@ -271,7 +279,6 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       mma_strip<Lt, true, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
       // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
       // out = y * silu(z) on 16-byte rows
-      const float Dh = pr.D ? pr.D[h] : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
