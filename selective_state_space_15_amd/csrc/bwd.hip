@@ -42,7 +42,8 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-constexpr int kMaxHeadBlock = 8;  // heads per bwd_main workgroup, at most
+constexpr int kMaxHeadBlock = 32;  // heads per bwd_main workgroup, at most
+constexpr int kDtTab = 8;          // heads whose dt / cs tables are in LDS at a time
 
 struct BwdArgs {
   Problem pr;
@@ -147,7 +148,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   constexpr int ldG = P + 4;
   __shared__ __align__(16) float sG2[kQ * ldG];  // dout silu'(z) [t][p] (fp32)
   // per head of the block: dt and the chunk-local cumsum cs of dt A
-  __shared__ float s_dtH[kMaxHeadBlock][kQ], s_csH[kMaxHeadBlock][kQ];
+  __shared__ float s_dtH[kDtTab][kQ], s_csH[kDtTab][kQ];
   __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
   __shared__ float s_red[2][NW];
   __shared__ float s_par[2][kMaxHeadBlock];  // A, D of the block's heads
@@ -225,17 +226,21 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   prefetch(h_first, 2);
   // dt and cs of every head of the block, once:
   // one wave per head, one token per lane (a barrier follows before any use)
-  for (int hh = wave; hh < a.hb_heads; hh += NW) {
-    const int h = h_first + hh;
-    const bool live = t0 + lane < pr.L;
-    const uint32_t r = live ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
-    const float u = T::to_f(*byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
-                                      r * static_cast<uint32_t>(pr.dt.st) * sizeof(E))) +
-                    (pr.dt_bias ? pr.dt_bias[h] : 0.f);
-    const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
-    s_dtH[hh][lane] = dtv;
-    s_csH[hh][lane] = wave_incl_scan(dtv * pr.A[h]);
-  }
+  // dt and cs of heads hh0 .. hh0 + kDtTab - 1: one wave per head, one token per lane
+  auto fill_dt = [&](int hh0) {
+    for (int i = wave; i < kDtTab && hh0 + i < a.hb_heads; i += NW) {
+      const int h = h_first + hh0 + i;
+      const bool live = t0 + lane < pr.L;
+      const uint32_t r = live ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
+      const float u = T::to_f(*byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
+                                        r * static_cast<uint32_t>(pr.dt.st) * sizeof(E))) +
+                      (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+      const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
+      s_dtH[i][lane] = dtv;
+      s_csH[i][lane] = wave_incl_scan(dtv * pr.A[h]);
+    }
+  };
+  fill_dt(0);
   // the block's per-head parameters, read once (a load right where a head needs them
   // would stall that head on its latency)
   if (threadIdx.x < a.hb_heads) {
@@ -274,8 +279,13 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     const int h = h_first + hh;
     const float Ah = s_par[0][hh];
     const float Dh = s_par[1][hh];
-    const float* s_dt = s_dtH[hh];
-    const float* s_cs = s_csH[hh];
+    if (hh > 0 && hh % kDtTab == 0) {
+      // every wave is past the previous head's last barrier: the tables are free
+      fill_dt(hh);
+      __syncthreads();
+    }
+    const float* s_dt = s_dtH[hh % kDtTab];
+    const float* s_cs = s_csH[hh % kDtTab];
     // chunk-state decay exp(cs_Q - cs_s)
     const float cs_last = s_cs[kQ - 1];
     auto dq = [&](int s) __attribute__((always_inline)) { return __expf(cs_last - s_cs[s]); };
@@ -689,8 +699,9 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 5. dB / dC: head-block sums (and the conv backward)
-  {
+  // 5. dB / dC: head-block sums (and the conv backward); with one head block per group
+  // and a conv, the partials already are the sums
+  if (pr.K == 0 || l.nhb != pr.G) {
     const int64_t n4 = pr.B * pr.L * 2LL * pr.G * pr.N / 4;
     const dim3 grid(static_cast<unsigned>((n4 + 255) / 256));
     TimingScope ts(kKDbcReduce, s);
