@@ -150,7 +150,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   // per head of the block: dt and the chunk-local cumsum cs of dt A
   __shared__ float s_dtH[kDtTab][kQ], s_csH[kDtTab][kQ];
   __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
-  __shared__ float s_red[2][NW];
+  // per-wave partials of <dH, H> and of dD, double-buffered by head parity: wave 0 reads
+  // head h's in (f) while the other waves already stage head h + 1
+  __shared__ float s_red[2][2][NW];
   __shared__ float s_par[2][kMaxHeadBlock];  // A, D of the block's heads
 
   const Problem& pr = a.pr;
@@ -280,7 +282,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     const float Ah = s_par[0][hh];
     const float Dh = s_par[1][hh];
     if (hh > 0 && hh % kDtTab == 0) {
-      // every wave is past the previous head's last barrier: the tables are free
+      __syncthreads();  // wave 0 is done with the previous head's (f): the tables are free
       fill_dt(hh);
       __syncthreads();
     }
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         }
       }
       dot = wave_sum(dot);
-      if (lane == 0) s_red[0][wave] = dot;
+      if (lane == 0) s_red[hh & 1][0][wave] = dot;
     }
     __syncthreads();
     // dy (hi + lo) and dout silu'(z) at this lane's accumulator positions
@@ -397,7 +399,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s_yo[hf][m0 + acc_row(e)] = yo_part[e];
     dD_part = wave_sum(dD_part);
-    if (lane == 0) s_red[1][wave] = dD_part;
+    if (lane == 0) s_red[hh & 1][1][wave] = dD_part;
 
     // (b) dYX = dY X^T, W, row / column sums of (C.B)(dy.x) e^{..} (dt)
     {
@@ -519,8 +521,8 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       float hdh = 0.f, dD_sum = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        hdh += s_red[0][w];
-        dD_sum += s_red[1][w];
+        hdh += s_red[hh & 1][0][w];
+        dD_sum += s_red[hh & 1][1][w];
       }
       const float sum_dtv = wave_sum(dts * vs);
       if (s == kQ - 1) dcs += __expf(s_cs[kQ - 1]) * hdh + sum_dtv;
@@ -545,7 +547,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         pp[2] = db_part;
       }
     }
-    __syncthreads();
+    // No barrier here: the next head's staging writes none of what (f) reads (the
+    // per-wave partials are double-buffered, the dt tables are refilled behind a
+    // barrier), so wave 0 finishes (f) while the other waves stage; they meet at the
+    // barrier after the staging.
   }
 
   // dB (rows s) and dC (rows t) of the block's heads -> fp32 partial
