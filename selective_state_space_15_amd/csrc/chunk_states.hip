@@ -98,6 +98,7 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
   const View rows = DS ? a.dout : (pr.K > 0 ? pr.xp : pr.xbc);  // x channels lead xbc rows
   const E* dbase = static_cast<const E*>(rows.p) + b * rows.sb;
   const bool gate = DS && pr.z.p != nullptr;
+  const float gw = gate ? 1.f : 0.f;
   // without a gate the z loads repeat the dout loads (and are not used)
   const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
   const int64_t zst = gate ? pr.z.st : rows.st;
@@ -147,39 +148,58 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
   constexpr int PT = P / 16, NT = N / 16, WPP = NW / PT, NJS = (NT + WPP - 1) / WPP;
   static_assert(NW % PT == 0, "waves must cover the state rows");
   const int s_pi = wave % PT, s_nj0 = (wave / PT) * NJS;
-  const bool owns = s_nj0 < NT;
+  // compile-time where every wave owns tiles: a branch here would be a control-flow
+  // merge with stores in flight, after which the next head's staging waits for all of
+  // them (not only for its own loads)
+  constexpr bool kAllOwn = NJS * WPP == NT;
+  const bool owns = kAllOwn || s_nj0 < NT;
   const int64_t PN = static_cast<int64_t>(P) * N;
 
-  for (int hh = 0; hh < a.hb; ++hh) {
-    const int h = hfirst + hh;
-    Lt* A = sA[hh & 1];
-    Lt* Alo = sAlo[SPLIT ? (hh & 1) : 0];
-    // this head's rows, scaled, into LDS (buffer hh & 1: the other one may still
-    // be read by the previous head's product)
+  // head hh's rows, scaled, into LDS buffer buf (the other buffer may still be read by
+  // the previous head's product)
+  auto stage = [&](int hh, int buf) __attribute__((always_inline)) {
+    Lt* A = sA[buf];
+    Lt* Alo = sAlo[SPLIT ? buf : 0];
 #pragma unroll
     for (int q = 0; q < NDT; ++q) {
       const int task = threadIdx.x + q * NTHR;
-      if (task >= (P / V) * kQ) continue;
+      if ((P / V) * kQ % NTHR != 0 && task >= (P / V) * kQ) continue;
       const int col = (task % (P / V)) * V, r = task / (P / V);
       const bool ok = interior || t0 + r < pr.L;  // rows past the end are zero
       const float sc = s_w[hh][r];
+      // masked as raw words and then computed without conditions: a per-element
+      // select around SiLU becomes a branch, and a branch here makes the wave wait for
+      // the previous head's state stores as well as for these rows (the z words are
+      // always read: without a gate they hold dout rows and are weighted by 0)
+      const uint4 dq = keep_if(ok, dvr[q]);
       float o[V], lo[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const float dv = raw_elem<IO>(dvr[q], v);
-        if constexpr (DS) {
-          o[v] = ok ? (gate ? dv * siluf_(raw_elem<IO>(zvr[q], v)) : dv) * sc : 0.f;
-          lo[v] = o[v] - T::to_f(T::from_f(o[v]));
-        } else {
-          o[v] = ok ? dv * sc : 0.f;
-        }
+        if constexpr (DS)
+          o[v] = raw_elem<IO>(dq, v) * fmaf(gw, siluf_(raw_elem<IO>(zvr[q], v)), 1.f - gw) * sc;
+        else
+          o[v] = raw_elem<IO>(dq, v) * sc;
       }
+      if constexpr (DS)
+#pragma unroll
+        for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
       lds_put_row<IO>(A + r * ldP + col, o);
       if constexpr (SPLIT) lds_put_row<IO>(Alo + r * ldP + col, lo);
     }
-    if (hh + 1 < a.hb) issue_head(h + 1);
-    __syncthreads();
+  };
+  stage(0, 0);
+  __syncthreads();
+  // Per head: the next head's loads, this head's product and state stores, then the
+  // next head's staging, all without branches, so the wait before the staging counts
+  // exactly the loads it needs and leaves the stores in flight.  (The last head loads
+  // and stages itself again, into the idle buffer.)
+  for (int hh = 0; hh < a.hb; ++hh) {
+    const int h = hfirst + hh;
+    const int hn = hh + 1 < a.hb ? hh + 1 : hh;
+    issue_head(hfirst + hn);
     if (owns) {
+      const Lt* A = sA[hh & 1];
+      const Lt* Alo = sAlo[SPLIT ? (hh & 1) : 0];
       f32x4 acc[NJS];
 #pragma unroll
       for (int j = 0; j < NJS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -195,6 +215,8 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
         for (int e = 0; e < 4; ++e)
           dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[j][e];
     }
+    stage(hn, (hh + 1) & 1);
+    __syncthreads();
   }
 }
 
