@@ -277,34 +277,26 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     accdC[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int hh = 0; hh < a.hb_heads; ++hh) {
-    const int h = h_first + hh;
-    const float Ah = s_par[0][hh];
-    const float Dh = s_par[1][hh];
-    if (hh > 0 && hh % kDtTab == 0) {
-      __syncthreads();  // wave 0 is done with the previous head's (f): the tables are free
-      fill_dt(hh);
-      __syncthreads();
-    }
-    const float* s_dt = s_dtH[hh % kDtTab];
-    const float* s_cs = s_csH[hh % kDtTab];
-    // chunk-state decay exp(cs_Q - cs_s)
-    const float cs_last = s_cs[kQ - 1];
-    auto dq = [&](int s) __attribute__((always_inline)) { return __expf(cs_last - s_cs[s]); };
-    // ---- stage head h from the prefetch registers into LDS
-    // (2) x rows; dy = dout silu(z) (and its low part); dout silu'(z)
+  // Head hs from the prefetch registers into LDS: x rows; dy = dout silu(z) (and its
+  // low part); dout silu'(z); H_{c-1} and dH_c, with the wave's part of <dH, H>.
+  // Masks are applied to the raw words and the gate is blended in arithmetically: a
+  // per-element select around SiLU becomes a branch, and a branch here would make the
+  // wave wait for every store in flight as well as for these loads.
+  const float gw = gate ? 1.f : 0.f;
+  auto stage_head = [&](int hs) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NXV; ++q) {
       const int i = threadIdx.x + q * kThreads;
       const int r = i / (P / V), cl = (i % (P / V)) * V;
       const bool ok = t0 + r < pr.L;  // rows past the end are zero
       *reinterpret_cast<uint4*>(sX + r * ldP + cl) = keep_if(ok, pf_x[q]);
+      const uint4 dq = keep_if(ok, pf_do[q]);
       float dy[V], lo[V], g2[V];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const float dv = raw_elem<IO>(pf_do[q], v), zv = raw_elem<IO>(pf_z[q], v);
-        dy[v] = ok ? (gate ? dv * siluf_(zv) : dv) : 0.f;
-        g2[v] = ok && gate ? dv * dsiluf_(zv) : 0.f;
+        const float dv = raw_elem<IO>(dq, v), zv = raw_elem<IO>(pf_z[q], v);
+        dy[v] = dv * fmaf(gw, siluf_(zv), 1.f - gw);
+        g2[v] = gw * dv * dsiluf_(zv);
         lo[v] = dy[v] - T::to_f(T::from_f(dy[v]));
       }
       lds_put_row<IO>(sDY + r * ldP + cl, dy);
@@ -313,28 +305,46 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       for (int v = 0; v < V; v += 4)
         *reinterpret_cast<float4*>(sG2 + r * ldG + cl + v) = make_float4(g2[v], g2[v + 1], g2[v + 2], g2[v + 3]);
     }
-    // (3) H_{c-1}, dH_c into LDS; <dH, H> on the way
-    {
-      float dot = 0.f;
+    float dot = 0.f;
 #pragma unroll
-      for (int q = 0; q < NH4; ++q) {
-        const int i = (threadIdx.x + q * kThreads) * 4;
-        if (i < P * N) {
-          const int p = i / N, n = i % N;
-          const float hf[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
-          const float df[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+    for (int q = 0; q < NH4; ++q) {
+      const int i = (threadIdx.x + q * kThreads) * 4;
+      if (NH4 * 4 * kThreads == P * N || i < P * N) {
+        const int p = i / N, n = i % N;
+        const float hf[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
+        const float df[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            sH[p * ldN + n + k] = T::to_lds(hf[k]);
-            sdH[p * ldN + n + k] = T::to_lds(df[k]);
-            dot += hf[k] * df[k];
-          }
+        for (int k = 0; k < 4; ++k) {
+          sH[p * ldN + n + k] = T::to_lds(hf[k]);
+          sdH[p * ldN + n + k] = T::to_lds(df[k]);
+          dot += hf[k] * df[k];
         }
       }
-      dot = wave_sum(dot);
-      if (lane == 0) s_red[hh & 1][0][wave] = dot;
     }
-    __syncthreads();
+    dot = wave_sum(dot);
+    if (lane == 0) s_red[hs & 1][0][wave] = dot;
+  };
+  stage_head(0);
+  __syncthreads();
+
+  for (int hh = 0; hh < a.hb_heads; ++hh) {
+    const int h = h_first + hh;
+    // the next head (the last head reloads and restages itself: no branch around the
+    // prefetch or the staging)
+    const int hn = hh + 1 < a.hb_heads ? hh + 1 : hh;
+    const float Ah = s_par[0][hh];
+    const float Dh = s_par[1][hh];
+    if (hh > 0 && hh % kDtTab == 0) {
+      // every wave, wave 0 with the previous head's (f) included, is past the barrier
+      // that ends the previous iteration: the tables are free
+      fill_dt(hh);
+      __syncthreads();
+    }
+    const float* s_dt = s_dtH[hh % kDtTab];
+    const float* s_cs = s_csH[hh % kDtTab];
+    // chunk-state decay exp(cs_Q - cs_s)
+    const float cs_last = s_cs[kQ - 1];
+    auto dq = [&](int s) __attribute__((always_inline)) { return __expf(cs_last - s_cs[s]); };
     // dy (hi + lo) and dout silu'(z) at this lane's accumulator positions
     // (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
     float dyr[PJw][4], g2r[PJw][4];
@@ -438,7 +448,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     __syncthreads();
 
     // the next head's inputs go in flight now, behind the remaining MFMA work
-    if (hh + 1 < a.hb_heads) prefetch(h + 1, 0);
+    prefetch(h_first + hn, 0);
     // (c) dx rows s = m0..: Mt^T dY + exp(cs_Q - cs_s) dt_s B dH^T + D dy
     {
       f32x4 dxd[PJw], dxs[PJw];
@@ -462,7 +472,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         }
       }
     }
-    if (hh + 1 < a.hb_heads) prefetch(h + 1, 1);
+    prefetch(h_first + hn, 1);
     // (d) dB rows s: W^T C + exp(cs_Q - cs_s) dt_s (X dH); chunk-state dcs term
     {
       f32x4 U[NTw];
@@ -488,7 +498,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = dq(m0 + acc_row(e)) * vp[e];
       mma_strip<Lt, false, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
     }
-    if (hh + 1 < a.hb_heads) prefetch(h + 1, 2);
+    prefetch(h_first + hn, 2);
     // (e) dC rows t: W B + exp(cs_t) dY H
     {
       mma_strip<Lt, true, false, NTw, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, n0, kQ);
@@ -547,10 +557,11 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         pp[2] = db_part;
       }
     }
-    // No barrier here: the next head's staging writes none of what (f) reads (the
-    // per-wave partials are double-buffered, the dt tables are refilled behind a
-    // barrier), so wave 0 finishes (f) while the other waves stage; they meet at the
-    // barrier after the staging.
+    // The next head's staging writes none of what (f) reads (the per-wave partials are
+    // double-buffered, the dt tables are refilled behind a barrier), so wave 0 finishes
+    // (f) while the other waves stage; they meet at the barrier after the staging.
+    stage_head(hh + 1);
+    __syncthreads();
   }
 
   // dB (rows s) and dC (rows t) of the block's heads -> fp32 partial
