@@ -226,23 +226,44 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   prefetch(h_first, 0);
   prefetch(h_first, 1);
   prefetch(h_first, 2);
-  // dt and cs of every head of the block, once:
-  // one wave per head, one token per lane (a barrier follows before any use)
-  // dt and cs of heads hh0 .. hh0 + kDtTab - 1: one wave per head, one token per lane
-  auto fill_dt = [&](int hh0) {
-    for (int i = wave; i < kDtTab && hh0 + i < a.hb_heads; i += NW) {
-      const int h = h_first + hh0 + i;
-      const bool live = t0 + lane < pr.L;
-      const uint32_t r = live ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
-      const float u = T::to_f(*byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
-                                        r * static_cast<uint32_t>(pr.dt.st) * sizeof(E))) +
-                      (pr.dt_bias ? pr.dt_bias[h] : 0.f);
-      const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
-      s_dtH[i][lane] = dtv;
-      s_csH[i][lane] = wave_incl_scan(dtv * pr.A[h]);
+  // dt and cs of heads hh0 .. hh0 + kDtTab - 1 into the LDS tables: one wave per head,
+  // one token per lane.  The raw dt, dt_bias and A of a group of heads are loaded one
+  // group ahead (load_dt), unconditionally from clamped rows and heads, and used by
+  // the next fill_dt: a use right after the loads would wait for them, and for every
+  // store in flight.
+  constexpr int DTW = (kDtTab + NW - 1) / NW;  // table rows per wave
+  E dtn_raw[DTW];
+  float dtn_bias[DTW], dtn_A[DTW];
+  auto load_dt = [&](int hh0) {
+    const uint32_t r = t0 + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - t0);
+#pragma unroll
+    for (int k = 0; k < DTW; ++k) {
+      const int i = wave + k * NW;
+      const int hc = min(hh0 + i, a.hb_heads - 1);
+      const int h = h_first + hc;
+      dtn_raw[k] = *byte_off(static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + t0 * pr.dt.st + h,
+                             r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
+      dtn_bias[k] = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+      dtn_A[k] = pr.A[h];
     }
   };
-  fill_dt(0);
+  auto fill_dt = [&]() {
+    const bool live = t0 + lane < pr.L;
+#pragma unroll
+    for (int k = 0; k < DTW; ++k) {
+      const int i = wave + k * NW;
+      const float u = T::to_f(dtn_raw[k]) + dtn_bias[k];
+      const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
+      const float cs = wave_incl_scan(dtv * dtn_A[k]);
+      if (i < kDtTab) {
+        s_dtH[i][lane] = dtv;
+        s_csH[i][lane] = cs;
+      }
+    }
+  };
+  load_dt(0);
+  fill_dt();
+  load_dt(kDtTab);
   // the block's per-head parameters, read once (a load right where a head needs them
   // would stall that head on its latency)
   if (threadIdx.x < a.hb_heads) {
@@ -337,7 +358,8 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     if (hh > 0 && hh % kDtTab == 0) {
       // every wave, wave 0 with the previous head's (f) included, is past the barrier
       // that ends the previous iteration: the tables are free
-      fill_dt(hh);
+      fill_dt();
+      load_dt(hh + kDtTab);
       __syncthreads();
     }
     const float* s_dt = s_dtH[hh % kDtTab];
