@@ -7,9 +7,9 @@
 // 2411.19460, skeptic critique) notes precedes the SSD in a Mamba-2 block, which
 // is why a sequence checkpoint must carry the conv buffer as well as h.
 //
-// Forward: one thread per (batch, 16-row tile, 16-byte channel vector); all 19 raw
+// Forward: one thread per (batch, 8-row tile, 16-byte channel vector); all 11 raw
 // rows are loaded up front (independent loads in flight), the taps are applied in
-// registers and the 16 output rows are stored as 16-byte vectors.  Adjacent threads
+// registers and the 8 output rows are stored as 16-byte vectors.  Adjacent threads
 // take adjacent channel vectors, so every row access is coalesced.
 //
 // Backward: one workgroup per (batch, 64-row tile, 64 channels) stages the tile's raw
@@ -25,7 +25,7 @@ namespace ssd {
 
 namespace {
 
-constexpr int kRowsF = 16;     // rows per thread, forward
+constexpr int kRowsF = 8;      // rows per thread, forward
 constexpr int kTileRows = 64;  // rows per workgroup, backward
 constexpr int kTileCh = 64;    // channels per workgroup, backward
 constexpr int kSegRows = 16;   // rows per thread, backward (four segments per tile)
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
     bias_raw[v + 2] = v4.z;
     bias_raw[v + 3] = v4.w;
   }
-  // raw rows t0-3 .. t0+15 from rows clamped into [0, L), and the carried-state rows
+  // raw rows t0-3 .. t0+kRowsF-1 from rows clamped into [0, L), and the carried-state rows
   // for the three rows before the tile (used on the first tile only)
   uint4 in[kRowsF + 3], sin[3];
 #pragma unroll
