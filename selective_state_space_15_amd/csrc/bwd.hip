@@ -50,9 +50,15 @@ struct BwdArgs {
   int64_t nch;
   int hb_heads;            // heads per block (all in one group)
   int nhb;                 // blocks of heads
-  const float* Hs;         // [B][nch][H][P][N] state entering each chunk
+  // States in chunk groups of kG chunks (chunk_states.hip): for chunk c of group g,
+  //   H_{c-1} = P_{c-1} + exp(l_{c0} + .. + l_{c-1}) H_in(g)   (no P term at c = c0)
+  //   dH_c    = Q_c + exp(l_{c+1} + .. + l_{c1}) dH_out(g)      (no Q term at c = c1)
+  const float* Ps;         // [B][nch][H][P][N] in-group prefix states P_c
+  const float* Qs;         // [B][nch][H][P][N] in-group suffix gradients Q_c
+  const float* Hin;        // [B][ngr][H][P][N] state entering each group
+  const float* dHout;      // [B][ngr][H][P][N] gradient leaving each group
   const float* lsum;       // [B][nch][H] chunk log-decay
-  float* dHs;              // [B][nch][H][P][N] dS_c, then dH_c (leaving chunk c)
+  int64_t ngr;
   View dout;
   MView dx;                // x-channel gradients [B][L][H*P] (dxbc itself, or scratch)
   MView dz;
@@ -154,6 +160,8 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   // head h's in (f) while the other waves already stage head h + 1
   __shared__ float s_red[2][2][NW];
   __shared__ float s_par[2][kMaxHeadBlock];  // A, D of the block's heads
+  // per head of the block: exp(l_{c0} + .. + l_{c-1}) and exp(l_{c+1} + .. + l_{c1})
+  __shared__ float s_gdec[2][kMaxHeadBlock];
 
   const Problem& pr = a.pr;
   const int64_t total = static_cast<int64_t>(pr.B) * a.nch * a.nhb;
@@ -170,6 +178,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   const int p0 = hf * PJw * 16, s0 = hf * QJw * 16, n0 = hf * NTw * 16;
   const int64_t t0 = c * kQ;
   const int64_t PN = static_cast<int64_t>(P) * N;
+  // chunk group of c: chunks [c_lo, c_hi)
+  const int64_t grp = c / kG, c_lo = grp * kG;
+  const int64_t c_hi = c_lo + kG < a.nch ? c_lo + kG : a.nch;
 
   // Every global input of a head (dt, post-conv x rows, dout, z, H_{c-1}, dH_c) is
   // loaded into registers by prefetch(), issued for head h+1 in three parts while
@@ -182,7 +193,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   static_assert(P * kQ % (V * kThreads) == 0, "the x / dout tiles must tile the block");
   constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
   uint4 pf_x[NXV], pf_do[NXV], pf_z[NXV];
-  float4 hv[NH4], gv[NH4];
+  float4 hv[NH4], hg[NH4], gv[NH4], gg[NH4];  // P or H_in, Q or dH_out
   // without conv, x is the raw xbc channels (fields selected one by one: a selected
   // struct copy of the kernel argument would go through scratch memory)
   const bool xpre = pr.xp.p != nullptr;
@@ -214,13 +225,23 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       pf_z[q] = *byte_off(reinterpret_cast<const uint4*>(zq_c + h * P),
                           (r * static_cast<uint32_t>(zst) + cl) * sizeof(E));
     }
-    const float* Hg = a.Hs + ((b * a.nch + c) * pr.H + h) * PN;
-    const float* dHg = a.dHs + ((b * a.nch + c) * pr.H + h) * PN;
+    // in-group terms from valid slots only (P_{c-1} for c > c0, Q_c for c < c1; the
+    // unused one reads slot c and is masked when staged)
+    const float* Pg = a.Ps + ((b * a.nch + (c > c_lo ? c - 1 : c)) * pr.H + h) * PN;
+    const float* Qg = a.Qs + ((b * a.nch + c) * pr.H + h) * PN;
+    const float* Hgg = a.Hin + ((b * a.ngr + grp) * pr.H + h) * PN;
+    const float* dHgg = a.dHout + ((b * a.ngr + grp) * pr.H + h) * PN;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
       const uint32_t i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
-      if (part == 1) hv[q] = *reinterpret_cast<const float4*>(Hg + i);
-      if (part == 2) gv[q] = *reinterpret_cast<const float4*>(dHg + i);
+      if (part == 1) {
+        hv[q] = *reinterpret_cast<const float4*>(Pg + i);
+        hg[q] = *reinterpret_cast<const float4*>(Hgg + i);
+      }
+      if (part == 2) {
+        gv[q] = *reinterpret_cast<const float4*>(Qg + i);
+        gg[q] = *reinterpret_cast<const float4*>(dHgg + i);
+      }
     }
   };
   prefetch(h_first, 0);
@@ -268,6 +289,14 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   // would stall that head on its latency)
   if (threadIdx.x < a.hb_heads) {
     const int h = h_first + threadIdx.x;
+    float before = 0.f, after = 0.f;
+    for (int64_t k = c_lo; k < c_hi; ++k) {
+      const float l = a.lsum[(b * a.nch + k) * pr.H + h];
+      if (k < c) before += l;
+      if (k > c) after += l;
+    }
+    s_gdec[0][threadIdx.x] = __expf(before);
+    s_gdec[1][threadIdx.x] = __expf(after);
     s_par[0][threadIdx.x] = pr.A[h];
     s_par[1][threadIdx.x] = pr.D ? pr.D[h] : 0.f;
   }
@@ -326,14 +355,22 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       for (int v = 0; v < V; v += 4)
         *reinterpret_cast<float4*>(sG2 + r * ldG + cl + v) = make_float4(g2[v], g2[v + 1], g2[v + 2], g2[v + 3]);
     }
+    // H_{c-1} and dH_c from the in-group and group states (fp32, before rounding)
+    const int hi = hs < a.hb_heads ? hs : a.hb_heads - 1;
+    const float aH = s_gdec[0][hi], bD = s_gdec[1][hi];
+    const bool useP = c > c_lo, useQ = c < c_hi - 1;
     float dot = 0.f;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
       const int i = (threadIdx.x + q * kThreads) * 4;
       if (NH4 * 4 * kThreads == P * N || i < P * N) {
         const int p = i / N, n = i % N;
-        const float hf[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
-        const float df[4] = {gv[q].x, gv[q].y, gv[q].z, gv[q].w};
+        const float4 pv = useP ? hv[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 qv = useQ ? gv[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float hf[4] = {fmaf(aH, hg[q].x, pv.x), fmaf(aH, hg[q].y, pv.y), fmaf(aH, hg[q].z, pv.z),
+                             fmaf(aH, hg[q].w, pv.w)};
+        const float df[4] = {fmaf(bD, gg[q].x, qv.x), fmaf(bD, gg[q].y, qv.y), fmaf(bD, gg[q].z, qv.z),
+                             fmaf(bD, gg[q].w, qv.w)};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           sH[p * ldN + n + k] = T::to_lds(hf[k]);
@@ -653,14 +690,15 @@ __global__ void __launch_bounds__(256) head_params_kernel(const float* par, int6
 }
 
 struct BwdLayout {
-  size_t bc, bc_lo, xp, H, lsum, dH, dbc, par, dx, conv, total;
-  int64_t nch;
+  size_t bc, bc_lo, xp, H, lsum, dH, Hg, dHg, glsum, dbc, par, dx, conv, total;
+  int64_t nch, ngr;
   int hb_heads, nhb;
 };
 
 BwdLayout bwd_layout(const Problem& pr) {
   BwdLayout l{};
   l.nch = (pr.L + kQ - 1) / kQ;
+  l.ngr = (l.nch + kG - 1) / kG;
   const int hpg = pr.H / pr.G;
   int hb = 1;
   for (int d = 1; d <= kMaxHeadBlock; ++d)
@@ -681,6 +719,9 @@ BwdLayout bwd_layout(const Problem& pr) {
   l.H = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
   l.lsum = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 4);
   l.dH = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
+  l.Hg = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * PN * 4);
+  l.dHg = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * PN * 4);
+  l.glsum = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * 4);
   l.dbc = take(static_cast<size_t>(l.nhb) * pr.B * pr.L * 2 * pr.N * 4);
   l.par = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 3 * 4);
   l.dx = take(pr.K > 0 ? static_cast<size_t>(pr.B) * pr.L * pr.H * pr.P * es : 0);
@@ -698,9 +739,18 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   a.nch = l.nch;
   a.hb_heads = l.hb_heads;
   a.nhb = l.nhb;
-  a.Hs = reinterpret_cast<float*>(ws + l.H);
-  a.lsum = reinterpret_cast<float*>(ws + l.lsum);
-  a.dHs = reinterpret_cast<float*>(ws + l.dH);
+  float* Ps = reinterpret_cast<float*>(ws + l.H);
+  float* Qs = reinterpret_cast<float*>(ws + l.dH);
+  float* Hg = reinterpret_cast<float*>(ws + l.Hg);
+  float* dHg = reinterpret_cast<float*>(ws + l.dHg);
+  float* lsum = reinterpret_cast<float*>(ws + l.lsum);
+  float* glsum = reinterpret_cast<float*>(ws + l.glsum);
+  a.Ps = Ps;
+  a.Qs = Qs;
+  a.Hin = Hg;
+  a.dHout = dHg;
+  a.lsum = lsum;
+  a.ngr = l.ngr;
   a.dout = in.dout;
   a.dz = o.dz;
   a.ddt = o.ddt;
@@ -714,17 +764,17 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   }
   const int64_t PN = static_cast<int64_t>(P) * N;
   const int64_t ne = pr.B * pr.H * PN;
-  // 1. forward states entering each chunk
-  hipError_t e = launch_chunk_states(pr, l.nch, reinterpret_cast<float*>(ws + l.H),
-                                     reinterpret_cast<float*>(ws + l.lsum), s);
+  // 1. in-group prefix states and, by a scan over groups, the state entering each group
+  hipError_t e = launch_group_chunk_states(pr, l.nch, Ps, Hg, lsum, glsum, s);
   if (e != hipSuccess) return e;
-  // 2. per-chunk dy C^T terms, 3. reverse scan -> dH_c, dh0
-  e = launch_chunk_dstates(pr, l.nch, in.dout, a.dHs, s);
+  // 2. in-group suffix gradients, 3. reverse scan over groups -> gradient leaving each
+  // group, dh0
+  e = launch_group_dstates(pr, l.nch, in.dout, Qs, dHg, s);
   if (e != hipSuccess) return e;
   {
     TimingScope ts(kKScanRev, s);
     hipLaunchKernelGGL(scan_rev_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0,
-                       s, in.dh_final, a.dHs, a.lsum, o.dh0, pr.B, pr.H, PN, l.nch);
+                       s, in.dh_final, dHg, glsum, o.dh0, pr.B, pr.H, PN, l.ngr);
   }
   // 4. main
   {

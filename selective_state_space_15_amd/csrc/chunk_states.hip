@@ -220,6 +220,271 @@ __global__ void __launch_bounds__(StateShape<DS>::waves * 64)
   }
 }
 
+// ------------------------------------------------------------------ chunk groups
+// The same contractions, walked over a group of kG consecutive chunks per workgroup,
+// so that the scans only see one state per group.  With l_c the log-decay of chunk c
+// and groups [c0, c1]:
+//   S walk (forward):   P_c = exp(l_c) P_{c-1} + S_c from P_{c0-1} = 0; P_c goes to
+//                       slot c for c < c1 and E_g = P_{c1} to the group buffer;
+//   dS walk (reverse):  Q_{c-1} = exp(l_c) Q_c + dS_c from Q_{c1} = 0; Q_c goes to
+//                       slot c for c0 <= c < c1 and F_g = Q_{c0-1} to the group buffer.
+// The group scans then give H_in(g) (the state entering group g) and dH_out(g) (the
+// gradient leaving it), and for chunk c of group g
+//   H_{c-1} = P_{c-1} + exp(l_{c0} + .. + l_{c-1}) H_in(g)      (P_{c0-1} = 0)
+//   dH_c    = Q_c + exp(l_{c+1} + .. + l_{c1}) dH_out(g)         (Q_{c1} = 0),
+// which the main backward kernel forms when it stages H and dH.
+struct GroupArgs {
+  Problem pr;
+  int64_t nch, ngr;
+  int hb;         // heads per workgroup (divides H / G, at most GroupShape::max_heads)
+  View dout;      // dS only
+  float* out;     // [B][nch][H][P][N]: P_c (S) or Q_c (dS)
+  float* grp;     // [B][ngr][H][P][N]: E_g (S) or F_g (dS)
+  float* lsum;    // S only: [B][nch][H] chunk log-decay
+  float* glsum;   // S only: [B][ngr][H] group log-decay
+};
+
+template <bool DS>
+struct GroupShape {
+  // the walked states of the block's heads stay in registers (32 x 16x16 fp32 tiles
+  // for 2 heads on 4 waves, or for 4 heads on 8 waves); two waves per SIMD
+  static constexpr int waves = DS ? 8 : 4;
+  static constexpr int waves_per_simd = 2;
+  static constexpr int max_heads = DS ? 4 : 2;
+};
+
+// HB heads per workgroup (a template parameter: the head loop is unrolled, so each
+// head's state tiles are addressed statically, with no branch around the products)
+template <typename IO, int P, int N, bool DS, int HB>
+__global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
+    __attribute__((amdgpu_waves_per_eu(GroupShape<DS>::waves_per_simd)))
+    group_state_kernel(GroupArgs a) {
+  constexpr int NW = GroupShape<DS>::waves;
+  constexpr int NTHR = NW * 64;
+  constexpr int HBM = HB;
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  using Lt = typename T::lds;
+  constexpr int V = T::vec;
+  constexpr int PADK = 16 / sizeof(Lt);
+  constexpr int ldN = N + PADK, ldP = P + PADK;
+  constexpr bool SPLIT = DS && sizeof(Lt) == 2;
+  __shared__ __align__(16) Lt sK[kQ * ldN];                       // B or C rows [t][n]
+  __shared__ __align__(16) Lt sKlo[SPLIT ? kQ * ldN : 8];         // C - bf16(C)
+  __shared__ __align__(16) Lt sA[2][kQ * ldP];                    // w x or exp(cs) dy, [t][p]
+  __shared__ __align__(16) Lt sAlo[SPLIT ? 2 : 1][SPLIT ? kQ * ldP : 8];
+  __shared__ float s_w[HBM][kQ];                                  // w_s (S) or exp(cs_t) (dS)
+  __shared__ float s_l[HBM];                                      // chunk log-decay per head
+
+  const Problem& pr = a.pr;
+  const int nhb = pr.H / HB;
+  const int64_t total = pr.B * a.ngr * nhb;
+  const int64_t lid = xcd_remap(blockIdx.x, total);
+  const int hblk = static_cast<int>(lid % nhb);
+  const int64_t grp = (lid / nhb) % a.ngr;
+  const int b = static_cast<int>(lid / (static_cast<int64_t>(nhb) * a.ngr));
+  const int hfirst = hblk * HB;
+  const int g = hfirst / (pr.H / pr.G);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t c_lo = grp * kG;
+  const int ng = static_cast<int>(min(static_cast<int64_t>(kG), a.nch - c_lo));  // chunks in the group
+  const int nsteps = ng * HB;
+  // walk order: step k = (chunk i, head hh), chunk c = c_lo + i (S) or c_lo + ng-1-i (dS)
+  auto chunk_of = [&](int k) -> int64_t {
+    const int i = k / HB;
+    return DS ? c_lo + (ng - 1 - i) : c_lo + i;
+  };
+
+  constexpr int RB = rows_per_task(N / V, NTHR);
+  const bool klo = SPLIT && pr.bc_lo.p != nullptr;
+  Problem prl = pr;
+  prl.bc = pr.bc_lo;
+
+  constexpr int NDT = ((P / V) * kQ + NTHR - 1) / NTHR;
+  uint4 dvr[NDT], zvr[DS ? NDT : 1];
+  const View rows = DS ? a.dout : (pr.K > 0 ? pr.xp : pr.xbc);
+  const E* dbase = static_cast<const E*>(rows.p) + b * rows.sb;
+  const bool gate = DS && pr.z.p != nullptr;
+  const float gw = gate ? 1.f : 0.f;
+  const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
+  const int64_t zst = gate ? pr.z.st : rows.st;
+  // rows of step k (unconditional loads from clamped rows; masked when staged)
+  auto issue_step = [&](int k) {
+    const int64_t c = chunk_of(k);
+    const int h = hfirst + k % HB;
+    const int64_t t0 = c * kQ;
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) {
+      const int task = min(static_cast<int>(threadIdx.x) + q * NTHR, (P / V) * kQ - 1);
+      const int col = (task % (P / V)) * V, r = task / (P / V);
+      const int64_t t = t0 + r < pr.L ? t0 + r : t0;
+      dvr[q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col);
+      if constexpr (DS) zvr[q] = *reinterpret_cast<const uint4*>(zbase + t * zst + h * P + col);
+    }
+  };
+  auto stage = [&](int k, int buf) __attribute__((always_inline)) {
+    const int hh = k % HB;
+    const int64_t t0 = chunk_of(k) * kQ;
+    Lt* A = sA[buf];
+    Lt* Alo = sAlo[SPLIT ? buf : 0];
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) {
+      const int task = threadIdx.x + q * NTHR;
+      if ((P / V) * kQ % NTHR != 0 && task >= (P / V) * kQ) continue;
+      const int col = (task % (P / V)) * V, r = task / (P / V);
+      const bool ok = t0 + r < pr.L;
+      const float sc = s_w[hh][r];
+      const uint4 dq = keep_if(ok, dvr[q]);
+      float o[V], lo[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if constexpr (DS)
+          o[v] = raw_elem<IO>(dq, v) * fmaf(gw, siluf_(raw_elem<IO>(zvr[q], v)), 1.f - gw) * sc;
+        else
+          o[v] = raw_elem<IO>(dq, v) * sc;
+      }
+      if constexpr (DS)
+#pragma unroll
+        for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
+      lds_put_row<IO>(A + r * ldP + col, o);
+      if constexpr (SPLIT) lds_put_row<IO>(Alo + r * ldP + col, lo);
+    }
+  };
+
+  constexpr int PT = P / 16, NT = N / 16, WPP = NW / PT, NJS = (NT + WPP - 1) / WPP;
+  static_assert(NW % PT == 0, "waves must cover the state rows");
+  const int s_pi = wave % PT, s_nj0 = (wave / PT) * NJS;
+  constexpr bool kAllOwn = NJS * WPP == NT;
+  const bool owns = kAllOwn || s_nj0 < NT;
+  const int64_t PN = static_cast<int64_t>(P) * N;
+  f32x4 acc[HBM][NJS];
+#pragma unroll
+  for (int i = 0; i < HBM; ++i)
+#pragma unroll
+    for (int j = 0; j < NJS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float glsum = 0.f;  // S: group log-decay of head (lane) (wave 0 keeps it)
+
+  issue_step(0);
+  for (int i = 0; i < ng; ++i) {
+    const int64_t c = DS ? c_lo + (ng - 1 - i) : c_lo + i;
+    const int64_t t0 = c * kQ;
+    // the chunk's group rows and the dt of the block's heads
+    ChunkLoader<IO, P, N, false, !DS, DS, NTHR, 2, RB> kl_hi, kl_lo;
+    kl_hi.issue(pr, b, hfirst, g, t0);
+    if (klo) kl_lo.issue(prl, b, hfirst, g, t0);
+    __syncthreads();  // the previous chunk's products are done with sK, s_w, s_l
+    for (int hh = wave; hh < HB; hh += NW) {
+      const int h = hfirst + hh;
+      float dtv = 0.f;
+      if (t0 + lane < pr.L) {
+        const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h]) +
+                        (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+        dtv = pr.softplus ? softplusf_(u) : u;
+      }
+      const float cs = wave_incl_scan(dtv * pr.A[h]);
+      const float csl = lane_value(cs, kWave - 1);
+      if constexpr (DS) {
+        s_w[hh][lane] = __expf(cs);
+      } else {
+        s_w[hh][lane] = dtv * __expf(csl - cs);
+        if (lane == 0 && a.lsum) a.lsum[(b * a.nch + c) * pr.H + h] = csl;
+      }
+      if (lane == 0) s_l[hh] = csl;
+    }
+    kl_hi.consume(pr, hfirst, t0, [&](int, int s, int cl, const float* o) {
+      lds_put_row<IO>(sK + s * ldN + cl, o);
+    });
+    if (klo)
+      kl_lo.consume(prl, hfirst, t0, [&](int, int s, int cl, const float* o) {
+        lds_put_row<IO>(sKlo + s * ldN + cl, o);
+      });
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      const int k = i * HB + hh;
+      const int h = hfirst + hh;
+      stage(k, k & 1);
+      issue_step(k + 1 < nsteps ? k + 1 : k);
+      __syncthreads();
+      if (owns) {
+        const Lt* A = sA[k & 1];
+        const Lt* Alo = sAlo[SPLIT ? (k & 1) : 0];
+        const float dec = __expf(s_l[hh]);
+        {
+          const int u = hh;
+#pragma unroll
+          for (int j = 0; j < NJS; ++j) acc[u][j] *= dec;
+          mma_strip<Lt, false, false, NJS>(acc[u], A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
+          if constexpr (SPLIT) {
+            mma_strip<Lt, false, false, NJS>(acc[u], Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
+            if (klo) mma_strip<Lt, false, false, NJS>(acc[u], A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
+          }
+          // S: P_c to slot c, or E_g (last chunk) to the group buffer;
+          // dS: Q_{c-1} to slot c - 1, or F_g (first chunk) to the group buffer
+          const bool to_grp = DS ? c == c_lo : c == c_lo + ng - 1;
+          const int64_t slot = DS ? c - 1 : c;
+          float* dst = to_grp ? a.grp + ((b * a.ngr + grp) * pr.H + h) * PN
+                              : a.out + ((b * a.nch + slot) * pr.H + h) * PN;
+#pragma unroll
+          for (int j = 0; j < NJS; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[u][j][e];
+        }
+      }
+    }
+    if constexpr (!DS)
+      if (wave == 0 && lane < HB) glsum += s_l[lane];
+  }
+  if constexpr (!DS)
+    if (wave == 0 && lane < HB && a.glsum) a.glsum[(b * a.ngr + grp) * pr.H + hfirst + lane] = glsum;
+}
+
+int heads_per_group_block(const Problem& pr, int max_heads) {
+  int hb = max_heads;
+  while ((pr.H / pr.G) % hb) hb /= 2;
+  return hb;
+}
+
+template <bool DS>
+hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, float* out, float* grp,
+                         float* lsum, float* glsum, hipStream_t s) {
+  GroupArgs a{};
+  a.pr = pr;
+  a.nch = nch;
+  a.ngr = (nch + kG - 1) / kG;
+  a.hb = heads_per_group_block(pr, GroupShape<DS>::max_heads);
+  a.dout = dout;
+  a.out = out;
+  a.grp = grp;
+  a.lsum = lsum;
+  a.glsum = glsum;
+  const dim3 grid(static_cast<unsigned>(pr.B * a.ngr * (pr.H / a.hb)));
+  const dim3 block(GroupShape<DS>::waves * 64);
+  TimingScope ts(DS ? kKDstate : kKChunkStates, s);
+#define SSD_CASE(IO, PP, NN)                                                                     \
+  if (pr.P == PP && pr.N == NN) {                                                                \
+    if (a.hb == GroupShape<DS>::max_heads)                                                       \
+      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, GroupShape<DS>::max_heads>), grid,   \
+                         block, 0, s, a);                                                        \
+    else if (a.hb >= 2)                                                                          \
+      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 2>), grid, block, 0, s, a);        \
+    else                                                                                         \
+      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 1>), grid, block, 0, s, a);        \
+    return hipGetLastError();                                                                    \
+  }
+  if (pr.bf16) {
+    SSD_CASE(bf16_t, 64, 128) SSD_CASE(bf16_t, 64, 64) SSD_CASE(bf16_t, 64, 32)
+    SSD_CASE(bf16_t, 64, 16) SSD_CASE(bf16_t, 32, 128) SSD_CASE(bf16_t, 32, 64)
+    SSD_CASE(bf16_t, 32, 32) SSD_CASE(bf16_t, 32, 16)
+  } else {
+    SSD_CASE(float, 64, 64) SSD_CASE(float, 64, 32) SSD_CASE(float, 64, 16)
+    SSD_CASE(float, 32, 64) SSD_CASE(float, 32, 32) SSD_CASE(float, 32, 16)
+  }
+#undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
 int heads_per_block(const Problem& pr) {
   int hb = kMaxHb;
   while ((pr.H / pr.G) % hb) hb /= 2;
@@ -266,6 +531,17 @@ hipError_t launch_chunk_local_states(const Problem& pr, int64_t nch, float* S, f
 
 hipError_t launch_chunk_dstates(const Problem& pr, int64_t nch, View dout, float* dS, hipStream_t s) {
   return launch_states<true>(pr, nch, dout, dS, nullptr, s);
+}
+
+hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
+                                     float* lsum, float* glsum, hipStream_t s) {
+  if (pr.K > 0 && !pr.xp.p) return hipErrorInvalidValue;  // post-conv x comes from the pre-pass
+  return launch_groups<false>(pr, nch, View{nullptr, 0, 0}, Pst, Eg, lsum, glsum, s);
+}
+
+hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float* Qst, float* Fg,
+                                hipStream_t s) {
+  return launch_groups<true>(pr, nch, dout, Qst, Fg, nullptr, nullptr, s);
 }
 
 }  // namespace ssd

@@ -535,6 +535,23 @@ hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, floa
   return hipGetLastError();
 }
 
+// The same with chunk groups: in-group prefix states P_c and group end states E_g
+// (group_state_kernel), then the exclusive scan over groups from h0 turns E_g into
+// H_in(g), the state entering group g, in place.
+hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
+                                     float* lsum, float* glsum, hipStream_t s) {
+  const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
+  hipError_t err = launch_group_local_states(pr, nch, Pst, Eg, lsum, glsum, s);
+  if (err != hipSuccess) return err;
+  const int64_t ne = pr.B * pr.H * PN, ngr = (nch + kG - 1) / kG;
+  {
+    TimingScope ts(kKScan, s);
+    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0, s,
+                       pr.h0, Eg, glsum, pr.B, pr.H, PN, ngr);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s) {
   const int64_t cd = static_cast<int64_t>(pr.H) * pr.P + 2LL * pr.G * pr.N;
   const int64_t ne = pr.B * (pr.K - 1) * cd;

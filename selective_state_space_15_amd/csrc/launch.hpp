@@ -89,6 +89,19 @@ hipError_t launch_fwd(const Problem& pr, const FwdOut& o, const Plan& pl, void* 
 // conv-state copy: dst rows j < K-1 = conv inputs at t = L-(K-1)+j
 hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s);
 
+// Chunk groups of kG chunks: in-group prefix states P_c (slot c < the group's last
+// chunk) and group end states E_g, with chunk and group log-decays; in-group suffix
+// gradients Q_c and group start gradients F_g (dout / z and C rows as for the chunk
+// form).  See chunk_states.hip for the recurrences.
+constexpr int kG = 4;
+hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
+                                     float* lsum, float* glsum, hipStream_t s);
+hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float* Qst, float* Fg,
+                                hipStream_t s);
+// group_local_states, then the scan over groups: Eg[b][g][h] <- H_in(g)
+hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
+                                     float* lsum, float* glsum, hipStream_t s);
+
 // ws_H[b][c][h] <- state entering chunk c (fp32), ws_lsum[b][c][h] <- chunk log-decay
 hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
                                hipStream_t s);
