@@ -225,12 +225,13 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       pf_z[q] = *byte_off(reinterpret_cast<const uint4*>(zq_c + h * P),
                           (r * static_cast<uint32_t>(zst) + cl) * sizeof(E));
     }
-    // in-group terms from valid slots only (P_{c-1} for c > c0, Q_c for c < c1; the
-    // unused one reads slot c and is masked when staged)
-    const float* Pg = a.Ps + ((b * a.nch + (c > c_lo ? c - 1 : c)) * pr.H + h) * PN;
-    const float* Qg = a.Qs + ((b * a.nch + c) * pr.H + h) * PN;
+    // in-group terms P_{c-1} (c > c0) and Q_c (c < c1); where there is none, the load
+    // repeats the group state's (an L1 hit instead of L2 traffic) and is masked when
+    // staged
     const float* Hgg = a.Hin + ((b * a.ngr + grp) * pr.H + h) * PN;
     const float* dHgg = a.dHout + ((b * a.ngr + grp) * pr.H + h) * PN;
+    const float* Pg = c > c_lo ? a.Ps + ((b * a.nch + c - 1) * pr.H + h) * PN : Hgg;
+    const float* Qg = c < c_hi - 1 ? a.Qs + ((b * a.nch + c) * pr.H + h) * PN : dHgg;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
       const uint32_t i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
