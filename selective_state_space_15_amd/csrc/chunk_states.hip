@@ -246,11 +246,12 @@ struct GroupArgs {
 
 template <bool DS>
 struct GroupShape {
-  // the walked states of the block's heads stay in registers (32 x 16x16 fp32 tiles
-  // for 2 heads on 4 waves, or for 4 heads on 8 waves); two waves per SIMD
+  // the walked states of the block's heads stay in registers (16x16 fp32 tiles: 16 per
+  // wave for 2 heads on 4 waves, 8 per wave for 2 heads on 8 waves); two waves per SIMD.
+  // Two heads per workgroup keep enough workgroups for the 8-chunk groups.
   static constexpr int waves = DS ? 8 : 4;
   static constexpr int waves_per_simd = 2;
-  static constexpr int max_heads = DS ? 4 : 2;
+  static constexpr int max_heads = 2;
 };
 
 // HB heads per workgroup (a template parameter: the head loop is unrolled, so each

@@ -93,7 +93,7 @@ hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s);
 // chunk) and group end states E_g, with chunk and group log-decays; in-group suffix
 // gradients Q_c and group start gradients F_g (dout / z and C rows as for the chunk
 // form).  See chunk_states.hip for the recurrences.
-constexpr int kG = 4;
+constexpr int kG = 8;
 hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
                                      float* lsum, float* glsum, hipStream_t s);
 hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float* Qst, float* Fg,
