@@ -22,11 +22,14 @@
 //   dl_r  = sum_{t >= r} dcs_t,   ddt_s = (direct terms) + A dl_s,   dA = sum dt dl,
 //   dD = sum dy . x,   ddt_raw = ddt sigmoid(dt_raw + dt_bias),  ddt_bias = sum ddt_raw.
 //
-// Kernels: chunk states H_{c-1} (each chunk's own state, then a scan); the
-// per-chunk dy C^T terms (both in chunk_states.hip); scan_rev_kernel (reverse scan, dh0); bwd_main_kernel (per chunk and block of
-// heads of one group: every gradient above, dB / dC summed over the block's
-// heads in registers and written as one fp32 partial per block); then the conv
-// backward (or the dB / dC finalize without conv) and ordered parameter reductions.
+// Kernels: the chunk states, walked in groups of kG chunks (in-group prefix states and
+// the state entering each group, by a scan over groups), and the dy C^T terms walked
+// the same way in reverse (both in chunk_states.hip); scan_rev_kernel (reverse scan
+// over groups, dh0); bwd_main_kernel (per chunk and block of heads of one group: H and
+// dH from the in-group and group terms, every gradient above, dB / dC summed over the
+// block's heads in registers and written as one fp32 partial per block); then the
+// conv backward (or the dB / dC finalize without conv) and ordered parameter
+// reductions.
 #include "chunk_io.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -68,7 +71,9 @@ struct BwdArgs {
 };
 
 // ------------------------------------------------------------------ reverse scan
-// dHs[c] <- gradient leaving chunk c; g runs dH_{c-1} = exp(lsum_c) dH_c + dS_c.
+// dHs[c] <- gradient leaving step c (a group of chunks here); g runs
+// dH_{c-1} = exp(lsum_c) dH_c + dS_c, with lsum_c and dS_c the step's total log-decay
+// and its own gradient term.
 // Each thread owns 4 consecutive state elements of one head, 8 chunks of loads in flight.
 __device__ __forceinline__ float4 axpy4(float a, const float4& x, const float4& y) {
   return make_float4(fmaf(a, x.x, y.x), fmaf(a, x.y, y.y), fmaf(a, x.z, y.z), fmaf(a, x.w, y.w));

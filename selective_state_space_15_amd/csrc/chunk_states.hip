@@ -9,14 +9,18 @@
 //             w_s = dt_s exp(cs_{Q-1} - cs_s);
 //   dH_{c-1} = exp(cs_{Q-1}) dH_c   + dS_c,  dS_c[p][n] = sum_t exp(cs_t) dy_t[p] C_t[n],
 //             dy = dout * silu(z) (dout alone without the gate).
-// The chunk terms S_c and dS_c are independent across chunks; the scans over
-// chunks that turn them into H and dH run afterwards.
+// The chunk terms S_c and dS_c are independent across chunks.  Here they are summed
+// along groups of kG consecutive chunks (one workgroup per group and block of heads,
+// the walked state in MFMA accumulators), so that only one state per group goes
+// through the scans; the per-chunk states inside a group are the in-group prefix
+// (S) and suffix (dS) sums, completed with the group's carried state where the main
+// backward kernel stages them.
 //
-// One workgroup takes one chunk and a block of heads of one group.  The group's
-// B rows (S) or C rows (dS) of the chunk are staged in LDS once and reused by
-// every head of the block; each head's own rows (x, or dout and z) are loaded one
-// head ahead, so they are in flight while the previous head's MFMA product is
-// computed and stored.  bf16 I/O: dS is accumulated from split operands
+// A workgroup takes one group of chunks and a block of heads of one group of B / C
+// channels.  Each chunk's B rows (S) or C rows (dS) are staged in LDS once and reused
+// by every head of the block; each (chunk, head) step's own rows (x, or dout and z)
+// are loaded one step ahead, so they are in flight while the previous step's MFMA
+// product is computed and stored.  bf16 I/O: dS is accumulated from split operands
 // (dy_hi C_hi + dy_lo C_hi + dy_hi C_lo), since the state gradient feeds the
 // log-decay gradient through an fp32 dot with H.
 #include "chunk_io.hpp"
@@ -27,201 +31,12 @@ namespace ssd {
 
 namespace {
 
-struct StateArgs {
-  Problem pr;
-  int64_t nch;
-  int hb;         // heads per workgroup (divides H / G, at most kMaxHb)
-  View dout;      // dS only: [B][L][H*P]
-  float* out;     // [B][nch][H][P][N]: S_c or dS_c
-  float* lsum;    // S only: [B][nch][H] chunk log-decay cs_{Q-1}
-};
-
-constexpr int kMaxHb = 8;
-
-template <bool DS>
-struct StateShape {
-  // S: 4 waves, ~38 KB LDS, four workgroups per CU; dS (split operands, twice
-  // the LDS): 8 waves, two workgroups per CU
-  static constexpr int waves = DS ? 8 : 4;
-  static constexpr int waves_per_simd = 4;
-};
-
 constexpr int rows_per_task(int vec_per_row, int nthr) {
   return vec_per_row * kQ / nthr < 1 ? 1 : (vec_per_row * kQ / nthr > 8 ? 8 : vec_per_row * kQ / nthr);
 }
 
-template <typename IO, int P, int N, bool DS>
-__global__ void __launch_bounds__(StateShape<DS>::waves * 64)
-    __attribute__((amdgpu_waves_per_eu(StateShape<DS>::waves_per_simd)))
-    chunk_state_kernel(StateArgs a) {
-  constexpr int NW = StateShape<DS>::waves;
-  constexpr int NTHR = NW * 64;
-  using T = io_traits<IO>;
-  using E = typename T::elem;
-  using Lt = typename T::lds;
-  constexpr int V = T::vec;
-  constexpr int PADK = 16 / sizeof(Lt);
-  constexpr int ldN = N + PADK, ldP = P + PADK;
-  constexpr bool SPLIT = DS && sizeof(Lt) == 2;
-  __shared__ __align__(16) Lt sK[kQ * ldN];                       // B or C rows [t][n]
-  __shared__ __align__(16) Lt sKlo[SPLIT ? kQ * ldN : 8];         // C - bf16(C)
-  __shared__ __align__(16) Lt sA[2][kQ * ldP];                    // w x or exp(cs) dy, [t][p]
-  __shared__ __align__(16) Lt sAlo[SPLIT ? 2 : 1][SPLIT ? kQ * ldP : 8];
-  __shared__ float s_w[kMaxHb][kQ];                               // w_s (S) or exp(cs_t) (dS)
-
-  const Problem& pr = a.pr;
-  const int nhb = pr.H / a.hb;
-  const int64_t total = pr.B * a.nch * nhb;
-  const int64_t lid = xcd_remap(blockIdx.x, total);  // a chunk's head blocks share an XCD
-  const int hblk = static_cast<int>(lid % nhb);
-  const int64_t c = (lid / nhb) % a.nch;
-  const int b = static_cast<int>(lid / (static_cast<int64_t>(nhb) * a.nch));
-  const int hfirst = hblk * a.hb;
-  const int g = hfirst / (pr.H / pr.G);
-  const int64_t t0 = c * kQ;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const bool interior = t0 + kQ <= pr.L;
-
-  // ---- group rows of the chunk (B for S, C and its low part for dS)
-  constexpr int RB = rows_per_task(N / V, NTHR);
-  ChunkLoader<IO, P, N, false, !DS, DS, NTHR, 2, RB> kl_hi, kl_lo;
-  kl_hi.issue(pr, b, hfirst, g, t0);
-  const bool klo = SPLIT && pr.bc_lo.p != nullptr;
-  Problem prl = pr;
-  prl.bc = pr.bc_lo;
-  if (klo) kl_lo.issue(prl, b, hfirst, g, t0);
-
-  // ---- per-head rows (S: post-conv x, which the conv pre-pass provides when there
-  // is a conv; dS: dout and z), one head ahead, 16 bytes per vector
-  constexpr int NDT = ((P / V) * kQ + NTHR - 1) / NTHR;  // vectors per thread
-  uint4 dvr[NDT], zvr[DS ? NDT : 1];
-  const View rows = DS ? a.dout : (pr.K > 0 ? pr.xp : pr.xbc);  // x channels lead xbc rows
-  const E* dbase = static_cast<const E*>(rows.p) + b * rows.sb;
-  const bool gate = DS && pr.z.p != nullptr;
-  const float gw = gate ? 1.f : 0.f;
-  // without a gate the z loads repeat the dout loads (and are not used)
-  const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
-  const int64_t zst = gate ? pr.z.st : rows.st;
-  // The loads are unconditional, from clamped (valid) rows, and their values are first
-  // used when the head is staged, where rows past the end are zeroed: a select right
-  // after a load would make the wave wait for it at the point of issue.
-  auto issue_head = [&](int h) {
-#pragma unroll
-    for (int q = 0; q < NDT; ++q) {
-      const int task = min(static_cast<int>(threadIdx.x) + q * NTHR, (P / V) * kQ - 1);
-      const int col = (task % (P / V)) * V, r = task / (P / V);
-      const int64_t t = interior || t0 + r < pr.L ? t0 + r : t0;
-      dvr[q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col);
-      if constexpr (DS) zvr[q] = *reinterpret_cast<const uint4*>(zbase + t * zst + h * P + col);
-    }
-  };
-  issue_head(hfirst);
-
-  // ---- dt -> w_s / exp(cs_t) for every head of the block (wave w: heads w, w + NW, ...)
-  for (int hh = wave; hh < a.hb; hh += NW) {
-    const int h = hfirst + hh;
-    float dtv = 0.f;
-    if (t0 + lane < pr.L) {
-      const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h]) +
-                      (pr.dt_bias ? pr.dt_bias[h] : 0.f);
-      dtv = pr.softplus ? softplusf_(u) : u;
-    }
-    const float cs = wave_incl_scan(dtv * pr.A[h]);
-    if constexpr (DS) {
-      s_w[hh][lane] = __expf(cs);
-    } else {
-      const float csl = lane_value(cs, kWave - 1);
-      s_w[hh][lane] = dtv * __expf(csl - cs);
-      if (lane == 0 && a.lsum) a.lsum[(b * a.nch + c) * pr.H + h] = csl;
-    }
-  }
-  kl_hi.consume(pr, hfirst, t0, [&](int, int s, int cl, const float* o) {
-    lds_put_row<IO>(sK + s * ldN + cl, o);
-  });
-  if (klo)
-    kl_lo.consume(prl, hfirst, t0, [&](int, int s, int cl, const float* o) {
-      lds_put_row<IO>(sKlo + s * ldN + cl, o);
-    });
-  __syncthreads();
-
-  // state tiles (16 x 16 of P x N) of this wave
-  constexpr int PT = P / 16, NT = N / 16, WPP = NW / PT, NJS = (NT + WPP - 1) / WPP;
-  static_assert(NW % PT == 0, "waves must cover the state rows");
-  const int s_pi = wave % PT, s_nj0 = (wave / PT) * NJS;
-  // compile-time where every wave owns tiles: a branch here would be a control-flow
-  // merge with stores in flight, after which the next head's staging waits for all of
-  // them (not only for its own loads)
-  constexpr bool kAllOwn = NJS * WPP == NT;
-  const bool owns = kAllOwn || s_nj0 < NT;
-  const int64_t PN = static_cast<int64_t>(P) * N;
-
-  // head hh's rows, scaled, into LDS buffer buf (the other buffer may still be read by
-  // the previous head's product)
-  auto stage = [&](int hh, int buf) __attribute__((always_inline)) {
-    Lt* A = sA[buf];
-    Lt* Alo = sAlo[SPLIT ? buf : 0];
-#pragma unroll
-    for (int q = 0; q < NDT; ++q) {
-      const int task = threadIdx.x + q * NTHR;
-      if ((P / V) * kQ % NTHR != 0 && task >= (P / V) * kQ) continue;
-      const int col = (task % (P / V)) * V, r = task / (P / V);
-      const bool ok = interior || t0 + r < pr.L;  // rows past the end are zero
-      const float sc = s_w[hh][r];
-      // masked as raw words and then computed without conditions: a per-element
-      // select around SiLU becomes a branch, and a branch here makes the wave wait for
-      // the previous head's state stores as well as for these rows (the z words are
-      // always read: without a gate they hold dout rows and are weighted by 0)
-      const uint4 dq = keep_if(ok, dvr[q]);
-      float o[V], lo[V];
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        if constexpr (DS)
-          o[v] = raw_elem<IO>(dq, v) * fmaf(gw, siluf_(raw_elem<IO>(zvr[q], v)), 1.f - gw) * sc;
-        else
-          o[v] = raw_elem<IO>(dq, v) * sc;
-      }
-      if constexpr (DS)
-#pragma unroll
-        for (int v = 0; v < V; ++v) lo[v] = o[v] - T::to_f(T::from_f(o[v]));
-      lds_put_row<IO>(A + r * ldP + col, o);
-      if constexpr (SPLIT) lds_put_row<IO>(Alo + r * ldP + col, lo);
-    }
-  };
-  stage(0, 0);
-  __syncthreads();
-  // Per head: the next head's loads, this head's product and state stores, then the
-  // next head's staging, all without branches, so the wait before the staging counts
-  // exactly the loads it needs and leaves the stores in flight.  (The last head loads
-  // and stages itself again, into the idle buffer.)
-  for (int hh = 0; hh < a.hb; ++hh) {
-    const int h = hfirst + hh;
-    const int hn = hh + 1 < a.hb ? hh + 1 : hh;
-    issue_head(hfirst + hn);
-    if (owns) {
-      const Lt* A = sA[hh & 1];
-      const Lt* Alo = sAlo[SPLIT ? (hh & 1) : 0];
-      f32x4 acc[NJS];
-#pragma unroll
-      for (int j = 0; j < NJS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, false, false, NJS>(acc, A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
-      if constexpr (SPLIT) {
-        mma_strip<Lt, false, false, NJS>(acc, Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
-        if (klo) mma_strip<Lt, false, false, NJS>(acc, A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
-      }
-      float* dst = a.out + ((b * a.nch + c) * pr.H + h) * PN;
-#pragma unroll
-      for (int j = 0; j < NJS; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[j][e];
-    }
-    stage(hn, (hh + 1) & 1);
-    __syncthreads();
-  }
-}
-
 // ------------------------------------------------------------------ chunk groups
-// The same contractions, walked over a group of kG consecutive chunks per workgroup,
+// The contractions above, walked over a group of kG consecutive chunks per workgroup,
 // so that the scans only see one state per group.  With l_c the log-decay of chunk c
 // and groups [c0, c1]:
 //   S walk (forward):   P_c = exp(l_c) P_{c-1} + S_c from P_{c0-1} = 0; P_c goes to
@@ -486,53 +301,7 @@ hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, float* out, 
   return hipErrorInvalidValue;
 }
 
-int heads_per_block(const Problem& pr) {
-  int hb = kMaxHb;
-  while ((pr.H / pr.G) % hb) hb /= 2;
-  return hb;
-}
-
-template <bool DS>
-hipError_t launch_states(const Problem& pr, int64_t nch, View dout, float* out, float* lsum,
-                         hipStream_t s) {
-  StateArgs a{};
-  a.pr = pr;
-  a.nch = nch;
-  a.hb = heads_per_block(pr);
-  a.dout = dout;
-  a.out = out;
-  a.lsum = lsum;
-  const dim3 grid(static_cast<unsigned>(pr.B * nch * (pr.H / a.hb)));
-  const dim3 block(StateShape<DS>::waves * 64);
-  TimingScope ts(DS ? kKDstate : kKChunkStates, s);
-#define SSD_CASE(IO, PP, NN)                                                       \
-  if (pr.P == PP && pr.N == NN) {                                                  \
-    hipLaunchKernelGGL((chunk_state_kernel<IO, PP, NN, DS>), grid, block, 0, s, a); \
-    return hipGetLastError();                                                      \
-  }
-  if (pr.bf16) {
-    SSD_CASE(bf16_t, 64, 128) SSD_CASE(bf16_t, 64, 64) SSD_CASE(bf16_t, 64, 32)
-    SSD_CASE(bf16_t, 64, 16) SSD_CASE(bf16_t, 32, 128) SSD_CASE(bf16_t, 32, 64)
-    SSD_CASE(bf16_t, 32, 32) SSD_CASE(bf16_t, 32, 16)
-  } else {
-    SSD_CASE(float, 64, 64) SSD_CASE(float, 64, 32) SSD_CASE(float, 64, 16)
-    SSD_CASE(float, 32, 64) SSD_CASE(float, 32, 32) SSD_CASE(float, 32, 16)
-  }
-#undef SSD_CASE
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
-
-hipError_t launch_chunk_local_states(const Problem& pr, int64_t nch, float* S, float* lsum,
-                                     hipStream_t s) {
-  if (pr.K > 0 && !pr.xp.p) return hipErrorInvalidValue;  // post-conv x comes from the pre-pass
-  return launch_states<false>(pr, nch, View{nullptr, 0, 0}, S, lsum, s);
-}
-
-hipError_t launch_chunk_dstates(const Problem& pr, int64_t nch, View dout, float* dS, hipStream_t s) {
-  return launch_states<true>(pr, nch, dout, dS, nullptr, s);
-}
 
 hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
                                      float* lsum, float* glsum, hipStream_t s) {

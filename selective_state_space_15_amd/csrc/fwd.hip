@@ -518,26 +518,9 @@ hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, voi
   return err;
 }
 
-// Chunk-start states for the backward pass: each chunk's own end state and
-// log-decay (computed independently per chunk), then the exclusive scan from h0
-// turns them into H_{c-1}, the state entering chunk c.
-hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
-                               hipStream_t s) {
-  const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
-  hipError_t err = launch_chunk_local_states(pr, nch, ws_H, ws_lsum, s);
-  if (err != hipSuccess) return err;
-  const int64_t ne = pr.B * pr.H * PN;
-  {
-    TimingScope ts(kKScan, s);
-    hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0, s,
-                       pr.h0, ws_H, ws_lsum, pr.B, pr.H, PN, nch);
-  }
-  return hipGetLastError();
-}
-
-// The same with chunk groups: in-group prefix states P_c and group end states E_g
-// (group_state_kernel), then the exclusive scan over groups from h0 turns E_g into
-// H_in(g), the state entering group g, in place.
+// Chunk-group states for the backward pass: in-group prefix states P_c and group end
+// states E_g (group_state_kernel), then the exclusive scan over groups from h0 turns
+// E_g into H_in(g), the state entering group g, in place.
 hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
                                      float* lsum, float* glsum, hipStream_t s) {
   const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;

@@ -102,15 +102,6 @@ hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float
 hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
                                      float* lsum, float* glsum, hipStream_t s);
 
-// ws_H[b][c][h] <- state entering chunk c (fp32), ws_lsum[b][c][h] <- chunk log-decay
-hipError_t launch_chunk_states(const Problem& pr, int64_t nch, float* ws_H, float* ws_lsum,
-                               hipStream_t s);
-// S[b][c][h] <- the state chunk c alone leaves from a zero start, lsum[b][c][h] <- its
-// log-decay; dS[b][c][h] <- sum_t exp(cs_t) dy_t C_t^T, dy = dout * silu(z)
-hipError_t launch_chunk_local_states(const Problem& pr, int64_t nch, float* S, float* lsum,
-                                     hipStream_t s);
-hipError_t launch_chunk_dstates(const Problem& pr, int64_t nch, View dout, float* dS, hipStream_t s);
-
 // ---------------------------------------------------------------- backward
 struct BwdIn {
   View dout;                // [B,L,H*P]
