@@ -111,10 +111,7 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     return DS ? c_lo + (ng - 1 - i) : c_lo + i;
   };
 
-  constexpr int RB = rows_per_task(N / V, NTHR);
   const bool klo = SPLIT && pr.bc_lo.p != nullptr;
-  Problem prl = pr;
-  prl.bc = pr.bc_lo;
 
   constexpr int NDT = ((P / V) * kQ + NTHR - 1) / NTHR;
   uint4 dvr[NDT], zvr[DS ? NDT : 1];
@@ -178,82 +175,154 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   for (int i = 0; i < HBM; ++i)
 #pragma unroll
     for (int j = 0; j < NJS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float glsum = 0.f;  // S: group log-decay of head (lane) (wave 0 keeps it)
+  float glsum = 0.f;  // S: group log-decay of head `wave` (its lane 0 writes it)
 
-  issue_step(0);
-  for (int i = 0; i < ng; ++i) {
-    const int64_t c = DS ? c_lo + (ng - 1 - i) : c_lo + i;
+  // Group rows of a chunk (B for S; C and its low part for dS): unconditional loads of
+  // clamped rows, masked when they go to LDS.
+  constexpr int GV = N / V;                     // 16-byte vectors per row
+  constexpr int GRB = rows_per_task(GV, NTHR);  // rows per task
+  constexpr int GT = GV * (kQ / GRB);           // tasks
+  constexpr int GQ = (GT + NTHR - 1) / NTHR;    // tasks per thread
+  uint4 gr[GQ][GRB], grl[SPLIT ? GQ : 1][SPLIT ? GRB : 1];
+  const bool bcpre = pr.bc.p != nullptr;
+  const E* gsrc = static_cast<const E*>(bcpre ? pr.bc.p : pr.xbc.p) + b * (bcpre ? pr.bc.sb : pr.xbc.sb);
+  const int64_t gst = bcpre ? pr.bc.st : pr.xbc.st;
+  const int gcol = (bcpre ? 0 : pr.H * P) + (DS ? pr.G * N : 0) + g * N;
+  const E* glsrc = klo ? static_cast<const E*>(pr.bc_lo.p) + b * pr.bc_lo.sb : gsrc;
+  const int64_t glst = klo ? pr.bc_lo.st : gst;
+  const int glcol = klo ? (DS ? pr.G * N : 0) + g * N : gcol;
+  auto issue_rows = [&](int64_t c) {
     const int64_t t0 = c * kQ;
-    // the chunk's group rows and the dt of the block's heads
-    ChunkLoader<IO, P, N, false, !DS, DS, NTHR, 2, RB> kl_hi, kl_lo;
-    kl_hi.issue(pr, b, hfirst, g, t0);
-    if (klo) kl_lo.issue(prl, b, hfirst, g, t0);
-    __syncthreads();  // the previous chunk's products are done with sK, s_w, s_l
-    for (int hh = wave; hh < HB; hh += NW) {
-      const int h = hfirst + hh;
-      float dtv = 0.f;
-      if (t0 + lane < pr.L) {
-        const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + (t0 + lane) * pr.dt.st + h]) +
-                        (pr.dt_bias ? pr.dt_bias[h] : 0.f);
-        dtv = pr.softplus ? softplusf_(u) : u;
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) {
+      const int task = min(static_cast<int>(threadIdx.x) + q * NTHR, GT - 1);
+      const int cv = (task % GV) * V, r0 = (task / GV) * GRB;
+#pragma unroll
+      for (int r = 0; r < GRB; ++r) {
+        const int64_t t = t0 + r0 + r < pr.L ? t0 + r0 + r : pr.L - 1;
+        gr[q][r] = *reinterpret_cast<const uint4*>(gsrc + t * gst + gcol + cv);
+        if constexpr (SPLIT) grl[q][r] = *reinterpret_cast<const uint4*>(glsrc + t * glst + glcol + cv);
       }
-      const float cs = wave_incl_scan(dtv * pr.A[h]);
+    }
+  };
+  auto put_rows = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+#pragma unroll
+    for (int q = 0; q < GQ; ++q) {
+      const int task = threadIdx.x + q * NTHR;
+      if (GT % NTHR != 0 && task >= GT) continue;
+      const int cv = (task % GV) * V, r0 = (task / GV) * GRB;
+#pragma unroll
+      for (int r = 0; r < GRB; ++r) {
+        const bool ok = t0 + r0 + r < pr.L;  // rows past the end are zero
+        *reinterpret_cast<uint4*>(sK + (r0 + r) * ldN + cv) = keep_if(ok, gr[q][r]);
+        if constexpr (SPLIT)
+          *reinterpret_cast<uint4*>(sKlo + (r0 + r) * ldN + cv) = keep_if(ok && klo, grl[q][r]);
+      }
+    }
+  };
+  // dt of the block's heads (wave w: heads w, w + NW, ..), loaded one chunk ahead
+  constexpr int DTK = (HB + NW - 1) / NW;
+  E dtr[DTK];
+  float hbias[DTK], hA[DTK];
+#pragma unroll
+  for (int k = 0; k < DTK; ++k) {
+    const int h = hfirst + min(wave + k * NW, HB - 1);
+    hbias[k] = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+    hA[k] = pr.A[h];
+  }
+  auto issue_dt = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+    const int64_t t = t0 + lane < pr.L ? t0 + lane : pr.L - 1;
+#pragma unroll
+    for (int k = 0; k < DTK; ++k) {
+      const int h = hfirst + min(wave + k * NW, HB - 1);
+      dtr[k] = static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h];
+    }
+  };
+  // w_s (S) or exp(cs_t) (dS) and the chunk log-decay of each head; S also records
+  // the chunk log-decays (and sums the group's, when count is set)
+  auto put_dt = [&](int64_t c, bool count) {
+    const int64_t t0 = c * kQ;
+    const bool live = t0 + lane < pr.L;
+#pragma unroll
+    for (int k = 0; k < DTK; ++k) {
+      const int hh = wave + k * NW;
+      if (hh >= HB) continue;
+      const float u = T::to_f(dtr[k]) + hbias[k];
+      const float dtv = live ? (pr.softplus ? softplusf_(u) : u) : 0.f;
+      const float cs = wave_incl_scan(dtv * hA[k]);
       const float csl = lane_value(cs, kWave - 1);
       if constexpr (DS) {
         s_w[hh][lane] = __expf(cs);
       } else {
         s_w[hh][lane] = dtv * __expf(csl - cs);
-        if (lane == 0 && a.lsum) a.lsum[(b * a.nch + c) * pr.H + h] = csl;
+        if (lane == 0 && a.lsum) a.lsum[(b * a.nch + c) * pr.H + hfirst + hh] = csl;
+        if (count) glsum += csl;  // wave hh's own lanes: lane 0 writes the sum
       }
       if (lane == 0) s_l[hh] = csl;
     }
-    kl_hi.consume(pr, hfirst, t0, [&](int, int s, int cl, const float* o) {
-      lds_put_row<IO>(sK + s * ldN + cl, o);
-    });
-    if (klo)
-      kl_lo.consume(prl, hfirst, t0, [&](int, int s, int cl, const float* o) {
-        lds_put_row<IO>(sKlo + s * ldN + cl, o);
-      });
-    __syncthreads();
+  };
+
+  // Per chunk: the HB head steps (unrolled); the last one also issues the next chunk's
+  // group rows and dt, and after its product they go to LDS.  Every load is consumed in
+  // the iteration that issues it, so each wait counts exactly the loads it needs and
+  // leaves the state stores in flight.  (The last chunk reloads itself.)
+  issue_rows(chunk_of(0));
+  issue_dt(chunk_of(0));
+  issue_step(0);
+  put_rows(chunk_of(0));
+  put_dt(chunk_of(0), true);
+  __syncthreads();
+  stage(0, 0);
+  __syncthreads();
+  for (int i = 0; i < ng; ++i) {
+    const int64_t c = chunk_of(i * HB);
+    const int64_t cn = chunk_of(min(i + 1, ng - 1) * HB);
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       const int k = i * HB + hh;
       const int h = hfirst + hh;
-      stage(k, k & 1);
       issue_step(k + 1 < nsteps ? k + 1 : k);
-      __syncthreads();
+      if (hh == HB - 1) {
+        issue_rows(cn);
+        issue_dt(cn);
+      }
       if (owns) {
         const Lt* A = sA[k & 1];
         const Lt* Alo = sAlo[SPLIT ? (k & 1) : 0];
         const float dec = __expf(s_l[hh]);
-        {
-          const int u = hh;
 #pragma unroll
-          for (int j = 0; j < NJS; ++j) acc[u][j] *= dec;
-          mma_strip<Lt, false, false, NJS>(acc[u], A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
-          if constexpr (SPLIT) {
-            mma_strip<Lt, false, false, NJS>(acc[u], Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
-            if (klo) mma_strip<Lt, false, false, NJS>(acc[u], A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
-          }
-          // S: P_c to slot c, or E_g (last chunk) to the group buffer;
-          // dS: Q_{c-1} to slot c - 1, or F_g (first chunk) to the group buffer
-          const bool to_grp = DS ? c == c_lo : c == c_lo + ng - 1;
-          const int64_t slot = DS ? c - 1 : c;
-          float* dst = to_grp ? a.grp + ((b * a.ngr + grp) * pr.H + h) * PN
-                              : a.out + ((b * a.nch + slot) * pr.H + h) * PN;
-#pragma unroll
-          for (int j = 0; j < NJS; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[u][j][e];
+        for (int j = 0; j < NJS; ++j) acc[hh][j] *= dec;
+        mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
+        if constexpr (SPLIT) {
+          mma_strip<Lt, false, false, NJS>(acc[hh], Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
+          if (klo) mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
         }
+        // S: P_c to slot c, or E_g (last chunk) to the group buffer;
+        // dS: Q_{c-1} to slot c - 1, or F_g (first chunk) to the group buffer
+        const bool to_grp = DS ? c == c_lo : c == c_lo + ng - 1;
+        const int64_t slot = DS ? c - 1 : c;
+        float* dst = to_grp ? a.grp + ((b * a.ngr + grp) * pr.H + h) * PN
+                            : a.out + ((b * a.nch + slot) * pr.H + h) * PN;
+#pragma unroll
+        for (int j = 0; j < NJS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
       }
+      if (hh == HB - 1) {
+        __syncthreads();  // every product of chunk c is done with sK, s_w, s_l
+        put_rows(cn);
+        put_dt(cn, i + 1 < ng);
+        __syncthreads();
+      }
+      stage(k + 1 < nsteps ? k + 1 : k, (k + 1) & 1);
+      __syncthreads();
     }
-    if constexpr (!DS)
-      if (wave == 0 && lane < HB) glsum += s_l[lane];
   }
   if constexpr (!DS)
-    if (wave == 0 && lane < HB && a.glsum) a.glsum[(b * a.ngr + grp) * pr.H + hfirst + lane] = glsum;
+    if (wave < HB && lane == 0 && a.glsum) a.glsum[(b * a.ngr + grp) * pr.H + hfirst + wave] = glsum;
 }
 
 int heads_per_group_block(const Problem& pr, int max_heads) {
