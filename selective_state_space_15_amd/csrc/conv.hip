@@ -368,7 +368,6 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
     return silu ? gv * dsiluf_(pre) : gv;
   };
   float dw[4] = {0.f, 0.f, 0.f, 0.f}, db = 0.f;
-  E* dxb = static_cast<E*>(a.dx) + b * a.dx_sb + t_lo * a.dx_st + cwc;
   // carried-state rows (tile 0, segment 0: one whole wave)
   if (tile == 0 && seg == 0 && a.dsi != nullptr) {
     E* dsib = static_cast<E*>(a.dsi) + b * a.dsi_sb + cwc;
@@ -390,6 +389,10 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
       if (cvalid) dsib[(tau + K - 1) * a.dsi_st] = T::from_f(o);
     }
   }
+  // the walk's dx rows, stored afterwards through LDS as 16-byte row vectors
+  float outv[kSegRows];
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r) outv[r] = 0.f;
   auto walk = [&](auto edge_tag) __attribute__((always_inline)) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     float rw[7], d[4];
@@ -409,13 +412,10 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) dw[jj] = fmaf(d[0], rw[jj], dw[jj]);
       if constexpr (EDGE) {
-        const int64_t tau = t_lo + lr;
-        const int64_t js = tau - (a.L - (K - 1));
+        const int64_t js = t_lo + lr - (a.L - (K - 1));
         if (js >= 0 && js < K - 1) o += sDso[js][cl];
-        if (cvalid && tau < a.L) dxb[lr * a.dx_st] = T::from_f(o);
-      } else {
-        if (cvalid) dxb[lr * a.dx_st] = T::from_f(o);
       }
+      outv[r] = o;
 #pragma unroll
       for (int i = 0; i < 6; ++i) rw[i] = rw[i + 1];
 #pragma unroll
@@ -427,15 +427,33 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
     walk(std::false_type{});
   else if (r0 < a.L)
     walk(std::true_type{});
-  // ---- dw / db: the four segments in order, one partial per (batch, tile, channel);
-  // the sums go through the raw tile's LDS once every thread is done with it
+  // ---- dx rows and the dw / db partials go through the tiles' LDS once every thread
+  // is done with it: dx as [row][channel] in the gradient tile, then stored as 16-byte
+  // row vectors; dw / db of the four segments added in segment order, one partial per
+  // (batch, tile, channel)
   __syncthreads();
+  E* sO = reinterpret_cast<E*>(sG);  // [kTileRows][kTileCh]
+  static_assert(kTileRows * kTileCh * sizeof(E) <= sizeof(sG), "dx rows fit the gradient tile");
+#pragma unroll
+  for (int r = 0; r < kSegRows; ++r) sO[(lr0 + r) * kTileCh + cl] = T::from_f(outv[r]);
   float* sPart = reinterpret_cast<float*>(sR);  // [4 segments][5][kTileCh]
   static_assert(4 * 5 * kTileCh * sizeof(float) <= sizeof(sR), "partials fit the raw tile");
 #pragma unroll
   for (int j = 0; j < 4; ++j) sPart[(seg * 5 + j) * kTileCh + cl] = dw[j];
   sPart[(seg * 5 + 4) * kTileCh + cl] = db;
   __syncthreads();
+  {
+    constexpr int OV = kTileCh / V;  // vectors per row
+    static_assert(kTileRows * OV % 256 == 0, "dx vectors tile the block");
+    E* dxt = static_cast<E*>(a.dx) + b * a.dx_sb + t_lo * a.dx_st + c0;
+#pragma unroll
+    for (int q = 0; q < kTileRows * OV / 256; ++q) {
+      const int k = tid + 256 * q;
+      const int row = k / OV, cv = (k % OV) * V;
+      if (t_lo + row < a.L && c0 + cv < climit)
+        *reinterpret_cast<uint4*>(dxt + row * a.dx_st + cv) = *reinterpret_cast<const uint4*>(sO + row * kTileCh + cv);
+    }
+  }
   if (seg == 0 && cvalid) {
     float* pp = a.part + ((b * ntile + tile) * a.C + c) * 5;
 #pragma unroll
