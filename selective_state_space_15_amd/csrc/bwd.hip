@@ -56,8 +56,13 @@ struct BwdArgs {
   // States in chunk groups of kG chunks (chunk_states.hip): for chunk c of group g,
   //   H_{c-1} = P_{c-1} + exp(l_{c0} + .. + l_{c-1}) H_in(g)   (no P term at c = c0)
   //   dH_c    = Q_c + exp(l_{c+1} + .. + l_{c1}) dH_out(g)      (no Q term at c = c1)
-  const float* Ps;         // [B][nch][H][P][N] in-group prefix states P_c
-  const float* Qs;         // [B][nch][H][P][N] in-group suffix gradients Q_c
+  // [B][nch][H][P][N] in-group prefix states P_c and suffix gradients Q_c: fp32 for
+  // fp32 I/O; fp16 for bf16 I/O, restored by the factors Psc / Qsc
+  // [B][nch][H][state_scale_blocks] (one per block of 16 rows x state_scale_cols)
+  const void* Ps;
+  const void* Qs;
+  const float* Psc;
+  const float* Qsc;
   const float* Hin;        // [B][ngr][H][P][N] state entering each group
   const float* dHout;      // [B][ngr][H][P][N] gradient leaving each group
   const float* lsum;       // [B][nch][H] chunk log-decay
@@ -198,7 +203,14 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   static_assert(P * kQ % (V * kThreads) == 0, "the x / dout tiles must tile the block");
   constexpr int NH4 = (P * N + 4 * kThreads - 1) / (4 * kThreads);
   uint4 pf_x[NXV], pf_do[NXV], pf_z[NXV];
-  float4 hv[NH4], hg[NH4], gv[NH4], gg[NH4];  // P or H_in, Q or dH_out
+  // P_{c-1}, Q_c: 4 fp16 each (bf16 I/O, with their scale factors) or 4 fp32
+  constexpr bool F16S = sizeof(E) == 2;
+  using SV = std::conditional_t<F16S, uint2, uint4>;
+  using SE = std::conditional_t<F16S, uint16_t, float>;
+  SV hv[NH4], gv[NH4];
+  float4 hg[NH4], gg[NH4];   // H_in, dH_out
+  float hsc[NH4], gsc[NH4];  // the scale factors of hv, gv
+  constexpr int SC = state_scale_cols(P, N), kSB = state_scale_blocks(P, N);
   // without conv, x is the raw xbc channels (fields selected one by one: a selected
   // struct copy of the kernel argument would go through scratch memory)
   const bool xpre = pr.xp.p != nullptr;
@@ -230,23 +242,27 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       pf_z[q] = *byte_off(reinterpret_cast<const uint4*>(zq_c + h * P),
                           (r * static_cast<uint32_t>(zst) + cl) * sizeof(E));
     }
-    // in-group terms P_{c-1} (c > c0) and Q_c (c < c1); where there is none, the load
-    // repeats the group state's (an L1 hit instead of L2 traffic) and is masked when
-    // staged
+    // in-group terms P_{c-1} (c > c0) and Q_c (c < c1); where there is none, the
+    // loads read a valid slot and are masked when staged
     const float* Hgg = a.Hin + ((b * a.ngr + grp) * pr.H + h) * PN;
     const float* dHgg = a.dHout + ((b * a.ngr + grp) * pr.H + h) * PN;
-    const float* Pg = c > c_lo ? a.Ps + ((b * a.nch + c - 1) * pr.H + h) * PN : Hgg;
-    const float* Qg = c < c_hi - 1 ? a.Qs + ((b * a.nch + c) * pr.H + h) * PN : dHgg;
+    const int64_t pslot = ((b * a.nch + (c > 0 ? c - 1 : 0)) * pr.H + h), qslot = (b * a.nch + c) * pr.H + h;
+    const SE* Pg = static_cast<const SE*>(a.Ps) + pslot * PN;
+    const SE* Qg = static_cast<const SE*>(a.Qs) + qslot * PN;
 #pragma unroll
     for (int q = 0; q < NH4; ++q) {
       const uint32_t i = min((static_cast<int>(threadIdx.x) + q * kThreads) * 4, P * N - 4);
+      // scale block of elements i .. i+3 (one row p, four columns n)
+      const uint32_t blk = (i / N) / 16 * (N / SC) + (i % N) / SC;
       if (part == 1) {
-        hv[q] = *reinterpret_cast<const float4*>(Pg + i);
+        hv[q] = *reinterpret_cast<const SV*>(Pg + i);
         hg[q] = *reinterpret_cast<const float4*>(Hgg + i);
+        if constexpr (F16S) hsc[q] = a.Psc[pslot * kSB + blk];
       }
       if (part == 2) {
-        gv[q] = *reinterpret_cast<const float4*>(Qg + i);
+        gv[q] = *reinterpret_cast<const SV*>(Qg + i);
         gg[q] = *reinterpret_cast<const float4*>(dHgg + i);
+        if constexpr (F16S) gsc[q] = a.Qsc[qslot * kSB + blk];
       }
     }
   };
@@ -371,8 +387,16 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       const int i = (threadIdx.x + q * kThreads) * 4;
       if (NH4 * 4 * kThreads == P * N || i < P * N) {
         const int p = i / N, n = i % N;
-        const float4 pv = useP ? hv[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 qv = useQ ? gv[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const SV ph = keep_if(useP, hv[q]), qh = keep_if(useQ, gv[q]);
+        float4 pv, qv;
+        if constexpr (F16S) {
+          const float ps = useP ? hsc[q] : 0.f, qs = useQ ? gsc[q] : 0.f;
+          pv = make_float4(ps * h2f_lo(ph.x), ps * h2f_hi(ph.x), ps * h2f_lo(ph.y), ps * h2f_hi(ph.y));
+          qv = make_float4(qs * h2f_lo(qh.x), qs * h2f_hi(qh.x), qs * h2f_lo(qh.y), qs * h2f_hi(qh.y));
+        } else {
+          pv = make_float4(__uint_as_float(ph.x), __uint_as_float(ph.y), __uint_as_float(ph.z), __uint_as_float(ph.w));
+          qv = make_float4(__uint_as_float(qh.x), __uint_as_float(qh.y), __uint_as_float(qh.z), __uint_as_float(qh.w));
+        }
         const float hf[4] = {fmaf(aH, hg[q].x, pv.x), fmaf(aH, hg[q].y, pv.y), fmaf(aH, hg[q].z, pv.z),
                              fmaf(aH, hg[q].w, pv.w)};
         const float df[4] = {fmaf(bD, gg[q].x, qv.x), fmaf(bD, gg[q].y, qv.y), fmaf(bD, gg[q].z, qv.z),
@@ -696,7 +720,7 @@ __global__ void __launch_bounds__(256) head_params_kernel(const float* par, int6
 }
 
 struct BwdLayout {
-  size_t bc, bc_lo, xp, H, lsum, dH, Hg, dHg, glsum, dbc, par, dx, conv, total;
+  size_t bc, bc_lo, xp, H, Hsc, lsum, dH, dHsc, Hg, dHg, glsum, dbc, par, dx, conv, total;
   int64_t nch, ngr;
   int hb_heads, nhb;
 };
@@ -722,9 +746,13 @@ BwdLayout bwd_layout(const Problem& pr) {
   l.bc = take(bc_prepass_bytes(pr));
   l.bc_lo = take(pr.bf16 ? bc_prepass_bytes(pr) : 0);
   l.xp = take(x_prepass_bytes(pr));
-  l.H = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
+  const size_t ss = pr.bf16 ? 2 : 4;  // slot state element: fp16 or fp32
+  l.H = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * ss);
+  const size_t nsb = pr.bf16 ? state_scale_blocks(pr.P, pr.N) : 0;
+  l.Hsc = take(static_cast<size_t>(pr.B) * l.nch * pr.H * nsb * 4);
   l.lsum = take(static_cast<size_t>(pr.B) * l.nch * pr.H * 4);
-  l.dH = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * 4);
+  l.dH = take(static_cast<size_t>(pr.B) * l.nch * pr.H * PN * ss);
+  l.dHsc = take(static_cast<size_t>(pr.B) * l.nch * pr.H * nsb * 4);
   l.Hg = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * PN * 4);
   l.dHg = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * PN * 4);
   l.glsum = take(static_cast<size_t>(pr.B) * l.ngr * pr.H * 4);
@@ -745,14 +773,18 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   a.nch = l.nch;
   a.hb_heads = l.hb_heads;
   a.nhb = l.nhb;
-  float* Ps = reinterpret_cast<float*>(ws + l.H);
-  float* Qs = reinterpret_cast<float*>(ws + l.dH);
+  void* Ps = ws + l.H;
+  void* Qs = ws + l.dH;
+  float* Psc = reinterpret_cast<float*>(ws + l.Hsc);
+  float* Qsc = reinterpret_cast<float*>(ws + l.dHsc);
   float* Hg = reinterpret_cast<float*>(ws + l.Hg);
   float* dHg = reinterpret_cast<float*>(ws + l.dHg);
   float* lsum = reinterpret_cast<float*>(ws + l.lsum);
   float* glsum = reinterpret_cast<float*>(ws + l.glsum);
   a.Ps = Ps;
   a.Qs = Qs;
+  a.Psc = Psc;
+  a.Qsc = Qsc;
   a.Hin = Hg;
   a.dHout = dHg;
   a.lsum = lsum;
@@ -771,11 +803,11 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   const int64_t PN = static_cast<int64_t>(P) * N;
   const int64_t ne = pr.B * pr.H * PN;
   // 1. in-group prefix states and, by a scan over groups, the state entering each group
-  hipError_t e = launch_group_chunk_states(pr, l.nch, Ps, Hg, lsum, glsum, s);
+  hipError_t e = launch_group_chunk_states(pr, l.nch, Ps, Psc, Hg, lsum, glsum, s);
   if (e != hipSuccess) return e;
   // 2. in-group suffix gradients, 3. reverse scan over groups -> gradient leaving each
   // group, dh0
-  e = launch_group_dstates(pr, l.nch, in.dout, Qs, dHg, s);
+  e = launch_group_dstates(pr, l.nch, in.dout, Qs, Qsc, dHg, s);
   if (e != hipSuccess) return e;
   {
     TimingScope ts(kKScanRev, s);

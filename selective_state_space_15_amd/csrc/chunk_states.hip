@@ -43,6 +43,9 @@ constexpr int rows_per_task(int vec_per_row, int nthr) {
 //                       slot c for c < c1 and E_g = P_{c1} to the group buffer;
 //   dS walk (reverse):  Q_{c-1} = exp(l_c) Q_c + dS_c from Q_{c1} = 0; Q_c goes to
 //                       slot c for c0 <= c < c1 and F_g = Q_{c0-1} to the group buffer.
+// (Slot c1, read by no chunk, takes the slot-format copy of E_g / F_g.)  The group
+// buffers are fp32; the slots are fp32 for fp32 I/O and, for bf16 I/O, fp16 with one
+// power-of-two scale per block of 16 rows x state_scale_cols columns.
 // The group scans then give H_in(g) (the state entering group g) and dH_out(g) (the
 // gradient leaving it), and for chunk c of group g
 //   H_{c-1} = P_{c-1} + exp(l_{c0} + .. + l_{c-1}) H_in(g)      (P_{c0-1} = 0)
@@ -53,7 +56,8 @@ struct GroupArgs {
   int64_t nch, ngr;
   int hb;         // heads per workgroup (divides H / G, at most GroupShape::max_heads)
   View dout;      // dS only
-  float* out;     // [B][nch][H][P][N]: P_c (S) or Q_c (dS)
+  void* out;      // [B][nch][H][P][N]: P_c (S) or Q_c (dS); bf16 I/O: fp16 times 2^k
+  float* oscale;  // [B][nch][H][state_scale_blocks]: 2^-k, restoring a block (bf16 I/O)
   float* grp;     // [B][ngr][H][P][N]: E_g (S) or F_g (dS)
   float* lsum;    // S only: [B][nch][H] chunk log-decay
   float* glsum;   // S only: [B][ngr][H] group log-decay
@@ -85,6 +89,9 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   constexpr int PADK = 16 / sizeof(Lt);
   constexpr int ldN = N + PADK, ldP = P + PADK;
   constexpr bool SPLIT = DS && sizeof(Lt) == 2;
+  // bf16 I/O keeps the slot states in fp16 (scaled); fp32 I/O keeps them in fp32
+  constexpr bool F16S = sizeof(E) == 2;
+  constexpr int SC = state_scale_cols(P, N), JB = SC / 16, kSB = state_scale_blocks(P, N);
   __shared__ __align__(16) Lt sK[kQ * ldN];                       // B or C rows [t][n]
   __shared__ __align__(16) Lt sKlo[SPLIT ? kQ * ldN : 8];         // C - bf16(C)
   __shared__ __align__(16) Lt sA[2][kQ * ldP];                    // w x or exp(cs) dy, [t][p]
@@ -164,11 +171,13 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     }
   };
 
+  // A wave holds NJS 16 x 16 tiles of one 16-row strip of the P x N state.
   constexpr int PT = P / 16, NT = N / 16, WPP = NW / PT, NJS = (NT + WPP - 1) / WPP;
   static_assert(NW % PT == 0, "waves must cover the state rows");
   const int s_pi = wave % PT, s_nj0 = (wave / PT) * NJS;
   constexpr bool kAllOwn = NJS * WPP == NT;
   const bool owns = kAllOwn || s_nj0 < NT;
+  static_assert(NJS % JB == 0, "a wave's state tiles cover whole scale blocks");
   const int64_t PN = static_cast<int64_t>(P) * N;
   f32x4 acc[HBM][NJS];
 #pragma unroll
@@ -299,17 +308,51 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
           mma_strip<Lt, false, false, NJS>(acc[hh], Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
           if (klo) mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
         }
-        // S: P_c to slot c, or E_g (last chunk) to the group buffer;
-        // dS: Q_{c-1} to slot c - 1, or F_g (first chunk) to the group buffer
-        const bool to_grp = DS ? c == c_lo : c == c_lo + ng - 1;
-        const int64_t slot = DS ? c - 1 : c;
-        float* dst = to_grp ? a.grp + ((b * a.ngr + grp) * pr.H + h) * PN
-                            : a.out + ((b * a.nch + slot) * pr.H + h) * PN;
+      }
+      // S: P_c to slot c; dS: Q_{c-1} to slot c - 1.  The group's end state (S, last
+      // chunk) and start gradient (dS, first chunk) go to the group buffer after the
+      // walk; their slot copies land in slot c1, which no chunk reads (every step stores
+      // the same way: no branch around the stores, whose waits would then take the
+      // loads in flight with them).
+      if (owns) {
+        const int64_t c1 = c_lo + ng - 1;
+        const int64_t slot = DS ? (c == c_lo ? c1 : c - 1) : c;
+        const int64_t so = ((b * a.nch + slot) * pr.H + h) * PN;
+        // a wave's stores cover whole rows of its columns: each cache line of the state
+        // is written by one wave, within a few instructions
+        if constexpr (!F16S) {
+          float* dst = static_cast<float*>(a.out) + so;
 #pragma unroll
-        for (int j = 0; j < NJS; ++j)
+          for (int j = 0; j < NJS; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
+            for (int e = 0; e < 4; ++e)
+              dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
+        } else {
+          // bf16 I/O: fp16 times 2^k per scale block, with k such that the block's
+          // largest magnitude lands in [2^14, 2^15): every value keeps fp16's 11-bit
+          // precision down to 2^-29 of that maximum, and none overflows.
+          uint16_t* dst = static_cast<uint16_t*>(a.out) + so;
+          float* sdst = a.oscale + ((b * a.nch + slot) * pr.H + h) * kSB;
+#pragma unroll
+          for (int jb = 0; jb < NJS; jb += JB) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = jb; j < jb + JB; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[hh][j][e]));
+            const int ex = static_cast<int>((__float_as_uint(wave_max(m)) >> 23) & 0xffu);
+            const int kx = min(141 - ex, 126);  // ex >= 15: 2^(ex-127) <= max < 2^(ex-126)
+            const float up = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+#pragma unroll
+            for (int j = jb; j < jb + JB; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] =
+                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[hh][j][e] * up));
+            // every lane stores the same value (a lane branch would be one around a store)
+            sdst[s_pi * (N / SC) + (s_nj0 + jb) * 16 / SC] = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+          }
+        }
       }
       if (hh == HB - 1) {
         __syncthreads();  // every product of chunk c is done with sK, s_w, s_l
@@ -319,6 +362,19 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
       }
       stage(k + 1 < nsteps ? k + 1 : k, (k + 1) & 1);
       __syncthreads();
+    }
+  }
+  // E_g (S: the state after the group's last chunk) or F_g (dS: the gradient after its
+  // first chunk), fp32
+  if (owns) {
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      float* dst = a.grp + ((b * a.ngr + grp) * pr.H + hfirst + hh) * PN;
+#pragma unroll
+      for (int j = 0; j < NJS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
     }
   }
   if constexpr (!DS)
@@ -332,8 +388,8 @@ int heads_per_group_block(const Problem& pr, int max_heads) {
 }
 
 template <bool DS>
-hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, float* out, float* grp,
-                         float* lsum, float* glsum, hipStream_t s) {
+hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, void* out, float* oscale,
+                         float* grp, float* lsum, float* glsum, hipStream_t s) {
   GroupArgs a{};
   a.pr = pr;
   a.nch = nch;
@@ -341,6 +397,7 @@ hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, float* out, 
   a.hb = heads_per_group_block(pr, GroupShape<DS>::max_heads);
   a.dout = dout;
   a.out = out;
+  a.oscale = oscale;
   a.grp = grp;
   a.lsum = lsum;
   a.glsum = glsum;
@@ -372,15 +429,15 @@ hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, float* out, 
 
 }  // namespace
 
-hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
-                                     float* lsum, float* glsum, hipStream_t s) {
+hipError_t launch_group_local_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
+                                     float* Eg, float* lsum, float* glsum, hipStream_t s) {
   if (pr.K > 0 && !pr.xp.p) return hipErrorInvalidValue;  // post-conv x comes from the pre-pass
-  return launch_groups<false>(pr, nch, View{nullptr, 0, 0}, Pst, Eg, lsum, glsum, s);
+  return launch_groups<false>(pr, nch, View{nullptr, 0, 0}, Pst, Psc, Eg, lsum, glsum, s);
 }
 
-hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float* Qst, float* Fg,
-                                hipStream_t s) {
-  return launch_groups<true>(pr, nch, dout, Qst, Fg, nullptr, nullptr, s);
+hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, void* Qst,
+                                float* Qsc, float* Fg, hipStream_t s) {
+  return launch_groups<true>(pr, nch, dout, Qst, Qsc, Fg, nullptr, nullptr, s);
 }
 
 }  // namespace ssd

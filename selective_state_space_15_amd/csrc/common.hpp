@@ -47,6 +47,19 @@ __device__ __forceinline__ uint32_t f2bf2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two fp32 -> packed fp16 pair (low half = a), each rounded to nearest even; and back.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2h2(float a, float b) {
+  const f16x2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float h2f_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2, w).x);
+}
+__device__ __forceinline__ float h2f_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(f16x2, w).y);
+}
+
 // ---------------------------------------------------------------- I/O traits
 template <typename IO>
 struct io_traits;
@@ -120,6 +133,9 @@ __device__ __forceinline__ float raw_elem(const uint4& raw, int v) {
 __device__ __forceinline__ uint4 keep_if(bool keep, const uint4& v) {
   return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
+__device__ __forceinline__ uint2 keep_if(bool keep, const uint2& v) {
+  return make_uint2(keep ? v.x : 0u, keep ? v.y : 0u);
+}
 
 template <typename IO>
 __device__ __forceinline__ void zero_vec16(vec16<IO>& out) {
@@ -185,6 +201,18 @@ __device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<kDppRowHalfMirror>(0.f, v);
   v += dpp_f<kDppRowMirror>(0.f, v);
   return v;
+}
+
+// Maximum over the 64 lanes of a wave, in every lane (row maxima, then the four rows).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuad1032>(0.f, v));
+  v = fmaxf(v, dpp_f<kDppQuad2301>(0.f, v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(0.f, v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(0.f, v));
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48))));
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele inside each

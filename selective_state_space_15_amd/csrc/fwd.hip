@@ -521,10 +521,10 @@ hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, voi
 // Chunk-group states for the backward pass: in-group prefix states P_c and group end
 // states E_g (group_state_kernel), then the exclusive scan over groups from h0 turns
 // E_g into H_in(g), the state entering group g, in place.
-hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
-                                     float* lsum, float* glsum, hipStream_t s) {
+hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
+                                     float* Eg, float* lsum, float* glsum, hipStream_t s) {
   const int64_t PN = static_cast<int64_t>(pr.P) * pr.N;
-  hipError_t err = launch_group_local_states(pr, nch, Pst, Eg, lsum, glsum, s);
+  hipError_t err = launch_group_local_states(pr, nch, Pst, Psc, Eg, lsum, glsum, s);
   if (err != hipSuccess) return err;
   const int64_t ne = pr.B * pr.H * PN, ngr = (nch + kG - 1) / kG;
   {

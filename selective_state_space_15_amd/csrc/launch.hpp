@@ -92,15 +92,24 @@ hipError_t launch_conv_state_out(const Problem& pr, MView dst, hipStream_t s);
 // Chunk groups of kG chunks: in-group prefix states P_c (slot c < the group's last
 // chunk) and group end states E_g, with chunk and group log-decays; in-group suffix
 // gradients Q_c and group start gradients F_g (dout / z and C rows as for the chunk
-// form).  See chunk_states.hip for the recurrences.
+// form).  See chunk_states.hip for the recurrences.  The slot states are
+// [B][nch][H][P][N]: fp32 for fp32 I/O; for bf16 I/O fp16, each block of 16 rows (p) x
+// state_scale_cols columns (n) scaled by a power of two, with Psc / Qsc
+// [B][nch][H][state_scale_blocks] holding the factors that restore them (block
+// p / 16 * (N / state_scale_cols) + n / state_scale_cols).  E_g and F_g are fp32.
 constexpr int kG = 8;
-hipError_t launch_group_local_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
-                                     float* lsum, float* glsum, hipStream_t s);
-hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, float* Qst, float* Fg,
-                                hipStream_t s);
+// the columns of one of 8 waves spread over the 16-row strips of a P x N state
+constexpr int state_scale_cols(int P, int N) {
+  return 16 * ((N / 16 + 8 / (P / 16) - 1) / (8 / (P / 16)));
+}
+constexpr int state_scale_blocks(int P, int N) { return (P / 16) * (N / state_scale_cols(P, N)); }
+hipError_t launch_group_local_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
+                                     float* Eg, float* lsum, float* glsum, hipStream_t s);
+hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, void* Qst,
+                                float* Qsc, float* Fg, hipStream_t s);
 // group_local_states, then the scan over groups: Eg[b][g][h] <- H_in(g)
-hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, float* Pst, float* Eg,
-                                     float* lsum, float* glsum, hipStream_t s);
+hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
+                                     float* Eg, float* lsum, float* glsum, hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 struct BwdIn {
