@@ -460,8 +460,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     f32x4 yacc[PJw];
 #pragma unroll
     for (int j = 0; j < PJw; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, p0, N);
-    if (clo) mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sClo, ldN, m0, sH, ldN, p0, N);
+    if (clo)
+      mma_strip2<Lt, true, true, PJw, kMainUnroll>(yacc, sC, sClo, ldN, m0, sH, ldN, p0, N);
+    else
+      mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, p0, N);
     float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -505,8 +507,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       f32x4 dyx[QJw];
 #pragma unroll
       for (int j = 0; j < QJw; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, s0, P);
-      if constexpr (SPLIT) mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDYlo, ldP, m0, sX, ldP, s0, P);
+      if constexpr (SPLIT)
+        mma_strip2<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, sDYlo, ldP, m0, sX, ldP, s0, P);
+      else
+        mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, s0, P);
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QJw; ++j) {

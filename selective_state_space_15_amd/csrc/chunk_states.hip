@@ -303,10 +303,11 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
         const float dec = __expf(s_l[hh]);
 #pragma unroll
         for (int j = 0; j < NJS; ++j) acc[hh][j] *= dec;
-        mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
         if constexpr (SPLIT) {
-          mma_strip<Lt, false, false, NJS>(acc[hh], Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
+          mma_strip2<Lt, false, false, NJS>(acc[hh], A, Alo, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
           if (klo) mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sKlo, ldN, s_nj0 * 16, kQ);
+        } else {
+          mma_strip<Lt, false, false, NJS>(acc[hh], A, ldP, s_pi * 16, sK, ldN, s_nj0 * 16, kQ);
         }
       }
       // S: P_c to slot c; dS: Q_{c-1} to slot c - 1.  The group's end state (S, last

@@ -324,6 +324,38 @@ __device__ __forceinline__ void mma_strip(f32x4 (&acc)[NJ], const L* A, int lda,
   }
 }
 
+// acc[j] += (A1 + A2)(16 x K) * B_j(K x 16), A1 and A2 stored alike (the two parts of
+// a split operand): each B fragment is read once for both products.  The A1 products
+// of all tiles issue before the A2 ones, so no MFMA waits on the one before it.
+template <typename L, bool akc, bool bkc, int NJ, int UNROLL = 1>
+__device__ __forceinline__ void mma_strip2(f32x4 (&acc)[NJ], const L* A1, const L* A2, int lda, int m0,
+                                           const L* B, int ldb, int n0, int K) {
+  constexpr int kstep = sizeof(L) == 2 ? 32 : 4;
+  constexpr int kpl = sizeof(L) == 2 ? 8 : 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  const int kg = lane >> 4;
+#pragma unroll UNROLL
+  for (int k0 = 0; k0 < K; k0 += kstep) {
+    const int kr = k0 + kpl * kg;
+    const bool kin = kr < K;
+    const int k = kin ? kr : 0;
+    const auto a1v = frag<L, akc>::get(A1, lda, m0 + r, k);
+    const auto a2v = frag<L, akc>::get(A2, lda, m0 + r, k);
+    const auto a1 = kin ? a1v : frag<L, akc>::zero();
+    const auto a2 = kin ? a2v : frag<L, akc>::zero();
+    typename frag<L, bkc>::type b[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const auto bv = frag<L, bkc>::get(B, ldb, n0 + 16 * j + r, k);
+      b[j] = kin ? bv : frag<L, bkc>::zero();
+      acc[j] = mfma_step(a1, b[j], acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mfma_step(a2, b[j], acc[j]);
+  }
+}
+
 // Ordered column sums of a row-major [rows][cols] fp32 matrix, 64 columns per
 // 256-thread block (column blockIdx.x * 64 + lane).  Wave w adds rows w, w + 4,
 // w + 8, ... with 16 loads in flight; the four wave partials are then added in
