@@ -39,6 +39,70 @@ struct ChunkLoader {
   static constexpr int BT = (NTB + NTHR - 1) / NTHR;             // B/C tasks per thread
   uint4 xin[XT > 0 ? XT : 1][RX + 3];
   uint4 bin[BT > 0 ? BT : 1][RB];
+  // issue_raw(): which loaded vectors are live (bit q (RX + 3) + i for x, then
+  // XT (RX + 3) + q RB + r for B / C); the others are zeroed when consumed
+  static constexpr int kXBits = DX ? XT * (RX + 3) : 0;
+  static_assert(kXBits + (DB || DC ? BT * RB : 0) <= 32, "mask bits fit one word");
+  uint32_t okm = 0;
+
+  // Branch-free form of issue(): every load reads a valid row (clamped into the
+  // sequence, or the carried conv state), nothing here uses the loaded values, and
+  // the masks are kept as bits for consume_raw_lds_taps().  Issued a chunk ahead, the
+  // loads stay in flight until the consuming chunk: a branch around a load, or a
+  // select right after it, would make the wave wait for it at once.
+  __device__ __forceinline__ void issue_raw(const Problem& pr, int b, int h, int g, int64_t t0) {
+    const int K = pr.K;
+    uint32_t m = 0;
+    if constexpr (DX) {
+      const bool pre = XPRE && pr.xp.p != nullptr;  // post-conv rows: slots 3 ..
+      const E* base = pre ? static_cast<const E*>(pr.xp.p) + b * pr.xp.sb
+                          : static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
+      const int64_t st = pre ? pr.xp.st : pr.xbc.st;
+      const E* csi = pr.cs_in.p ? static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb : nullptr;
+#pragma unroll
+      for (int q = 0; q < XT; ++q) {
+        const int task = threadIdx.x + q * NTHR;
+        const int cl = (task % (P / V)) * V;
+        const int r0 = (task / (P / V)) * RX;
+        const int c = h * P + cl;
+#pragma unroll
+        for (int i = 0; i < RX + 3; ++i) {
+          const int64_t t = t0 + r0 - 3 + i;
+          const bool live = task < NTX && !((K == 0 || pre) && i < 3) && t < pr.L;
+          const bool from_state = t < 0 && !pre && csi && t >= -(K - 1);
+          const bool ok = live && (t >= 0 || from_state);
+          const int64_t tc = t < 0 ? 0 : (t < pr.L ? t : pr.L - 1);
+          const E* src = from_state ? csi + (t + K - 1) * pr.cs_in.st + c : base + tc * st + c;
+          xin[q][i] = *reinterpret_cast<const uint4*>(src);
+          m |= (ok ? 1u : 0u) << (q * (RX + 3) + i);
+        }
+      }
+    }
+    if constexpr (DB || DC) {
+      const bool pre = pr.bc.p != nullptr;
+      const E* src = pre ? static_cast<const E*>(pr.bc.p) + b * pr.bc.sb
+                         : static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb;
+      const int64_t sst = pre ? pr.bc.st : pr.xbc.st;
+      const int cB = (pre ? 0 : pr.H * P) + g * N;
+      const int cC = (pre ? 0 : pr.H * P) + pr.G * N + g * N;
+#pragma unroll
+      for (int q = 0; q < BT; ++q) {
+        const int task = threadIdx.x + q * NTHR;
+        const int grp = task % (GB + GC);
+        const int r0 = (task / (GB + GC)) * RB;
+        const bool isB = grp < GB;
+        const E* col = src + (isB ? cB + grp * V : cC + (grp - GB) * V);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int64_t t = t0 + r0 + r;
+          const bool ok = task < NTB && t < pr.L;
+          bin[q][r] = *reinterpret_cast<const uint4*>(col + (t < pr.L ? t : pr.L - 1) * sst);
+          m |= (ok ? 1u : 0u) << (kXBits + q * RB + r);
+        }
+      }
+    }
+    okm = m;
+  }
 
   __device__ __forceinline__ void issue(const Problem& pr, int b, int h, int g, int64_t t0) {
     // interior chunk: every row it touches (conv halo included) is inside the
@@ -158,10 +222,24 @@ struct ChunkLoader {
                                                    const float* wl) const {
     consume_impl<true>(pr, h, t0, put, wl);
   }
+  // after issue_raw(): the masks are applied here
+  template <typename F>
+  __device__ __forceinline__ void consume_raw_lds_taps(const Problem& pr, int h, int64_t t0, F&& put,
+                                                       const float* wl) const {
+    consume_impl<true, true>(pr, h, t0, put, wl);
+  }
 
-  template <bool WLDS, typename F>
+  template <bool WLDS, bool RAW = false, typename F>
   __device__ __forceinline__ void consume_impl(const Problem& pr, int h, int64_t t0, F&& put,
                                                const float* wl) const {
+    auto xv = [&](int q, int i) -> uint4 {
+      if constexpr (RAW) return keep_if((okm >> (q * (RX + 3) + i)) & 1u, xin[q][i]);
+      else return xin[q][i];
+    };
+    auto bv = [&](int q, int r) -> uint4 {
+      if constexpr (RAW) return keep_if((okm >> (kXBits + q * RB + r)) & 1u, bin[q][r]);
+      else return bin[q][r];
+    };
     const int K = pr.K;
     if constexpr (DX) {
 #pragma unroll
@@ -201,12 +279,12 @@ struct ChunkLoader {
             for (int v = 0; v < V; ++v) {
               float pre = bias[v];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(xin[q][r + j], v), pre);
+              for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(xv(q, r + j), v), pre);
               o[v] = siluf_(pre);
             }
           } else {
 #pragma unroll
-            for (int v = 0; v < V; ++v) o[v] = raw_elem<IO>(xin[q][r + 3], v);
+            for (int v = 0; v < V; ++v) o[v] = raw_elem<IO>(xv(q, r + 3), v);
           }
           if (t0 + r0 + r >= pr.L)
 #pragma unroll
@@ -228,7 +306,7 @@ struct ChunkLoader {
         for (int r = 0; r < RB; ++r) {
           float o[V];
 #pragma unroll
-          for (int v = 0; v < V; ++v) o[v] = raw_elem<IO>(bin[q][r], v);
+          for (int v = 0; v < V; ++v) o[v] = raw_elem<IO>(bv(q, r), v);
           put(seg, r0 + r, cl, o);
         }
       }

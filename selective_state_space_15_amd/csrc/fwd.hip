@@ -153,13 +153,18 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   }
 
   // Everything a chunk reads from global memory (raw x rows, post-conv B/C rows,
-  // dt, z) is prefetched into registers one chunk ahead, so those loads are in
-  // flight while the previous chunk computes.
+  // dt) is prefetched into registers one chunk ahead, so those loads are in flight
+  // while the previous chunk computes; z is loaded when the chunk is staged and used
+  // in its epilogue.
   const E* dtp = static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + h;
   const E* zp = OUT && gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
   const int64_t tbeg = k * a.cps * kQ;
   constexpr int RXL = HALVES == 1 ? 2 : 1;  // x rows per loader task: all threads busy
-  constexpr int RBL = 8 / HALVES;           // B/C rows per loader task
+  // B/C rows per loader task: as many tasks as threads (every thread's loads are
+  // issued, a task's or not)
+  constexpr int RBL = (OUT ? 2 : 1) * (N / (16 / static_cast<int>(sizeof(E)))) * kQ / NTHR > 0
+                          ? (OUT ? 2 : 1) * (N / (16 / static_cast<int>(sizeof(E)))) * kQ / NTHR
+                          : 1;
   ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL, !OUT> ld;
   E dt_raw{};
   // gate inputs of this thread's output vectors (row k / (P / V), columns
@@ -182,10 +187,9 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       }
     }
   };
-  // dt is prefetched one chunk ahead; the row loads are issued right before use
-  // (holding them across the MFMA phase costs more registers than 2 waves/SIMD allow)
-  // (unconditional, from a clamped row: a load under a branch would be waited for at
-  // once, and with it every load still in flight; rows past the end are masked in (1))
+  // dt of the next chunk (unconditional, from a clamped row: a load under a branch
+  // would be waited for at once, and with it every load still in flight; rows past
+  // the end are masked in (1))
   // The raw element is kept as loaded and converted in (1): converting it here would
   // make the wave wait for the load at once.  Every wave loads it (no branch); wave 0
   // uses it.
@@ -194,6 +198,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     dt_raw = *byte_off(dtp + tn * pr.dt.st, r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
   };
   prefetch(tbeg);
+  ld.issue_raw(pr, b, h, g, tbeg);
 
   float lsum = 0.f;
   for (int64_t c = 0; c < a.cps; ++c) {
@@ -227,10 +232,10 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     lsum += cs_last;
     // (2) conv + stores into LDS
     //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
-    ld.issue(pr, b, h, g, t0);
-    // issued after the row loads, so waiting for those does not wait for these
-    prefetch_z(t0);  // consumed in the epilogue, after the MFMAs
-    ld.consume_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
+    // z first: the epilogue's wait for it then leaves the next chunk's loads, issued
+    // after it, in flight
+    prefetch_z(t0);
+    ld.consume_raw_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
       if (seg == 0) {
         const float ws = s_w[s];
         float ow[V];
@@ -242,8 +247,13 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
       }
     }, s_conv);
-    // next chunk's loads go in flight now
-    if (c + 1 < a.cps && t0 + kQ < pr.L) prefetch(t0 + kQ);
+    // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
+    // the row loads in flight); the last chunk reloads its own rows
+    {
+      const int64_t tn = c + 1 < a.cps && t0 + kQ < pr.L ? t0 + kQ : t0;
+      prefetch(tn);
+      ld.issue_raw(pr, b, h, g, tn);
+    }
     __syncthreads();
 
     if constexpr (OUT) {
