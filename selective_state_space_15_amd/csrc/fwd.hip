@@ -159,13 +159,54 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   const E* dtp = static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + h;
   const E* zp = OUT && gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
   const int64_t tbeg = k * a.cps * kQ;
-  constexpr int RXL = HALVES == 1 ? 2 : 1;  // x rows per loader task: all threads busy
   // B/C rows per loader task: as many tasks as threads (every thread's loads are
   // issued, a task's or not)
   constexpr int RBL = (OUT ? 2 : 1) * (N / (16 / static_cast<int>(sizeof(E)))) * kQ / NTHR > 0
                           ? (OUT ? 2 : 1) * (N / (16 / static_cast<int>(sizeof(E)))) * kQ / NTHR
                           : 1;
-  ChunkLoader<IO, P, N, true, true, OUT, NTHR, RXL, RBL, !OUT> ld;
+  ChunkLoader<IO, P, N, false, true, OUT, NTHR, 1, RBL, false> ld;  // B (and C) rows
+  // x rows: thread tid loads the XPT 16-byte vectors v = tid + NTHR i of the chunk's raw
+  // 64 x P rows (row v / XV, columns V (v % XV)), one chunk ahead.  At the chunk they go
+  // to LDS staging rows 3 .., behind the 3 rows before the chunk (the conv halo, kept
+  // in registers since the previous chunk by the threads that loaded those rows), and
+  // each conv task reads its rows from there: every x row is read from memory once.
+  // (The forward has no post-conv x pre-pass: x is always raw here.)
+  constexpr int XV = P / V;
+  constexpr int XPT = kQ * XV / NTHR;
+  static_assert(kQ * XV % NTHR == 0 && 3 * XV <= NTHR, "x vectors tile the threads");
+  const E* xsrc = static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb + h * P;
+  uint4 xr[XPT];
+  uint32_t xok = 0;
+  uint4 xhalo = make_uint4(0u, 0u, 0u, 0u);
+  const int vlast = static_cast<int>(threadIdx.x) + NTHR * (XPT - 1);
+  const bool holds_halo = vlast >= (kQ - 3) * XV;  // rows kQ-3 .. kQ-1 of the chunk
+  auto issue_x = [&](int64_t tn) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int v = static_cast<int>(threadIdx.x) + NTHR * i;
+      const int64_t t = tn + v / XV;
+      m |= (t < pr.L ? 1u : 0u) << i;
+      xr[i] = *reinterpret_cast<const uint4*>(xsrc + (t < pr.L ? t : pr.L - 1) * pr.xbc.st + (v % XV) * V);
+    }
+    xok = m;
+  };
+  // the halo of the walk's first chunk: rows tbeg-3 .. tbeg-1 of x, or of the carried
+  // conv state before the sequence (zero before that, and without conv)
+  if (holds_halo && pr.K > 0) {
+    const int64_t t = k * a.cps * kQ - 3 + (vlast / XV - (kQ - 3));
+    const int cv = (vlast % XV) * V;
+    if (t >= 0) {
+      xhalo = *reinterpret_cast<const uint4*>(xsrc + t * pr.xbc.st + cv);
+    } else if (pr.cs_in.p && t >= -(pr.K - 1)) {
+      const E* csi = static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb + h * P;
+      xhalo = *reinterpret_cast<const uint4*>(csi + (t + pr.K - 1) * pr.cs_in.st + cv);
+    }
+  }
+  // staging rows: the dead M tile (output walk) or a buffer of its own
+  __shared__ __align__(16) uint4 sRawBuf[OUT ? 1 : (kQ + 3) * XV];
+  static_assert(!OUT || (kQ + 3) * XV * 16 <= sizeof(Lt) * kQ * ldQ, "x staging fits the M tile");
+  uint4* const sRaw = OUT ? reinterpret_cast<uint4*>(sM) : sRawBuf;
   E dt_raw{};
   // gate inputs of this thread's output vectors (row k / (P / V), columns
   // V (k % (P / V)) for k = tid + NTHR q), loaded one chunk phase ahead as 16-byte rows
@@ -198,6 +239,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     dt_raw = *byte_off(dtp + tn * pr.dt.st, r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
   };
   prefetch(tbeg);
+  issue_x(tbeg);
   ld.issue_raw(pr, b, h, g, tbeg);
 
   float lsum = 0.f;
@@ -235,23 +277,57 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     // z first: the epilogue's wait for it then leaves the next chunk's loads, issued
     // after it, in flight
     prefetch_z(t0);
-    ld.consume_raw_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
-      if (seg == 0) {
-        const float ws = s_w[s];
-        float ow[V];
+    // raw x rows (masked past the end) and the halo to the staging rows
 #pragma unroll
-        for (int v = 0; v < V; ++v) ow[v] = o[v] * ws;
-        if constexpr (OUT) lds_put_row<IO>(sX + s * ldP + cl, o);
-        lds_put_row<IO>(sXw + s * ldP + cl, ow);
-      } else {
-        lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
-      }
+    for (int i = 0; i < XPT; ++i) {
+      const int v = static_cast<int>(threadIdx.x) + NTHR * i;
+      sRaw[(3 + v / XV) * XV + v % XV] = keep_if((xok >> i) & 1u, xr[i]);
+    }
+    if (holds_halo) sRaw[(vlast / XV - (kQ - 3)) * XV + vlast % XV] = xhalo;
+    xhalo = keep_if((xok >> (XPT - 1)) & 1u, xr[XPT - 1]);  // the next chunk's halo
+    ld.consume_raw_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
+      lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
     }, s_conv);
+    __syncthreads();
+    // post-conv x (SiLU; taps right-aligned on 4 in s_conv) of XPT rows per task:
+    // sX = x (output walk), sXw = x * w_s; rows past the end are zero
+    {
+      const int cg = static_cast<int>(threadIdx.x) % XV, r0 = (static_cast<int>(threadIdx.x) / XV) * XPT;
+      const int cl = cg * V;
+      uint4 raw[XPT + 3];
+#pragma unroll
+      for (int i = 0; i < XPT + 3; ++i) raw[i] = sRaw[(r0 + i) * XV + cg];
+      const bool conv = pr.K > 0;
+      float w4[4][V], bias[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w4[j][v] = s_conv[(cl + v) * 5 + j];
+        bias[v] = s_conv[(cl + v) * 5 + 4];
+      }
+#pragma unroll
+      for (int r = 0; r < XPT; ++r) {
+        float o[V], ow[V];
+        const float ws = t0 + r0 + r < pr.L ? s_w[r0 + r] : 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float pre = bias[v];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
+          o[v] = conv ? siluf_(pre) : raw_elem<IO>(raw[r + 3], v);
+          if (t0 + r0 + r >= pr.L) o[v] = 0.f;
+          ow[v] = o[v] * ws;
+        }
+        if constexpr (OUT) lds_put_row<IO>(sX + (r0 + r) * ldP + cl, o);
+        lds_put_row<IO>(sXw + (r0 + r) * ldP + cl, ow);
+      }
+    }
     // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
     // the row loads in flight); the last chunk reloads its own rows
     {
       const int64_t tn = c + 1 < a.cps && t0 + kQ < pr.L ? t0 + kQ : t0;
       prefetch(tn);
+      issue_x(tn);
       ld.issue_raw(pr, b, h, g, tn);
     }
     __syncthreads();
