@@ -356,6 +356,37 @@ __device__ __forceinline__ void mma_strip2(f32x4 (&acc)[NJ], const L* A1, const 
   }
 }
 
+// acc1[j] += A * B1_j and acc2[j] += A * B2_j with one 16-row A strip: each A fragment
+// is read once for both products, and their MFMAs interleave.
+template <typename L, bool akc, bool bkc, int NJ1, int NJ2>
+__device__ __forceinline__ void mma_strip_ab(f32x4 (&acc1)[NJ1], f32x4 (&acc2)[NJ2], const L* A, int lda,
+                                             int m0, const L* B1, int ldb1, int n01, const L* B2,
+                                             int ldb2, int n02, int K) {
+  constexpr int kstep = sizeof(L) == 2 ? 32 : 4;
+  constexpr int kpl = sizeof(L) == 2 ? 8 : 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15;
+  const int kg = lane >> 4;
+  for (int k0 = 0; k0 < K; k0 += kstep) {
+    const int kr = k0 + kpl * kg;
+    const bool kin = kr < K;
+    const int k = kin ? kr : 0;
+    const auto av = frag<L, akc>::get(A, lda, m0 + r, k);
+    const auto a = kin ? av : frag<L, akc>::zero();
+#pragma unroll
+    for (int j = 0; j < (NJ1 > NJ2 ? NJ1 : NJ2); ++j) {
+      if (j < NJ1) {
+        const auto bv = frag<L, bkc>::get(B1, ldb1, n01 + 16 * j + r, k);
+        acc1[j] = mfma_step(a, kin ? bv : frag<L, bkc>::zero(), acc1[j]);
+      }
+      if (j < NJ2) {
+        const auto bv = frag<L, bkc>::get(B2, ldb2, n02 + 16 * j + r, k);
+        acc2[j] = mfma_step(a, kin ? bv : frag<L, bkc>::zero(), acc2[j]);
+      }
+    }
+  }
+}
+
 // Ordered column sums of a row-major [rows][cols] fp32 matrix, 64 columns per
 // 256-thread block (column blockIdx.x * 64 + lane).  Wave w adds rows w, w + 4,
 // w + 8, ... with 16 loads in flight; the four wave partials are then added in

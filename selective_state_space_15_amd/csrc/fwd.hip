@@ -333,12 +333,17 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     __syncthreads();
 
     if constexpr (OUT) {
-      // C B^T -> masked, decayed, dt-scaled intra-chunk matrix Mt
+      // C B^T (-> masked, decayed, dt-scaled intra-chunk matrix Mt) and the carried-state
+      // term C H_{c-1}^T in one pass over the C strip
+      f32x4 yacc[YJ];
+#pragma unroll
+      for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
         f32x4 cb[CBJ];
 #pragma unroll
         for (int j = 0; j < CBJ; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma_strip<Lt, true, true, CBJ>(cb, sC, ldN, m0, sB, ldN, 16 * CBJ * half, N);
+        mma_strip_ab<Lt, true, true, CBJ, YJ>(cb, yacc, sC, ldN, m0, sB, ldN, 16 * CBJ * half, sH, ldN,
+                                             16 * YJ * half, N);
 #pragma unroll
         for (int j = 0; j < CBJ; ++j)
 #pragma unroll
@@ -349,12 +354,6 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
             sM[t * ldQ + s] = T::to_lds(v);
           }
       }
-      // carried-state term with H_{c-1}, rows scaled by exp(cs_t) in place, then the
-      // intra-chunk term accumulated on top by the same MFMA accumulators
-      f32x4 yacc[YJ];
-#pragma unroll
-      for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mma_strip<Lt, true, true, YJ>(yacc, sC, ldN, m0, sH, ldN, 16 * YJ * half, N);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float ecs = __expf(s_cs[m0 + acc_row(e)]);
