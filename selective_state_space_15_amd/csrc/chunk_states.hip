@@ -178,6 +178,14 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   constexpr bool kAllOwn = NJS * WPP == NT;
   const bool owns = kAllOwn || s_nj0 < NT;
   static_assert(NJS % JB == 0, "a wave's state tiles cover whole scale blocks");
+  // bf16 I/O, S walk: each wave's fp16 tiles go through a private LDS row buffer, so
+  // that the global stores are 16-byte rows covering whole 128-byte lines (a store per
+  // element writes 32-byte pieces, and the state stores are bound by their count).
+  // The dS walk, whose LDS traffic per step is 2.4 times the S walk's, measured slower
+  // with it and stores per element.
+  constexpr bool kStageOut = F16S && !DS;
+  constexpr int ldO = 16 * NJS + 8;  // halves per staged row (16 bytes of padding)
+  __shared__ __align__(16) uint16_t sOut[kStageOut ? NW : 1][kStageOut ? 16 * ldO : 8];
   const int64_t PN = static_cast<int64_t>(P) * N;
   f32x4 acc[HBM][NJS];
 #pragma unroll
@@ -347,11 +355,25 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
 #pragma unroll
             for (int j = jb; j < jb + JB; ++j)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] =
-                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[hh][j][e] * up));
+              for (int e = 0; e < 4; ++e) {
+                const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[hh][j][e] * up));
+                if constexpr (kStageOut)
+                  sOut[wave][acc_row(e) * ldO + j * 16 + acc_col()] = hv;
+                else
+                  dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = hv;
+              }
             // every lane stores the same value (a lane branch would be one around a store)
             sdst[s_pi * (N / SC) + (s_nj0 + jb) * 16 / SC] = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+          }
+          // the wave's 16 rows x 16 NJS columns back as 16-byte row pieces (LDS accesses of
+          // one wave complete in order: no barrier)
+          constexpr int VPR = 16 * NJS / 8;  // 16-byte pieces per row
+#pragma unroll
+          for (int q = 0; q < (kStageOut ? (16 * VPR + kWave - 1) / kWave : 0); ++q) {
+            const int idx = lane + kWave * q, row = idx / VPR, cv = idx % VPR;
+            if (16 * VPR % kWave == 0 || idx < 16 * VPR)
+              *reinterpret_cast<uint4*>(dst + (s_pi * 16 + row) * N + s_nj0 * 16 + cv * 8) =
+                  *reinterpret_cast<const uint4*>(&sOut[wave][row * ldO + cv * 8]);
           }
         }
       }
