@@ -183,9 +183,10 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   // element writes 32-byte pieces, and the state stores are bound by their count).
   // The dS walk, whose LDS traffic per step is 2.4 times the S walk's, measured slower
   // with it and stores per element.
-  constexpr bool kStageOut = F16S && !DS;
+  // fp16 slot stores: 0 per element, 1 staged in LDS, 2 transposed across lanes
+  constexpr int kStoreMode = !F16S ? 0 : (!DS ? 1 : (NJS % 4 == 0 ? 2 : 0));
   constexpr int ldO = 16 * NJS + 8;  // halves per staged row (16 bytes of padding)
-  __shared__ __align__(16) uint16_t sOut[kStageOut ? NW : 1][kStageOut ? 16 * ldO : 8];
+  __shared__ __align__(16) uint16_t sOut[kStoreMode == 1 ? NW : 1][kStoreMode == 1 ? 16 * ldO : 8];
   const int64_t PN = static_cast<int64_t>(P) * N;
   f32x4 acc[HBM][NJS];
 #pragma unroll
@@ -342,6 +343,7 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
           // precision down to 2^-29 of that maximum, and none overflows.
           uint16_t* dst = static_cast<uint16_t*>(a.out) + so;
           float* sdst = a.oscale + ((b * a.nch + slot) * pr.H + h) * kSB;
+          float upb[NJS / JB];
 #pragma unroll
           for (int jb = 0; jb < NJS; jb += JB) {
             float m = 0.f;
@@ -351,25 +353,52 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
               for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[hh][j][e]));
             const int ex = static_cast<int>((__float_as_uint(wave_max(m)) >> 23) & 0xffu);
             const int kx = min(141 - ex, 126);  // ex >= 15: 2^(ex-127) <= max < 2^(ex-126)
-            const float up = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+            upb[jb / JB] = __uint_as_float(static_cast<uint32_t>(kx + 127) << 23);
+            // every lane stores the same value (a lane branch would be one around a store)
+            sdst[s_pi * (N / SC) + (s_nj0 + jb) * 16 / SC] = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
+          }
+          auto hval = [&](int j, int e) { return acc[hh][j][e] * upb[j / JB]; };
+          if constexpr (kStoreMode == 2) {
+            // Per group of 4 tiles and pair of accumulator rows e: the 4 tiles' packed
+            // pairs, transposed between registers and 16-lane rows by two lane swaps,
+            // leave register q holding rows 4q + e, e + 1 of tile g in lane row g: each
+            // store then writes one row's 64 consecutive columns (128 bytes).
 #pragma unroll
-            for (int j = jb; j < jb + JB; ++j)
+            for (int jg = 0; jg < NJS; jg += 4)
+#pragma unroll
+              for (int ep = 0; ep < 4; ep += 2) {
+                uint32_t R[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) R[jj] = f2h2(hval(jg + jj, ep), hval(jg + jj, ep + 1));
+                const auto x02 = __builtin_amdgcn_permlane32_swap(R[0], R[2], false, false);
+                const auto x13 = __builtin_amdgcn_permlane32_swap(R[1], R[3], false, false);
+                const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+                const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+                const uint32_t Q[4] = {y01[0], y01[1], y23[0], y23[1]};
+                uint16_t* col = dst + s_pi * 16 * N + (s_nj0 + jg) * 16 + lane;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  col[(4 * q + ep) * N] = static_cast<uint16_t>(Q[q] & 0xffffu);
+                  col[(4 * q + ep + 1) * N] = static_cast<uint16_t>(Q[q] >> 16);
+                }
+              }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJS; ++j)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[hh][j][e] * up));
-                if constexpr (kStageOut)
+                const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hval(j, e)));
+                if constexpr (kStoreMode == 1)
                   sOut[wave][acc_row(e) * ldO + j * 16 + acc_col()] = hv;
                 else
                   dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = hv;
               }
-            // every lane stores the same value (a lane branch would be one around a store)
-            sdst[s_pi * (N / SC) + (s_nj0 + jb) * 16 / SC] = __uint_as_float(static_cast<uint32_t>(127 - kx) << 23);
           }
-          // the wave's 16 rows x 16 NJS columns back as 16-byte row pieces (LDS accesses of
-          // one wave complete in order: no barrier)
+          // staged: the wave's 16 rows x 16 NJS columns back as 16-byte row pieces (LDS
+          // accesses of one wave complete in order: no barrier)
           constexpr int VPR = 16 * NJS / 8;  // 16-byte pieces per row
 #pragma unroll
-          for (int q = 0; q < (kStageOut ? (16 * VPR + kWave - 1) / kWave : 0); ++q) {
+          for (int q = 0; q < (kStoreMode == 1 ? (16 * VPR + kWave - 1) / kWave : 0); ++q) {
             const int idx = lane + kWave * q, row = idx / VPR, cv = idx % VPR;
             if (16 * VPR % kWave == 0 || idx < 16 * VPR)
               *reinterpret_cast<uint4*>(dst + (s_pi * 16 + row) * N + s_nj0 * 16 + cv * 8) =
