@@ -415,6 +415,34 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   stage_head(0);
   __syncthreads();
 
+  // bf16 with two column tiles per wave: rows m0 .. m0 + 15, columns p0 .. p0 + 31 of a
+  // [rows][cols] bf16 output from accumulator-layout values v[j][e] (tile j, row
+  // 4 (lane / 16) + e).  For each pair of rows e, e + 1 the two tiles' packed pairs swap
+  // odd and even 16-lane rows (v_permlane16_swap), so that each lane then holds two
+  // rows of one column of 32 consecutive ones: every store writes 64-byte row pieces
+  // (per-element stores write 32-byte ones).  Rows at or past L are skipped.
+  constexpr bool kPairStore = sizeof(E) == 2 && PJw == 2;
+  auto store_rows2 = [&](E* base, uint32_t st, const float (&v)[PJw][4]) __attribute__((always_inline)) {
+    if constexpr (kPairStore)
+#pragma unroll
+    for (int ep = 0; ep < 4; ep += 2) {
+      const uint32_t r0 = f2bf2(v[0][ep], v[0][ep + 1]), r1 = f2bf2(v[1][ep], v[1][ep + 1]);
+      const auto y = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int row = m0 + 4 * (w + 2 * (lane >> 5)) + ep;
+        const uint32_t col = p0 + (lane & 31);
+        const uint32_t word = w == 0 ? y[0] : y[1];
+        if (t0 + row < pr.L)
+          *byte_off(base, (row * st + col) * static_cast<uint32_t>(sizeof(E))) =
+              __builtin_bit_cast(E, static_cast<uint16_t>(word & 0xffffu));
+        if (t0 + row + 1 < pr.L)
+          *byte_off(base, ((row + 1) * st + col) * static_cast<uint32_t>(sizeof(E))) =
+              __builtin_bit_cast(E, static_cast<uint16_t>(word >> 16));
+      }
+    }
+  };
+
   for (int hh = 0; hh < a.hb_heads; ++hh) {
     const int h = h_first + hh;
     // the next head (the last head reloads and restages itself: no branch around the
@@ -479,6 +507,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + t0 * a.dz.st + h * P : nullptr;
+      float dzv[PJw][4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
@@ -489,9 +518,13 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
           const float xv = T::lds_to_f(sX[t * ldP + p]);
           const float y = yacc[j][e] + Dh * xv;
           dD_part += dyr[j][e] * xv;
-          if (dzp && t0 + t < pr.L) dzr[16 * j] = T::from_f(g2r[j][e] * y);
+          dzv[j][e] = g2r[j][e] * y;
+          if constexpr (!kPairStore)
+            if (dzp && t0 + t < pr.L) dzr[16 * j] = T::from_f(dzv[j][e]);
         }
       }
+      if constexpr (kPairStore)
+        if (dzp) store_rows2(dzp, static_cast<uint32_t>(a.dz.st), dzv);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -553,6 +586,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       mma_strip<Lt, false, false, PJw, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, p0, kQ);
       mma_strip<Lt, true, true, PJw, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, p0, N);
       E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + t0 * a.dx.st + h * P;
+      float dxv[PJw][4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
@@ -560,10 +594,12 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         E* dxr = byte_off(dxp, (s * static_cast<uint32_t>(a.dx.st) + p0 + acc_col()) * sizeof(E));
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
-          const float dxv = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
-          if (t0 + s < pr.L) dxr[16 * j] = T::from_f(dxv);
+          dxv[j][e] = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
+          if constexpr (!kPairStore)
+            if (t0 + s < pr.L) dxr[16 * j] = T::from_f(dxv[j][e]);
         }
       }
+      if constexpr (kPairStore) store_rows2(dxp, static_cast<uint32_t>(a.dx.st), dxv);
     }
     prefetch(h_first + hn, 1);
     // (d) dB rows s: W^T C + exp(cs_Q - cs_s) dt_s (X dH); chunk-state dcs term
