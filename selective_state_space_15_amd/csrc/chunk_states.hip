@@ -422,11 +422,31 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       float* dst = a.grp + ((b * a.ngr + grp) * pr.H + hfirst + hh) * PN;
+      if constexpr (NJS % 4 == 0) {
+        // per group of 4 tiles and accumulator row e, transposed between registers and
+        // 16-lane rows by two lane swaps: each store writes 64 columns of one row
 #pragma unroll
-      for (int j = 0; j < NJS; ++j)
+        for (int jg = 0; jg < NJS; jg += 4)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
+          for (int e = 0; e < 4; ++e) {
+            const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[hh][jg][e]),
+                                                              __float_as_uint(acc[hh][jg + 2][e]), false, false);
+            const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[hh][jg + 1][e]),
+                                                              __float_as_uint(acc[hh][jg + 3][e]), false, false);
+            const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+            const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+            const uint32_t Q[4] = {y01[0], y01[1], y23[0], y23[1]};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              dst[(s_pi * 16 + 4 * q + e) * N + (s_nj0 + jg) * 16 + lane] = __uint_as_float(Q[q]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = acc[hh][j][e];
+      }
     }
   }
   if constexpr (!DS)
