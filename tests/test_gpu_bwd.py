@@ -56,6 +56,23 @@ def test_other_head_shapes_bwd(P, N):
     bwd_check(Case(d, seed=32, states=True))
 
 
+@pytest.mark.parametrize("what,scale", [("dout", 1e-6), ("dout", 1e3), ("x", 64.0)])
+def test_bwd_magnitudes(what, scale):
+    # bf16 I/O keeps the in-group chunk states as fp16 with a power-of-two scale per
+    # block: gradients of training size (dout ~ 1e-6) must not underflow, large ones and
+    # large inputs must not overflow.  Every gradient is linear in dout, so the relative
+    # errors must stay within the same bar at any scale.
+    d = synth.Dims(B=1, L=700, H=4, P=64, N=128, G=1, K=4, d_model=256)
+    case = Case(d, seed=51)
+    if what == "dout":
+        case._dout = synth.bf16_bits(synth.bf16_to_f32(synth.dout(d, case.seed + 7)) * scale)
+    else:  # the x channels of the in_proj rows [z | x B C | dt]
+        zx = synth.bf16_to_f32(case.zx)
+        zx[..., d.hp:2 * d.hp] *= scale
+        case.zx = synth.bf16_bits(zx)
+    bwd_check(case)
+
+
 @pytest.mark.parametrize("K", [2, 3])
 def test_narrow_conv_bwd(K):
     d = synth.Dims(B=1, L=200, H=2, P=64, N=64, G=1, K=K, d_model=128)
