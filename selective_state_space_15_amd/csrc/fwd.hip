@@ -90,6 +90,10 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
   __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
   __shared__ float s_dt[kQ], s_cs[kQ], s_w[kQ];
+  // state walk: w_s and the log-decay of every chunk of the sub-segment, computed
+  // before the walk (one wave per chunk), so no chunk waits on a one-wave step
+  constexpr int kMaxCps = 64;
+  __shared__ float s_wall[OUT ? 1 : kMaxCps * kQ], s_lall[OUT ? 1 : kMaxCps];
   __shared__ float s_conv[P * 5];  // head h's conv taps (right-aligned on 4) and bias
 
   const Problem& pr = a.pr;
@@ -238,7 +242,33 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     const uint32_t r = tn + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - tn);
     dt_raw = *byte_off(dtp + tn * pr.dt.st, r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
   };
-  prefetch(tbeg);
+  if constexpr (OUT) {
+    prefetch(tbeg);
+  } else {
+    // every chunk's dt (16 chunks per wave at most: all loads first, then the scans)
+    constexpr int kPer = kMaxCps / NW;
+    E dtr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t t = tbeg + (wave + NW * i) * kQ + lane;
+      dtr[i] = dtp[(t < pr.L ? t : pr.L - 1) * pr.dt.st];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int ci = wave + NW * i;
+      const int64_t t = tbeg + ci * kQ + lane;
+      float dtv = 0.f;
+      if (ci < a.cps && t < pr.L) {
+        const float u = T::to_f(dtr[i]) + bias_h;
+        dtv = pr.softplus ? softplusf_(u) : u;
+      }
+      const float cs = wave_incl_scan(dtv * Ah);
+      const float csl = lane_value(cs, kWave - 1);
+      s_wall[ci * kQ + lane] = dtv * __expf(csl - cs);
+      if (lane == 0) s_lall[ci] = csl;
+    }
+    __syncthreads();
+  }
   issue_x(tbeg);
   ld.issue_raw(pr, b, h, g, tbeg);
 
@@ -257,7 +287,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       }
     }
     // (1) dt = softplus(dt_raw + bias), l = dt * A, chunk-local cumsum (wave 0)
-    if (wave == 0) {
+    if (OUT && wave == 0) {
       float dtv = 0.f;
       if (t0 + lane < pr.L) {
         const float u = T::to_f(dt_raw) + bias_h;
@@ -269,8 +299,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       s_cs[lane] = cs;
       s_w[lane] = dtv * __expf(csl - cs);
     }
-    __syncthreads();
-    const float cs_last = s_cs[kQ - 1];
+    if constexpr (OUT) __syncthreads();
+    const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
     lsum += cs_last;
     // (2) conv + stores into LDS
     //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
@@ -308,7 +338,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
 #pragma unroll
       for (int r = 0; r < XPT; ++r) {
         float o[V], ow[V];
-        const float ws = t0 + r0 + r < pr.L ? s_w[r0 + r] : 0.f;
+        const float ws = t0 + r0 + r < pr.L ? (OUT ? s_w[r0 + r] : s_wall[c * kQ + r0 + r]) : 0.f;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           float pre = bias[v];
@@ -326,7 +356,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     // the row loads in flight); the last chunk reloads its own rows
     {
       const int64_t tn = c + 1 < a.cps && t0 + kQ < pr.L ? t0 + kQ : t0;
-      prefetch(tn);
+      if constexpr (OUT) prefetch(tn);
       issue_x(tn);
       ld.issue_raw(pr, b, h, g, tn);
     }
