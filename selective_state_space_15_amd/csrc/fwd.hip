@@ -299,10 +299,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       s_cs[lane] = cs;
       s_w[lane] = dtv * __expf(csl - cs);
     }
-    if constexpr (OUT) __syncthreads();
-    const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
-    lsum += cs_last;
-    // (2) conv + stores into LDS
+    // (2) conv + stores into LDS (the raw rows are staged while wave 0 finishes (1);
+    // one barrier then covers both)
     //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
     // z first: the epilogue's wait for it then leaves the next chunk's loads, issued
     // after it, in flight
@@ -319,6 +317,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
     }, s_conv);
     __syncthreads();
+    const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
+    lsum += cs_last;
     // post-conv x (SiLU; taps right-aligned on 4 in s_conv) of XPT rows per task:
     // sX = x (output walk), sXw = x * w_s; rows past the end are zero
     {
