@@ -130,6 +130,78 @@ def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups=1, chunk=0, conv_w
     return ssd_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, conv_width)
 
 
+# ------------------------------------------------------------------ argument checks
+#
+# The C ABI receives raw device pointers and cannot see sizes, so a short or
+# mistyped tensor would turn into an out-of-bounds device access.  Every entry point
+# below therefore checks, before the call, that each tensor is on the same CUDA
+# device, has the dtype the call expects and at least the extent the kernels touch.
+
+def _dev_of(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError(f"tensor on {t.device}: every argument must be a CUDA (HIP) tensor")
+    return t.device
+
+
+def _same_device(ts, where):
+    devs = {_dev_of(t) for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{where}: tensors on several devices {sorted(map(str, devs))}")
+
+
+def _act(t, name, B, T, C, dtype, required=True):
+    """[B, T, >=C] activation view in the I/O dtype."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 3 or tuple(t.shape[:2]) != (B, T) or t.shape[2] != C:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected ({B}, {T}, {C})")
+
+
+def _f32(t, name, shape, required=False):
+    """fp32 contiguous tensor of exactly `shape`."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected torch.float32")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _ws_ok(ws, need, where):
+    if need == 0:
+        return
+    if ws is None or ws.numel() * ws.element_size() < need:
+        have = 0 if ws is None else ws.numel() * ws.element_size()
+        raise ValueError(f"{where}: workspace of {have} bytes < {need} needed")
+
+
+def _ssd_common(d: ssd_dims, xbc, A, dt, conv_w, conv_b, conv_states, dt_bias, D, z, h0):
+    B, L, H, P, N, G, K = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.ngroups, d.conv_width
+    cd = H * P + 2 * G * N
+    if xbc is None:
+        raise ValueError("xbc is required")
+    io = xbc.dtype
+    _act(xbc, "xbc", B, L, cd, io)
+    _act(dt, "dt", B, L, H, io)
+    _act(z, "z", B, L, H * P, io, required=False)
+    _f32(A, "A", (H,), required=True)
+    _f32(D, "D", (H,))
+    _f32(dt_bias, "dt_bias", (H,))
+    _f32(h0, "h0", (B, H, P, N))
+    if K > 0:
+        _f32(conv_w, "conv_w", (cd, K), required=True)
+        _f32(conv_b, "conv_b", (cd,))
+        for name, t in conv_states.items():
+            _act(t, name, B, K - 1, cd, io, required=False)
+    return io, cd
+
+
 # ------------------------------------------------------------------ entry points
 
 def ssd_abi_version() -> int:
@@ -169,6 +241,19 @@ def ssd_fwd(d: ssd_dims, xbc, A, dt, out, *, conv_w=None, conv_b=None, conv_stat
     """Enqueue ssd_fwd.  Tensor views: xbc [B,L,Cd], dt [B,L,H], z/out [B,L,H*P],
     conv states [B,K-1,Cd]; fp32 contiguous A, D, dt_bias, conv_w, conv_b, h0,
     h_final, h_ckpt; ws a byte tensor of ssd_fwd_workspace() bytes (or None)."""
+    io, cd = _ssd_common(d, xbc, A, dt, conv_w, conv_b,
+                         dict(conv_state_in=conv_state_in, conv_state_out=conv_state_out),
+                         dt_bias, D, z, h0)
+    B, L, H, P, N = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate
+    _act(out, "out", B, L, H * P, io)
+    _f32(h_final, "h_final", (B, H, P, N))
+    if h_ckpt is not None:
+        if ckpt_every <= 0:
+            raise ValueError("ckpt_every must be positive with h_ckpt")
+        _f32(h_ckpt, "h_ckpt", ((L + ckpt_every - 1) // ckpt_every, B, H, P, N))
+    _same_device([xbc, A, dt, out, conv_w, conv_b, conv_state_in, conv_state_out, dt_bias, D, z, h0,
+                  h_final, h_ckpt, ws], "ssd_fwd")
+    _ws_ok(ws, ssd_fwd_workspace(d, io_dtype(xbc)), "ssd_fwd")
     wsp, wsn = _ws(ws)
     st = lib().ssd_fwd(ctypes.byref(d), io_dtype(xbc), view(xbc), fptr(conv_w), fptr(conv_b),
                        view(conv_state_in), view(conv_state_out), view(dt), fptr(dt_bias),
@@ -182,6 +267,25 @@ def ssd_bwd(d: ssd_dims, xbc, A, dt, dout, dxbc, ddt, dA, *, conv_w=None, conv_b
             dh_final=None, dconv_state_out=None, dz=None, dD=None, ddt_bias=None, dconv_w=None,
             dconv_b=None, dh0=None, dconv_state_in=None, accumulate=False, ws=None, stream=None):
     """Enqueue ssd_bwd (gradients of ssd_fwd; see include/ssd.h)."""
+    io, cd = _ssd_common(d, xbc, A, dt, conv_w, conv_b,
+                         dict(conv_state_in=conv_state_in, dconv_state_out=dconv_state_out,
+                              dconv_state_in=dconv_state_in), dt_bias, D, z, h0)
+    B, L, H, P, N, K = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.conv_width
+    _act(dout, "dout", B, L, H * P, io)
+    _act(dxbc, "dxbc", B, L, cd, io)
+    _act(ddt, "ddt", B, L, H, io)
+    _act(dz, "dz", B, L, H * P, io, required=z is not None)
+    for name, t in (("dA", dA), ("dD", dD), ("ddt_bias", ddt_bias)):
+        _f32(t, name, (H,), required=name == "dA")
+    _f32(dh_final, "dh_final", (B, H, P, N))
+    _f32(dh0, "dh0", (B, H, P, N))
+    if K > 0:
+        _f32(dconv_w, "dconv_w", (cd, K))
+        _f32(dconv_b, "dconv_b", (cd,))
+    _same_device([xbc, A, dt, dout, dxbc, ddt, dA, conv_w, conv_b, conv_state_in, dt_bias, D, z, h0,
+                  dh_final, dconv_state_out, dz, dD, ddt_bias, dconv_w, dconv_b, dh0, dconv_state_in,
+                  ws], "ssd_bwd")
+    _ws_ok(ws, ssd_bwd_workspace(d, io_dtype(xbc)), "ssd_bwd")
     wsp, wsn = _ws(ws)
     st = lib().ssd_bwd(ctypes.byref(d), io_dtype(xbc), view(xbc), fptr(conv_w), fptr(conv_b),
                        view(conv_state_in), view(dt), fptr(dt_bias), int(bool(dt_softplus)),
@@ -194,6 +298,14 @@ def ssd_bwd(d: ssd_dims, xbc, A, dt, dout, dxbc, ddt, dA, *, conv_w=None, conv_b
 
 def conv1d_fwd(x, w, out, *, b=None, silu=True, state_in=None, state_out=None, stream=None):
     B, L, C = x.shape
+    K = w.shape[1] if w is not None and w.dim() == 2 else 0
+    _act(x, "x", B, L, C, x.dtype)
+    _act(out, "out", B, L, C, x.dtype)
+    _f32(w, "w", (C, K), required=True)
+    _f32(b, "b", (C,))
+    _act(state_in, "state_in", B, K - 1, C, x.dtype, required=False)
+    _act(state_out, "state_out", B, K - 1, C, x.dtype, required=False)
+    _same_device([x, w, out, b, state_in, state_out], "conv1d_fwd")
     st = lib().conv1d_fwd(B, L, C, w.shape[1], io_dtype(x), view(x), fptr(w), fptr(b),
                           int(bool(silu)), view(state_in), view(out), view(state_out),
                           stream_ptr(stream))
@@ -203,6 +315,18 @@ def conv1d_fwd(x, w, out, *, b=None, silu=True, state_in=None, state_out=None, s
 def conv1d_bwd(x, w, dout, dx, dw, *, b=None, silu=True, state_in=None, dstate_out=None, db=None,
                dstate_in=None, accumulate=False, ws=None, stream=None):
     B, L, C = x.shape
+    K = w.shape[1] if w is not None and w.dim() == 2 else 0
+    for name, t in (("x", x), ("dout", dout), ("dx", dx)):
+        _act(t, name, B, L, C, x.dtype)
+    _f32(w, "w", (C, K), required=True)
+    _f32(dw, "dw", (C, K), required=True)
+    _f32(b, "b", (C,))
+    _f32(db, "db", (C,))
+    for name, t in (("state_in", state_in), ("dstate_out", dstate_out), ("dstate_in", dstate_in)):
+        _act(t, name, B, K - 1, C, x.dtype, required=False)
+    _same_device([x, w, dout, dx, dw, b, state_in, dstate_out, db, dstate_in, ws], "conv1d_bwd")
+    if K >= 2:
+        _ws_ok(ws, conv1d_bwd_workspace(B, L, C, K), "conv1d_bwd")
     wsp, wsn = _ws(ws)
     st = lib().conv1d_bwd(B, L, C, w.shape[1], io_dtype(x), view(x), fptr(w), fptr(b),
                           int(bool(silu)), view(state_in), view(dout), view(dstate_out), view(dx),

@@ -670,7 +670,7 @@ size_t x_prepass_bytes(const Problem& pr) {
 }
 
 hipError_t launch_xbc_prepass(const Problem& pr, void* xp, void* bc, void* bc_lo, hipStream_t s) {
-  TimingScope ts(kKBcPrepass, s);
+  TimingScope ts(kKXbcPrepass, s);
   const int hp = pr.H * pr.P, gn2 = 2 * pr.G * pr.N, C = hp + gn2;
   ConvFwdArgs a{};
   a.B = pr.B;

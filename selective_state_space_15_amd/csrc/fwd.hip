@@ -643,7 +643,7 @@ hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, void* Pst, 
   if (err != hipSuccess) return err;
   const int64_t ne = pr.B * pr.H * PN, ngr = (nch + kG - 1) / kG;
   {
-    TimingScope ts(kKScan, s);
+    TimingScope ts(kKScanGroups, s);
     hipLaunchKernelGGL(scan_kernel, dim3(static_cast<unsigned>((ne / 4 + 255) / 256)), dim3(256), 0, s,
                        pr.h0, Eg, glsum, pr.B, pr.H, PN, ngr);
   }

@@ -17,7 +17,8 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 // Kernel kinds of the timing instrumentation (ssd_timing_* in ssd.h).
 enum KernelKind {
   kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
-  kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKernelKinds
+  kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKScanGroups, kKXbcPrepass,
+  kKernelKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events on stream `s`

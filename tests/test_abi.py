@@ -171,3 +171,62 @@ def test_conv_checkpoint_views():
     j = segmented.conv_ckpt(x, st, 2, 4)          # shorter than the buffer: carried + new rows
     assert torch.equal(j, torch.cat([st[:, 2:], x[:, :2]], dim=1))
     assert segmented.conv_ckpt(x, st, 5, 0) is None
+
+
+# ------------------------------------------------------------------ binding argument checks
+def _cpu_fwd_args(L=100, H=4, P=64, N=64, K=4, dtype=torch.bfloat16):
+    cd = H * P + 2 * N
+    d = bd.make_dims(1, L, H, P, N, 1, 0, K)
+    a = dict(xbc=torch.zeros(1, L, cd, dtype=dtype), A=torch.zeros(H), dt=torch.zeros(1, L, H, dtype=dtype),
+             out=torch.zeros(1, L, H * P, dtype=dtype))
+    kw = dict(conv_w=torch.zeros(cd, K), conv_b=torch.zeros(cd), dt_bias=torch.zeros(H), D=torch.zeros(H),
+              z=torch.zeros(1, L, H * P, dtype=dtype))
+    return d, a, kw
+
+
+def test_binding_rejects_host_tensors_before_the_call():
+    d, a, kw = _cpu_fwd_args()
+    with pytest.raises(ValueError, match="CUDA"):
+        bd.ssd_fwd(d, a["xbc"], a["A"], a["dt"], a["out"], **kw)
+
+
+@pytest.mark.parametrize("bad", ["dt_dtype", "out_short", "z_channels", "A_len", "h0_shape",
+                                 "conv_w_shape", "ckpt_rows", "ckpt_every"])
+def test_binding_rejects_mismatched_shapes_and_dtypes(bad):
+    d, a, kw = _cpu_fwd_args()
+    if bad == "dt_dtype":
+        a["dt"] = a["dt"].float()
+    elif bad == "out_short":
+        a["out"] = a["out"][:, :50]
+    elif bad == "z_channels":
+        kw["z"] = kw["z"][..., :128]
+    elif bad == "A_len":
+        a["A"] = torch.zeros(3)
+    elif bad == "h0_shape":
+        kw["h0"] = torch.zeros(1, 4, 64, 32)
+    elif bad == "conv_w_shape":
+        kw["conv_w"] = torch.zeros(10, 4)
+    elif bad == "ckpt_rows":
+        kw.update(h_ckpt=torch.zeros(1, 1, 4, 64, 64), ckpt_every=64)   # needs 2 rows at L=100
+    elif bad == "ckpt_every":
+        kw.update(h_ckpt=torch.zeros(1, 1, 4, 64, 64), ckpt_every=0)
+    with pytest.raises(ValueError):
+        bd.ssd_fwd(d, a["xbc"], a["A"], a["dt"], a["out"], **kw)
+
+
+def test_binding_bwd_and_conv_checks():
+    d, a, kw = _cpu_fwd_args(L=64)
+    L, cd = 64, a["xbc"].shape[2]
+    dout = torch.zeros(1, L, 256, dtype=torch.bfloat16)
+    dxbc = torch.zeros(1, L, cd, dtype=torch.bfloat16)
+    ddt = torch.zeros(1, L, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dz"):          # gate given, dz missing
+        bd.ssd_bwd(d, a["xbc"], a["A"], a["dt"], dout, dxbc, ddt, torch.zeros(4), **kw)
+    with pytest.raises(ValueError, match="dxbc"):
+        bd.ssd_bwd(d, a["xbc"], a["A"], a["dt"], dout, dxbc[..., :cd - 8], ddt, torch.zeros(4),
+                   dz=torch.zeros(1, L, 256, dtype=torch.bfloat16), **kw)
+    x = torch.zeros(2, 10, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="w"):
+        bd.conv1d_fwd(x, torch.zeros(32, 4), torch.zeros_like(x))
+    with pytest.raises(ValueError, match="dw"):
+        bd.conv1d_bwd(x, torch.zeros(64, 4), x, torch.zeros_like(x), torch.zeros(64, 3))

@@ -15,6 +15,8 @@ from selective_state_space_15_amd import segmented, synth
 from tests.gpu_cases import (TOL, Case, _bwd_outputs, _dout, bwd_check, compare_grads, fdev,
                              gpu_bwd, oracle_bwd, rel_l2, to_dev, to_host)
 
+SEG = 16384
+
 pytestmark = pytest.mark.gpu
 
 
@@ -41,13 +43,29 @@ def test_c1_full_length_bwd():
 
 
 def test_c4_shapes_batch16_80_heads_bwd():
-    # d_model 2560 mixer shapes (80 heads: head blocks of 8, conv channels 5376) at batch 16
+    # d_model 2560 mixer shapes (80 heads: 4 head blocks of 20, conv channels 5376) at
+    # batch 16 and a ragged length inside one 8-chunk group
     bwd_check(Case(synth.CONFIGS["c4"].with_(L=333), seed=41, states=True))
+
+
+def test_c4_full_shape_bwd():
+    """The batched 2.7B-style workload at its own size: batch 16, L = 4096 (64 chunks =
+    8 chunk groups per sequence), 80 heads in 4 head blocks of 20.  Every gradient of
+    every sequence against the oracle: the group scans and the [batch][group] state
+    indexing run with batch > 1 and several groups."""
+    bwd_check(Case(synth.CONFIGS["c4"], seed=42))
 
 
 def test_grouped_batched_bwd():
     d = synth.Dims(B=2, L=333, H=8, P=64, N=64, G=2, K=4, d_model=256)
     bwd_check(Case(d, seed=31, states=True))
+
+
+def test_grouped_batched_multigroup_bwd():
+    # batch 2, two B/C groups, ragged L = 1100 (18 chunks: 3 chunk groups, the last one
+    # partial), carried (h, conv) states in and gradients of both returned states
+    d = synth.Dims(B=2, L=1100, H=8, P=64, N=64, G=2, K=4, d_model=256)
+    bwd_check(Case(d, seed=35, states=True))
 
 
 @pytest.mark.parametrize("P,N", [(32, 16), (32, 128), (64, 16), (64, 32)])
@@ -147,6 +165,7 @@ def _segmented_case(d, seed, seg):
                                  dconv_state_out=to_dev(st["dconv_state"], d.dtype), dh0=o["dh0"],
                                  dconv_state_in=o["dconv_state"], ws=bws)
     torch.cuda.synchronize()
+    o["out"], o["h_ckpt"] = out, h_ckpt
     return c, o
 
 
@@ -177,3 +196,33 @@ def test_reviewer_spec_fp32_segmented():
     for k in ("dxbc", "ddt", "dz", "dA", "dD", "ddt_bias", "dconv_w", "dconv_b", "dh0", "dconv_state"):
         e = rel_l2(to_host(g[k]), to_host(full[k]))
         assert e <= 1e-5, (k, e)
+
+
+def test_c3_full_length_segmented_bwd():
+    """The segmented training step at its own size: L = 262,144 tokens in 16 segments
+    of 16,384 (d_model 1024 shapes, bf16).  The forward keeps only the (h, conv
+    buffer) checkpoints; the backward recomputes each segment.  Every gradient --
+    dxbc (x, B and C paths), ddt, dz, dA, dD, ddt_bias, conv weight and bias, dh0 --
+    against the oracle's full-storage backprop over the whole sequence, with the
+    per-chunk bar on the per-token gradients (segment and chunk-group seams)."""
+    d = synth.CONFIGS["c3"]
+    assert d.L == 262144 and d.seg == SEG
+    print("[c3] GPU segmented fwd+bwd", flush=True)
+    c, g = _segmented_case(d, 43, SEG)
+    st = c.st
+    print("[c3] oracle full-storage backward", flush=True)
+    r = oracle_bwd(c, h0=st["h0"], conv_state=st["conv_state"], dh_final=st["dh_final"],
+                   dconv_state=st["dconv_state"])
+    compare_grads(g, r, TOL["bf16"], "c3 full length")
+
+
+def test_segmented_fwd_bwd_is_deterministic():
+    """No atomics: two runs of the segmented forward + backward on the same inputs and
+    workspaces give bitwise-equal outputs, checkpoints and gradients."""
+    d = synth.CONFIGS["c3"].with_(L=2 * SEG + 1000)
+    runs = []
+    for _ in range(2):
+        c, g = _segmented_case(d, 44, SEG)
+        runs.append({k: v.clone() for k, v in g.items() if v is not None})
+    for k in runs[0]:
+        assert torch.equal(runs[0][k], runs[1][k]), k

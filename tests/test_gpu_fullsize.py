@@ -8,16 +8,21 @@ in reverse, carrying (dh, dconv) between segments.
 The fp64 oracle cannot replay a million tokens for all 32 heads within a test, so
 it checks outputs it can compute one by one:
 
-* forward, one sampled head over the whole sequence: its gated output at every
+* forward, three sampled heads (the first, one inside, the last) over the whole
+  sequence: each head's gated output at every
   token, its state at every one of the 64 checkpoints and at the end (the oracle
   runs the head's own recurrence segment by segment, which is the unsplit
   recurrence exactly);
-* backward, every per-token gradient of that head in the last segment (the
+* backward, every per-token gradient of each sampled head in the last segment (the
   pre-conv gradient of its x channels, the dt gradient, the z gradient), from the
   oracle's backward of that segment started at the oracle's own state.  Nothing
   after the last segment feeds these, so they are exact targets; the B / C
-  gradients (sums over all heads) and the sequence-wide parameter sums are covered
-  by the smaller cases.
+  gradients (sums over all heads) and the sequence-wide parameter sums at 16,384-token
+  segments are covered by the full-length segmented test of 262,144 tokens.
+
+Besides the whole-tensor relative L2, every 64-token chunk must meet the per-chunk
+bar, so a wrong chunk, segment seam or sub-segment boundary cannot hide in the norm
+of a million tokens.
 """
 import numpy as np
 import pytest
@@ -26,12 +31,12 @@ import torch
 from oracle import oracle as orc
 from selective_state_space_15_amd import binding as bd
 from selective_state_space_15_amd import segmented, synth
-from tests.gpu_cases import TOL, f64, rel_l2, to_host
+from tests.gpu_cases import TOL, check_chunks, f64, rel_l2, to_host
 
 pytestmark = pytest.mark.gpu
 
 SEG = 16384
-HEAD = 11  # the sampled head
+HEADS = (0, 11, 31)  # the sampled heads
 
 
 def test_full_length_segmented_fwd_bwd_sampled_head():
@@ -68,20 +73,29 @@ def test_full_length_segmented_fwd_bwd_sampled_head():
                                  D=p["D"], z=z, dz=dzg, dD=dD, ddt_bias=ddtb, dconv_w=dcw,
                                  dconv_b=dcb, ws=bws)
     torch.cuda.synchronize()
-    cols = slice(HEAD * P, (HEAD + 1) * P)
-    g_out = to_host(out[0, :, cols])
-    g_ck = h_ckpt[:, 0, HEAD].cpu().numpy().astype(np.float64)
-    g_hf = h_final[0, HEAD].cpu().numpy().astype(np.float64)
     t0 = L - SEG
-    g_dx = to_host(dxbc[0, t0:, cols])
-    g_ddt = to_host(ddt[0, t0:, HEAD])
-    g_dz = to_host(dzg[0, t0:, cols])
-    assert np.isfinite(to_host(dA)).all() and np.isfinite(g_dx).all()
+    gh = {}
+    for hd in HEADS:
+        cols = slice(hd * P, (hd + 1) * P)
+        gh[hd] = dict(out=to_host(out[0, :, cols]), ck=h_ckpt[:, 0, hd].cpu().numpy().astype(np.float64),
+                      hf=h_final[0, hd].cpu().numpy().astype(np.float64),
+                      dx=to_host(dxbc[0, t0:, cols]), ddt=to_host(ddt[0, t0:, hd]),
+                      dz=to_host(dzg[0, t0:, cols]))
+        assert np.isfinite(gh[hd]["dx"]).all()
+    assert np.isfinite(to_host(dA)).all()
     del zx, dout, out, dxbc, dzg, fws, bws
     torch.cuda.empty_cache()
     print("[full] GPU done", flush=True)
+    tol = TOL["bf16"]
+    for hd in HEADS:
+        _check_head(hd, gh[hd], zx_bits, do_bits, prm, d, tol)
 
-    # ---------------------------------------------------------------- oracle, one head
+
+def _check_head(HEAD, g, zx_bits, do_bits, prm, d, tol):
+    """The oracle's recurrence of one head over the whole sequence, against the GPU's."""
+    L, H, P, N, K = d.L, d.H, d.P, d.N, d.K
+    hp, cd = d.hp, d.cd
+    t0 = L - SEG
     # the head's channels of the conv input: its 64 x channels, then B and C
     ch = np.r_[hp + HEAD * P: hp + (HEAD + 1) * P, 2 * hp: 2 * hp + 2 * N]
     wch = np.r_[HEAD * P:(HEAD + 1) * P, hp:hp + 2 * N]
@@ -102,20 +116,24 @@ def test_full_length_segmented_fwd_bwd_sampled_head():
         o, _, h = orc.ssd_fwd(x[:, s], dtr[:, s], A, Bm[:, s], Cm[:, s], dtb, True, D, zh[:, s], h)
         outs.append(o.reshape(SEG, P))
     r_out = np.concatenate(outs)
-    e_out = rel_l2(g_out, r_out)
-    e_ck = rel_l2(g_ck, np.stack(ck))
-    e_hf = rel_l2(g_hf, h[0, 0])
+    e_out = rel_l2(g["out"], r_out)
+    e_ck = rel_l2(g["ck"], np.stack(ck))
+    e_hf = rel_l2(g["hf"], h[0, 0])
     # the last segment's backward from the oracle's own state at its start
     s = slice(t0, L)
     dout_h = f64(do_bits[:, s, HEAD * P:(HEAD + 1) * P]).reshape(1, SEG, 1, P)
     r = orc.mixer_bwd(xraw[:, s], conv_w, conv_b, dtr[:, s], A, 1, P, 1, N, dout_h, dt_bias=dtb,
                       D=D, z=zh[:, s], h0=np.asarray(ck[-1])[None, None], conv_state=xraw[:, t0 - (K - 1):t0])
-    e_dx = rel_l2(g_dx, r["dxbc_raw"][0, :, :P])
-    e_ddt = rel_l2(g_ddt, r["ddt"][0, :, 0])
-    e_dz = rel_l2(g_dz, r["dz"].reshape(SEG, P))
+    e_dx = rel_l2(g["dx"], r["dxbc_raw"][0, :, :P])
+    e_ddt = rel_l2(g["ddt"], r["ddt"][0, :, 0])
+    e_dz = rel_l2(g["dz"], r["dz"].reshape(SEG, P))
     print(f"[full] head {HEAD}: out={e_out:.2e} ckpt={e_ck:.2e} h_final={e_hf:.2e} "
           f"last-seg dx={e_dx:.2e} ddt={e_ddt:.2e} dz={e_dz:.2e}", flush=True)
-    tol = TOL["bf16"]
     for name, e in [("out", e_out), ("ckpt", e_ck), ("h_final", e_hf), ("dx", e_dx), ("ddt", e_ddt),
                     ("dz", e_dz)]:
-        assert e <= tol, (name, e)
+        assert e <= tol, (HEAD, name, e)
+    tag = f"head {HEAD}"
+    check_chunks("out", g["out"][None], r_out[None], tol, tag)
+    check_chunks("dx", g["dx"][None], r["dxbc_raw"][:, :, :P], tol, tag)
+    check_chunks("ddt", g["ddt"][None], r["ddt"][:, :, 0], tol, tag)
+    check_chunks("dz", g["dz"][None], r["dz"].reshape(1, SEG, P), tol, tag)

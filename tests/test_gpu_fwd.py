@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from selective_state_space_15_amd import synth
-from tests.gpu_cases import TOL, Case, fdev, rel_l2, to_dev, to_host
+from tests.gpu_cases import TOL, Case, check_chunks, fdev, rel_l2, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,7 @@ def check_fwd(case: Case, h0=None, conv_state=None, **kw):
     tol = TOL[d.dtype]
     assert e_out <= tol, e_out
     assert e_h <= tol, e_h
+    check_chunks("out", to_host(g["out"]), r["out"], tol, str(d.L))
     if d.K and g["conv_state_out"] is not None:
         assert np.array_equal(to_host(g["conv_state_out"]), r["conv_state_out"])
     return g, r

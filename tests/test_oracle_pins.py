@@ -325,3 +325,96 @@ def test_segmented_without_conv_buffer_fails_spec():
         dw = dw + g["dconv_w"]
         dh = g["dh0"]
     assert np.max(np.abs(dw - full["dconv_w"]) / np.abs(full["dconv_w"])) > 1e-5
+
+
+# ------------------------------------------------------------------ P7' branches without gate / SiLU / softplus
+def _fd_check(loss, grads, params, seed, eps=1e-6, trials=2):
+    """Directional central differences of `loss` against the analytic gradient of
+    every entry of `params` (a dict name -> array); `grads` maps name -> gradient."""
+    r = np.random.default_rng(seed)
+    for key, val in params.items():
+        for _ in range(trials):
+            v = r.standard_normal(np.shape(val))
+            fd = (loss(key, val + eps * v) - loss(key, val - eps * v)) / (2 * eps)
+            an = float(np.sum(grads[key] * v))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (key, fd, an)
+
+
+@pytest.mark.parametrize("softplus,with_D", [(True, True), (False, True), (True, False)])
+def test_ssd_gradients_without_gate_match_finite_differences(softplus, with_D):
+    """oracle_ssd_bwd with z absent (out = y), with and without softplus on dt and
+    with and without the skip term D."""
+    d = small_ssd(40 + int(softplus) + 2 * int(with_D), B=2, L=19, H=4, P=2, N=3, G=2, z=False)
+    if not softplus:
+        # the raw dt is used as is (plus the bias): keep it positive, as the method assumes
+        r = np.random.default_rng(47)
+        d["dt_raw"] = r.uniform(0.05, 0.5, d["dt_raw"].shape)
+        d["dt_bias"] = r.uniform(0.0, 0.1, d["dt_bias"].shape)
+    if not with_D:
+        d["D"] = None
+    r = np.random.default_rng(48)
+    w_out = r.standard_normal(d["x"].shape)
+    w_h = r.standard_normal(d["h0"].shape)
+    g = orc.ssd_bwd(d["x"], d["dt_raw"], d["A"], d["Bm"], d["Cm"], w_out, d["dt_bias"], softplus,
+                    d["D"], None, d["h0"], w_h, block=7)
+    assert g["dz"] is None
+    names = dict(x="dx", dt_raw="ddt", A="dA", Bm="dB", Cm="dC", h0="dh0", dt_bias="ddt_bias")
+    if with_D:
+        names["D"] = "dD"
+    else:
+        assert g["dD"] is None
+
+    def loss(key, val):
+        e = dict(d)
+        e[key] = val
+        out, y, hf = orc.ssd_fwd(e["x"], e["dt_raw"], e["A"], e["Bm"], e["Cm"], e["dt_bias"],
+                                 softplus, e["D"], None, e["h0"])
+        assert np.array_equal(out, y)                      # no gate: out is y
+        return float(np.sum(out * w_out) + np.sum(hf * w_h))
+
+    _fd_check(loss, {k: g[v] for k, v in names.items()}, {k: d[k] for k in names}, 49)
+
+
+def test_conv_gradients_without_silu_match_finite_differences():
+    """oracle_conv1d_bwd with use_silu = 0 (a plain causal depthwise conv plus bias)."""
+    r = np.random.default_rng(50)
+    B, L, Cd, K = 2, 17, 5, 4
+    p = dict(x=r.standard_normal((B, L, Cd)), w=r.uniform(-0.5, 0.5, (Cd, K)),
+             b=r.uniform(-0.5, 0.5, Cd), st=r.standard_normal((B, K - 1, Cd)))
+    w_out = r.standard_normal((B, L, Cd))
+    w_st = r.standard_normal((B, K - 1, Cd))
+    dx, dw, db, dst = orc.conv1d_bwd(p["x"], p["w"], p["b"], p["st"], False, w_out, w_st)
+
+    def loss(key, val):
+        e = dict(p)
+        e[key] = val
+        out, so = orc.conv1d_fwd(e["x"], e["w"], e["b"], e["st"], silu=False)
+        return float(np.sum(out * w_out) + np.sum(so * w_st))
+
+    _fd_check(loss, dict(x=dx, w=dw, b=db, st=dst), p, 51)
+    # without SiLU the conv is linear in (x, state): the gradient of x is a correlation
+    # with the flipped taps, independent of x itself
+    dx2, _, _, _ = orc.conv1d_bwd(2 * p["x"], p["w"], p["b"], p["st"], False, w_out, w_st)
+    assert np.array_equal(dx, dx2)
+
+
+def test_mixer_gradients_without_softplus_match_finite_differences():
+    """The mixer with dt_softplus = 0 (dt = dt_raw + dt_bias, kept positive)."""
+    d = small_mixer(52, L=21, H=2, P=2, N=3, G=1)
+    r = np.random.default_rng(53)
+    d["dt_raw"] = r.uniform(0.05, 0.5, d["dt_raw"].shape)
+    d["dt_bias"] = r.uniform(0.0, 0.1, d["dt_bias"].shape)
+    w = dict(out=r.standard_normal((1, 21, 2, 2)), h=r.standard_normal(d["h0"].shape),
+             cs=r.standard_normal(d["conv_state"].shape))
+    g = orc.mixer_bwd(**d, dout=w["out"], dh_final=w["h"], dconv_state_out=w["cs"], softplus=False,
+                      block=4)
+    keys = ["xbc_raw", "dt_raw", "z", "conv_w", "conv_b", "dt_bias", "A", "D", "h0", "conv_state"]
+
+    def loss(key, val):
+        e = dict(d)
+        e[key] = val
+        rr = orc.mixer_fwd(**e, softplus=False)
+        return float(np.sum(rr["out"] * w["out"]) + np.sum(rr["h_final"] * w["h"]) +
+                     np.sum(rr["conv_state_out"] * w["cs"]))
+
+    _fd_check(loss, {k: g[_GRAD_NAMES[k]] for k in keys}, {k: d[k] for k in keys}, 54)
