@@ -146,6 +146,32 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
                    float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ssd_fwd_noalloc -- ssd_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as ssd_fwd, without (ws, ws_bytes): its scratch is a
+ * fixed array of SSD_FWD_NOALLOC_SCRATCH_BYTES in the library's device image, which
+ * each GPU the library runs on holds until the process ends.  The call itself
+ * allocates nothing.
+ *
+ *   Limit    dims whose ssd_fwd_workspace() exceeds SSD_FWD_NOALLOC_SCRATCH_BYTES
+ *            return SSD_ERR_WORKSPACE before anything is enqueued (at d_model 1024
+ *            shapes -- 32 heads x 64, d_state 128, batch 1 -- up to about 130K tokens
+ *            per call; longer sequences run as several calls with carried state, or
+ *            through ssd_fwd).
+ *   Device   the scratch of the *current* device is used; `stream` must belong to it.
+ *            The first call on a device looks up the array's address on that device.
+ *   Races    every call on one GPU shares that GPU's array: calls that overlap on one
+ *            device (other streams, other host threads) race.  Calls on one stream
+ *            are ordered and safe.  The scratch needs no initialisation.
+ */
+#define SSD_FWD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ssd_status ssd_fwd_noalloc(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                           const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                           ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                           const float* D, ssd_view z, const float* h0, ssd_view out,
+                           float* h_final, float* h_ckpt, int64_t ckpt_every, void* stream);
+
+/*
  * ssd_bwd -- gradients of ssd_fwd (same inputs) given dout = dLoss/dout, the
  * gradient dh_final of the returned state and dconv_state_out of the returned conv
  * state (both optional: NULL / ptr NULL = zero).  Recomputes the forward from

@@ -53,6 +53,7 @@ _SIGS = {
     "ssd_fwd_workspace": ([_D, _I, ctypes.POINTER(_SZ)], _I),
     "ssd_bwd_workspace": ([_D, _I, ctypes.POINTER(_SZ)], _I),
     "ssd_fwd": ([_D, _I, _V, _F, _F, _V, _V, _V, _F, _I, _F, _F, _V, _F, _V, _F, _F, _I64, _P, _SZ, _P], _I),
+    "ssd_fwd_noalloc": ([_D, _I, _V, _F, _F, _V, _V, _V, _F, _I, _F, _F, _V, _F, _V, _F, _F, _I64, _P], _I),
     "ssd_bwd": ([_D, _I, _V, _F, _F, _V, _V, _F, _I, _F, _F, _V, _F, _V, _F, _V, _V, _V, _V,
                  _F, _F, _F, _F, _F, _F, _V, _I, _P, _SZ, _P], _I),
     "conv1d_fwd": ([_I64, _I64, _I64, ctypes.c_int32, _I, _V, _F, _F, _I, _V, _V, _V, _P], _I),
@@ -260,6 +261,33 @@ def ssd_fwd(d: ssd_dims, xbc, A, dt, out, *, conv_w=None, conv_b=None, conv_stat
                        int(bool(dt_softplus)), fptr(A), fptr(D), view(z), fptr(h0), view(out),
                        fptr(h_final), fptr(h_ckpt), int(ckpt_every), wsp, wsn, stream_ptr(stream))
     _check(st, "ssd_fwd")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # SSD_FWD_NOALLOC_SCRATCH_BYTES in include/ssd.h
+
+
+def ssd_fwd_noalloc(d: ssd_dims, xbc, A, dt, out, *, conv_w=None, conv_b=None, conv_state_in=None,
+                    conv_state_out=None, dt_bias=None, dt_softplus=True, D=None, z=None, h0=None,
+                    h_final=None, h_ckpt=None, ckpt_every=0, stream=None):
+    """Enqueue ssd_fwd_noalloc: ssd_fwd whose scratch is the library's fixed per-device
+    array (no workspace argument, nothing allocated).  Same tensors as ssd_fwd."""
+    io, cd = _ssd_common(d, xbc, A, dt, conv_w, conv_b,
+                         dict(conv_state_in=conv_state_in, conv_state_out=conv_state_out),
+                         dt_bias, D, z, h0)
+    B, L, H, P, N = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate
+    _act(out, "out", B, L, H * P, io)
+    _f32(h_final, "h_final", (B, H, P, N))
+    if h_ckpt is not None:
+        if ckpt_every <= 0:
+            raise ValueError("ckpt_every must be positive with h_ckpt")
+        _f32(h_ckpt, "h_ckpt", ((L + ckpt_every - 1) // ckpt_every, B, H, P, N))
+    _same_device([xbc, A, dt, out, conv_w, conv_b, conv_state_in, conv_state_out, dt_bias, D, z, h0,
+                  h_final, h_ckpt], "ssd_fwd_noalloc")
+    st = lib().ssd_fwd_noalloc(ctypes.byref(d), io_dtype(xbc), view(xbc), fptr(conv_w), fptr(conv_b),
+                               view(conv_state_in), view(conv_state_out), view(dt), fptr(dt_bias),
+                               int(bool(dt_softplus)), fptr(A), fptr(D), view(z), fptr(h0), view(out),
+                               fptr(h_final), fptr(h_ckpt), int(ckpt_every), stream_ptr(stream))
+    _check(st, "ssd_fwd_noalloc")
 
 
 def ssd_bwd(d: ssd_dims, xbc, A, dt, dout, dxbc, ddt, dA, *, conv_w=None, conv_b=None,

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/ssd.h"
@@ -154,11 +155,22 @@ ssd_status ssd_fwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes) {
   return SSD_OK;
 }
 
-ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
-                   const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
-                   ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
-                   const float* D, ssd_view z, const float* h0, ssd_view out, float* h_final,
-                   float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ssd_fwd with its scratch given as (ws, ws_bytes).  When `scratch` is non-null it is
+// called after validation, with the bytes needed, and returns the scratch to use (or
+// an error status through *st): the no-alloc entry point supplies the per-device
+// static array this way, so nothing device-side happens before every check passed.
+using ScratchFn = void* (*)(size_t need, ssd_status* st);
+
+ssd_status fwd_impl(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                    const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                    ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                    const float* D, ssd_view z, const float* h0, ssd_view out, float* h_final,
+                    float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream,
+                    ScratchFn scratch) {
   g_last_error.clear();
   TRY(check_dims(d, io));
   const int64_t L = d->seqlen, Cd = cdim(d), HP = d->nheads * d->headdim;
@@ -184,6 +196,12 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
   ssd::Problem pr = make_problem(d, io);
   const ssd::Plan pl = ssd::make_plan(pr.B, pr.L, pr.H);
   const size_t need = ssd::fwd_workspace_bytes(pr, pl);
+  if (scratch) {
+    ssd_status st = SSD_OK;
+    ws = scratch(need, &st);
+    if (st != SSD_OK) return st;
+    ws_bytes = need;
+  }
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SSD_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   pr.xbc = cv(xbc);
@@ -206,6 +224,75 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
   const hipError_t e = ssd::launch_fwd(pr, o, pl, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ssd_fwd launch");
   return SSD_OK;
+}
+
+// ---------------------------------------------------------------- no-alloc scratch
+//
+// Scratch of ssd_fwd_noalloc: one file-scope device array, which every GPU the
+// library runs on holds (at its own address) until the process ends.  Host code never
+// uses the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = SSD_FWD_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* noalloc_scratch(size_t need, ssd_status* st) {
+  if (need > kNoAllocScratchBytes) {
+    *st = fail(SSD_ERR_WORKSPACE,
+               "ssd_fwd_noalloc: these dims need %zu bytes of scratch, above its fixed %zu bytes "
+               "(use ssd_fwd with a caller workspace)", need, kNoAllocScratchBytes);
+    return nullptr;
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_fail(e, "ssd_fwd_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(SSD_ERR_UNSUPPORTED, "ssd_fwd_noalloc: device %d beyond %d", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *st = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                     "ssd_fwd_noalloc: hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                   const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                   ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                   const float* D, ssd_view z, const float* h0, ssd_view out, float* h_final,
+                   float* h_ckpt, int64_t ckpt_every, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(d, io, xbc, conv_w, conv_b, conv_state_in, conv_state_out, dt, dt_bias,
+                  dt_softplus, A, D, z, h0, out, h_final, h_ckpt, ckpt_every, ws, ws_bytes, stream,
+                  nullptr);
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                           const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                           ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                           const float* D, ssd_view z, const float* h0, ssd_view out,
+                           float* h_final, float* h_ckpt, int64_t ckpt_every, void* stream) {
+  return fwd_impl(d, io, xbc, conv_w, conv_b, conv_state_in, conv_state_out, dt, dt_bias,
+                  dt_softplus, A, D, z, h0, out, h_final, h_ckpt, ckpt_every, nullptr, 0, stream,
+                  noalloc_scratch);
 }
 
 ssd_status ssd_bwd_workspace(const ssd_dims* d, ssd_dtype io, size_t* bytes) {

@@ -230,3 +230,21 @@ def test_binding_bwd_and_conv_checks():
         bd.conv1d_fwd(x, torch.zeros(32, 4), torch.zeros_like(x))
     with pytest.raises(ValueError, match="dw"):
         bd.conv1d_bwd(x, torch.zeros(64, 4), x, torch.zeros_like(x), torch.zeros(64, 3))
+
+
+def test_noalloc_refuses_oversize_dims_before_any_device_call():
+    """The scratch limit is checked after validation and before the device lookup:
+    with dims beyond it the call returns SSD_ERR_WORKSPACE (no GPU needed; the
+    pointers are never dereferenced)."""
+    lib = bd.lib()
+    L, H, P, N, K = 1 << 20, 32, 64, 128, 4
+    cd = H * P + 2 * N
+    d = bd.make_dims(1, L, H, P, N, 1, 0, K)
+    assert bd.ssd_fwd_workspace(d, bd.SSD_BF16) > bd.NOALLOC_SCRATCH_BYTES
+    base = 1 << 20                                   # a fake, aligned device address
+    v = lambda c: bd.ssd_view(base, L * c, c)
+    st = lib.ssd_fwd_noalloc(ctypes.byref(d), bd.SSD_BF16, v(cd), base, base, bd.ssd_view(None, 0, 0),
+                             bd.ssd_view(None, 0, 0), bd.ssd_view(base, L * H, H), None, 1, base, None,
+                             bd.ssd_view(None, 0, 0), None, v(H * P), None, None, 0, None)
+    assert st == bd.SSD_ERR_WORKSPACE, st
+    assert b"scratch" in lib.ssd_last_error()
