@@ -182,3 +182,52 @@ def mixer_bwd(xbc_raw, conv_w, conv_b, dt_raw, A, H, P, G, N, dout, dt_bias=None
     dxr, dw, db, dst = conv1d_bwd(xbc_raw, conv_w, conv_b, conv_state, True, dxbc, dconv_state_out)
     r.update(dxbc=dxbc, dxbc_raw=dxr, dconv_w=dw, dconv_b=db, dconv_state=dst)
     return r
+
+
+# --------------------------------------------------------------------------- projections, norms
+#
+# The mixer around the hot path (Video-Ma2mba model card, architecture diagram and
+# specification table: a Mamba-2 LM with d_model 1024 in bf16; the Mamba-2 block of
+# the arXiv index page's "Builds on" list):
+#     zxbcdt = in_proj(u)            [z | xBC | dt_raw]
+#     out    = hot path (conv1d + SiLU -> SSD -> SiLU(z) gate)
+#     final  = out_proj(out)
+# and the full block with its two RMSNorms and the residual:
+#     final  = u + out_proj(RMSNorm(out) * g_out),   in_proj applied to RMSNorm(u) * g_in
+# All in fp64 with numpy; the matrix products are numpy matmuls.
+
+def rmsnorm(x, g, eps):
+    """Root-mean-square norm over the last axis: x / sqrt(mean(x^2) + eps) * g."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def linear(x, w, norm_w=None, eps=1e-5, residual=None):
+    """y = x' w^T (+ residual), w in the nn.Linear layout [out, in]; x' = x, or its
+    RMSNorm times norm_w over the `in` axis when norm_w is given."""
+    x = np.asarray(x, dtype=np.float64)
+    if norm_w is not None:
+        x = rmsnorm(x, norm_w, eps)
+    y = x @ np.asarray(w, dtype=np.float64).T
+    if residual is not None:
+        y = y + np.asarray(residual, dtype=np.float64)
+    return y
+
+
+def mixer_full_fwd(u, w_in, conv_w, conv_b, A, H, P, G, N, w_out, dt_bias=None, D=None, h0=None,
+                   conv_state=None, norm_in=None, norm_out=None, eps=1e-5, residual=False):
+    """in_proj -> conv1d + SiLU -> SSD -> SiLU(z) gate -> out_proj over u [B, L, d_model].
+    With norm_in / norm_out / residual: the full block (pre-norm, gated norm, skip).
+    Returns dict(final, zxbcdt, out, h_final, conv_state_out)."""
+    u = np.asarray(u, dtype=np.float64)
+    Bsz, L, _ = u.shape
+    hp, cd = H * P, H * P + 2 * G * N
+    zx = linear(u, w_in, norm_in, eps)
+    z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+    r = mixer_fwd(xbc, conv_w, conv_b, dt, A, H, P, G, N, dt_bias=dt_bias, D=D,
+                  z=z.reshape(Bsz, L, H, P), h0=h0, conv_state=conv_state)
+    out = r["out"].reshape(Bsz, L, hp)
+    final = linear(out, w_out, norm_out, eps, u if residual else None)
+    return dict(final=final, zxbcdt=zx, out=out, h_final=r["h_final"],
+                conv_state_out=r["conv_state_out"])

@@ -418,3 +418,66 @@ def test_mixer_gradients_without_softplus_match_finite_differences():
                      np.sum(rr["conv_state_out"] * w["cs"]))
 
     _fd_check(loss, {k: g[_GRAD_NAMES[k]] for k in keys}, {k: d[k] for k in keys}, 54)
+
+
+# ------------------------------------------------------------------ projections and norms
+def test_linear_matches_explicit_loops():
+    """The projection step against a brute-force triple loop on a tiny input."""
+    r = np.random.default_rng(60)
+    x = r.standard_normal((2, 3, 5))
+    w = r.standard_normal((4, 5))
+    res = r.standard_normal((2, 3, 4))
+    y = orc.linear(x, w, residual=res)
+    for b in range(2):
+        for t in range(3):
+            for n in range(4):
+                acc = res[b, t, n]
+                for k in range(5):
+                    acc += x[b, t, k] * w[n, k]
+                assert abs(y[b, t, n] - acc) < 1e-13
+
+
+def test_rmsnorm_closed_forms():
+    # worked example: [3, 4] has mean square 12.5
+    assert np.allclose(orc.rmsnorm([3.0, 4.0], [1.0, 1.0], 0.0), [3 / np.sqrt(12.5), 4 / np.sqrt(12.5)],
+                       rtol=0, atol=1e-15)
+    # eps enters under the root next to the mean square: [1, 1] with eps 3 -> 1/2
+    assert np.allclose(orc.rmsnorm([1.0, 1.0], [1.0, 1.0], 3.0), [0.5, 0.5], rtol=0, atol=1e-15)
+    r = np.random.default_rng(61)
+    x = r.standard_normal((7, 33))
+    g = r.uniform(0.5, 2.0, 33)
+    # unit gain, no eps: every row has mean square exactly 1
+    y = orc.rmsnorm(x, np.ones(33), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+    # scale invariance (eps = 0) and the gain acts per channel
+    assert np.allclose(orc.rmsnorm(5.5 * x, g, 0.0), orc.rmsnorm(x, g, 0.0), rtol=1e-14)
+    assert np.allclose(orc.rmsnorm(x, g, 0.0), y * g, rtol=1e-14)
+
+
+def test_mixer_full_in_proj_selects_and_skip_is_exact():
+    """A 0/1 selection matrix as in_proj hands u's channels to the hot path unchanged,
+    so the composed mixer equals the hot-path oracle on those channels; with a zero
+    out_proj the full block is exactly its residual."""
+    r = np.random.default_rng(62)
+    H, P, G, N, K = 2, 2, 1, 3, 4
+    hp, cd = H * P, H * P + 2 * G * N
+    dip = hp + cd + H
+    dm = dip + 3
+    u = r.standard_normal((1, 17, dm))
+    sel = np.zeros((dip, dm))
+    perm = r.permutation(dm)[:dip]
+    sel[np.arange(dip), perm] = 1.0
+    w_out = r.standard_normal((5, hp))
+    cw, cb = r.uniform(-0.5, 0.5, (cd, K)), r.uniform(-0.5, 0.5, cd)
+    A, D, dtb = -np.exp(r.uniform(0, 2, H)), r.standard_normal(H), r.uniform(-3, 0, H)
+    m = orc.mixer_full_fwd(u, sel, cw, cb, A, H, P, G, N, w_out, dt_bias=dtb, D=D)
+    zx = u[..., perm]
+    ref = orc.mixer_fwd(zx[..., hp:hp + cd], cw, cb, zx[..., hp + cd:], A, H, P, G, N, dt_bias=dtb, D=D,
+                        z=zx[..., :hp].reshape(1, 17, H, P))
+    assert np.array_equal(m["zxbcdt"], zx)
+    assert np.array_equal(m["out"], ref["out"].reshape(1, 17, hp))
+    assert np.allclose(m["final"], m["out"] @ w_out.T, rtol=1e-14, atol=0)
+    blk = orc.mixer_full_fwd(u[..., :5], r.standard_normal((dip, 5)), cw, cb, A, H, P, G, N,
+                             np.zeros((5, hp)), dt_bias=dtb, D=D, norm_in=np.ones(5),
+                             norm_out=np.ones(hp), residual=True)
+    assert np.array_equal(blk["final"], u[..., :5])
