@@ -221,6 +221,30 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
                       size_t ws_bytes, void* stream);
 
 /*
+ * mixer_proj -- the mixer's linear layers (in_proj, out_proj) on MFMA:
+ *
+ *     y[m][n] = sum_k x'[m][k] * w[n][k]  (+ residual[m][n])
+ *
+ * with x' = x, or, when norm_w != NULL, each row RMS-normalised over its K entries
+ * and scaled: x'[m][k] = x[m][k] * rsqrt(mean_k' x[m][k']^2 + norm_eps) * norm_w[k]
+ * (the pre-norm before in_proj and the gated norm before out_proj of the Mamba-2
+ * block; the gate itself is already applied by ssd_fwd's output).
+ *   x         [M][ldx] bf16, row m = one token's input vector (K contiguous)
+ *   w         [N][ldw] bf16, the nn.Linear weight layout [out][in]
+ *   norm_w    [K] fp32 or NULL;  norm_eps >= 0
+ *   residual  [M][ldr] bf16 or NULL, added in fp32 before the bf16 rounding of y
+ *   y         [M][ldy] bf16 (may not overlap x or w; may equal residual)
+ * fp32 accumulation; y rounded to nearest even.  Supported: io = SSD_BF16, K a
+ * multiple of 64, N a multiple of 8; 16-byte aligned base pointers and leading
+ * dimensions that are multiples of 8 elements.  Sources: the Video-Ma2mba model
+ * card's architecture diagram and specification table (Mamba-2 LM, d_model 1024,
+ * bf16) and the Mamba-2 block of the arXiv index page's "Builds on" list.
+ */
+ssd_status mixer_proj(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void* x, int64_t ldx,
+                      const void* w, int64_t ldw, const float* norm_w, float norm_eps,
+                      const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream);
+
+/*
  * Timing instrumentation (off by default).  While enabled, every kernel the
  * library enqueues is bracketed by HIP events on the caller's stream.
  *   ssd_timing_enable(1) clears the totals and starts recording; (0) stops.

@@ -60,6 +60,8 @@ _SIGS = {
     "conv1d_bwd_workspace": ([_I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(_SZ)], _I),
     "conv1d_bwd": ([_I64, _I64, _I64, ctypes.c_int32, _I, _V, _F, _F, _I, _V, _V, _V, _V, _F, _F, _V,
                     _I, _P, _SZ, _P], _I),
+    "mixer_proj": ([_I64, _I64, _I64, _I, _P, _I64, _P, _I64, _F, ctypes.c_float, _P, _I64, _P, _I64,
+                    _P], _I),
     "ssd_timing_enable": ([_I], _I),
     "ssd_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I),
     "ssd_timing_name": ([_I], ctypes.c_char_p),
@@ -361,6 +363,32 @@ def conv1d_bwd(x, w, dout, dx, dw, *, b=None, silu=True, state_in=None, dstate_o
                           fptr(dw), fptr(db), view(dstate_in), int(bool(accumulate)), wsp, wsn,
                           stream_ptr(stream))
     _check(st, "conv1d_bwd")
+
+
+def _mat(t, name, rows, cols):
+    """[rows, >=cols] bf16 matrix with a contiguous last dim (a 2-D view of [.., C] rows)."""
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected torch.bfloat16")
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] != cols or (cols > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} strides {t.stride()}, expected ({rows}, {cols}) "
+                         "with a contiguous last dim")
+    return t.data_ptr(), t.stride(0)
+
+
+def mixer_proj(x, w, y, *, norm_w=None, norm_eps=1e-5, residual=None, stream=None):
+    """y = RMSNorm?(x) w^T (+ residual): x [M, K], w [N, K] (nn.Linear layout), y and
+    residual [M, N]; bf16 2-D views with a contiguous last dim; norm_w [K] fp32."""
+    M, K = x.shape
+    N = w.shape[0]
+    xp, ldx = _mat(x, "x", M, K)
+    wp, ldw = _mat(w, "w", N, K)
+    yp, ldy = _mat(y, "y", M, N)
+    rp, ldr = _mat(residual, "residual", M, N) if residual is not None else (None, 0)
+    _f32(norm_w, "norm_w", (K,))
+    _same_device([x, w, y, residual, norm_w], "mixer_proj")
+    st = lib().mixer_proj(M, N, K, SSD_BF16, xp, ldx, wp, ldw, fptr(norm_w), float(norm_eps), rp, ldr,
+                          yp, ldy, stream_ptr(stream))
+    _check(st, "mixer_proj")
 
 
 # ------------------------------------------------------------------ timing instrumentation

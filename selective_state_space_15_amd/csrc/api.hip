@@ -462,4 +462,30 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
   return SSD_OK;
 }
 
+ssd_status mixer_proj(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void* x, int64_t ldx,
+                      const void* w, int64_t ldw, const float* norm_w, float norm_eps,
+                      const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream) {
+  g_last_error.clear();
+  if (io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "mixer_proj: bf16 I/O only");
+  if (M < 1 || N < 1 || K < 1 || M > (int64_t(1) << 40) || N > (1 << 24) || K > (1 << 24))
+    return fail(SSD_ERR_SHAPE, "mixer_proj: dims out of range (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 64) return fail(SSD_ERR_UNSUPPORTED, "mixer_proj: K=%lld not a multiple of 64", (long long)K);
+  if (N % 8) return fail(SSD_ERR_UNSUPPORTED, "mixer_proj: N=%lld not a multiple of 8", (long long)N);
+  if (!x || !w || !y) return fail(SSD_ERR_NULL, "mixer_proj: x, w and y are required");
+  if (ldx < K || ldw < K || ldy < N || (residual && ldr < N))
+    return fail(SSD_ERR_SHAPE, "mixer_proj: a leading dimension is below its row length");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)) ||
+      (norm_w && !aligned16(norm_w)))
+    return fail(SSD_ERR_ALIGN, "mixer_proj: base pointers must be 16-byte aligned");
+  if (ldx % 8 || ldw % 8 || ldy % 8 || (residual && ldr % 8))
+    return fail(SSD_ERR_ALIGN, "mixer_proj: leading dimensions must be multiples of 8 elements");
+  if (norm_w && !(norm_eps >= 0.f))
+    return fail(SSD_ERR_SHAPE, "mixer_proj: norm_eps must be >= 0");
+  ssd::LinearProblem lp{M, N, K, x, ldx, w, ldw, norm_w, norm_eps, residual, ldr, y, ldy};
+  const hipError_t e = ssd::launch_linear(lp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mixer_proj launch");
+  return SSD_OK;
+}
+
 }  // extern "C"

@@ -18,7 +18,7 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 enum KernelKind {
   kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
   kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKScanGroups, kKXbcPrepass,
-  kKernelKinds
+  kKLinear, kKernelKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events on stream `s`
@@ -160,5 +160,23 @@ size_t x_prepass_bytes(const Problem& pr);
 size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);
 hipError_t launch_conv_bwd(const ConvProblem& cp, View dout, View dstate_out, MView dx, float* dw,
                            float* db, MView dstate_in, int accumulate, void* ws, hipStream_t s);
+
+// ---------------------------------------------------------------- mixer projections
+// y[M][N] = x[M][K] w[N][K]^T (bf16, fp32 accumulation), optionally with x's rows
+// RMS-normalised over K and scaled by norm_w[K] first, and a residual r[M][N] added.
+struct LinearProblem {
+  int64_t M, N, K;
+  const void* x;
+  int64_t ldx;
+  const void* w;
+  int64_t ldw;
+  const float* norm_w;
+  float eps;
+  const void* residual;
+  int64_t ldr;
+  void* y;
+  int64_t ldy;
+};
+hipError_t launch_linear(const LinearProblem& lp, hipStream_t s);
 
 }  // namespace ssd

@@ -45,6 +45,7 @@ BLOCK = 4096
 # tensor ids for the counter-derived streams
 _T_ZXBCDT, _T_DOUT, _T_X, _T_DT, _T_B, _T_C, _T_DRIFT = 1, 2, 3, 4, 5, 6, 7
 _T_A, _T_D, _T_DTB, _T_CW, _T_CB, _T_H0, _T_CS, _T_DH, _T_DCS = 11, 12, 13, 14, 15, 16, 17, 18, 19
+_T_U, _T_WIN, _T_WOUT, _T_NIN, _T_NOUT, _T_DFINAL = 21, 22, 23, 24, 25, 26
 
 
 @dataclass(frozen=True)
@@ -235,4 +236,54 @@ def states(d: Dims, seed: int = 0, scale: float = 0.5) -> dict:
         dcs = _rng(seed, _T_DCS).standard_normal((B, d.K - 1, d.cd)) * scale
         out["conv_state"] = round_io(cs.astype(np.float32), d.dtype)
         out["dconv_state"] = round_io(dcs.astype(np.float32), d.dtype)
+    return out
+
+
+# ----------------------------------------------------------------- mixer projections
+
+def tokens(d: Dims, seed: int = 0, t0: int = 0, t1: int | None = None) -> np.ndarray:
+    """Token embeddings u [B, t1-t0, d_model] ~ N(0, 1) (plus the per-frame mean drift,
+    a per-channel random walk over frames with step std 0.1, when d.drift), as bf16
+    bit patterns."""
+    t1 = d.L if t1 is None else t1
+    out = np.empty((d.B, t1 - t0, d.d_model), dtype=np.uint16)
+    if d.drift:
+        # same drift construction as the in_proj rows, in token space (step std 0.1)
+        def table(b):
+            nf = (d.L + d.frame - 1) // d.frame
+            return np.cumsum(_rng(seed, _T_DRIFT, b, 1).standard_normal((nf, d.d_model)) * 0.1, axis=0)
+        _fill_rows_table(d, seed, _T_U, d.d_model, 1.0, out, t0, t1, table)
+    else:
+        _fill_rows(d, seed, _T_U, d.d_model, 1.0, out, t0, t1, False)
+    return out
+
+
+def _fill_rows_table(d, seed, tid, width, scale, out, t0, t1, table_of):
+    bf = out.dtype == np.uint16
+    for b in range(out.shape[0]):
+        table = table_of(b)
+        for blk in range(t0 // BLOCK, (t1 + BLOCK - 1) // BLOCK):
+            lo, hi = max(t0, blk * BLOCK), min(t1, (blk + 1) * BLOCK)
+            v = _rng(seed, tid, b, blk).standard_normal((BLOCK, width), dtype=np.float32)[lo - blk * BLOCK:hi - blk * BLOCK]
+            v = v * np.float32(scale) + table[np.arange(lo, hi) // d.frame].astype(np.float32)
+            out[b, lo - t0:hi - t0] = bf16_bits(v) if bf else v
+
+
+def mixer_weights(d: Dims, seed: int = 0) -> dict:
+    """Random-init projection weights of the mixer (nn.Linear layout [out, in]), as bf16
+    bit patterns: W_in [d_in_proj, d_model] and W_out [d_model, H*P] ~ N(0, 0.02^2);
+    RMSNorm gains (fp32) of the full block ~ 1 + N(0, 0.1^2): norm_in [d_model] before
+    in_proj, norm_out [H*P] before out_proj."""
+    w_in = _rng(seed, _T_WIN).standard_normal((d.d_in_proj, d.d_model), dtype=np.float32) * np.float32(0.02)
+    w_out = _rng(seed, _T_WOUT).standard_normal((d.d_model, d.hp), dtype=np.float32) * np.float32(0.02)
+    n_in = 1.0 + 0.1 * _rng(seed, _T_NIN).standard_normal(d.d_model)
+    n_out = 1.0 + 0.1 * _rng(seed, _T_NOUT).standard_normal(d.hp)
+    return dict(w_in=bf16_bits(w_in), w_out=bf16_bits(w_out), norm_in=n_in.astype(np.float32),
+                norm_out=n_out.astype(np.float32))
+
+
+def dfinal(d: Dims, seed: int = 0) -> np.ndarray:
+    """Upstream gradient at the mixer's final output [B, L, d_model] ~ N(0, 1), bf16 bits."""
+    out = np.empty((d.B, d.L, d.d_model), dtype=np.uint16)
+    _fill_rows(d, seed, _T_DFINAL, d.d_model, 1.0, out, 0, d.L, False)
     return out
