@@ -1,21 +1,28 @@
 """Benchmark of the Mamba-2 mixer hot path on one MI355X.
 
-Step = one pass of the whole hot path over one batch: the forward over L tokens
-(causal conv1d + SiLU -> chunked SSD -> SiLU(z) gate, keeping only the (h, conv
-buffer) checkpoints every `seg` tokens), then the backward segment by segment in
+Headline step = one pass of the whole hot path over one batch: the forward over L
+tokens (causal conv1d + SiLU -> chunked SSD -> SiLU(z) gate, keeping only the (h,
+conv buffer) checkpoints every `seg` tokens), then the backward segment by segment in
 reverse (recompute from the checkpoint, all gradients).  Workload: d_model 1024
 shapes (32 heads x 64, d_state 128, conv 4), batch 1, L = 1,048,576 tokens as 64
 segments of 16,384, bf16 I/O, seeded synthetic in_proj rows (see synth.py).
 
-Prints one JSON line with tokens/s of the whole step, the forward alone, the
-roofline of the dominant kernel (HIP events on the launch stream) and the fp64
-oracle timed on a bounded prefix on the host cores.
+Prints one JSON line: tokens/s of that step (value), per-step median / min, the
+forward alone with its own roofline, the per-kernel device times, the roofline of the
+dominant kernel (HIP events on the launch stream), the path-level roofline, and extra
+measurements that are not the headline:
+  c4       the batched 2.7B-style shapes (B = 16, L = 4096, 80 heads), fwd + bwd
+  c1_mixer in_proj -> hot path -> out_proj at L = 8192 (MFMA projections; the working
+           set fits the 256 MB last-level cache)
+  decode   one-token streaming decode latency at d_model 1024 and the 80-head shapes
+and the fp64 oracle timed on a bounded prefix on the host cores (all of them, and one).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -23,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 
 def parse():
@@ -35,9 +43,13 @@ def parse():
     ap.add_argument("--seg", type=int, default=16384)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=49152, help="oracle prefix tokens (0 = skip)")
+    ap.add_argument("--cpu-sample-1t", type=int, default=4096,
+                    help="oracle prefix tokens for the one-thread figure (0 = skip)")
+    ap.add_argument("--extras", type=int, default=1, help="0 = headline step only")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for counter runs: one 256 MiB device copy (byte-counter calibration), "
                          "then two fwd+bwd passes over a single segment; prints no JSON")
+    ap.add_argument("--oracle-only", type=int, default=0, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -47,6 +59,7 @@ COPY_BYTES = 256 << 20
 TRAFFIC_REPORT = os.path.join(ROOT, "profiles", "bwd_main_seg16k_hbm_bytes.md")
 KERNEL_SYMBOL = {"bwd_main": "bwd_main_kernel", "walk_out": "walk_kernel", "walk_state": "walk_kernel",
                  "conv_bwd": "conv_bwd_kernel"}
+FWD_KINDS = {"prepass", "walk_state", "scan", "walk_out", "conv_state_out"}
 
 
 def measured_traffic(kind: str):
@@ -62,8 +75,57 @@ def measured_traffic(kind: str):
     return rec["hbm_bytes_per_launch"]
 
 
+def hot_bytes(d):
+    """Algorithmic bytes per token (each input read once, each output written once):
+    forward = xBC raw + z + dt in, out; backward = the forward's inputs + dout in,
+    dxBC + dz + ddt out."""
+    es = 2
+    fwd = es * (d.cd + 2 * d.hp + d.H)
+    bwd = es * (d.cd + 2 * d.hp + d.H) + es * (d.cd + d.hp + d.H)
+    return fwd, bwd
+
+
+def timed(fn, steps, stream):
+    """Per-call device times (ms) of `steps` back-to-back calls, HIP events on `stream`."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def oracle_sample(n: int, seed: int) -> dict:
+    """fp64 oracle fwd + bwd over the first n tokens of the headline workload."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    from selective_state_space_15_amd import synth
+    d = synth.CONFIGS["c2"]
+    B, H, hp, cd = d.B, d.H, d.hp, d.cd
+    f = synth.bf16_to_f32(synth.zxbcdt(d, seed, 0, n)).astype(np.float64)
+    zz, xr, dtr = f[..., :hp], f[..., hp:hp + cd], f[..., hp + cd:hp + cd + H]
+    p64 = {k: v.astype(np.float64) for k, v in synth.params(d, seed).items()}
+    do = synth.bf16_to_f32(synth.dout(d, seed + 7, 0, n)).astype(np.float64)
+    t = time.perf_counter()
+    orc.mixer_fwd(xr, p64["conv_w"], p64["conv_b"], dtr, p64["A"], H, d.P, d.G, d.N,
+                  dt_bias=p64["dt_bias"], D=p64["D"], z=zz.reshape(B, n, H, d.P))
+    orc.mixer_bwd(xr, p64["conv_w"], p64["conv_b"], dtr, p64["A"], H, d.P, d.G, d.N,
+                  do.reshape(B, n, H, d.P), dt_bias=p64["dt_bias"], D=p64["D"],
+                  z=zz.reshape(B, n, H, d.P))
+    sec = time.perf_counter() - t
+    return {"value": B * n / sec, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"fwd+bwd over the first {n} tokens of the same workload (fp64, {sec:.1f} s)"}
+
+
 def main():
     args = parse()
+    if args.oracle_only:
+        print(json.dumps(oracle_sample(args.oracle_only, args.seed)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the path has no collectives and shards by sequence only in its design notes.",
@@ -134,27 +196,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    per_step = timed(step, args.steps, stream)
     wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = sum(per_step) / args.steps
+    print(f"[bench] headline: {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
 
     # forward alone (same launches), for the forward-only rate
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(args.steps):
-        fwd()
-    f1.record(stream)
-    torch.cuda.synchronize()
-    ms_fwd = f0.elapsed_time(f1) / args.steps
+    ms_fwd = float(np.mean(timed(fwd, args.steps, stream)))
 
-    # one more step with per-kernel HIP events (library instrumentation, same stream)
+    # one more set of steps with per-kernel HIP events (library instrumentation, same stream)
     bd.ssd_timing_enable(True)
     for _ in range(args.steps):
         step()
@@ -163,24 +215,21 @@ def main():
     bd.ssd_timing_enable(False)
 
     tokens = B * L
-    # algorithmic bytes per token (each input read once, each output written once)
-    es = 2
-    fwd_bytes = es * (cd + 2 * hp + H)                    # xBC raw, z, dt in; out
-    bwd_bytes = es * (cd + 2 * hp + H) + es * (cd + hp + H)  # + dout in; dxBC, dz, ddt out
+    fwd_bytes, bwd_bytes = hot_bytes(d)
     step_bytes = fwd_bytes + bwd_bytes
     roof_tok_s = HBM_PEAK_GBS * 1e9 / step_bytes
     # dominant kernel: the largest summed device time; its algorithmic bytes per
     # launch = the per-token bytes of its pass x the tokens one launch covers
-    fwd_kinds = {"walk_state", "scan", "walk_out", "conv_state_out"}
     dom = max(ktimes, key=lambda k: ktimes[k][0])
     dom_ms, dom_n = ktimes[dom]
     dom_avg_ms = dom_ms / max(dom_n, 1)
-    if dom in fwd_kinds:
+    if dom in FWD_KINDS:
         per_tok, tok_per_launch = fwd_bytes, tokens
     else:
         per_tok, tok_per_launch = bwd_bytes, B * args.seg
     achieved = per_tok * tok_per_launch / (dom_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(dom)
+    fwd_gbs = fwd_bytes * tokens / (ms_fwd * 1e-3) / 1e9
 
     res = {
         "metric": "SSD mixer fwd+bwd tokens/sec at d=1024, L=1M (segmented 64 x 16384)",
@@ -190,6 +239,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(np.min(per_step)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -200,6 +251,8 @@ def main():
                    "global_batch": B, "seq_len": L},
         "fwd_tokens_per_s": tokens / (ms_fwd * 1e-3),
         "ms_fwd": ms_fwd,
+        "fwd_roofline": {"bound": "hbm", "achieved": fwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": fwd_gbs / HBM_PEAK_GBS, "alg_bytes_per_token": fwd_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
                      "kernel_avg_ms": dom_avg_ms, "kernel_launches_per_step": dom_n / args.steps,
@@ -209,27 +262,191 @@ def main():
         "kernel_ms_per_step": {k: v[0] / args.steps for k, v in ktimes.items() if v[1]},
         "wall_s": wall,
     }
+    del zx, dout, out, fws, bws, g
+    torch.cuda.empty_cache()
+
+    if args.extras:
+        res["c4"] = bench_c4(args, stream)
+        print("[bench] c4 done", file=sys.stderr, flush=True)
+        res["c1_mixer"] = bench_c1_mixer(args, stream)
+        print("[bench] c1 mixer done", file=sys.stderr, flush=True)
+        res["decode"] = bench_decode(args, stream)
+        print("[bench] decode done", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if args.cpu_sample > 0:
-        from oracle import oracle as orc
-        n = min(args.cpu_sample, L)
-        f = synth.bf16_to_f32(synth.zxbcdt(d, args.seed, 0, n)).astype(np.float64)
-        zz, xr, dtr = f[..., :hp], f[..., hp:hp + cd], f[..., hp + cd:hp + cd + H]
-        p64 = {k: v.astype(np.float64) for k, v in synth.params(d, args.seed).items()}
-        do = synth.bf16_to_f32(synth.dout(d, args.seed + 7, 0, n)).astype(np.float64)
-        t = time.perf_counter()
-        orc.mixer_fwd(xr, p64["conv_w"], p64["conv_b"], dtr, p64["A"], H, d.P, d.G, d.N,
-                      dt_bias=p64["dt_bias"], D=p64["D"], z=zz.reshape(B, n, H, d.P))
-        orc.mixer_bwd(xr, p64["conv_w"], p64["conv_b"], dtr, p64["A"], H, d.P, d.G, d.N,
-                      do.reshape(B, n, H, d.P), dt_bias=p64["dt_bias"], D=p64["D"],
-                      z=zz.reshape(B, n, H, d.P))
-        sec = time.perf_counter() - t
-        res["cpu_baseline"] = {"value": B * n / sec, "unit": "tokens/s", "cores": orc.num_threads(),
-                               "kind": "oracle",
-                               "sample": f"fwd+bwd over the first {n} tokens of the same workload "
-                                         f"(fp64, {sec:.1f} s)"}
+        res["cpu_baseline"] = oracle_sample(min(args.cpu_sample, L), args.seed)
+    if args.cpu_sample_1t > 0:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-only",
+                            str(args.cpu_sample_1t), "--seed", str(args.seed)],
+                           capture_output=True, text=True, env=env, timeout=600)
+        if r.returncode == 0:
+            res["cpu_baseline_1thread"] = json.loads(r.stdout.strip().splitlines()[-1])
     print(json.dumps(res), flush=True)
+
+
+def bench_c4(args, stream):
+    """Batched 2.7B-style hot path (B=16, L=4096, 80 heads x 64, d_state 128), one
+    forward and one backward over the whole batch per step."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_15_amd import binding as bd
+    from selective_state_space_15_amd import synth
+    d = synth.CONFIGS["c4"]
+    dev = stream.device
+    B, L, H, hp, cd = d.B, d.L, d.H, d.hp, d.cd
+    zx = torch.from_numpy(synth.zxbcdt(d, args.seed).view(np.int16)).to(dev).view(torch.bfloat16)
+    dout = torch.from_numpy(synth.dout(d, args.seed + 7).view(np.int16)).to(dev).view(torch.bfloat16)
+    p = {k: torch.from_numpy(v).to(dev) for k, v in synth.params(d, args.seed).items()}
+    z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+    dims = bd.make_dims(B, L, H, d.P, d.N, d.G, 0, d.K)
+    out = torch.empty(B, L, hp, dtype=torch.bfloat16, device=dev)
+    fws = torch.empty(max(bd.ssd_fwd_workspace(dims, bd.SSD_BF16), 1), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(bd.ssd_bwd_workspace(dims, bd.SSD_BF16), 1), dtype=torch.uint8, device=dev)
+    dxbc = torch.empty(B, L, cd, dtype=torch.bfloat16, device=dev)
+    ddt = torch.empty(B, L, H, dtype=torch.bfloat16, device=dev)
+    dz = torch.empty(B, L, hp, dtype=torch.bfloat16, device=dev)
+    gp = {k: torch.empty(H, device=dev) for k in ("dA", "dD", "ddt_bias")}
+    dcw, dcb = torch.empty(cd, d.K, device=dev), torch.empty(cd, device=dev)
+
+    def fwd():
+        bd.ssd_fwd(dims, xbc, p["A"], dt, out, conv_w=p["conv_w"], conv_b=p["conv_b"],
+                   dt_bias=p["dt_bias"], D=p["D"], z=z, ws=fws)
+
+    def step():
+        fwd()
+        bd.ssd_bwd(dims, xbc, p["A"], dt, dout, dxbc, ddt, gp["dA"], conv_w=p["conv_w"],
+                   conv_b=p["conv_b"], dt_bias=p["dt_bias"], D=p["D"], z=z, dz=dz, dD=gp["dD"],
+                   ddt_bias=gp["ddt_bias"], dconv_w=dcw, dconv_b=dcb, ws=bws)
+
+    for _ in range(2):
+        step()
+    n = max(args.steps, 5)
+    ms = timed(step, n, stream)
+    msf = timed(fwd, n, stream)
+    fb, bb = hot_bytes(d)
+    tok = B * L
+    med, medf = float(np.median(ms)), float(np.median(msf))
+    gbs = (fb + bb) * tok / (med * 1e-3) / 1e9
+    gbsf = fb * tok / (medf * 1e-3) / 1e9
+    return {"workload": f"hot path fwd+bwd, 2.7B-style shapes: B={B}, L={L}, {H}x{d.P} heads, "
+                        f"d_state {d.N}, conv {d.K}, bf16",
+            "tokens_per_s": tok / (med * 1e-3), "ms_per_step_median": med, "ms_per_step_min": min(ms),
+            "fwd_tokens_per_s": tok / (medf * 1e-3), "ms_fwd_median": medf,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "alg_bytes_per_token": fb + bb},
+            "fwd_roofline": {"bound": "hbm", "achieved": gbsf, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbsf / HBM_PEAK_GBS, "alg_bytes_per_token": fb}}
+
+
+def bench_c1_mixer(args, stream):
+    """in_proj (mixer_proj) -> ssd_fwd -> out_proj (mixer_proj) at the d_model 1024
+    shapes, L = 8192; the projections' flops against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_15_amd import binding as bd
+    from selective_state_space_15_amd import synth
+    d = synth.CONFIGS["c1"]
+    dev = stream.device
+    B, L, H, hp, cd, dm, dip = d.B, d.L, d.H, d.hp, d.cd, d.d_model, d.d_in_proj
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    u = bits(synth.tokens(d, args.seed)).view(B * L, dm)
+    w = synth.mixer_weights(d, args.seed)
+    w_in, w_out = bits(w["w_in"]), bits(w["w_out"])
+    p = {k: torch.from_numpy(v).to(dev) for k, v in synth.params(d, args.seed).items()}
+    zx = torch.empty(B, L, dip, dtype=torch.bfloat16, device=dev)
+    z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+    out = torch.empty(B, L, hp, dtype=torch.bfloat16, device=dev)
+    final = torch.empty(B * L, dm, dtype=torch.bfloat16, device=dev)
+    dims = bd.make_dims(B, L, H, d.P, d.N, d.G, 0, d.K)
+    fws = torch.empty(max(bd.ssd_fwd_workspace(dims, bd.SSD_BF16), 1), dtype=torch.uint8, device=dev)
+
+    def in_proj():
+        bd.mixer_proj(u, w_in, zx.view(B * L, dip))
+
+    def hot():
+        bd.ssd_fwd(dims, xbc, p["A"], dt, out, conv_w=p["conv_w"], conv_b=p["conv_b"],
+                   dt_bias=p["dt_bias"], D=p["D"], z=z, ws=fws)
+
+    def out_proj():
+        bd.mixer_proj(out.view(B * L, hp), w_out, final)
+
+    def mixer():
+        in_proj()
+        hot()
+        out_proj()
+
+    for _ in range(3):
+        mixer()
+    n = max(args.steps, 20)
+    t_mix = float(np.median(timed(mixer, n, stream)))
+    t_in = float(np.median(timed(in_proj, n, stream)))
+    t_out = float(np.median(timed(out_proj, n, stream)))
+    tok = B * L
+    f_in, f_out = 2.0 * tok * dm * dip, 2.0 * tok * hp * dm
+    tf_in, tf_out = f_in / (t_in * 1e-3) / 1e12, f_out / (t_out * 1e-3) / 1e12
+    tf = (f_in + f_out) / ((t_in + t_out) * 1e-3) / 1e12
+    return {"workload": f"mixer forward in_proj -> hot path -> out_proj, d_model {dm}, B={B}, L={L}, bf16 "
+                        "(working set cache-resident)",
+            "tokens_per_s": tok / (t_mix * 1e-3), "ms_median": t_mix,
+            "in_proj_ms": t_in, "out_proj_ms": t_out,
+            "gemm_roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                              "frac": tf / MFMA_BF16_PEAK_TFS, "in_proj_tflops": tf_in,
+                              "out_proj_tflops": tf_out, "flops_per_token": (f_in + f_out) / tok}}
+
+
+def bench_decode(args, stream):
+    """One-token streaming decode (ssd_decode, T = 1 per call, carried state), at the
+    d_model 1024 shapes (B = 1) and the 80-head shapes (B = 16)."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_15_amd import binding as bd
+    from selective_state_space_15_amd import synth
+    dev = stream.device
+    res = {}
+    for name, d in (("d1024_b1", synth.CONFIGS["c1"].with_(L=256)), ("d2560_b16", synth.CONFIGS["c4"].with_(L=64))):
+        B, T, H, hp, cd = d.B, d.L, d.H, d.hp, d.cd
+        zx = torch.from_numpy(synth.zxbcdt(d, args.seed).view(np.int16)).to(dev).view(torch.bfloat16)
+        p = {k: torch.from_numpy(v).to(dev) for k, v in synth.params(d, args.seed).items()}
+        z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+        h = torch.zeros(B, H, d.P, d.N, device=dev)
+        cs = [torch.zeros(B, d.K - 1, cd, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        out = torch.empty(B, T, hp, dtype=torch.bfloat16, device=dev)
+        dims = bd.make_dims(B, 1, H, d.P, d.N, d.G, 0, d.K)
+        state = {"t": 0}
+
+        def one():
+            t = state["t"] % T
+            i = state["t"] % 2
+            bd.ssd_decode(dims, xbc[:, t:t + 1], p["A"], dt[:, t:t + 1], out[:, t:t + 1], h,
+                          conv_w=p["conv_w"], conv_b=p["conv_b"], conv_state_in=cs[i],
+                          conv_state_out=cs[1 - i], dt_bias=p["dt_bias"], D=p["D"], z=z[:, t:t + 1],
+                          h_in=h)
+            state["t"] += 1
+
+        for _ in range(10):
+            one()
+        ms = timed(one, 200, stream)
+        med = float(np.median(ms))
+        bd.ssd_timing_enable(True)
+        for _ in range(200):
+            one()
+        torch.cuda.synchronize()
+        kt = bd.ssd_timing_read()["decode"]
+        bd.ssd_timing_enable(False)
+        state_bytes = 2 * B * H * d.P * d.N * 4
+        k_us = kt[0] / max(kt[1], 1) * 1e3
+        res[name] = {"batch": B, "heads": H, "us_per_call_median": med * 1e3,
+                     "kernel_us_avg": k_us, "tokens_per_s": B / (med * 1e-3),
+                     "state_bytes_per_call": state_bytes,
+                     "kernel_state_gbs": state_bytes / (k_us * 1e-6) / 1e9,
+                     "note": "one call per token step from Python (host launch overhead included in "
+                             "us_per_call); the kernel reads and writes the state once per call"}
+    return res
 
 
 if __name__ == "__main__":

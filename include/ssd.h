@@ -221,6 +221,30 @@ ssd_status conv1d_bwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t w
                       size_t ws_bytes, void* stream);
 
 /*
+ * ssd_decode -- streaming decode: d->seqlen new tokens (usually 1) stepped one at a
+ * time from the carried state, for inference over streams longer than any single
+ * forward call (the two-million-token inference mode of the pith.science review of
+ * Video-Ma2mba, referee report summary).  The same function as ssd_fwd over these
+ * tokens with (h0, conv_state_in) = (h_in, conv_state_in): conv1d + SiLU of the new
+ * raw rows against the carried conv inputs, the recurrence of Eq. (1) in its selective
+ * form one step per token, y + D x, SiLU(z) gate.
+ *
+ *   xbc, dt, z, out   [B,T,.] views as in ssd_fwd (element alignment suffices)
+ *   conv_state_in     [B,K-1,Cd] carried raw rows (ptr NULL = zeros)
+ *   conv_state_out    [B,K-1,Cd] required when conv_width > 1; must not alias
+ *                     conv_state_in (callers ping-pong two buffers)
+ *   h_in              [B,H,P,N] fp32 state in (NULL = zeros)
+ *   h_out             [B,H,P,N] fp32 state out (required; may equal h_in)
+ * The state is read once and written once per call; cost per call is latency-bound
+ * (one workgroup per (batch, head)).  No workspace.
+ */
+ssd_status ssd_decode(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                      const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                      ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                      const float* D, ssd_view z, const float* h_in, float* h_out, ssd_view out,
+                      void* stream);
+
+/*
  * mixer_proj -- the mixer's linear layers (in_proj, out_proj) on MFMA:
  *
  *     y[m][n] = sum_k x'[m][k] * w[n][k]  (+ residual[m][n])

@@ -60,6 +60,7 @@ _SIGS = {
     "conv1d_bwd_workspace": ([_I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(_SZ)], _I),
     "conv1d_bwd": ([_I64, _I64, _I64, ctypes.c_int32, _I, _V, _F, _F, _I, _V, _V, _V, _V, _F, _F, _V,
                     _I, _P, _SZ, _P], _I),
+    "ssd_decode": ([_D, _I, _V, _F, _F, _V, _V, _V, _F, _I, _F, _F, _V, _F, _F, _V, _P], _I),
     "mixer_proj": ([_I64, _I64, _I64, _I, _P, _I64, _P, _I64, _F, ctypes.c_float, _P, _I64, _P, _I64,
                     _P], _I),
     "ssd_timing_enable": ([_I], _I),
@@ -363,6 +364,28 @@ def conv1d_bwd(x, w, dout, dx, dw, *, b=None, silu=True, state_in=None, dstate_o
                           fptr(dw), fptr(db), view(dstate_in), int(bool(accumulate)), wsp, wsn,
                           stream_ptr(stream))
     _check(st, "conv1d_bwd")
+
+
+def ssd_decode(d: ssd_dims, xbc, A, dt, out, h_out, *, conv_w=None, conv_b=None, conv_state_in=None,
+               conv_state_out=None, dt_bias=None, dt_softplus=True, D=None, z=None, h_in=None,
+               stream=None):
+    """Enqueue ssd_decode: d.seqlen new tokens stepped from (h_in, conv_state_in);
+    h_out (may be h_in) and conv_state_out (not conv_state_in) receive the state."""
+    io, cd = _ssd_common(d, xbc, A, dt, conv_w, conv_b,
+                         dict(conv_state_in=conv_state_in, conv_state_out=conv_state_out),
+                         dt_bias, D, z, h_in)
+    B, L, H, P, N, K = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.conv_width
+    _act(out, "out", B, L, H * P, io)
+    _f32(h_out, "h_out", (B, H, P, N), required=True)
+    if K > 1 and conv_state_out is None:
+        raise ValueError("conv_state_out is required with a conv")
+    _same_device([xbc, A, dt, out, h_out, conv_w, conv_b, conv_state_in, conv_state_out, dt_bias, D, z,
+                  h_in], "ssd_decode")
+    st = lib().ssd_decode(ctypes.byref(d), io_dtype(xbc), view(xbc), fptr(conv_w), fptr(conv_b),
+                          view(conv_state_in), view(conv_state_out), view(dt), fptr(dt_bias),
+                          int(bool(dt_softplus)), fptr(A), fptr(D), view(z), fptr(h_in), fptr(h_out),
+                          view(out), stream_ptr(stream))
+    _check(st, "ssd_decode")
 
 
 def _mat(t, name, rows, cols):

@@ -488,4 +488,48 @@ ssd_status mixer_proj(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void*
   return SSD_OK;
 }
 
+ssd_status ssd_decode(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* conv_w,
+                      const float* conv_b, ssd_view conv_state_in, ssd_view conv_state_out,
+                      ssd_view dt, const float* dt_bias, int dt_softplus, const float* A,
+                      const float* D, ssd_view z, const float* h_in, float* h_out, ssd_view out,
+                      void* stream) {
+  g_last_error.clear();
+  TRY(check_dims(d, io));
+  const int64_t T = d->seqlen, Cd = cdim(d), HP = d->nheads * d->headdim;
+  const int64_t K = d->conv_width;
+  // element-aligned views: the decode step reads single elements
+  TRY(check_view(xbc, "xbc", io, true, false, T, Cd));
+  TRY(check_view(dt, "dt", io, true, false, T, d->nheads));
+  TRY(check_view(z, "z", io, false, false, T, HP));
+  TRY(check_view(out, "out", io, true, false, T, HP));
+  if (!A) return fail(SSD_ERR_NULL, "A: NULL");
+  if (!h_out) return fail(SSD_ERR_NULL, "h_out: NULL (the decode state is always returned)");
+  if (K > 1) {
+    if (!conv_w) return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+    TRY(check_view(conv_state_in, "conv_state_in", io, false, false, K - 1, Cd));
+    TRY(check_view(conv_state_out, "conv_state_out", io, true, false, K - 1, Cd));
+    if (conv_state_in.ptr && conv_state_in.ptr == conv_state_out.ptr)
+      return fail(SSD_ERR_SHAPE, "conv_state_out must not alias conv_state_in");
+  } else if (K > 0 && !conv_w) {
+    return fail(SSD_ERR_NULL, "conv_w: NULL with conv_width %lld", (long long)K);
+  }
+  ssd::Problem pr = make_problem(d, io);
+  pr.xbc = cv(xbc);
+  pr.conv_w = K > 0 ? conv_w : nullptr;
+  pr.conv_b = K > 0 ? conv_b : nullptr;
+  pr.cs_in = K > 1 ? cv(conv_state_in) : ssd::View{nullptr, 0, 0};
+  pr.dt = cv(dt);
+  pr.dt_bias = dt_bias;
+  pr.softplus = dt_softplus ? 1 : 0;
+  pr.A = A;
+  pr.D = D;
+  pr.z = cv(z);
+  pr.h0 = h_in;
+  const hipError_t e = ssd::launch_decode(pr, h_out, mv(out),
+                                          K > 1 ? mv(conv_state_out) : ssd::MView{nullptr, 0, 0},
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ssd_decode launch");
+  return SSD_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,192 @@
+// Streaming decode of the mixer hot path on gfx950: new tokens stepped one at a time
+// from the carried (h, conv buffer) state, for inference over streams longer than any
+// one forward call (the two-million-token inference mode in the pith.science review
+// of Video-Ma2mba, referee report summary).
+//
+// Per token t and head h (group g):
+//   xin = the K-1 carried raw rows, then the new raw row xbc[t]
+//   x, B, C = SiLU(bias + sum_k w[k] xin[k])  for the head's P x channels and the
+//             group's N B and N C channels
+//   dt = softplus(dt_raw + dt_bias), a = exp(dt A)
+//   h[p][n] <- a h[p][n] + dt x[p] B[n];   y[p] = sum_n h[p][n] C[n] + D x[p]
+//   out[p] = y[p] SiLU(z[p])
+// which is the recurrence of the forward pass taken one step at a time.
+//
+// One workgroup of 256 threads owns one (batch, head): its P x N fp32 state lives in
+// registers for the whole call (N / (256 / P) elements per thread), each conv channel
+// keeps its window of K-1 raw inputs in a register file, and the post-conv x, B and C
+// of the current token pass through LDS.  The state is read once and written once per
+// call, whatever the number of tokens.  The B / C conv runs in every workgroup of the
+// group (a few hundred channels); the group's first head writes their carried rows.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+namespace {
+
+constexpr int kDecThreads = 256;
+
+struct DecodeArgs {
+  Problem pr;          // L = tokens in this call; h0 = state in (null = zeros)
+  float* h_out;        // [B][H][P][N] (may equal h0)
+  MView out;           // [B][T][H*P]
+  MView cs_out;        // [B][K-1][Cd] conv state out (distinct from cs_in)
+};
+
+template <int NT>
+__device__ __forceinline__ float sum_lanes(float v) {
+  static_assert(NT == 4 || NT == 8, "lanes per state row");
+  v += dpp_f<kDppQuad1032>(0.f, v);
+  v += dpp_f<kDppQuad2301>(0.f, v);
+  if constexpr (NT == 8) v += dpp_f<kDppRowHalfMirror>(0.f, v);
+  return v;
+}
+
+template <typename IO, int P, int N, int K>
+__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
+  using E = typename io_traits<IO>::elem;
+  constexpr int NT = kDecThreads / P;   // threads per state row p
+  constexpr int NPT = N / NT;           // state elements per thread
+  constexpr int NCH = P + 2 * N;        // conv channels of one (head, group)
+  constexpr int CPT = (NCH + kDecThreads - 1) / kDecThreads;  // channels per thread
+  constexpr int KW = K > 1 ? K - 1 : 1;  // carried window
+  static_assert(NT * P == kDecThreads && NPT * NT == N, "thread layout");
+  const Problem& pr = a.pr;
+  __shared__ float s_x[P], s_B[N], s_C[N];
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / pr.H, h = blockIdx.x % pr.H;
+  const int hpg = pr.H / pr.G, g = h / hpg;
+  const int64_t HP = static_cast<int64_t>(pr.H) * P;
+  const int64_t GN = static_cast<int64_t>(pr.G) * N;
+
+  // conv channels of this thread: list slot j = tid + 256 i; xbc channel ch[i]
+  int64_t ch[CPT];
+  bool live[CPT];
+  float win[CPT][KW], wk[CPT][K > 0 ? K : 1], bias[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int j = tid + kDecThreads * i;
+    live[i] = j < NCH;
+    const int jj = live[i] ? j : 0;
+    ch[i] = jj < P ? h * P + jj : jj < P + N ? HP + g * N + (jj - P) : HP + GN + g * N + (jj - P - N);
+    if constexpr (K > 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) wk[i][k] = pr.conv_w[ch[i] * K + k];
+      bias[i] = pr.conv_b ? pr.conv_b[ch[i]] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < KW; ++k) {
+      float v = 0.f;
+      if (K > 1 && pr.cs_in.p)
+        v = io_traits<IO>::to_f(static_cast<const E*>(pr.cs_in.p)[b * pr.cs_in.sb + k * pr.cs_in.st + ch[i]]);
+      win[i][k] = v;
+    }
+  }
+
+  // state rows p = tid / NT, columns n0 .. n0 + NPT
+  const int p = tid / NT, n0 = (tid % NT) * NPT;
+  float st[NPT];
+  const int64_t soff = ((static_cast<int64_t>(b) * pr.H + h) * P + p) * N + n0;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) st[j] = pr.h0 ? pr.h0[soff + j] : 0.f;
+  const float A = pr.A[h], Dh = pr.D ? pr.D[h] : 0.f;
+  const float dtb = pr.dt_bias ? pr.dt_bias[h] : 0.f;
+  const E* xbc = static_cast<const E*>(pr.xbc.p);
+  const E* dtp = static_cast<const E*>(pr.dt.p);
+  const E* zp = static_cast<const E*>(pr.z.p);
+
+  for (int64_t t = 0; t < pr.L; ++t) {
+    // post-conv x, B, C of token t
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      if (!live[i]) continue;
+      const float raw = io_traits<IO>::to_f(xbc[b * pr.xbc.sb + t * pr.xbc.st + ch[i]]);
+      float v = raw;
+      if constexpr (K > 0) {
+        float pre = bias[i] + wk[i][K - 1] * raw;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) pre += wk[i][k] * win[i][k];
+        v = siluf_(pre);
+#pragma unroll
+        for (int k = 0; k + 1 < K - 1; ++k) win[i][k] = win[i][k + 1];
+        if constexpr (K > 1) win[i][K - 2] = raw;
+      }
+      const int j = tid + kDecThreads * i;
+      if (j < P) s_x[j] = v;
+      else if (j < P + N) s_B[j - P] = v;
+      else s_C[j - P - N] = v;
+    }
+    __syncthreads();
+    float dt = io_traits<IO>::to_f(dtp[b * pr.dt.sb + t * pr.dt.st + h]) + dtb;
+    if (pr.softplus) dt = softplusf_(dt);
+    const float decay = __expf(dt * A);
+    const float dtx = dt * s_x[p];
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      st[j] = decay * st[j] + dtx * s_B[n0 + j];
+      part += st[j] * s_C[n0 + j];
+    }
+    const float y = sum_lanes<NT>(part) + Dh * s_x[p];
+    if (tid % NT == 0) {
+      float o = y;
+      if (zp) o *= siluf_(io_traits<IO>::to_f(zp[b * pr.z.sb + t * pr.z.st + h * P + p]));
+      static_cast<E*>(a.out.p)[b * a.out.sb + t * a.out.st + h * P + p] = io_traits<IO>::from_f(o);
+    }
+    __syncthreads();  // the next token rewrites s_x / s_B / s_C
+  }
+
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) a.h_out[soff + j] = st[j];
+  if (K > 1 && a.cs_out.p) {
+    // the last K-1 conv inputs: the window now (carried rows first when T < K-1)
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int j = tid + kDecThreads * i;
+      if (!live[i] || (j >= P && h % hpg != 0)) continue;  // B / C rows: the group's first head
+#pragma unroll
+      for (int k = 0; k < KW; ++k)
+        static_cast<E*>(a.cs_out.p)[b * a.cs_out.sb + k * a.cs_out.st + ch[i]] = io_traits<IO>::from_f(win[i][k]);
+    }
+  }
+}
+
+template <typename IO, int P, int N>
+hipError_t launch_decode_pn(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H));
+  switch (a.pr.K) {
+    case 0: hipLaunchKernelGGL((decode_kernel<IO, P, N, 0>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<IO, P, N, 2>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<IO, P, N, 3>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<IO, P, N, 4>), grid, dim3(kDecThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_decode_io(const DecodeArgs& a, hipStream_t s) {
+#define SSD_DEC(PP, NN) \
+  if (a.pr.P == PP && a.pr.N == NN) return launch_decode_pn<IO, PP, NN>(a, s);
+  SSD_DEC(64, 128)
+  SSD_DEC(64, 64)
+  SSD_DEC(64, 32)
+  SSD_DEC(64, 16)
+  SSD_DEC(32, 128)
+  SSD_DEC(32, 64)
+  SSD_DEC(32, 32)
+  SSD_DEC(32, 16)
+#undef SSD_DEC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Problem& pr, float* h_out, MView out, MView cs_out, hipStream_t s) {
+  DecodeArgs a{pr, h_out, out, cs_out};
+  TimingScope ts(kKDecode, s);
+  return pr.bf16 ? launch_decode_io<bf16_t>(a, s) : launch_decode_io<float>(a, s);
+}
+
+}  // namespace ssd

@@ -18,7 +18,7 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 enum KernelKind {
   kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
   kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKScanGroups, kKXbcPrepass,
-  kKLinear, kKernelKinds
+  kKLinear, kKDecode, kKernelKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events on stream `s`
@@ -178,5 +178,10 @@ struct LinearProblem {
   int64_t ldy;
 };
 hipError_t launch_linear(const LinearProblem& lp, hipStream_t s);
+
+// ---------------------------------------------------------------- streaming decode
+// pr.L tokens stepped one at a time from (pr.h0, pr.cs_in); state out to h_out (may
+// equal pr.h0), conv state out to cs_out (distinct from pr.cs_in), outputs to out.
+hipError_t launch_decode(const Problem& pr, float* h_out, MView out, MView cs_out, hipStream_t s);
 
 }  // namespace ssd
