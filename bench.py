@@ -187,6 +187,16 @@ def main():
         torch.cuda.synchronize()
         for _ in range(2):
             step()
+        # the mixer projections at the d_model 1024 shapes (in_proj and out_proj, L = 8192)
+        c1 = synth.CONFIGS["c1"]
+        u = torch.randn(c1.L, c1.d_model, device=dev).to(torch.bfloat16)
+        w_in = (0.02 * torch.randn(c1.d_in_proj, c1.d_model, device=dev)).to(torch.bfloat16)
+        zxp = torch.empty(c1.L, c1.d_in_proj, dtype=torch.bfloat16, device=dev)
+        w_out = (0.02 * torch.randn(c1.d_model, c1.hp, device=dev)).to(torch.bfloat16)
+        fin = torch.empty(c1.L, c1.d_model, dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            bd.mixer_proj(u, w_in, zxp)
+            bd.mixer_proj(zxp[:, :c1.hp], w_out, fin)
         torch.cuda.synchronize()
         print("pmc probe done", flush=True)
         return

@@ -231,3 +231,64 @@ def mixer_full_fwd(u, w_in, conv_w, conv_b, A, H, P, G, N, w_out, dt_bias=None, 
     final = linear(out, w_out, norm_out, eps, u if residual else None)
     return dict(final=final, zxbcdt=zx, out=out, h_final=r["h_final"],
                 conv_state_out=r["conv_state_out"])
+
+
+def rmsnorm_bwd(x, g, eps, dy):
+    """Gradients of y = rmsnorm(x, g, eps) over the last axis: returns (dx, dg), dg summed
+    over every leading axis.  With r = (mean(x^2) + eps)^(-1/2): y_j = g_j x_j r and
+    dr/dx_k = -r^3 x_k / K, so dx_k = r g_k dy_k - (r^3 x_k / K) sum_j g_j dy_j x_j."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    K = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    s = np.sum(g * dy * x, axis=-1, keepdims=True)
+    dx = r * g * dy - x * (r ** 3) * s / K
+    dg = np.sum((dy * x * r).reshape(-1, K), axis=0)
+    return dx, dg
+
+
+def block_bwd(u, w_in, conv_w, conv_b, A, H, P, G, N, w_out, dfinal, dt_bias=None, D=None,
+              norm_in=None, norm_out=None, eps=1e-5, residual=True, h0=None, conv_state=None,
+              dh_final=None, dconv_state_out=None):
+    """Backward of mixer_full_fwd (the full block when norm_in, norm_out and residual are
+    set) given dfinal = dLoss/dfinal.  Returns dict with du, dw_in, dw_out, dnorm_in,
+    dnorm_out and the hot-path gradients (dconv_w, dconv_b, dA, dD, ddt_bias, dh0,
+    dconv_state)."""
+    u = np.asarray(u, dtype=np.float64)
+    dF = np.asarray(dfinal, dtype=np.float64)
+    w_in = np.asarray(w_in, dtype=np.float64)
+    w_out = np.asarray(w_out, dtype=np.float64)
+    Bsz, L, dm = u.shape
+    hp, cd = H * P, H * P + 2 * G * N
+    un = rmsnorm(u, norm_in, eps) if norm_in is not None else u
+    zx = un @ w_in.T
+    z, xbc, dt = zx[..., :hp], zx[..., hp:hp + cd], zx[..., hp + cd:hp + cd + H]
+    f = mixer_fwd(xbc, conv_w, conv_b, dt, A, H, P, G, N, dt_bias=dt_bias, D=D,
+                  z=z.reshape(Bsz, L, H, P), h0=h0, conv_state=conv_state)
+    out = f["out"].reshape(Bsz, L, hp)
+    on = rmsnorm(out, norm_out, eps) if norm_out is not None else out
+    # out_proj
+    d_on = dF @ w_out
+    dw_out = dF.reshape(-1, dm).T @ on.reshape(-1, hp)
+    if norm_out is not None:
+        d_out, dnorm_out = rmsnorm_bwd(out, norm_out, eps, d_on)
+    else:
+        d_out, dnorm_out = d_on, None
+    # hot path
+    r = mixer_bwd(xbc, conv_w, conv_b, dt, A, H, P, G, N, d_out.reshape(Bsz, L, H, P),
+                  dt_bias=dt_bias, D=D, z=z.reshape(Bsz, L, H, P), h0=h0, conv_state=conv_state,
+                  dh_final=dh_final, dconv_state_out=dconv_state_out)
+    dzx = np.concatenate([r["dz"].reshape(Bsz, L, hp), r["dxbc_raw"], r["ddt"]], axis=-1)
+    # in_proj
+    d_un = dzx @ w_in
+    dw_in = dzx.reshape(-1, zx.shape[-1]).T @ un.reshape(-1, dm)
+    if norm_in is not None:
+        du, dnorm_in = rmsnorm_bwd(u, norm_in, eps, d_un)
+    else:
+        du, dnorm_in = d_un, None
+    if residual:
+        du = du + dF
+    return dict(du=du, dw_in=dw_in, dw_out=dw_out, dnorm_in=dnorm_in, dnorm_out=dnorm_out,
+                dconv_w=r["dconv_w"], dconv_b=r["dconv_b"], dA=r["dA"], dD=r["dD"],
+                ddt_bias=r["ddt_bias"], dh0=r["dh0"], dconv_state=r["dconv_state"], dzx=dzx)

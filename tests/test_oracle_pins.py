@@ -481,3 +481,61 @@ def test_mixer_full_in_proj_selects_and_skip_is_exact():
                              np.zeros((5, hp)), dt_bias=dtb, D=D, norm_in=np.ones(5),
                              norm_out=np.ones(hp), residual=True)
     assert np.array_equal(blk["final"], u[..., :5])
+
+
+def test_rmsnorm_bwd_matches_finite_differences():
+    r = np.random.default_rng(63)
+    x = r.standard_normal((3, 4, 9))
+    g = r.uniform(0.5, 1.5, 9)
+    dy = r.standard_normal((3, 4, 9))
+    eps = 1e-3
+    dx, dg = orc.rmsnorm_bwd(x, g, eps, dy)
+    loss = lambda xx, gg: float(np.sum(orc.rmsnorm(xx, gg, eps) * dy))
+    for _ in range(3):
+        vx, vg = r.standard_normal(x.shape), r.standard_normal(g.shape)
+        e = 1e-6
+        fdx = (loss(x + e * vx, g) - loss(x - e * vx, g)) / (2 * e)
+        fdg = (loss(x, g + e * vg) - loss(x, g - e * vg)) / (2 * e)
+        assert abs(fdx - np.sum(dx * vx)) <= 1e-7 * max(1.0, abs(fdx))
+        assert abs(fdg - np.sum(dg * vg)) <= 1e-7 * max(1.0, abs(fdg))
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_block_bwd_matches_finite_differences(full):
+    """The full block (pre-norm, in_proj, hot path, gated norm, out_proj, residual) and
+    the bare mixer: every input, weight, norm gain and carried-state gradient."""
+    r = np.random.default_rng(64 + int(full))
+    H, P, G, N, K, dm, L = 2, 2, 1, 3, 4, 5, 13
+    hp, cd = H * P, H * P + 2 * G * N
+    dip = hp + cd + H
+    d = dict(u=r.standard_normal((1, L, dm)), w_in=0.4 * r.standard_normal((dip, dm)),
+             conv_w=r.uniform(-0.5, 0.5, (cd, K)), conv_b=r.uniform(-0.5, 0.5, cd),
+             A=-np.exp(r.uniform(0, 1.5, H)), w_out=0.4 * r.standard_normal((dm, hp)),
+             dt_bias=r.uniform(-2, 0, H), D=r.standard_normal(H), h0=r.standard_normal((1, H, P, N)),
+             conv_state=r.standard_normal((1, K - 1, cd)))
+    if full:
+        d["norm_in"] = r.uniform(0.5, 1.5, dm)
+        d["norm_out"] = r.uniform(0.5, 1.5, hp)
+    w = dict(f=r.standard_normal((1, L, dm)), h=r.standard_normal((1, H, P, N)),
+             cs=r.standard_normal((1, K - 1, cd)))
+    kw = dict(H=H, P=P, G=G, N=N, eps=1e-3, residual=full)
+
+    def loss(e):
+        m = orc.mixer_full_fwd(**e, **kw)
+        return float(np.sum(m["final"] * w["f"]) + np.sum(m["h_final"] * w["h"]) +
+                     np.sum(m["conv_state_out"] * w["cs"]))
+
+    g = orc.block_bwd(**d, **kw, dfinal=w["f"], dh_final=w["h"], dconv_state_out=w["cs"])
+    names = dict(u="du", w_in="dw_in", w_out="dw_out", conv_w="dconv_w", conv_b="dconv_b", A="dA",
+                 dt_bias="ddt_bias", D="dD", h0="dh0", conv_state="dconv_state")
+    if full:
+        names.update(norm_in="dnorm_in", norm_out="dnorm_out")
+    for key, gname in names.items():
+        for _ in range(2):
+            v = r.standard_normal(np.shape(d[key]))
+            eps = 1e-6
+            dp = dict(d); dp[key] = d[key] + eps * v
+            dmn = dict(d); dmn[key] = d[key] - eps * v
+            fd = (loss(dp) - loss(dmn)) / (2 * eps)
+            an = float(np.sum(g[gname] * v))
+            assert abs(fd - an) <= 2e-7 * max(1.0, abs(an)), (key, fd, an)
