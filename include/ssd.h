@@ -269,6 +269,40 @@ ssd_status mixer_proj(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void*
                       const void* residual, int64_t ldr, void* y, int64_t ldy, void* stream);
 
 /*
+ * mixer_proj_bwd -- backward of y = x w^T (mixer_proj without its options):
+ *     dx[m][k]  = sum_n dy[m][n] w[n][k]            (bf16; skipped when dx == NULL)
+ *     dw[n][k] (+)= sum_m dy[m][n] x[m][k]          (fp32; added to when accumulate = 1;
+ *                                                   skipped when dw == NULL)
+ * dy [M][lddy], x [M][ldx], w [N][ldw], dx [M][lddx] bf16; dw [N][lddw] fp32.  The
+ * norm and residual of a fused forward are differentiated by rmsnorm_bwd and by adding
+ * dy itself, by the caller.  Supported: io = SSD_BF16, N and K multiples of 8, any M;
+ * bf16 base pointers 16-byte aligned with leading dimensions that are multiples of 8.
+ * MFMA products with both operands staged in LDS (transposed ones read with the gfx950
+ * LDS transpose loads); deterministic.
+ */
+ssd_status mixer_proj_bwd(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void* dy, int64_t lddy,
+                          const void* x, int64_t ldx, const void* w, int64_t ldw, void* dx, int64_t lddx,
+                          float* dw, int64_t lddw, int accumulate, void* stream);
+
+/*
+ * rmsnorm_fwd / rmsnorm_bwd -- the block's RMSNorm over rows of K bf16 entries (the
+ * norm before in_proj, and the gated norm before out_proj applied to ssd_fwd's gated
+ * output; Mamba-2 block of the arXiv index page's "Builds on" list):
+ *     r[m] = (mean_k x[m][k]^2 + eps)^(-1/2),   y[m][k] = x[m][k] r[m] g[k]
+ *     dx[m][k] = r g[k] dy[m][k] - x[m][k] r^3 / K sum_j g[j] dy[m][j] x[m][j]  (+ dres[m][k])
+ *     dg[k] (+)= sum_m dy[m][k] x[m][k] r[m]       (ordered sum: deterministic)
+ * x, y, dy, dres, dx bf16 [M][ld] (dx may equal dy or dres); g, dg fp32 [K], 16-byte
+ * aligned; rstd fp32 [M] or NULL.  K a multiple of 8, at most 5120.  rmsnorm_bwd needs
+ * rmsnorm_bwd_workspace(K) bytes of scratch (partial sums of dg).
+ */
+ssd_status rmsnorm_fwd(int64_t M, int64_t K, ssd_dtype io, const void* x, int64_t ldx, const float* g,
+                       float eps, void* y, int64_t ldy, float* rstd, void* stream);
+ssd_status rmsnorm_bwd_workspace(int64_t K, size_t* bytes);
+ssd_status rmsnorm_bwd(int64_t M, int64_t K, ssd_dtype io, const void* x, int64_t ldx, const float* g,
+                       float eps, const void* dy, int64_t lddy, const void* dres, int64_t ldres, void* dx,
+                       int64_t lddx, float* dg, int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Timing instrumentation (off by default).  While enabled, every kernel the
  * library enqueues is bracketed by HIP events on the caller's stream.
  *   ssd_timing_enable(1) clears the totals and starts recording; (0) stops.

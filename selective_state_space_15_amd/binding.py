@@ -63,6 +63,11 @@ _SIGS = {
     "ssd_decode": ([_D, _I, _V, _F, _F, _V, _V, _V, _F, _I, _F, _F, _V, _F, _F, _V, _P], _I),
     "mixer_proj": ([_I64, _I64, _I64, _I, _P, _I64, _P, _I64, _F, ctypes.c_float, _P, _I64, _P, _I64,
                     _P], _I),
+    "mixer_proj_bwd": ([_I64, _I64, _I64, _I, _P, _I64, _P, _I64, _P, _I64, _P, _I64, _F, _I64, _I, _P], _I),
+    "rmsnorm_fwd": ([_I64, _I64, _I, _P, _I64, _F, ctypes.c_float, _P, _I64, _F, _P], _I),
+    "rmsnorm_bwd_workspace": ([_I64, ctypes.POINTER(_SZ)], _I),
+    "rmsnorm_bwd": ([_I64, _I64, _I, _P, _I64, _F, ctypes.c_float, _P, _I64, _P, _I64, _P, _I64, _F, _I, _P,
+                     _SZ, _P], _I),
     "ssd_timing_enable": ([_I], _I),
     "ssd_timing_read": ([_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)], _I),
     "ssd_timing_name": ([_I], ctypes.c_char_p),
@@ -412,6 +417,60 @@ def mixer_proj(x, w, y, *, norm_w=None, norm_eps=1e-5, residual=None, stream=Non
     st = lib().mixer_proj(M, N, K, SSD_BF16, xp, ldx, wp, ldw, fptr(norm_w), float(norm_eps), rp, ldr,
                           yp, ldy, stream_ptr(stream))
     _check(st, "mixer_proj")
+
+
+def mixer_proj_bwd(dy, *, x=None, w=None, dx=None, dw=None, accumulate=False, stream=None):
+    """dx = dy w (bf16) and/or dw (+)= dy^T x (fp32) for y = x w^T: dy [M, N], x [M, K],
+    w [N, K], dx [M, K] bf16 2-D views; dw [N, K] fp32 contiguous."""
+    M, N = dy.shape
+    K = (w.shape[1] if w is not None else x.shape[1])
+    dyp, lddy = _mat(dy, "dy", M, N)
+    xp, ldx = _mat(x, "x", M, K) if x is not None else (None, 0)
+    wp, ldw = _mat(w, "w", N, K) if w is not None else (None, 0)
+    dxp, lddx = _mat(dx, "dx", M, K) if dx is not None else (None, 0)
+    if dx is not None and w is None:
+        raise ValueError("dx needs w")
+    if dw is not None and x is None:
+        raise ValueError("dw needs x")
+    _f32(dw, "dw", (N, K))
+    _same_device([dy, x, w, dx, dw], "mixer_proj_bwd")
+    st = lib().mixer_proj_bwd(M, N, K, SSD_BF16, dyp, lddy, xp, ldx, wp, ldw, dxp, lddx, fptr(dw), K,
+                              int(bool(accumulate)), stream_ptr(stream))
+    _check(st, "mixer_proj_bwd")
+
+
+def rmsnorm_fwd(x, g, y, *, eps=1e-5, rstd=None, stream=None):
+    """y = RMSNorm(x) * g over the last dim of 2-D bf16 views x, y [M, K]; g [K] fp32."""
+    M, K = x.shape
+    xp, ldx = _mat(x, "x", M, K)
+    yp, ldy = _mat(y, "y", M, K)
+    _f32(g, "g", (K,), required=True)
+    _f32(rstd, "rstd", (M,))
+    _same_device([x, g, y, rstd], "rmsnorm_fwd")
+    _check(lib().rmsnorm_fwd(M, K, SSD_BF16, xp, ldx, fptr(g), float(eps), yp, ldy, fptr(rstd),
+                             stream_ptr(stream)), "rmsnorm_fwd")
+
+
+def rmsnorm_bwd_workspace(K) -> int:
+    n = _SZ(0)
+    _check(lib().rmsnorm_bwd_workspace(K, ctypes.byref(n)), "rmsnorm_bwd_workspace")
+    return n.value
+
+
+def rmsnorm_bwd(x, g, dy, dx, *, eps=1e-5, dres=None, dg=None, accumulate=False, ws=None, stream=None):
+    """dx = d RMSNorm(x)*g / dx . dy (+ dres); dg (+)= gradient of g.  2-D bf16 views."""
+    M, K = x.shape
+    xp, ldx = _mat(x, "x", M, K)
+    dyp, lddy = _mat(dy, "dy", M, K)
+    dxp, lddx = _mat(dx, "dx", M, K)
+    rp, ldr = _mat(dres, "dres", M, K) if dres is not None else (None, 0)
+    _f32(g, "g", (K,), required=True)
+    _f32(dg, "dg", (K,))
+    _same_device([x, g, dy, dx, dres, dg, ws], "rmsnorm_bwd")
+    _ws_ok(ws, rmsnorm_bwd_workspace(K), "rmsnorm_bwd")
+    wsp, wsn = _ws(ws)
+    _check(lib().rmsnorm_bwd(M, K, SSD_BF16, xp, ldx, fptr(g), float(eps), dyp, lddy, rp, ldr, dxp, lddx,
+                             fptr(dg), int(bool(accumulate)), wsp, wsn, stream_ptr(stream)), "rmsnorm_bwd")
 
 
 # ------------------------------------------------------------------ timing instrumentation

@@ -532,4 +532,95 @@ ssd_status ssd_decode(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float
   return SSD_OK;
 }
 
+namespace {
+ssd_status check_mat(const void* p, int64_t ld, int64_t cols, const char* name) {
+  if (!p) return fail(SSD_ERR_NULL, "%s: NULL", name);
+  if (ld < cols) return fail(SSD_ERR_SHAPE, "%s: leading dimension %lld below its row length %lld", name,
+                             (long long)ld, (long long)cols);
+  if (!aligned16(p) || ld % 8)
+    return fail(SSD_ERR_ALIGN, "%s: base 16-byte aligned and leading dimension a multiple of 8 required", name);
+  return SSD_OK;
+}
+}  // namespace
+
+ssd_status mixer_proj_bwd(int64_t M, int64_t N, int64_t K, ssd_dtype io, const void* dy, int64_t lddy,
+                          const void* x, int64_t ldx, const void* w, int64_t ldw, void* dx, int64_t lddx,
+                          float* dw, int64_t lddw, int accumulate, void* stream) {
+  g_last_error.clear();
+  if (io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "mixer_proj_bwd: bf16 I/O only");
+  if (M < 1 || N < 1 || K < 1 || M > (int64_t(1) << 40) || N > (1 << 24) || K > (1 << 24))
+    return fail(SSD_ERR_SHAPE, "mixer_proj_bwd: dims out of range (M=%lld N=%lld K=%lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (N % 8 || K % 8)
+    return fail(SSD_ERR_UNSUPPORTED, "mixer_proj_bwd: N=%lld and K=%lld must be multiples of 8", (long long)N,
+                (long long)K);
+  if (!dx && !dw) return fail(SSD_ERR_NULL, "mixer_proj_bwd: neither dx nor dw requested");
+  TRY(check_mat(dy, lddy, N, "dy"));
+  if (dx) {
+    TRY(check_mat(w, ldw, K, "w"));
+    TRY(check_mat(dx, lddx, K, "dx"));
+  }
+  if (dw) {
+    TRY(check_mat(x, ldx, K, "x"));
+    if (lddw < K) return fail(SSD_ERR_SHAPE, "dw: leading dimension below K");
+    if (reinterpret_cast<uintptr_t>(dw) % 4) return fail(SSD_ERR_ALIGN, "dw: not 4-byte aligned");
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (dx) e = ssd::launch_linear_dgrad(M, N, K, dy, lddy, w, ldw, dx, lddx, s);
+  if (e == hipSuccess && dw) e = ssd::launch_linear_wgrad(M, N, K, dy, lddy, x, ldx, dw, lddw, accumulate, s);
+  if (e != hipSuccess) return hip_fail(e, "mixer_proj_bwd launch");
+  return SSD_OK;
+}
+
+ssd_status rmsnorm_fwd(int64_t M, int64_t K, ssd_dtype io, const void* x, int64_t ldx, const float* g,
+                       float eps, void* y, int64_t ldy, float* rstd, void* stream) {
+  g_last_error.clear();
+  if (io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "rmsnorm_fwd: bf16 I/O only");
+  if (M < 1 || K < 8 || M > (int64_t(1) << 40)) return fail(SSD_ERR_SHAPE, "rmsnorm_fwd: dims out of range");
+  if (K % 8 || K > ssd::rmsnorm_max_k())
+    return fail(SSD_ERR_UNSUPPORTED, "rmsnorm_fwd: K=%lld (multiples of 8 up to %d)", (long long)K,
+                ssd::rmsnorm_max_k());
+  TRY(check_mat(x, ldx, K, "x"));
+  TRY(check_mat(y, ldy, K, "y"));
+  if (!g || !aligned16(g)) return fail(SSD_ERR_ALIGN, "rmsnorm_fwd: g NULL or not 16-byte aligned");
+  if (!(eps >= 0.f)) return fail(SSD_ERR_SHAPE, "rmsnorm_fwd: eps must be >= 0");
+  const hipError_t e = ssd::launch_rmsnorm_fwd(M, static_cast<int>(K), x, ldx, g, eps, y, ldy, rstd,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm_fwd launch");
+  return SSD_OK;
+}
+
+ssd_status rmsnorm_bwd_workspace(int64_t K, size_t* bytes) {
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes: NULL");
+  if (K < 8 || K % 8 || K > ssd::rmsnorm_max_k())
+    return fail(SSD_ERR_UNSUPPORTED, "rmsnorm_bwd: K=%lld (multiples of 8 up to %d)", (long long)K,
+                ssd::rmsnorm_max_k());
+  *bytes = ssd::rmsnorm_bwd_workspace_bytes(K);
+  return SSD_OK;
+}
+
+ssd_status rmsnorm_bwd(int64_t M, int64_t K, ssd_dtype io, const void* x, int64_t ldx, const float* g,
+                       float eps, const void* dy, int64_t lddy, const void* dres, int64_t ldres, void* dx,
+                       int64_t lddx, float* dg, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (io != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "rmsnorm_bwd: bf16 I/O only");
+  if (M < 1 || M > (int64_t(1) << 40)) return fail(SSD_ERR_SHAPE, "rmsnorm_bwd: dims out of range");
+  size_t need = 0;
+  TRY(rmsnorm_bwd_workspace(K, &need));
+  TRY(check_mat(x, ldx, K, "x"));
+  TRY(check_mat(dy, lddy, K, "dy"));
+  TRY(check_mat(dx, lddx, K, "dx"));
+  if (dres) TRY(check_mat(dres, ldres, K, "dres"));
+  if (!g || !aligned16(g)) return fail(SSD_ERR_ALIGN, "rmsnorm_bwd: g NULL or not 16-byte aligned");
+  if (dg && !aligned16(dg)) return fail(SSD_ERR_ALIGN, "rmsnorm_bwd: dg not 16-byte aligned");
+  if (!(eps >= 0.f)) return fail(SSD_ERR_SHAPE, "rmsnorm_bwd: eps must be >= 0");
+  if (!ws || ws_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "rmsnorm_bwd: workspace %zu bytes < %zu needed", ws_bytes, need);
+  const hipError_t e = ssd::launch_rmsnorm_bwd(M, static_cast<int>(K), x, ldx, g, eps, dy, lddy, dres, ldres,
+                                               dx, lddx, dg, accumulate, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm_bwd launch");
+  return SSD_OK;
+}
+
 }  // extern "C"

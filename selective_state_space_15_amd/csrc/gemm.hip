@@ -45,18 +45,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #endif
 
 struct LinArgs {
-  const uint16_t* x;
+  const uint16_t* x;  // A operand: [M][ldx] (K contiguous) or, transposed, [K][ldx]
   int64_t ldx;
-  const uint16_t* w;
+  const uint16_t* w;  // B operand: [N][ldw] (K contiguous) or, transposed, [K][ldw]
   int64_t ldw;
   const float* g;  // RMSNorm gain [K] (NORM)
   float eps;
   const uint16_t* r;  // residual [M][ldr] (RES)
   int64_t ldr;
-  uint16_t* y;
+  void* y;            // [M][ldy]: bf16, or fp32 (OF32)
   int64_t ldy;
-  int64_t M;
-  int N, K;
+  int64_t M, K;
+  int N;
+  int accumulate;     // OF32: y += product
   int tiles_n;
   int64_t tiles;
 };
@@ -69,8 +70,81 @@ __device__ __forceinline__ float sum8(float v) {
   return v;
 }
 
-// RMSNorm bookkeeping of one K-tile: the rows' squares (unscaled) go into ss, and the
-// x pieces become x * g[k] rounded to the bf16 operand.
+// LDS tile of one operand for one K-tile of 64: K-contiguous operands are staged as
+// [rows][64 + 8], transposed ones (stored [K][rows] in memory) as [64][rows + 8]; the
+// MFMA fragments of the latter are read with the gfx950 LDS transpose loads.
+template <int ROWS, bool TR>
+struct OpTile {
+  static constexpr int ld = TR ? ROWS + 8 : kLd;
+  static constexpr int elems = TR ? kBK * ld : ROWS * kLd;
+  static constexpr int pieces = ROWS * kBK / 8 / kLinThreads;  // 16-byte pieces per thread
+  // piece i of thread t: (row, k) of the tile it covers
+  __device__ static __forceinline__ int row(int t, int i) {
+    return TR ? 8 * ((t + kLinThreads * i) % (ROWS / 8)) : (t + kLinThreads * i) / 8;
+  }
+  __device__ static __forceinline__ int kk(int t, int i) {
+    return TR ? (t + kLinThreads * i) / (ROWS / 8) : 8 * ((t + kLinThreads * i) % 8);
+  }
+  __device__ static __forceinline__ int lds_off(int t, int i) {
+    return TR ? kk(t, i) * ld + row(t, i) : row(t, i) * kLd + kk(t, i);
+  }
+};
+
+// One K-tile's pieces of an operand into registers.  rows: the block's first row r0
+// and the operand's row count R (rows past it are clamped: their products land in
+// masked outputs); K-tile k0 of K (reduction entries past K read as zero).
+template <int ROWS, bool TR, bool RAG, int NP>
+__device__ __forceinline__ void load_op(u32x4 (&v)[NP], uint32_t& keep, const uint16_t* base,
+                                        int64_t ld, int64_t r0, int64_t R, int64_t k0, int64_t K) {
+  using OT = OpTile<ROWS, TR>;
+  const int t = threadIdx.x;
+  keep = 0;
+  if constexpr (TR) {
+    const uint16_t* tb = base + k0 * ld + r0;  // uniform
+#pragma unroll
+    for (int i = 0; i < OT::pieces; ++i) {
+      const int64_t rr = r0 + OT::row(t, i);
+      const int cr = static_cast<int>((rr + 8 <= R ? rr : R - 8) - r0);
+      const int kr = OT::kk(t, i);
+      const bool kin = !RAG || k0 + kr < K;
+      const int kc = kin ? kr : static_cast<int>(K - 1 - k0);
+      v[i] = *reinterpret_cast<const u32x4*>(
+          byte_off(tb, static_cast<uint32_t>((static_cast<int64_t>(kc) * ld + cr) * 2)));
+      keep |= (kin ? 1u : 0u) << i;
+    }
+  } else {
+    const uint16_t* tb = base + r0 * ld + k0;  // uniform
+#pragma unroll
+    for (int i = 0; i < OT::pieces; ++i) {
+      const int64_t rr = r0 + OT::row(t, i);
+      const int cr = static_cast<int>((rr < R ? rr : R - 1) - r0);
+      // a ragged K (a multiple of 8) ends inside the last tile: pieces past it read the
+      // last valid piece and are zeroed
+      const int kr = OT::kk(t, i);
+      const bool kin = !RAG || k0 + kr < K;
+      const int kc = kin ? kr : static_cast<int>(K - 8 - k0);
+      v[i] = *reinterpret_cast<const u32x4*>(
+          byte_off(tb, static_cast<uint32_t>((static_cast<int64_t>(cr) * ld + kc) * 2)));
+      keep |= (kin ? 1u : 0u) << i;
+    }
+  }
+}
+
+// The pieces into the LDS tile; pieces past K (clear bits of keep) become zeros here,
+// where the values are consumed, not right after their loads.
+template <int ROWS, bool TR, bool RAG, int NP>
+__device__ __forceinline__ void store_op(const u32x4 (&v)[NP], uint32_t keep, uint16_t* s) {
+  using OT = OpTile<ROWS, TR>;
+#pragma unroll
+  for (int i = 0; i < OT::pieces; ++i) {
+    const bool k = !RAG || ((keep >> i) & 1u);
+    *reinterpret_cast<u32x4*>(s + OT::lds_off(threadIdx.x, i)) =
+        u32x4{k ? v[i].x : 0u, k ? v[i].y : 0u, k ? v[i].z : 0u, k ? v[i].w : 0u};
+  }
+}
+
+// RMSNorm bookkeeping of one K-tile (K-contiguous x only): the rows' squares
+// (unscaled) go into ss, and the x pieces become x * g[k] rounded to the bf16 operand.
 template <int AV>
 __device__ __forceinline__ void norm_pieces(u32x4 (&ra)[AV], float (&ss)[AV], const float* gp) {
   const float4 g0 = *reinterpret_cast<const float4*>(gp);
@@ -90,41 +164,19 @@ __device__ __forceinline__ void norm_pieces(u32x4 (&ra)[AV], float (&ss)[AV], co
   }
 }
 
-// One K-tile's 16-byte row pieces of x and w into registers (tile kt; the pieces'
-// offsets are relative to the block's first rows).
-template <int AV, int BV>
-__device__ __forceinline__ void load_tile(u32x4 (&ra)[AV], u32x4 (&rb)[BV], const uint16_t* xb,
-                                          const uint32_t (&xo)[AV], const uint16_t* wb,
-                                          const uint32_t (&wo)[BV], int kt) {
-  const uint32_t kb = static_cast<uint32_t>(kt * kBK * 2);
-#pragma unroll
-  for (int i = 0; i < AV; ++i) ra[i] = *reinterpret_cast<const u32x4*>(byte_off(xb, xo[i] + kb));
-#pragma unroll
-  for (int i = 0; i < BV; ++i) rb[i] = *reinterpret_cast<const u32x4*>(byte_off(wb, wo[i] + kb));
-}
-
-// The pieces into the LDS tiles: piece i of this thread at row lrow + 32 i.
-template <int AV, int BV>
-__device__ __forceinline__ void store_tile(const u32x4 (&ra)[AV], const u32x4 (&rb)[BV], uint16_t* sA,
-                                           uint16_t* sB, int off) {
-  constexpr int kStep = (kLinThreads / 8) * kLd;
-#pragma unroll
-  for (int i = 0; i < AV; ++i) *reinterpret_cast<u32x4*>(sA + off + kStep * i) = ra[i];
-#pragma unroll
-  for (int i = 0; i < BV; ++i) *reinterpret_cast<u32x4*>(sB + off + kStep * i) = rb[i];
-}
-
 // The MFMAs of one staged K-tile: the wave's TM x TN tiles of 16 x 16 at (wm, wn).
-template <int TM, int TN>
+template <int TM, int TN, int BM, int BN, bool TA, bool TB>
 __device__ __forceinline__ void mma_tile(f32x4 (&acc)[TM][TN], const uint16_t* sA, const uint16_t* sB,
                                          int wm, int wn, int r, int kg) {
 #pragma unroll
   for (int kk = 0; kk < kBK; kk += 32) {
     bf16x8 af[TM], bfr[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = frag<uint16_t, true>::get(sA, kLd, wm + 16 * i + r, kk + 8 * kg);
+    for (int i = 0; i < TM; ++i)
+      af[i] = frag<uint16_t, !TA>::get(sA, OpTile<BM, TA>::ld, wm + 16 * i + r, kk + 8 * kg);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = frag<uint16_t, true>::get(sB, kLd, wn + 16 * j + r, kk + 8 * kg);
+    for (int j = 0; j < TN; ++j)
+      bfr[j] = frag<uint16_t, !TB>::get(sB, OpTile<BN, TB>::ld, wn + 16 * j + r, kk + 8 * kg);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -132,47 +184,29 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[TM][TN], const uint16_t* s
   }
 }
 
-template <int BM, int BN, bool NORM, bool RES>
+template <int BM, int BN, bool TA, bool TB, bool NORM, bool RES, bool OF32, bool RAG>
 __global__ void __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(SSD_LINEAR_WAVES, SSD_LINEAR_WAVES)))
 linear_kernel(LinArgs a) {
+  static_assert(!(NORM && TA), "the norm prologue needs K-contiguous rows");
+  static_assert(!(NORM && RAG), "the norm prologue needs whole K-tiles");
   constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-block
   constexpr int TM = WM / 16, TN = WN / 16;  // MFMA tiles per wave
-  constexpr int AV = BM * 8 / kLinThreads;   // 16-byte A pieces per thread per K-tile
-  constexpr int BV = BN * 8 / kLinThreads;
-  constexpr int kRowsPerPass = kLinThreads / 8;  // rows one pass of the block covers
+  using OA = OpTile<BM, TA>;
+  using OB = OpTile<BN, TB>;
+  constexpr int AV = OA::pieces, BV = OB::pieces;
   // operand tiles during the K loop; the bf16 output block afterwards
-  constexpr int kOpElems = (BM + BN) * kLd;
-  constexpr int kOutElems = BM * (BN + 8);
+  constexpr int kOpElems = OA::elems + OB::elems;
+  constexpr int kOutElems = OF32 ? 8 : BM * (BN + 8);
   __shared__ __align__(16) uint16_t smem[kOpElems > kOutElems ? kOpElems : kOutElems];
-  __shared__ float s_rstd[BM];
+  __shared__ float s_rstd[NORM ? BM : 1];
   uint16_t* sA = smem;
-  uint16_t* sB = smem + BM * kLd;
+  uint16_t* sB = smem + OA::elems;
 
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t lid = xcd_remap(blockIdx.x, a.tiles);
   const int64_t m0 = (lid / a.tiles_n) * BM;
-  const int n0 = static_cast<int>(lid % a.tiles_n) * BN;
+  const int64_t n0 = static_cast<int64_t>(lid % a.tiles_n) * BN;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
-
-  // loader: piece (row = tid / 8 + 32 i, k = 8 (tid % 8)) of each tile, addressed as
-  // the block's first row (uniform) plus a 32-bit byte offset per piece; rows past M
-  // or N are clamped to the last one
-  const int lrow = tid >> 3, lk = 8 * (tid & 7);
-  const uint16_t* xb = a.x + m0 * a.ldx;
-  const uint16_t* wb = a.w + static_cast<int64_t>(n0) * a.ldw;
-  uint32_t xo[AV], wo[BV];
-#pragma unroll
-  for (int i = 0; i < AV; ++i) {
-    int64_t m = m0 + lrow + kRowsPerPass * i;
-    m = (m < a.M ? m : a.M - 1) - m0;
-    xo[i] = static_cast<uint32_t>((m * a.ldx + lk) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < BV; ++i) {
-    int n = n0 + lrow + kRowsPerPass * i;
-    n = (n < a.N ? n : a.N - 1) - n0;
-    wo[i] = static_cast<uint32_t>((static_cast<int64_t>(n) * a.ldw + lk) * 2);
-  }
 
   float ss[AV];
 #pragma unroll
@@ -184,87 +218,119 @@ linear_kernel(LinArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int lane = tid & 63, r = lane & 15, kg = lane >> 4;
-  const int nk = a.K / kBK;
+  const int64_t nk = (a.K + kBK - 1) / kBK;
 
-  // one K-tile: norm bookkeeping, stage to LDS, refill the registers with the tile two
-  // ahead (clamped to the last: no branch), then the MFMAs on the staged tile
-#define SSD_LINEAR_STEP(ra, rb, kt)                                                              \
+  // One K-tile: norm bookkeeping, stage to LDS, refill the registers with the tile two
+  // ahead (clamped to the last: no branch), then the MFMAs on the staged tile.
+#define SSD_LINEAR_STEP(ra, rb, ka, kb, kt)                                                      \
   do {                                                                                           \
-    if constexpr (NORM) norm_pieces<AV>(ra, ss, a.g + (kt) * kBK + lk);                         \
+    if constexpr (NORM) norm_pieces<AV>(ra, ss, a.g + (kt) * kBK + OA::kk(tid, 0));              \
     __syncthreads(); /* every wave is done reading the previous tile */                         \
-    store_tile<AV, BV>(ra, rb, sA, sB, lrow * kLd + lk);                                        \
+    store_op<BM, TA, RAG>(ra, ka, sA);                                                                \
+    store_op<BN, TB, RAG>(rb, kb, sB);                                                                \
     __syncthreads();                                                                             \
-    load_tile<AV, BV>(ra, rb, xb, xo, wb, wo, (kt) + 2 < nk ? (kt) + 2 : nk - 1);               \
-    mma_tile<TM, TN>(acc, sA, sB, wm, wn, r, kg);                                                \
+    const int64_t kn_ = (kt) + 2 < nk ? (kt) + 2 : nk - 1;                                      \
+    load_op<BM, TA, RAG>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                                \
+    load_op<BN, TB, RAG>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                                \
+    mma_tile<TM, TN, BM, BN, TA, TB>(acc, sA, sB, wm, wn, r, kg);                                \
   } while (0)
 
   // two tiles in flight: buffer 0 holds even tiles, buffer 1 odd ones
   u32x4 a0[AV], b0[BV], a1[AV], b1[BV];
-  load_tile<AV, BV>(a0, b0, xb, xo, wb, wo, 0);
-  load_tile<AV, BV>(a1, b1, xb, xo, wb, wo, nk > 1 ? 1 : 0);
-  int kt = 0;
+  uint32_t ka0, kb0, ka1, kb1;
+  load_op<BM, TA, RAG>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
+  load_op<BN, TB, RAG>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
+  load_op<BM, TA, RAG>(a1, ka1, a.x, a.ldx, m0, a.M, (nk > 1 ? 1 : 0) * kBK, a.K);
+  load_op<BN, TB, RAG>(b1, kb1, a.w, a.ldw, n0, a.N, (nk > 1 ? 1 : 0) * kBK, a.K);
+  int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    SSD_LINEAR_STEP(a0, b0, kt);
-    SSD_LINEAR_STEP(a1, b1, kt + 1);
+    SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt);
+    SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1);
   }
-  if (kt < nk) SSD_LINEAR_STEP(a0, b0, kt);
+  if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt);
 #undef SSD_LINEAR_STEP
 
   if constexpr (NORM) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const float t = sum8(ss[i]);
-      if ((tid & 7) == 0) s_rstd[lrow + kRowsPerPass * i] = rsqrtf(t / static_cast<float>(a.K) + a.eps);
+      if ((tid & 7) == 0) s_rstd[OA::row(tid, i)] = rsqrtf(t / static_cast<float>(a.K) + a.eps);
     }
   }
   __syncthreads();  // operand tiles dead; s_rstd complete
 
-  // stage the block as bf16 rows in LDS (after the norm scale and the residual, in
-  // fp32), then store 16-byte row pieces
-  constexpr int kOutLd = BN + 8;
-  uint16_t* sC = smem;
+  if constexpr (OF32) {
+    // fp32 result (weight gradients), optionally added to what y holds
+    float* y = static_cast<float*>(a.y);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = wm + 16 * i + 4 * kg + e;
-      const float sc = NORM ? s_rstd[row] : 1.f;
-      int64_t gm = m0 + row;
-      gm = gm < a.M ? gm : a.M - 1;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t gm = m0 + wm + 16 * i + 4 * kg + e;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = wn + 16 * j + r;
-        float v = acc[i][j][e] * sc;
-        if constexpr (RES) {
-          int gn = n0 + col;
-          gn = gn < a.N ? gn : a.N - 1;
-          v += bf2f(a.r[gm * a.ldr + gn]);
+        for (int j = 0; j < TN; ++j) {
+          const int64_t gn = n0 + wn + 16 * j + r;
+          if (gm < a.M && gn < a.N) {
+            float* p = y + gm * a.ldy + gn;
+            *p = a.accumulate ? *p + acc[i][j][e] : acc[i][j][e];
+          }
         }
-        sC[row * kOutLd + col] = f2bf(v);
+      }
+    return;
+  } else {
+    // stage the block as bf16 rows in LDS (after the norm scale and the residual, in
+    // fp32), then store 16-byte row pieces
+    constexpr int kOutLd = BN + 8;
+    uint16_t* sC = smem;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = wm + 16 * i + 4 * kg + e;
+        const float sc = NORM ? s_rstd[row] : 1.f;
+        int64_t gm = m0 + row;
+        gm = gm < a.M ? gm : a.M - 1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = wn + 16 * j + r;
+          float v = acc[i][j][e] * sc;
+          if constexpr (RES) {
+            int64_t gn = n0 + col;
+            gn = gn < a.N ? gn : a.N - 1;
+            v += bf2f(a.r[gm * a.ldr + gn]);
+          }
+          sC[row * kOutLd + col] = f2bf(v);
+        }
       }
     }
-  }
-  __syncthreads();
-  constexpr int kPieces = BM * BN / 8;
+    __syncthreads();
+    uint16_t* y = static_cast<uint16_t*>(a.y);
+    constexpr int kPieces = BM * BN / 8;
 #pragma unroll
-  for (int q = 0; q < kPieces / kLinThreads; ++q) {
-    const int p = tid + kLinThreads * q;
-    const int row = p / (BN / 8), c8 = 8 * (p % (BN / 8));
-    const int64_t gm = m0 + row;
-    const int gn = n0 + c8;
-    if (gm < a.M && gn < a.N)
-      *reinterpret_cast<u32x4*>(a.y + gm * a.ldy + gn) =
-          *reinterpret_cast<const u32x4*>(sC + row * kOutLd + c8);
+    for (int q = 0; q < kPieces / kLinThreads; ++q) {
+      const int p = tid + kLinThreads * q;
+      const int row = p / (BN / 8), c8 = 8 * (p % (BN / 8));
+      const int64_t gm = m0 + row;
+      const int64_t gn = n0 + c8;
+      if (gm < a.M && gn < a.N)
+        *reinterpret_cast<u32x4*>(y + gm * a.ldy + gn) = *reinterpret_cast<const u32x4*>(sC + row * kOutLd + c8);
+    }
   }
 }
 
-template <int BM, int BN, bool NORM, bool RES>
+template <bool TA, bool TB, bool NORM, bool RES, bool OF32>
 hipError_t launch_linear_t(const LinArgs& a0, hipStream_t s) {
+  constexpr int BM = SSD_LINEAR_BM, BN = SSD_LINEAR_BN;
   LinArgs a = a0;
-  a.tiles_n = (a.N + BN - 1) / BN;
+  a.tiles_n = static_cast<int>((a.N + BN - 1) / BN);
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
-  hipLaunchKernelGGL((linear_kernel<BM, BN, NORM, RES>), dim3(static_cast<unsigned>(a.tiles)),
-                     dim3(kLinThreads), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(a.tiles)), block(kLinThreads);
+  if (a.K % kBK == 0)
+    hipLaunchKernelGGL((linear_kernel<BM, BN, TA, TB, NORM, RES, OF32, false>), grid, block, 0, s, a);
+  else if constexpr (!NORM)
+    hipLaunchKernelGGL((linear_kernel<BM, BN, TA, TB, NORM, RES, OF32, true>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -280,18 +346,53 @@ hipError_t launch_linear(const LinearProblem& lp, hipStream_t s) {
   a.eps = lp.eps;
   a.r = static_cast<const uint16_t*>(lp.residual);
   a.ldr = lp.ldr;
-  a.y = static_cast<uint16_t*>(lp.y);
+  a.y = lp.y;
   a.ldy = lp.ldy;
   a.M = lp.M;
   a.N = static_cast<int>(lp.N);
-  a.K = static_cast<int>(lp.K);
+  a.K = lp.K;
   TimingScope ts(kKLinear, s);
   const bool norm = lp.norm_w != nullptr, res = lp.residual != nullptr;
-  constexpr int BM = SSD_LINEAR_BM, BN = SSD_LINEAR_BN;
-  if (norm && res) return launch_linear_t<BM, BN, true, true>(a, s);
-  if (norm) return launch_linear_t<BM, BN, true, false>(a, s);
-  if (res) return launch_linear_t<BM, BN, false, true>(a, s);
-  return launch_linear_t<BM, BN, false, false>(a, s);
+  if (norm && res) return launch_linear_t<false, false, true, true, false>(a, s);
+  if (norm) return launch_linear_t<false, false, true, false, false>(a, s);
+  if (res) return launch_linear_t<false, false, false, true, false>(a, s);
+  return launch_linear_t<false, false, false, false, false>(a, s);
+}
+
+// dx[M][K] = dy[M][N] w[N][K]  (the input gradient of y = x w^T)
+hipError_t launch_linear_dgrad(int64_t M, int64_t N, int64_t K, const void* dy, int64_t lddy,
+                               const void* w, int64_t ldw, void* dx, int64_t lddx, hipStream_t s) {
+  LinArgs a{};
+  a.x = static_cast<const uint16_t*>(dy);  // A = dy, reduction over N (contiguous)
+  a.ldx = lddy;
+  a.w = static_cast<const uint16_t*>(w);   // B[k][n] = w[n][k]: stored [N][K], transposed
+  a.ldw = ldw;
+  a.y = dx;
+  a.ldy = lddx;
+  a.M = M;
+  a.N = static_cast<int>(K);
+  a.K = N;
+  TimingScope ts(kKLinear, s);
+  return launch_linear_t<false, true, false, false, false>(a, s);
+}
+
+// dw[N][K] (+)= dy[M][N]^T x[M][K]  (the weight gradient of y = x w^T, fp32)
+hipError_t launch_linear_wgrad(int64_t M, int64_t N, int64_t K, const void* dy, int64_t lddy,
+                               const void* x, int64_t ldx, float* dw, int64_t lddw, int accumulate,
+                               hipStream_t s) {
+  LinArgs a{};
+  a.x = static_cast<const uint16_t*>(dy);  // A[n][m] = dy[m][n]: stored [M][N], transposed
+  a.ldx = lddy;
+  a.w = static_cast<const uint16_t*>(x);   // B[k][m] = x[m][k]: stored [M][K], transposed
+  a.ldw = ldx;
+  a.y = dw;
+  a.ldy = lddw;
+  a.M = N;
+  a.N = static_cast<int>(K);
+  a.K = M;
+  a.accumulate = accumulate;
+  TimingScope ts(kKLinear, s);
+  return launch_linear_t<true, true, false, false, true>(a, s);
 }
 
 }  // namespace ssd

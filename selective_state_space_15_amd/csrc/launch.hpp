@@ -18,7 +18,7 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 24;
 enum KernelKind {
   kKBcPrepass, kKWalkState, kKScan, kKWalkOut, kKConvStateOut, kKConvFwd, kKChunkStates,
   kKDstate, kKScanRev, kKBwdMain, kKConvBwd, kKDbcReduce, kKParams, kKScanGroups, kKXbcPrepass,
-  kKLinear, kKDecode, kKernelKinds
+  kKLinear, kKDecode, kKNorm, kKernelKinds
 };
 
 // Brackets the launches made during its lifetime with HIP events on stream `s`
@@ -178,6 +178,21 @@ struct LinearProblem {
   int64_t ldy;
 };
 hipError_t launch_linear(const LinearProblem& lp, hipStream_t s);
+// backward of y = x w^T: dx = dy w (bf16) and dw (+)= dy^T x (fp32)
+hipError_t launch_linear_dgrad(int64_t M, int64_t N, int64_t K, const void* dy, int64_t lddy,
+                               const void* w, int64_t ldw, void* dx, int64_t lddx, hipStream_t s);
+hipError_t launch_linear_wgrad(int64_t M, int64_t N, int64_t K, const void* dy, int64_t lddy,
+                               const void* x, int64_t ldx, float* dw, int64_t lddw, int accumulate,
+                               hipStream_t s);
+
+// ---------------------------------------------------------------- RMSNorm of the block
+size_t rmsnorm_bwd_workspace_bytes(int64_t K);
+int rmsnorm_max_k();
+hipError_t launch_rmsnorm_fwd(int64_t M, int K, const void* x, int64_t ldx, const float* g, float eps,
+                              void* y, int64_t ldy, float* rstd, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(int64_t M, int K, const void* x, int64_t ldx, const float* g, float eps,
+                              const void* dy, int64_t lddy, const void* dres, int64_t ldres, void* dx,
+                              int64_t lddx, float* dg, int accumulate, void* ws, hipStream_t s);
 
 // ---------------------------------------------------------------- streaming decode
 // pr.L tokens stepped one at a time from (pr.h0, pr.cs_in); state out to h_out (may
