@@ -292,3 +292,25 @@ def block_bwd(u, w_in, conv_w, conv_b, A, H, P, G, N, w_out, dfinal, dt_bias=Non
     return dict(du=du, dw_in=dw_in, dw_out=dw_out, dnorm_in=dnorm_in, dnorm_out=dnorm_out,
                 dconv_w=r["dconv_w"], dconv_b=r["dconv_b"], dA=r["dA"], dD=r["dD"],
                 ddt_bias=r["ddt_bias"], dh0=r["dh0"], dconv_state=r["dconv_state"], dzx=dzx)
+
+
+def stack_fwd_bwd(u, layers, H, P, G, N, dfinal, eps=1e-5):
+    """A stack of full blocks (each layer a dict of w_in, conv_w, conv_b, A, w_out,
+    dt_bias, D, norm_in, norm_out) over u [B, L, d_model], all states starting at zero:
+    the forward through the layers, then the backward layer by layer from the top with
+    block_bwd.  Returns (final, du, [per-layer gradient dicts])."""
+    xs = [np.asarray(u, dtype=np.float64)]
+    for p in layers:
+        xs.append(mixer_full_fwd(xs[-1], p["w_in"], p["conv_w"], p["conv_b"], p["A"], H, P, G, N, p["w_out"],
+                                 dt_bias=p["dt_bias"], D=p["D"], norm_in=p["norm_in"], norm_out=p["norm_out"],
+                                 eps=eps, residual=True)["final"])
+    g = np.asarray(dfinal, dtype=np.float64)
+    grads = [None] * len(layers)
+    for i in reversed(range(len(layers))):
+        p = layers[i]
+        r = block_bwd(xs[i], p["w_in"], p["conv_w"], p["conv_b"], p["A"], H, P, G, N, p["w_out"], g,
+                      dt_bias=p["dt_bias"], D=p["D"], norm_in=p["norm_in"], norm_out=p["norm_out"], eps=eps,
+                      residual=True)
+        grads[i] = r
+        g = r["du"]
+    return xs[-1], g, grads

@@ -539,3 +539,36 @@ def test_block_bwd_matches_finite_differences(full):
             fd = (loss(dp) - loss(dmn)) / (2 * eps)
             an = float(np.sum(g[gname] * v))
             assert abs(fd - an) <= 2e-7 * max(1.0, abs(an)), (key, fd, an)
+
+
+def test_stack_bwd_matches_finite_differences():
+    """Two stacked blocks: the input gradient and one weight of each layer by central
+    differences of the stack's output."""
+    r = np.random.default_rng(66)
+    H, P, G, N, K, dm, L = 2, 2, 1, 3, 4, 5, 11
+    hp, cd = H * P, H * P + 2 * G * N
+    dip = hp + cd + H
+
+    def layer():
+        return dict(w_in=0.4 * r.standard_normal((dip, dm)), conv_w=r.uniform(-0.5, 0.5, (cd, K)),
+                    conv_b=r.uniform(-0.5, 0.5, cd), A=-np.exp(r.uniform(0, 1.5, H)),
+                    w_out=0.4 * r.standard_normal((dm, hp)), dt_bias=r.uniform(-2, 0, H), D=r.standard_normal(H),
+                    norm_in=r.uniform(0.5, 1.5, dm), norm_out=r.uniform(0.5, 1.5, hp))
+    layers = [layer(), layer()]
+    u = r.standard_normal((1, L, dm))
+    wf = r.standard_normal((1, L, dm))
+    fin, du, grads = orc.stack_fwd_bwd(u, layers, H, P, G, N, wf, eps=1e-3)
+    loss = lambda uu, ls: float(np.sum(orc.stack_fwd_bwd(uu, ls, H, P, G, N, wf, eps=1e-3)[0] * wf))
+    e = 1e-6
+    v = r.standard_normal(u.shape)
+    fd = (loss(u + e * v, layers) - loss(u - e * v, layers)) / (2 * e)
+    assert abs(fd - np.sum(du * v)) <= 2e-7 * max(1.0, abs(fd))
+    for i in range(2):
+        for key, gk in (("w_in", "dw_in"), ("norm_out", "dnorm_out"), ("A", "dA")):
+            v = r.standard_normal(np.shape(layers[i][key]))
+            lp = [dict(x) for x in layers]
+            lm = [dict(x) for x in layers]
+            lp[i][key] = layers[i][key] + e * v
+            lm[i][key] = layers[i][key] - e * v
+            fd = (loss(u, lp) - loss(u, lm)) / (2 * e)
+            assert abs(fd - np.sum(grads[i][gk] * v)) <= 2e-7 * max(1.0, abs(fd)), (i, key)
