@@ -282,6 +282,8 @@ def main():
         print("[bench] c1 mixer done", file=sys.stderr, flush=True)
         res["decode"] = bench_decode(args, stream)
         print("[bench] decode done", file=sys.stderr, flush=True)
+        res["magc"] = bench_magc(args, stream)
+        print("[bench] magc done", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if args.cpu_sample > 0:
@@ -457,6 +459,54 @@ def bench_decode(args, stream):
                      "note": "one call per token step from Python (host launch overhead included in "
                              "us_per_call); the kernel reads and writes the state once per call"}
     return res
+
+
+def bench_magc(args, stream):
+    """Multi-axis gradient checkpointing of a 48-layer stack of full blocks at d_model 1024
+    (random weights): for S = 16K .. 128K tokens, the intervals (l, s) minimising the
+    memory model, the measured peak activation memory of one training pass (forward,
+    backward, all parameter gradients) next to the model, and the pass's time."""
+    import numpy as np
+    import torch
+
+    from selective_state_space_15_amd import block, magc, synth
+    dev = stream.device
+    d = synth.CONFIGS["c1"]
+    n_layers = 48
+    sh = block.Shape(d.d_model, d.H, d.P, d.N, d.G, d.K)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    layers = []
+    for i in range(n_layers):
+        w, p = synth.mixer_weights(d, args.seed + i), synth.params(d, args.seed + i)
+        layers.append(block.Weights(w_in=bits(w["w_in"]), w_out=bits(w["w_out"]), norm_in=f32(w["norm_in"]),
+                                    norm_out=f32(w["norm_out"]), conv_w=f32(p["conv_w"]), conv_b=f32(p["conv_b"]),
+                                    A=f32(p["A"]), D=f32(p["D"]), dt_bias=f32(p["dt_bias"])))
+    grads = [block.zero_grads(w) for w in layers]
+    rows = []
+    for S in (16384, 32768, 65536, 131072):
+        l, s = magc.best_intervals(sh, n_layers, S)
+        dS = d.with_(L=S)
+        u, dF = bits(synth.tokens(dS, args.seed)), bits(synth.dfinal(dS, args.seed))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        t = time.perf_counter()
+        sc = block.Scratch(sh, 1, s, dev)
+        _, ck = magc.stack_forward(sh, layers, u, sc, l, s)
+        magc.stack_backward(sh, layers, ck, dF, grads, sc, l, s)
+        torch.cuda.synchronize()
+        sec = time.perf_counter() - t
+        peak = torch.cuda.max_memory_allocated() - base
+        model = sum(magc.model_bytes(sh, n_layers, S, l, s).values())
+        rows.append({"S": S, "l": l, "s": s, "peak_MiB": peak / 2**20, "model_MiB": model / 2**20,
+                     "train_pass_s": sec, "tokens_per_s": S / sec})
+        del u, dF, sc, ck
+    ratios = [rows[i + 1]["peak_MiB"] / rows[i]["peak_MiB"] for i in range(len(rows) - 1)]
+    return {"workload": f"{n_layers}-layer stack of full Mamba-2 blocks, d_model 1024 (32x64 heads, d_state 128), "
+                        "batch 1, bf16, forward + backward with multi-axis gradient checkpointing",
+            "rows": rows, "peak_ratio_per_doubling": ratios}
 
 
 if __name__ == "__main__":
