@@ -343,6 +343,39 @@ def bench_c4(args, stream):
     med, medf = float(np.median(ms)), float(np.median(msf))
     gbs = (fb + bb) * tok / (med * 1e-3) / 1e9
     gbsf = fb * tok / (medf * 1e-3) / 1e9
+    # the full block around it (RMSNorm, in_proj, hot path, gated RMSNorm, out_proj,
+    # residual), forward + backward with every parameter gradient
+    from selective_state_space_15_amd import block
+    del zx, dout, out, fws, bws, dxbc, ddt, dz
+    torch.cuda.empty_cache()
+    sh = block.Shape(d.d_model, H, d.P, d.N, d.G, d.K)
+    bits = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    wt = synth.mixer_weights(d, args.seed)
+    w = block.Weights(w_in=bits(wt["w_in"]), w_out=bits(wt["w_out"]), norm_in=torch.from_numpy(wt["norm_in"]).to(dev),
+                      norm_out=torch.from_numpy(wt["norm_out"]).to(dev), conv_w=p["conv_w"], conv_b=p["conv_b"],
+                      A=p["A"], D=p["D"], dt_bias=p["dt_bias"])
+    u = bits(synth.tokens(d, args.seed))
+    dF = bits(synth.dfinal(d, args.seed))
+    fin, du = torch.empty_like(u), torch.empty_like(u)
+    sc = block.Scratch(sh, B, L, dev)
+    grads = block.zero_grads(w)
+
+    def blk():
+        block.block_fwd(sh, w, u, fin, sc)
+        block.block_bwd(sh, w, u, dF, du, grads, sc, accumulate=False)
+
+    blk()
+    msb = float(np.median(timed(blk, n, stream)))
+    bd.ssd_timing_enable(True)
+    blk()
+    torch.cuda.synchronize()
+    kt = bd.ssd_timing_read()
+    bd.ssd_timing_enable(False)
+    lin_ms = kt["linear"][0]
+    gemm_flops = 3 * 2.0 * tok * d.d_model * (d.d_in_proj + hp)  # forward, input and weight gradients
+    block_res = {"tokens_per_s": tok / (msb * 1e-3), "ms_per_step_median": msb,
+                 "projection_ms": lin_ms, "projection_tflops": gemm_flops / (lin_ms * 1e-3) / 1e12,
+                 "note": "forward + backward of the full block; the backward recomputes the block's forward"}
     return {"workload": f"hot path fwd+bwd, 2.7B-style shapes: B={B}, L={L}, {H}x{d.P} heads, "
                         f"d_state {d.N}, conv {d.K}, bf16",
             "tokens_per_s": tok / (med * 1e-3), "ms_per_step_median": med, "ms_per_step_min": min(ms),
@@ -350,7 +383,8 @@ def bench_c4(args, stream):
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "alg_bytes_per_token": fb + bb},
             "fwd_roofline": {"bound": "hbm", "achieved": gbsf, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbsf / HBM_PEAK_GBS, "alg_bytes_per_token": fb}}
+                             "frac": gbsf / HBM_PEAK_GBS, "alg_bytes_per_token": fb},
+            "full_block": block_res}
 
 
 def bench_c1_mixer(args, stream):

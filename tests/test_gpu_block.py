@@ -87,12 +87,14 @@ def oracle_block_bwd(d, u, wts, prm, dF, st):
                          dconv_state_out=f(st["dconv_state"]))
 
 
-@pytest.mark.parametrize("name", ["small", "c1"])
+@pytest.mark.parametrize("name", ["small", "c1", "c4"])
 def test_block_fwd_bwd(name):
     if name == "small":
         d = synth.Dims(B=2, L=777, H=8, P=32, N=64, G=1, K=4, d_model=256)
-    else:
+    elif name == "c1":
         d = synth.CONFIGS["c1"]
+    else:  # the batched 2.7B-style shapes (d_model 2560, 80 heads) at batch 2, L = 1000
+        d = synth.CONFIGS["c4"].with_(B=2, L=1000)
     seed = 91
     sh, w, wts, prm = make_block(d, seed)
     u = synth.tokens(d, seed)
