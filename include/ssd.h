@@ -63,8 +63,13 @@
  *   Preconditions (documented, not checked on the device): A <= 0 and dt >= 0
  *              (always true with dt_softplus = 1).
  *   Supported  headdim P in {32, 64}; dstate N in {16, 32, 64, 128}; conv width
- *              K in {0 (no conv), 2, 3, 4}; chunk in {0, 64} (0 selects 64); any
- *              seqlen >= 1, any batch >= 1, nheads % ngroups == 0.
+ *              K in {0 (no conv), 2, 3, 4}; chunk in {0, 64} (0 selects 64; the result
+ *              does not depend on the chunk length up to rounding, and other lengths
+ *              return SSD_ERR_UNSUPPORTED rather than being remapped); any seqlen >= 1,
+ *              any batch >= 1, nheads % ngroups == 0.
+ *   Entry points beyond the hot path: ssd_fwd_noalloc (no workspace), ssd_decode
+ *              (streaming one-token steps), mixer_proj / mixer_proj_bwd (the block's
+ *              projections), rmsnorm_fwd / rmsnorm_bwd (the block's norms).
  */
 #ifndef SSD_H
 #define SSD_H
@@ -197,7 +202,11 @@ ssd_status ssd_bwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
 
 /*
  * conv1d_fwd -- causal depthwise conv of width K in [2,4] over [B,L,C] rows, plus
- * bias and optional SiLU (the first stage of the hot path, as a standalone call).
+ * bias and optional SiLU (the first stage of the hot path, as a standalone call):
+ *     pre[t,c] = b[c] + sum_{k<K} w[c,k] xin[t-K+1+k, c],  out = silu(pre) or pre,
+ * xin[t < 0] = the carried state rows.  Source: the pith.science review of
+ * Video-Ma2mba, skeptic critique ("load-bearing attack": the causal Conv1d of the
+ * Mamba-2 block before the SSD, whose last K-1 inputs a sequence checkpoint must keep).
  *   x [B,L,C] -> out [B,L,C];  state_in / state_out [B,K-1,C] as in ssd_fwd.
  */
 ssd_status conv1d_fwd(int64_t batch, int64_t seqlen, int64_t channels, int32_t width,
@@ -210,7 +219,9 @@ ssd_status conv1d_bwd_workspace(int64_t batch, int64_t seqlen, int64_t channels,
 
 /*
  * conv1d_bwd -- gradients of conv1d_fwd given dout [B,L,C] and the gradient
- * dstate_out of the returned state (ptr NULL = zero).
+ * dstate_out of the returned state (ptr NULL = zero) -- the conv-buffer gradient that
+ * crosses a segment boundary backwards (same review, skeptic critique, "concrete test":
+ * segmented gradients equal full-storage backprop only with the conv buffer carried).
  *   dx [B,L,C]; dw [C,K] and db [C] (fp32, db may be NULL; overwritten or added to
  *   per `accumulate`); dstate_in [B,K-1,C] (ptr NULL = skip).
  */

@@ -244,45 +244,63 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   const E* xb = static_cast<const E*>(a.x) + b * a.x_sb;
   const E* sbp = has_st ? static_cast<const E*>(a.st) + b * a.st_sb : xb;
   const int64_t sst = has_st ? a.st_st : 0;
+  // thread tid loads the vectors tid + 256 q; 256 is a multiple of the vectors per row,
+  // so its column is the same in every row: the column is resolved once and each load
+  // adds a row offset
+  static_assert(256 % RVPR == 0, "raw vectors per row divide the block");
+  const int rcv = (tid % RVPR) * V;
+  const int rcc = c0 + rcv < climit ? c0 + rcv : c0;
+  const E* xcol = xb + rcc;
+  const E* scol = sbp + rcc;
   uint4 rr[NRV];
 #pragma unroll
   for (int q = 0; q < NRV; ++q) {
-    const int k = min(tid + 256 * q, RROWS * RVPR - 1);
-    const int row = k / RVPR, cv = (k % RVPR) * V;
-    const int cc = c0 + cv < climit ? c0 + cv : c0;
+    const int row = min(tid / RVPR + (256 / RVPR) * q, RROWS - 1);
     const int64_t t = t_lo - 3 + row;
     const bool in_st = has_st && t < 0 && t >= -(K - 1);
     const int64_t tc = t < 0 ? 0 : (t >= a.L ? a.L - 1 : t);
-    const E* src = in_st ? sbp + (t + K - 1) * sst + cc : xb + tc * a.x_st + cc;
+    const E* src = in_st ? scol + (t + K - 1) * sst : xcol + tc * a.x_st;
     rr[q] = *reinterpret_cast<const uint4*>(src);
   }
   // gradient rows: 16-byte vectors of cw channels (the I/O view, or the fp32 group
   // sums for the fused B / C channels); gvpr = vectors per row (a power of two)
   const int gsh = from_f32 ? 4 : (V == 8 ? 3 : 4);
   const int cw = from_f32 ? 4 : V;
+  // as for the raw rows, the column of a thread's gradient vectors is the same in every
+  // row: its address is resolved once (the block is uniformly I/O or fp32 gradients, so
+  // only one kind is computed), and each row adds rows x the row stride
   uint4 gr[NGV];
   {
-    const int gn = FUSED ? a.G * a.N : 0;
-#pragma unroll
-    for (int q = 0; q < NGV; ++q) {
-      const int k = min(tid + 256 * q, (GROWS << gsh) - 1);
-      const int row = k >> gsh, cv = (k & ((1 << gsh) - 1)) * cw;
-      const int cc = c0 + cv < climit ? c0 + cv : c0;
-      const int64_t t = t_lo + row;
-      const int64_t tt = t < a.L ? t : a.L - 1;
-      const char* src;
-      if constexpr (FUSED) {
-        const int rel = cc > a.hp ? cc - a.hp : 0;
+    const int gcv = (tid & ((1 << gsh) - 1)) * cw;
+    const int gcc = c0 + gcv < climit ? c0 + gcv : c0;
+    const char* gcol;
+    int64_t gst;  // bytes between rows
+    if constexpr (FUSED) {
+      if (from_f32) {
+        // fp32 group sums [group][B][L][2N] of B (first N) and C (next N)
+        const int gn = a.G * a.N, lgN = __builtin_ctz(a.N);  // N is a power of two
+        const int rel = gcc - a.hp;
         const bool isC = rel >= gn;
         const int rc = isC ? rel - gn : rel;
-        const float* pf = a.dbc + ((static_cast<int64_t>(rc / a.N) * a.per_g * a.B + b) * a.L + tt) * (2LL * a.N) +
-                          (isC ? a.N : 0) + rc % a.N;
-        const E* pe = static_cast<const E*>(a.g) + (b * a.L + tt) * a.hp + cc;
-        src = from_f32 ? reinterpret_cast<const char*>(pf) : reinterpret_cast<const char*>(pe);
+        gcol = reinterpret_cast<const char*>(
+            a.dbc + ((static_cast<int64_t>(rc >> lgN) * a.per_g * a.B + b) * a.L) * (2LL * a.N) +
+            (isC ? a.N : 0) + (rc & (a.N - 1)));
+        gst = 2LL * a.N * sizeof(float);
       } else {
-        src = reinterpret_cast<const char*>(static_cast<const E*>(a.g) + b * a.g_sb + tt * a.g_st + cc);
+        gcol = reinterpret_cast<const char*>(static_cast<const E*>(a.g) + b * a.L * a.hp + gcc);
+        gst = static_cast<int64_t>(a.hp) * sizeof(E);
       }
-      gr[q] = *reinterpret_cast<const uint4*>(src);
+    } else {
+      gcol = reinterpret_cast<const char*>(static_cast<const E*>(a.g) + b * a.g_sb + gcc);
+      gst = a.g_st * static_cast<int64_t>(sizeof(E));
+    }
+    const int growq = 256 >> gsh;  // rows one pass of the block covers
+#pragma unroll
+    for (int q = 0; q < NGV; ++q) {
+      const int row = min((tid >> gsh) + growq * q, GROWS - 1);
+      const int64_t t = t_lo + row;
+      const int64_t tt = t < a.L ? t : a.L - 1;
+      gr[q] = *reinterpret_cast<const uint4*>(gcol + tt * gst);
     }
   }
   // gradient of the returned state rows L-(K-1) .. L-1 (zero without one), fp32 in LDS
@@ -332,9 +350,10 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
       if (from_f32) {
         *reinterpret_cast<uint4*>(dst) = keep_if(ok, gr[q]);
       } else {
+        const uint4 gk = keep_if(ok, gr[q]);  // masked as packed words, then widened
         float f[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) f[v] = ok ? raw_elem<IO>(gr[q], v) : 0.f;
+        for (int v = 0; v < V; ++v) f[v] = raw_elem<IO>(gk, v);
 #pragma unroll
         for (int v = 0; v < V; v += 4) *reinterpret_cast<float4*>(dst + v) = make_float4(f[v], f[v + 1], f[v + 2], f[v + 3]);
       }

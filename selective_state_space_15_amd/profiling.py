@@ -118,6 +118,138 @@ def report_bytes(fetch_db, write_db, kernel, copy_bytes, cmd_fetch, cmd_write, t
     return "\n".join(out) + "\n"
 
 
+# ---------------------------------------------------------------------------- table
+# Per-kernel counter table of `bench.py --pmc-probe` (one 16,384-token segment forward
+# and backward at d_model 1024 shapes, then the two projections at L = 8192), from five
+# runs: kernel trace, FETCH_SIZE, WRITE_SIZE, and two SQ counter sets.  Kernels that
+# run twice per step under one name (the conv pre-pass of each pass, the scan of each
+# pass) are told apart by their order inside the step.
+PROBE_TOKENS = 16384
+PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
+    ("conv_fwd_kernel<bf16_t, 4>", 0): "conv pre-pass (fwd: B, C)",
+    ("conv_fwd_kernel<bf16_t, 4>", 1): "conv pre-pass (bwd: x, B, C)",
+    ("walk_kernel<bf16_t, 64, 128, 0>", 0): "walk_state (fwd)",
+    ("walk_kernel<bf16_t, 64, 128, 1>", 0): "walk_out (fwd)",
+    ("scan_kernel", 0): "scan (fwd, sub-segments)",
+    ("scan_kernel", 1): "scan (bwd, chunk groups)",
+    ("group_state_kernel<bf16_t, 64, 128, false, 2>", 0): "chunk_states (bwd)",
+    ("group_state_kernel<bf16_t, 64, 128, true, 2>", 0): "dstate (bwd)",
+    ("scan_rev_kernel", 0): "scan_rev (bwd)",
+    ("bwd_main_kernel<bf16_t, 64, 128, 8>", 0): "bwd_main (bwd)",
+    ("conv_bwd_kernel<bf16_t, true>", 0): "conv_bwd (bwd)",
+    ("linear_kernel<128, 128, false, false, false, false, false, false>", 0): "in_proj 8192x4384x1024",
+    ("linear_kernel<128, 128, false, false, false, false, false, false>", 1): "out_proj 8192x1024x2048",
+}
+# algorithmic bytes per token of each kernel's own inputs and outputs (bf16, d_model 1024
+# shapes; fp16 in-group states of 64 x 128 per chunk of 64 and head, 32 heads)
+_STATE = 32 * 64 * 128 * 2 // 64
+PROBE_ALG_BYTES_PER_TOKEN = {
+    "conv pre-pass (fwd: B, C)": 512 + 512,
+    "conv pre-pass (bwd: x, B, C)": 4608 + 4096 + 512 + 512,
+    "walk_state (fwd)": 4096 + 256 + 64,
+    "walk_out (fwd)": 4608 + 4096 + 64 + 4096,
+    "chunk_states (bwd)": 4096 + 256 + 64 + _STATE,
+    "dstate (bwd)": 512 + 4096 + 4096 + 64 + _STATE,
+    "bwd_main (bwd)": 4096 + 768 + 4096 + 4096 + 64 + 2 * _STATE + 4096 + 4096 + 64 + 1024,
+    "conv_bwd (bwd)": 4608 + 4096 + 1024 + 4608,
+}
+PROBE_ALG_BYTES = {  # the projections: operands and result once
+    "in_proj 8192x4384x1024": 2 * (8192 * 1024 + 4384 * 1024 + 8192 * 4384),
+    "out_proj 8192x1024x2048": 2 * (8192 * 2048 + 1024 * 2048 + 8192 * 1024),
+}
+CLOCK_HZ = 2.4e9
+SIMDS = 256 * 4
+HBM_PEAK = 8.0e12
+
+
+def _dispatches(db: str):
+    """[(dispatch_id, short kernel name)] in dispatch order, and {dispatch_id: {counter: value}}."""
+    con = sqlite3.connect(db)
+    vals = {}
+    names = {}
+    for d, k, c, v in con.execute("select dispatch_id, kernel_name, counter_name, sum(value) from "
+                                  "counters_collection group by dispatch_id, kernel_name, counter_name"):
+        vals.setdefault(d, {})[c] = v
+        names[d] = short_name(k)
+    return sorted(names.items()), vals
+
+
+def _labelled(db: str):
+    """{label: [counter dicts]} with labels from PROBE_LABELS (occurrence within each step)."""
+    order, vals = _dispatches(db)
+    out, seen, steps = {}, {}, 0
+    for d, k in order:
+        if k.startswith("bwd_main"):
+            steps += 1
+        key = (k, seen.get((k, steps), 0))
+        seen[(k, steps)] = key[1] + 1
+        lab = PROBE_LABELS.get(key) or PROBE_LABELS.get((k, key[1] % 2))
+        if lab and "copyBuffer" not in k:
+            out.setdefault(lab, []).append(vals[d])
+        if "copyBuffer" in k:
+            out.setdefault("copy", []).append(vals[d])
+    return out
+
+
+def _trace_durations(db: str):
+    con = sqlite3.connect(db)
+    out = {}
+    order = list(con.execute("select name, duration from kernels order by start"))
+    seen, steps = {}, 0
+    for n, du in order:
+        k = short_name(n)
+        if k.startswith("bwd_main"):
+            steps += 1
+        occ = seen.get((k, steps), 0)
+        seen[(k, steps)] = occ + 1
+        lab = PROBE_LABELS.get((k, occ)) or PROBE_LABELS.get((k, occ % 2))
+        if lab:
+            out.setdefault(lab, []).append(du)
+    return out
+
+
+def report_table(trace, fetch, write, inst, util, copy_bytes, cmds, title):
+    mean = lambda xs: sum(xs) / len(xs) if xs else float("nan")
+    cval = lambda rows, c: mean([r.get(c, 0.0) for r in rows])
+    dur = _trace_durations(trace)
+    F, W, I, U = _labelled(fetch), _labelled(write), _labelled(inst), _labelled(util)
+    f_scale = copy_bytes / (max(r["FETCH_SIZE"] for r in F["copy"]) * 1024.0)
+    w_scale = copy_bytes / (max(r["WRITE_SIZE"] for r in W["copy"]) * 1024.0)
+    out = [f"# {title}", "", "Commands (from the repository root on one MI355X; one counter set per run):", "",
+           "```", *cmds, "```", "",
+           f"Byte counters are scaled by what they read for a plain device copy of {copy_bytes} bytes in the "
+           f"same run: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.  MFMA figures: flops = 512 x "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 (16,384 per 16x16x32 instruction); SQ_VALU_MFMA_BUSY_CYCLES counts "
+           "SIMD cycles at 1,024 flops each, so MFMA busy = busy cycles / (duration x 2.4 GHz x 1,024 SIMDs).  "
+           "VALU issue = SQ_INSTS_VALU x 4 cycles / (duration x 2.4 GHz x 1,024 SIMDs).  LDS conflict = "
+           "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.  Algorithmic bytes: each kernel's own inputs and "
+           "outputs, read or written once (the state kernels include their in-group state tiles).", "",
+           "| kernel | avg us | HBM MB (counters) | alg MB | counter / alg | HBM TB/s | MFMA TFLOP/s | MFMA busy | "
+           "VALU issue | LDS conflict | VALU insts / MFMA insts |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    labels = [l for l in list(PROBE_ALG_BYTES_PER_TOKEN) + list(PROBE_ALG_BYTES) if l in F]
+    recs = {}
+    for lab in labels:
+        us = mean(dur.get(lab, [])) / 1e3
+        hbm = cval(F[lab], "FETCH_SIZE") * 1024 * f_scale + cval(W[lab], "WRITE_SIZE") * 1024 * w_scale
+        alg = PROBE_ALG_BYTES_PER_TOKEN.get(lab, 0) * PROBE_TOKENS or PROBE_ALG_BYTES.get(lab, 0)
+        flops = 512 * cval(U[lab], "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        busy = cval(U[lab], "SQ_VALU_MFMA_BUSY_CYCLES")
+        cyc = us * 1e-6 * CLOCK_HZ * SIMDS
+        valu = cval(I[lab], "SQ_INSTS_VALU")
+        mfma_i = cval(I[lab], "SQ_INSTS_MFMA")
+        conf = cval(U[lab], "SQ_LDS_BANK_CONFLICT") / max(cval(U[lab], "SQ_ACTIVE_INST_LDS"), 1.0)
+        rec = dict(us=us, hbm=hbm, alg=alg, tbs=hbm / (us * 1e-6) / 1e12, tflops=flops / (us * 1e-6) / 1e12,
+                   mfma_busy=busy / cyc, valu_issue=valu * 4 / cyc, lds_conflict=conf,
+                   valu_per_mfma=valu / max(mfma_i, 1.0))
+        recs[lab] = rec
+        out.append(f"| {lab} | {us:.1f} | {hbm / 1e6:.1f} | {alg / 1e6:.1f} | {hbm / alg:.2f} | {rec['tbs']:.2f} | "
+                   f"{rec['tflops']:.0f} | {100 * rec['mfma_busy']:.1f}% | {100 * rec['valu_issue']:.1f}% | "
+                   f"{conf:.2f} | {rec['valu_per_mfma']:.1f} |")
+    out += ["", "Machine-readable:", "", "```json", json.dumps(recs), "```"]
+    return "\n".join(out) + "\n"
+
+
 def read_bytes_report(path: str):
     """The JSON record of a `bytes` report, or None."""
     try:
@@ -143,7 +275,16 @@ def main():
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
     b.add_argument("--title", required=True)
+    t = sub.add_parser("table")
+    for k in ("trace", "fetch", "write", "inst", "util"):
+        t.add_argument("--" + k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--cmd", action="append", required=True)
+    t.add_argument("--title", required=True)
     a = ap.parse_args()
+    if a.what == "table":
+        print(report_table(a.trace, a.fetch, a.write, a.inst, a.util, a.copy_bytes, a.cmd, a.title), end="")
+        return
     if a.what == "stats":
         print(report_stats(a.db, a.cmd, a.title), end="")
     else:
