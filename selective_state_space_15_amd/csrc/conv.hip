@@ -18,6 +18,8 @@
 // recomputed from the raw rows, dx[tau] = sum_k dpre[tau + K-1-k] w[k] (plus the
 // gradient of the returned conv state for the last K-1 rows), and per-tile partial
 // sums of dw and db go to scratch for an ordered reduction (deterministic, no atomics).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -125,22 +127,34 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
                   : (a.out_lo ? static_cast<E*>(a.out_lo) + b * a.o_sb + a.o_c0 + c : nullptr);
   const int64_t ost = second ? a.o2_st : a.o_st;
 
-  // input value of row index i (t = t0 - 3 + i), channel v; zero outside the sequence
-  // and before the carried state
-  auto raw = [&](int i, int v) __attribute__((always_inline)) {
+  // row index i (t = t0 - 3 + i): the carried-state row before the sequence, zero
+  // outside the sequence and before the carried state -- resolved once per row on the
+  // packed words, so each tap reads a plain element
+#pragma unroll
+  for (int i = 0; i < kRowsF + 3; ++i) {
     const int64_t t = t0 - 3 + i;
-    float x = raw_elem<IO>(in[i], v);
-    if (i < 3) x = t < 0 ? raw_elem<IO>(sin[i], v) : x;
+    uint4 v = in[i];
+    if (i < 3) {
+      const bool from_st = t < 0;
+      v = make_uint4(from_st ? sin[i].x : v.x, from_st ? sin[i].y : v.y, from_st ? sin[i].z : v.z,
+                     from_st ? sin[i].w : v.w);
+    }
     const bool ok = t < a.L && t >= -(K - 1) && (t >= 0 || has_st);
-    return ok ? x : 0.f;
-  };
-  auto row = [&](int r, float* o) __attribute__((always_inline)) {
+    in[i] = keep_if(ok, v);
+  }
+  auto raw = [&](int i, int v) __attribute__((always_inline)) { return raw_elem<IO>(in[i], v); };
+  float bias[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) bias[v] = has_bias ? bias_raw[v] : 0.f;
+  // SILU is the (uniform) activation flag as a compile-time value: one branch for the
+  // tile instead of a select per element
+  auto row = [&](int r, float* o, auto silu_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      float pre = has_bias ? bias_raw[v] : 0.f;
+      float pre = bias[v];
 #pragma unroll
       for (int k = 0; k < K; ++k) pre = fmaf(wf[v * K + k], raw(r + 4 - K + k, v), pre);
-      o[v] = a.silu ? siluf_(pre) : pre;
+      o[v] = decltype(silu_tag)::value ? siluf_(pre) : pre;
     }
   };
   auto put = [&](int r, const float* o) __attribute__((always_inline)) {
@@ -152,21 +166,27 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
       store_vec16<IO>(olb + (t0 + r) * ost, lo);
     }
   };
-  if (t0 + kRowsF <= a.L) {
+  auto tile_rows = [&](auto silu_tag) __attribute__((always_inline)) {
+    if (t0 + kRowsF <= a.L) {
 #pragma unroll
-    for (int r = 0; r < kRowsF; ++r) {
-      float o[V];
-      row(r, o);
-      put(r, o);
-    }
-  } else {
+      for (int r = 0; r < kRowsF; ++r) {
+        float o[V];
+        row(r, o, silu_tag);
+        put(r, o);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < kRowsF; ++r) {
-      float o[V];
-      row(r, o);
-      if (t0 + r < a.L) put(r, o);
+      for (int r = 0; r < kRowsF; ++r) {
+        float o[V];
+        row(r, o, silu_tag);
+        if (t0 + r < a.L) put(r, o);
+      }
     }
-  }
+  };
+  if (a.silu)
+    tile_rows(std::true_type{});
+  else
+    tile_rows(std::false_type{});
 }
 
 // ------------------------------------------------------------------ backward
