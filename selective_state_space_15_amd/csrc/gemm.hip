@@ -203,9 +203,17 @@ linear_kernel(LinArgs a) {
   uint16_t* sB = smem + OA::elems;
 
   const int tid = threadIdx.x, wave = tid >> 6;
+  // Tile order: consecutive logical ids run on one XCD (xcd_remap); they walk groups of
+  // kGroupM row blocks, all column blocks of a group, row block fastest -- so the row
+  // blocks of a group and each column block stay in that XCD's L2 while they are reused
+  // (row block first would stream every column block of w through L2 once per row block).
+  constexpr int64_t kGroupM = 8;
   const int64_t lid = xcd_remap(blockIdx.x, a.tiles);
-  const int64_t m0 = (lid / a.tiles_n) * BM;
-  const int64_t n0 = static_cast<int64_t>(lid % a.tiles_n) * BN;
+  const int64_t tiles_m = a.tiles / a.tiles_n;
+  const int64_t grp = lid / (kGroupM * a.tiles_n), in_grp = lid % (kGroupM * a.tiles_n);
+  const int64_t gm_rows = tiles_m - grp * kGroupM < kGroupM ? tiles_m - grp * kGroupM : kGroupM;
+  const int64_t m0 = (grp * kGroupM + in_grp % gm_rows) * BM;
+  const int64_t n0 = (in_grp / gm_rows) * BN;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
 
   float ss[AV];
