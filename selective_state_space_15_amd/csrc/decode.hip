@@ -12,12 +12,13 @@
 //   out[p] = y[p] SiLU(z[p])
 // which is the recurrence of the forward pass taken one step at a time.
 //
-// One workgroup of 256 threads owns one (batch, head): its P x N fp32 state lives in
-// registers for the whole call (N / (256 / P) elements per thread), each conv channel
-// keeps its window of K-1 raw inputs in a register file, and the post-conv x, B and C
+// The rows p of a head's state are independent given B, C and dt, so one workgroup of
+// 256 threads owns kRows rows of one (batch, head): those rows of the fp32 state live
+// in registers for the whole call (N / (256 / kRows) elements per thread), each conv
+// channel keeps its window of K-1 raw inputs in registers, and the post-conv x, B and C
 // of the current token pass through LDS.  The state is read once and written once per
 // call, whatever the number of tokens.  The B / C conv runs in every workgroup of the
-// group (a few hundred channels); the group's first head writes their carried rows.
+// group (a few hundred channels); the group's first workgroup writes their carried rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,6 +26,7 @@ namespace ssd {
 namespace {
 
 constexpr int kDecThreads = 256;
+constexpr int kRows = 16;  // state rows (head channels p) per workgroup
 
 struct DecodeArgs {
   Problem pr;          // L = tokens in this call; h0 = state in (null = zeros)
@@ -35,7 +37,8 @@ struct DecodeArgs {
 
 template <int NT>
 __device__ __forceinline__ float sum_lanes(float v) {
-  static_assert(NT == 4 || NT == 8, "lanes per state row");
+  static_assert(NT == 4 || NT == 8 || NT == 16, "lanes per state row");
+  if constexpr (NT == 16) return row_sum16(v);
   v += dpp_f<kDppQuad1032>(0.f, v);
   v += dpp_f<kDppQuad2301>(0.f, v);
   if constexpr (NT == 8) v += dpp_f<kDppRowHalfMirror>(0.f, v);
@@ -45,17 +48,20 @@ __device__ __forceinline__ float sum_lanes(float v) {
 template <typename IO, int P, int N, int K>
 __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   using E = typename io_traits<IO>::elem;
-  constexpr int NT = kDecThreads / P;   // threads per state row p
+  constexpr int SPLIT = P / kRows;      // workgroups per (batch, head)
+  constexpr int NT = kDecThreads / kRows;  // threads per state row p
   constexpr int NPT = N / NT;           // state elements per thread
-  constexpr int NCH = P + 2 * N;        // conv channels of one (head, group)
+  constexpr int NCH = kRows + 2 * N;    // conv channels of one workgroup: its x rows, B, C
   constexpr int CPT = (NCH + kDecThreads - 1) / kDecThreads;  // channels per thread
   constexpr int KW = K > 1 ? K - 1 : 1;  // carried window
-  static_assert(NT * P == kDecThreads && NPT * NT == N, "thread layout");
+  static_assert(NT * kRows == kDecThreads && NPT * NT == N && SPLIT * kRows == P, "thread layout");
   const Problem& pr = a.pr;
-  __shared__ float s_x[P], s_B[N], s_C[N];
+  __shared__ float s_x[kRows], s_B[N], s_C[N];
 
   const int tid = threadIdx.x;
-  const int b = blockIdx.x / pr.H, h = blockIdx.x % pr.H;
+  const int part = blockIdx.x % SPLIT;
+  const int b = blockIdx.x / (SPLIT * pr.H), h = (blockIdx.x / SPLIT) % pr.H;
+  const int p0 = part * kRows;  // this workgroup's first state row
   const int hpg = pr.H / pr.G, g = h / hpg;
   const int64_t HP = static_cast<int64_t>(pr.H) * P;
   const int64_t GN = static_cast<int64_t>(pr.G) * N;
@@ -69,7 +75,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     const int j = tid + kDecThreads * i;
     live[i] = j < NCH;
     const int jj = live[i] ? j : 0;
-    ch[i] = jj < P ? h * P + jj : jj < P + N ? HP + g * N + (jj - P) : HP + GN + g * N + (jj - P - N);
+    ch[i] = jj < kRows ? h * P + p0 + jj
+                       : jj < kRows + N ? HP + g * N + (jj - kRows) : HP + GN + g * N + (jj - kRows - N);
     if constexpr (K > 0) {
 #pragma unroll
       for (int k = 0; k < K; ++k) wk[i][k] = pr.conv_w[ch[i] * K + k];
@@ -84,8 +91,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     }
   }
 
-  // state rows p = tid / NT, columns n0 .. n0 + NPT
-  const int p = tid / NT, n0 = (tid % NT) * NPT;
+  // state row p0 + pl (pl = tid / NT), columns n0 .. n0 + NPT
+  const int pl = tid / NT, p = p0 + pl, n0 = (tid % NT) * NPT;
   float st[NPT];
   const int64_t soff = ((static_cast<int64_t>(b) * pr.H + h) * P + p) * N + n0;
 #pragma unroll
@@ -113,22 +120,22 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
         if constexpr (K > 1) win[i][K - 2] = raw;
       }
       const int j = tid + kDecThreads * i;
-      if (j < P) s_x[j] = v;
-      else if (j < P + N) s_B[j - P] = v;
-      else s_C[j - P - N] = v;
+      if (j < kRows) s_x[j] = v;
+      else if (j < kRows + N) s_B[j - kRows] = v;
+      else s_C[j - kRows - N] = v;
     }
     __syncthreads();
     float dt = io_traits<IO>::to_f(dtp[b * pr.dt.sb + t * pr.dt.st + h]) + dtb;
     if (pr.softplus) dt = softplusf_(dt);
     const float decay = __expf(dt * A);
-    const float dtx = dt * s_x[p];
-    float part = 0.f;
+    const float dtx = dt * s_x[pl];
+    float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       st[j] = decay * st[j] + dtx * s_B[n0 + j];
-      part += st[j] * s_C[n0 + j];
+      acc += st[j] * s_C[n0 + j];
     }
-    const float y = sum_lanes<NT>(part) + Dh * s_x[p];
+    const float y = sum_lanes<NT>(acc) + Dh * s_x[pl];
     if (tid % NT == 0) {
       float o = y;
       if (zp) o *= siluf_(io_traits<IO>::to_f(zp[b * pr.z.sb + t * pr.z.st + h * P + p]));
@@ -144,7 +151,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int j = tid + kDecThreads * i;
-      if (!live[i] || (j >= P && h % hpg != 0)) continue;  // B / C rows: the group's first head
+      // B / C rows: the group's first workgroup
+      if (!live[i] || (j >= kRows && (h % hpg != 0 || part != 0))) continue;
 #pragma unroll
       for (int k = 0; k < KW; ++k)
         static_cast<E*>(a.cs_out.p)[b * a.cs_out.sb + k * a.cs_out.st + ch[i]] = io_traits<IO>::from_f(win[i][k]);
@@ -154,7 +162,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
 
 template <typename IO, int P, int N>
 hipError_t launch_decode_pn(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H));
+  const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H * (P / kRows)));
   switch (a.pr.K) {
     case 0: hipLaunchKernelGGL((decode_kernel<IO, P, N, 0>), grid, dim3(kDecThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((decode_kernel<IO, P, N, 2>), grid, dim3(kDecThreads), 0, s, a); break;
