@@ -164,7 +164,8 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   constexpr int ldG = P + 4;
   __shared__ __align__(16) float sG2[kQ * ldG];  // dout silu'(z) [t][p] (fp32)
   // per head of the block: dt and the chunk-local cumsum cs of dt A
-  __shared__ float s_dtH[kDtTab][kQ], s_csH[kDtTab][kQ];
+  __shared__ __align__(16) float s_dtH[kDtTab][kQ];
+  __shared__ __align__(16) float s_csH[kDtTab][kQ];
   __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
   // per-wave partials of <dH, H> and of dD, double-buffered by head parity: wave 0 reads
   // head h's in (f) while the other waves already stage head h + 1
@@ -459,31 +460,57 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     }
     const float* s_dt = s_dtH[hh % kDtTab];
     const float* s_cs = s_csH[hh % kDtTab];
-    // chunk-state decay exp(cs_Q - cs_s)
+    // The head's per-lane scalars, read once: cs and dt at this lane's accumulator rows
+    // t = m0 + acc_row(e) (four consecutive rows) and columns s = s0 + 16 j + acc_col().
     const float cs_last = s_cs[kQ - 1];
-    auto dq = [&](int s) __attribute__((always_inline)) { return __expf(cs_last - s_cs[s]); };
+    float cst[4], dtt[4], css[QJw], dts[QJw];
+    {
+      const float4 c4 = *reinterpret_cast<const float4*>(s_cs + m0 + acc_row(0));
+      const float4 d4 = *reinterpret_cast<const float4*>(s_dt + m0 + acc_row(0));
+      cst[0] = c4.x; cst[1] = c4.y; cst[2] = c4.z; cst[3] = c4.w;
+      dtt[0] = d4.x; dtt[1] = d4.y; dtt[2] = d4.z; dtt[3] = d4.w;
+    }
+#pragma unroll
+    for (int j = 0; j < QJw; ++j) {
+      css[j] = s_cs[s0 + 16 * j + acc_col()];
+      dts[j] = s_dt[s0 + 16 * j + acc_col()];
+    }
+    // exp(cs_t) (carried-state terms) and, at rows s, the chunk-state decay
+    // exp(cs_Q - cs_s) alone (dqe) and times dt_s (dqd)
+    float ecs[4], dqe[4], dqd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ecs[e] = __expf(cst[e]);
+      dqe[e] = __expf(cs_last - cst[e]);
+      dqd[e] = dqe[e] * dtt[e];
+    }
     // dy (hi + lo) and dout silu'(z) at this lane's accumulator positions
     // (rows m0 + 4*(lane/16)+e, cols 16j + lane%16)
     float dyr[PJw][4], g2r[PJw][4];
 #pragma unroll
-    for (int j = 0; j < PJw; ++j)
+    for (int j = 0; j < PJw; ++j) {
+      acc_gather(dyr[j], sDY, ldP, m0, p0 + 16 * j);
+      if constexpr (SPLIT) {
+        float lo4[4];
+        acc_gather(lo4, sDYlo, ldP, m0, p0 + 16 * j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = m0 + acc_row(e), p = p0 + 16 * j + acc_col();
-        dyr[j][e] = T::lds_to_f(sDY[t * ldP + p]);
-        if constexpr (SPLIT) dyr[j][e] += T::lds_to_f(sDYlo[t * ldP + p]);
-        g2r[j][e] = sG2[t * ldG + p];
+        for (int e = 0; e < 4; ++e) dyr[j][e] += lo4[e];
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g2r[j][e] = sG2[(m0 + acc_row(e)) * ldG + p0 + 16 * j + acc_col()];
+    }
 
     // (a) Mt, y, dz, carried-state dcs term, dD
-    float lt[QJw][4];  // exp(cs_t - cs_s) masked, at the cb positions
+    // exp(cs_t - cs_s) masked, at the cb positions: no branch (exp(-inf) = 0 above the
+    // diagonal, where the difference would also overflow)
+    float lt[QJw][4];
 #pragma unroll
     for (int j = 0; j < QJw; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e), s = s0 + 16 * j + acc_col();
-        lt[j][e] = s <= t ? __expf(s_cs[t] - s_cs[s]) : 0.f;
-        sM[t * ldQ + s] = T::to_lds(cb[j][e] * lt[j][e] * s_dt[s]);
+        lt[j][e] = __expf(s <= t ? cst[e] - css[j] : -__builtin_inff());
+        sM[t * ldQ + s] = T::to_lds(cb[j][e] * lt[j][e] * dts[j]);
       }
     f32x4 yacc[PJw];
 #pragma unroll
@@ -495,10 +522,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ecs = __expf(s_cs[m0 + acc_row(e)]);
 #pragma unroll
       for (int j = 0; j < PJw; ++j) {
-        yacc[j][e] *= ecs;
+        yacc[j][e] *= ecs[e];
         yo_part[e] += dyr[j][e] * yacc[j][e];
       }
     }
@@ -507,15 +533,16 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + t0 * a.dz.st + h * P : nullptr;
-      float dzv[PJw][4];
+      float dzv[PJw][4], xg[PJw][4];
+#pragma unroll
+      for (int j = 0; j < PJw; ++j) acc_gather(xg[j], sX, ldP, m0, p0 + 16 * j);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
         E* dzr = dzp ? byte_off(dzp, (t * static_cast<uint32_t>(a.dz.st) + p0 + acc_col()) * sizeof(E)) : nullptr;
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
-          const int p = p0 + 16 * j + acc_col();
-          const float xv = T::lds_to_f(sX[t * ldP + p]);
+          const float xv = xg[j][e];
           const float y = yacc[j][e] + Dh * xv;
           dD_part += dyr[j][e] * xv;
           dzv[j][e] = g2r[j][e] * y;
@@ -549,18 +576,16 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       for (int j = 0; j < QJw; ++j) {
         float csum = 0.f;
         const int s = s0 + 16 * j + acc_col();
-        const float dts = s_dt[s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = m0 + acc_row(e);
           const float wp = dyx[j][e] * lt[j][e];  // (dy_t.x_s) e^{cs_t-cs_s}, masked
           const float m2 = wp * cb[j][e];
-          rs[e] += m2 * dts;
+          rs[e] += m2 * dts[j];
           csum += m2;
-          sW[t * ldQ + s] = T::to_lds(wp * dts);
+          sW[t * ldQ + s] = T::to_lds(wp * dts[j]);
         }
-        csum += __shfl_xor(csum, 16, kWave);
-        csum += __shfl_xor(csum, 32, kWave);
+        csum = col_sum4(csum);
         if (lane < 16) s_col[strip][s] = csum;
       }
 #pragma unroll
@@ -590,11 +615,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = m0 + acc_row(e);
-        const float sc = dq(s) * s_dt[s];
         E* dxr = byte_off(dxp, (s * static_cast<uint32_t>(a.dx.st) + p0 + acc_col()) * sizeof(E));
 #pragma unroll
         for (int j = 0; j < PJw; ++j) {
-          dxv[j][e] = dxd[j][e] + sc * dxs[j][e] + Dh * dyr[j][e];
+          dxv[j][e] = dxd[j][e] + dqd[e] * dxs[j][e] + Dh * dyr[j][e];
           if constexpr (!kPairStore)
             if (t0 + s < pr.L) dxr[16 * j] = T::from_f(dxv[j][e]);
         }
@@ -610,13 +634,13 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       mma_strip<Lt, true, false, NTw, kMainUnroll>(U, sX, ldP, m0, sdH, ldN, n0, P);
       float vp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = m0 + acc_row(e);
-        const float sc = dq(s) * s_dt[s];
+      for (int j = 0; j < NTw; ++j) {
+        float bg[4];
+        acc_gather(bg, sB, ldN, m0, n0 + 16 * j);
 #pragma unroll
-        for (int j = 0; j < NTw; ++j) {
-          vp[e] += U[j][e] * T::lds_to_f(sB[s * ldN + n0 + 16 * j + acc_col()]);
-          accdB[j][e] += sc * U[j][e];
+        for (int e = 0; e < 4; ++e) {
+          vp[e] += U[j][e] * bg[e];
+          accdB[j][e] += dqd[e] * U[j][e];
         }
       }
 #pragma unroll
@@ -624,7 +648,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         vp[e] = row_sum16(vp[e]);
       if (acc_col() == 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = dq(m0 + acc_row(e)) * vp[e];
+        for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = dqe[e] * vp[e];
       mma_strip<Lt, false, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
     }
     prefetch(h_first + hn, 2);
@@ -636,11 +660,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       for (int j = 0; j < NTw; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       mma_strip<Lt, true, false, NTw, kMainUnroll>(tmp, sDY, ldP, m0, sH, ldN, n0, P);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ecs = __expf(s_cs[m0 + acc_row(e)]);
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int j = 0; j < NTw; ++j) accdC[j][e] += ecs * tmp[j][e];
-      }
+        for (int j = 0; j < NTw; ++j) accdC[j][e] += ecs[e] * tmp[j][e];
     }
     __syncthreads();
 

@@ -427,6 +427,41 @@ __device__ __forceinline__ Ptr byte_off(Ptr base, uint32_t bytes) {
 __device__ __forceinline__ int acc_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
 
+// The four values T[m0 + acc_row(e)][c0 + acc_col()], e = 0..3, of a row-major LDS tile
+// (element (r, c) at base[r * ld + c]) as floats: the accumulator layout of one 16x16
+// tile.  bf16 tiles take one gfx950 transpose read (ds_read_b64_tr_b16): inside each
+// 16-lane group, lane a points at row m0 + 4 (lane / 16) + a / 4, columns
+// c0 + 4 (a % 4) .. + 3, and lane i gets back element i % 4 of the chunks of lanes
+// i / 4 + 4 e, which is column c0 + i of row m0 + 4 (lane / 16) + e.  Needs ld and c0 to
+// be multiples of 4 elements.  fp32 tiles read the four values one by one.
+template <typename L>
+__device__ __forceinline__ void acc_gather(float (&v)[4], const L* base, int ld, int m0, int c0) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (sizeof(L) == 2) {
+    const int a = lane & 15;
+    const L* p = base + (m0 + 4 * (lane >> 4) + (a >> 2)) * ld + c0 + 4 * (a & 3);
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(r[e])) << 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = base[(m0 + acc_row(e)) * ld + c0 + (lane & 15)];
+  }
+}
+
+// Sum of v over the four lanes l % 16 + 16 k (k = 0..3), in each of them: two gfx950
+// row swaps (v_permlane32_swap, v_permlane16_swap), no LDS round trip.
+__device__ __forceinline__ float col_sum4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float s2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const uint32_t u2 = __float_as_uint(s2);
+  const auto q = __builtin_amdgcn_permlane16_swap(u2, u2, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Map a hardware workgroup id to a logical id so that consecutive logical ids
 // run on the same XCD (dispatch places workgroup i on XCD i % 8).  Bijective for
 // any grid size.
