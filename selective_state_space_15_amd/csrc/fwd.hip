@@ -89,7 +89,9 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   __shared__ __align__(16) Lt sX[OUT ? kQ * ldP : 8];
   __shared__ __align__(16) Lt sM[OUT ? kQ * ldQ : 8];
   __shared__ __align__(16) Lt sH[OUT ? P * ldN : 8];
-  __shared__ float s_dt[kQ], s_cs[kQ], s_w[kQ];
+  __shared__ __align__(16) float s_dt[kQ];
+  __shared__ __align__(16) float s_cs[kQ];
+  __shared__ float s_w[kQ];
   // state walk: w_s and the log-decay of every chunk of the sub-segment, computed
   // before the walk (one wave per chunk), so no chunk waits on a one-wave step
   constexpr int kMaxCps = 64;
@@ -368,25 +370,32 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       f32x4 yacc[YJ];
 #pragma unroll
       for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float cst[4];
       {
         f32x4 cb[CBJ];
 #pragma unroll
         for (int j = 0; j < CBJ; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         mma_strip_ab<Lt, true, true, CBJ, YJ>(cb, yacc, sC, ldN, m0, sB, ldN, 16 * CBJ * half, sH, ldN,
                                              16 * YJ * half, N);
+        // cs at this lane's rows t = m0 + acc_row(e) (four consecutive) and cs, dt at its
+        // columns s; the decay mask without a branch (exp(-inf) = 0 above the diagonal)
+        const float4 c4 = *reinterpret_cast<const float4*>(s_cs + m0 + acc_row(0));
+        cst[0] = c4.x; cst[1] = c4.y; cst[2] = c4.z; cst[3] = c4.w;
 #pragma unroll
-        for (int j = 0; j < CBJ; ++j)
+        for (int j = 0; j < CBJ; ++j) {
+          const int s = 16 * CBJ * half + 16 * j + acc_col();
+          const float css = s_cs[s], dts = s_dt[s];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = m0 + acc_row(e);
-            const int s = 16 * CBJ * half + 16 * j + acc_col();
-            const float v = s <= t ? cb[j][e] * __expf(s_cs[t] - s_cs[s]) * s_dt[s] : 0.f;
+            const float v = cb[j][e] * __expf(s <= t ? cst[e] - css : -__builtin_inff()) * dts;
             sM[t * ldQ + s] = T::to_lds(v);
           }
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float ecs = __expf(s_cs[m0 + acc_row(e)]);
+        const float ecs = __expf(cst[e]);
 #pragma unroll
         for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
       }
@@ -394,13 +403,16 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       mma_strip<Lt, true, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
       // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
       // out = y * silu(z) on 16-byte rows
+      float xg[YJ][4];
+#pragma unroll
+      for (int j = 0; j < YJ; ++j) acc_gather(xg[j], sX, ldP, m0, 16 * (YJ * half + j));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e);
 #pragma unroll
         for (int j = 0; j < YJ; ++j) {
           const int p = 16 * (YJ * half + j) + acc_col();
-          sY[t * ldY + p] = yacc[j][e] + Dh * T::lds_to_f(sX[t * ldP + p]);
+          sY[t * ldY + p] = yacc[j][e] + Dh * xg[j][e];
         }
       }
       __syncthreads();
