@@ -34,6 +34,10 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef SSD_BWD_EARLY_UNROLL
+#define SSD_BWD_EARLY_UNROLL 2
+#endif
+
 namespace ssd {
 
 hipError_t launch_conv_bwd_fused(const Problem& pr, const void* dx_ws, const float* dbc_sum,
@@ -142,6 +146,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   constexpr int kThreads = MainShape<NW>::threads;
   constexpr int NHALF = MainShape<NW>::halves;
   constexpr int kMainUnroll = MainShape<NW>::unroll;
+  // (a) and (b) run while no next-head prefetch is held in registers: their K loops are
+  // unrolled so that the fragment reads of later K-steps issue ahead of the MFMAs
+  constexpr int kEarlyUnroll = SSD_BWD_EARLY_UNROLL;
   constexpr int PADK = 16 / sizeof(Lt);
   constexpr int ldN = N + PADK, ldQ = kQ + PADK, ldP = P + PADK;
   constexpr int NTn = N / 16, PJ = P / 16;
@@ -166,6 +173,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   // per head of the block: dt and the chunk-local cumsum cs of dt A
   __shared__ __align__(16) float s_dtH[kDtTab][kQ];
   __shared__ __align__(16) float s_csH[kDtTab][kQ];
+  // d dt / d dt_raw = sigmoid(dt_raw + dt_bias), tabulated with dt for bf16 I/O (the
+  // fp32 tiles leave no LDS for it: there (f) computes it from dt)
+  constexpr bool kSigTab = sizeof(Lt) == 2;
+  __shared__ float s_sgH[kSigTab ? kDtTab : 1][kQ];
   __shared__ float s_row[NHALF][kQ], s_yo[NHALF][kQ], s_v[NHALF][kQ], s_col[4][kQ];
   // per-wave partials of <dH, H> and of dD, double-buffered by head parity: wave 0 reads
   // head h's in (f) while the other waves already stage head h + 1
@@ -302,6 +313,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       if (i < kDtTab) {
         s_dtH[i][lane] = dtv;
         s_csH[i][lane] = cs;
+        if constexpr (kSigTab) s_sgH[i][lane] = pr.softplus ? 1.f / (1.f + __expf(-u)) : 1.f;
       }
     }
   };
@@ -516,9 +528,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < PJw; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (clo)
-      mma_strip2<Lt, true, true, PJw, kMainUnroll>(yacc, sC, sClo, ldN, m0, sH, ldN, p0, N);
+      mma_strip2<Lt, true, true, PJw, kEarlyUnroll>(yacc, sC, sClo, ldN, m0, sH, ldN, p0, N);
     else
-      mma_strip<Lt, true, true, PJw, kMainUnroll>(yacc, sC, ldN, m0, sH, ldN, p0, N);
+      mma_strip<Lt, true, true, PJw, kEarlyUnroll>(yacc, sC, ldN, m0, sH, ldN, p0, N);
     float yo_part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -529,7 +541,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    mma_strip<Lt, true, false, PJw, kMainUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
+    mma_strip<Lt, true, false, PJw, kEarlyUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + t0 * a.dz.st + h * P : nullptr;
@@ -568,9 +580,9 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < QJw; ++j) dyx[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (SPLIT)
-        mma_strip2<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, sDYlo, ldP, m0, sX, ldP, s0, P);
+        mma_strip2<Lt, true, true, QJw, kEarlyUnroll>(dyx, sDY, sDYlo, ldP, m0, sX, ldP, s0, P);
       else
-        mma_strip<Lt, true, true, QJw, kMainUnroll>(dyx, sDY, ldP, m0, sX, ldP, s0, P);
+        mma_strip<Lt, true, true, QJw, kEarlyUnroll>(dyx, sDY, ldP, m0, sX, ldP, s0, P);
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QJw; ++j) {
@@ -687,14 +699,18 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       }
       const float sum_dtv = wave_sum(dts * vs);
       if (s == kQ - 1) dcs += __expf(s_cs[kQ - 1]) * hdh + sum_dtv;
-      // dl_s = sum_{t >= s} dcs_t: inclusive scan over reversed lanes
-      const float rev = __shfl(dcs, kWave - 1 - lane, kWave);
-      const float rscan = wave_incl_scan(rev);
-      const float dl = __shfl(rscan, kWave - 1 - lane, kWave);
+      // dl_s = sum_{t >= s} dcs_t = (sum of all) - (inclusive prefix at s) + dcs_s
+      // (exact at the last lane, where the prefix is the sum itself)
+      const float incl = wave_incl_scan(dcs);
+      const float dl = (lane_value(incl, kWave - 1) - incl) + dcs;
       const float ddt = colsum + vs + Ah * dl;
       const bool valid = t0 + s < pr.L;
       // d softplus(u)/du = sigmoid(u) = 1 - exp(-softplus(u))
-      const float sig = pr.softplus ? -expm1f(-dts) : 1.f;
+      float sig;
+      if constexpr (kSigTab)
+        sig = s_sgH[hh % kDtTab][s];
+      else
+        sig = pr.softplus ? -expm1f(-dts) : 1.f;
       const float ddt_raw = valid ? ddt * sig : 0.f;
       if (valid)
         *byte_off(static_cast<E*>(a.ddt.p) + b * a.ddt.sb + t0 * a.ddt.st + h,
