@@ -400,13 +400,18 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       const int i = (threadIdx.x + q * kThreads) * 4;
       if (NH4 * 4 * kThreads == P * N || i < P * N) {
         const int p = i / N, n = i % N;
-        const SV ph = keep_if(useP, hv[q]), qh = keep_if(useQ, gv[q]);
         float4 pv, qv;
         if constexpr (F16S) {
+          // A zero scale masks a slot (a slot without a term still holds finite values),
+          // and the power-of-two scaling is exact; each fp16 -> fp32 conversion folds
+          // into that fma (v_fma_mix_f32).
           const float ps = useP ? hsc[q] : 0.f, qs = useQ ? gsc[q] : 0.f;
-          pv = make_float4(ps * h2f_lo(ph.x), ps * h2f_hi(ph.x), ps * h2f_lo(ph.y), ps * h2f_hi(ph.y));
-          qv = make_float4(qs * h2f_lo(qh.x), qs * h2f_hi(qh.x), qs * h2f_lo(qh.y), qs * h2f_hi(qh.y));
+          pv = make_float4(fmaf(h2f_lo(hv[q].x), ps, 0.f), fmaf(h2f_hi(hv[q].x), ps, 0.f),
+                           fmaf(h2f_lo(hv[q].y), ps, 0.f), fmaf(h2f_hi(hv[q].y), ps, 0.f));
+          qv = make_float4(fmaf(h2f_lo(gv[q].x), qs, 0.f), fmaf(h2f_hi(gv[q].x), qs, 0.f),
+                           fmaf(h2f_lo(gv[q].y), qs, 0.f), fmaf(h2f_hi(gv[q].y), qs, 0.f));
         } else {
+          const SV ph = keep_if(useP, hv[q]), qh = keep_if(useQ, gv[q]);
           pv = make_float4(__uint_as_float(ph.x), __uint_as_float(ph.y), __uint_as_float(ph.z), __uint_as_float(ph.w));
           qv = make_float4(__uint_as_float(qh.x), __uint_as_float(qh.y), __uint_as_float(qh.z), __uint_as_float(qh.w));
         }
