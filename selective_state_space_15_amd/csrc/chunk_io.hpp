@@ -229,6 +229,25 @@ struct ChunkLoader {
     consume_impl<true, true>(pr, h, t0, put, wl);
   }
 
+  // The B / C rows of issue_raw() as the loaded 16-byte vectors (zero where masked),
+  // for tiles that keep the I/O element type: put_raw(seg, row, local_channel, uint4).
+  // No conversion round trip through fp32.
+  template <typename F>
+  __device__ __forceinline__ void consume_bc_raw(F&& put_raw) const {
+    static_assert(DB || DC, "B / C rows only");
+#pragma unroll
+    for (int q = 0; q < BT; ++q) {
+      const int task = threadIdx.x + q * NTHR;
+      if (NTB % NTHR != 0 && task >= NTB) continue;
+      const int grp = task % (GB + GC);
+      const int r0 = (task / (GB + GC)) * RB;
+      const int seg = grp < GB ? 1 : 2;
+      const int cl = (seg == 1 ? grp : grp - GB) * V;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) put_raw(seg, r0 + r, cl, keep_if((okm >> (kXBits + q * RB + r)) & 1u, bin[q][r]));
+    }
+  }
+
   template <bool WLDS, bool RAW = false, typename F>
   __device__ __forceinline__ void consume_impl(const Problem& pr, int h, int64_t t0, F&& put,
                                                const float* wl) const {

@@ -315,9 +315,11 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     }
     if (holds_halo) sRaw[(vlast / XV - (kQ - 3)) * XV + vlast % XV] = xhalo;
     xhalo = keep_if((xok >> (XPT - 1)) & 1u, xr[XPT - 1]);  // the next chunk's halo
-    ld.consume_raw_lds_taps(pr, h, t0, [&](int seg, int s, int cl, const float* o) {
-      lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
-    }, s_conv);
+    // B / C rows go to LDS as loaded (the tiles keep the I/O element type)
+    static_assert(sizeof(Lt) == sizeof(E), "LDS tiles hold I/O elements");
+    ld.consume_bc_raw([&](int seg, int s, int cl, const uint4& v) {
+      *reinterpret_cast<uint4*>((seg == 1 ? sB : sC) + s * ldN + cl) = v;
+    });
     __syncthreads();
     const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
     lsum += cs_last;
