@@ -108,7 +108,6 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const float Ah = pr.A[h];
-  const float bias_h = pr.dt_bias ? pr.dt_bias[h] : 0.f;
   const float Dh = OUT && pr.D ? pr.D[h] : 0.f;
   const bool gate = OUT && pr.z.p != nullptr;
 
@@ -162,7 +161,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   // dt) is prefetched into registers one chunk ahead, so those loads are in flight
   // while the previous chunk computes; z is loaded when the chunk is staged and used
   // in its epilogue.
-  const E* dtp = static_cast<const E*>(pr.dt.p) + b * pr.dt.sb + h;
+  // dt of head h from the pre-pass table ([B][L][H] fp32, softplus applied)
+  const float* dtp = pr.dtsp + b * pr.L * pr.H + h;
   const E* zp = OUT && gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P : nullptr;
   const int64_t tbeg = k * a.cps * kQ;
   // B/C rows per loader task: as many tasks as threads (every thread's loads are
@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   __shared__ __align__(16) uint4 sRawBuf[OUT ? 1 : (kQ + 3) * XV];
   static_assert(!OUT || (kQ + 3) * XV * 16 <= sizeof(Lt) * kQ * ldQ, "x staging fits the M tile");
   uint4* const sRaw = OUT ? reinterpret_cast<uint4*>(sM) : sRawBuf;
-  E dt_raw{};
+  float dt_pre = 0.f;
   // gate inputs of this thread's output vectors (row k / (P / V), columns
   // V (k % (P / V)) for k = tid + NTHR q), loaded one chunk phase ahead as 16-byte rows
   constexpr int NYV = (kQ * P / V + NTHR - 1) / NTHR;
@@ -236,34 +236,27 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   };
   // dt of the next chunk (unconditional, from a clamped row: a load under a branch
   // would be waited for at once, and with it every load still in flight; rows past
-  // the end are masked in (1))
-  // The raw element is kept as loaded and converted in (1): converting it here would
-  // make the wave wait for the load at once.  Every wave loads it (no branch); wave 0
-  // uses it.
+  // the end are masked in (1)).  Every wave loads it (no branch); wave 0 uses it.
   auto prefetch = [&](int64_t tn) {
     const uint32_t r = tn + lane < pr.L ? lane : static_cast<uint32_t>(pr.L - 1 - tn);
-    dt_raw = *byte_off(dtp + tn * pr.dt.st, r * static_cast<uint32_t>(pr.dt.st) * sizeof(E));
+    dt_pre = *byte_off(dtp + tn * pr.H, r * static_cast<uint32_t>(pr.H) * sizeof(float));
   };
   if constexpr (OUT) {
     prefetch(tbeg);
   } else {
     // every chunk's dt (16 chunks per wave at most: all loads first, then the scans)
     constexpr int kPer = kMaxCps / NW;
-    E dtr[kPer];
+    float dtr[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int64_t t = tbeg + (wave + NW * i) * kQ + lane;
-      dtr[i] = dtp[(t < pr.L ? t : pr.L - 1) * pr.dt.st];
+      dtr[i] = dtp[(t < pr.L ? t : pr.L - 1) * pr.H];
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int ci = wave + NW * i;
       const int64_t t = tbeg + ci * kQ + lane;
-      float dtv = 0.f;
-      if (ci < a.cps && t < pr.L) {
-        const float u = T::to_f(dtr[i]) + bias_h;
-        dtv = pr.softplus ? softplusf_(u) : u;
-      }
+      const float dtv = ci < a.cps && t < pr.L ? dtr[i] : 0.f;
       const float cs = wave_incl_scan(dtv * Ah);
       const float csl = lane_value(cs, kWave - 1);
       s_wall[ci * kQ + lane] = dtv * __expf(csl - cs);
@@ -288,13 +281,9 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
             dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
       }
     }
-    // (1) dt = softplus(dt_raw + bias), l = dt * A, chunk-local cumsum (wave 0)
+    // (1) dt (softplus applied by the pre-pass), l = dt * A, chunk-local cumsum (wave 0)
     if (OUT && wave == 0) {
-      float dtv = 0.f;
-      if (t0 + lane < pr.L) {
-        const float u = T::to_f(dt_raw) + bias_h;
-        dtv = pr.softplus ? softplusf_(u) : u;
-      }
+      const float dtv = t0 + lane < pr.L ? dt_pre : 0.f;
       const float cs = wave_incl_scan(dtv * Ah);
       const float csl = lane_value(cs, kWave - 1);
       s_dt[lane] = dtv;
@@ -534,6 +523,21 @@ __global__ void conv_state_out_kernel(Problem pr, MView dst) {
   static_cast<E*>(dst.p)[b * dst.sb + j * dst.st + c] = v;
 }
 
+// dt = softplus(dt_raw + dt_bias) (or the sum alone), once per (token, head) for both
+// walks: fp32 [B][L][H], one element per thread.
+template <typename IO>
+__global__ void __launch_bounds__(256) dt_prepass_kernel(Problem pr, float* out) {
+  using T = io_traits<IO>;
+  using E = typename T::elem;
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= pr.B * pr.L * pr.H) return;
+  const int h = static_cast<int>(i % pr.H);
+  const int64_t t = (i / pr.H) % pr.L, b = i / (pr.H * pr.L);
+  const float u = T::to_f(static_cast<const E*>(pr.dt.p)[b * pr.dt.sb + t * pr.dt.st + h]) +
+                  (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+  out[i] = pr.softplus ? softplusf_(u) : u;
+}
+
 template <typename IO, int P, int N>
 hipError_t run_walks(const Problem& pr, const FwdOut& o, const Plan& pl, float* ws_state,
                      float* ws_lsum, hipStream_t s) {
@@ -612,9 +616,13 @@ Plan make_plan(int64_t B, int64_t L, int H) {
   return pl;
 }
 
-// Scratch layout: [B|C post-conv rows][sub-segment states][sub-segment log-decays]
+// Scratch layout: [B|C post-conv rows][dt table][sub-segment states][sub-segment log-decays]
+size_t dt_table_bytes(const Problem& pr) {
+  return align256(static_cast<size_t>(pr.B) * pr.L * pr.H * sizeof(float));
+}
+
 size_t fwd_workspace_bytes(const Problem& pr, const Plan& pl) {
-  size_t n = bc_prepass_bytes(pr);
+  size_t n = bc_prepass_bytes(pr) + dt_table_bytes(pr);
   if (pl.n_sub > 1) {
     const size_t st = static_cast<size_t>(pr.B) * pl.n_sub * pr.H * pr.P * pr.N * sizeof(float);
     const size_t ls = static_cast<size_t>(pr.B) * pl.n_sub * pr.H * sizeof(float);
@@ -634,6 +642,21 @@ hipError_t launch_fwd(const Problem& pr_in, const FwdOut& o, const Plan& pl, voi
     const int64_t gn2 = 2LL * pr.G * pr.N;
     pr.bc = View{w, pr.L * gn2, gn2};
     w += bc_prepass_bytes(pr);
+  }
+  {
+    float* dts = reinterpret_cast<float*>(w);
+    const int64_t n = pr.B * pr.L * pr.H;
+    TimingScope ts(kKBcPrepass, s);
+    if (pr.bf16)
+      hipLaunchKernelGGL(dt_prepass_kernel<bf16_t>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                         s, pr, dts);
+    else
+      hipLaunchKernelGGL(dt_prepass_kernel<float>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                         s, pr, dts);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    pr.dtsp = dts;
+    w += dt_table_bytes(pr);
   }
   float* st = reinterpret_cast<float*>(w);
   float* ls = nullptr;

@@ -72,6 +72,8 @@ struct Problem {
   View bc;     // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
   View bc_lo;  // bf16 I/O backward: post-conv B|C minus its bf16 rounding (p null: none)
   View xp;     // post-conv x rows [B][L][H*P] from a pre-pass (p null: conv in the loaders)
+  const float* dtsp;  // forward: dt = softplus(dt_raw + dt_bias) (or the sum alone without
+                      // softplus) as fp32 [B][L][H], from the dt pre-pass
 };
 
 struct FwdOut {
