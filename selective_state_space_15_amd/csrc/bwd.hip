@@ -158,8 +158,10 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
   __shared__ __align__(16) Lt sC[kQ * ldN];   // C rows [t][n]
   __shared__ __align__(16) Lt sB[kQ * ldN];   // B rows [s][n]
   __shared__ __align__(16) Lt sX[kQ * ldP];   // x [s][p]
-  __shared__ __align__(16) Lt sM[kQ * ldQ];   // Mt [t][s]
-  __shared__ __align__(16) Lt sW[kQ * ldQ];   // W  [t][s]
+  // Mt and W stored transposed, [s][t]: a lane's four accumulator rows t are then one
+  // 8-byte (bf16) or 16-byte (fp32) piece of a row
+  __shared__ __align__(16) Lt sM[kQ * ldQ];   // Mt [s][t]
+  __shared__ __align__(16) Lt sW[kQ * ldQ];   // W  [s][t]
   __shared__ __align__(16) Lt sDY[kQ * ldP];  // dy [t][p]
   __shared__ __align__(16) Lt sH[P * ldN];    // H_{c-1} [p][n]
   __shared__ __align__(16) Lt sdH[P * ldN];   // dH_c [p][n]
@@ -527,8 +529,11 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int t = m0 + acc_row(e), s = s0 + 16 * j + acc_col();
         lt[j][e] = __expf(s <= t ? cst[e] - css[j] : -__builtin_inff());
-        sM[t * ldQ + s] = T::to_lds(cb[j][e] * lt[j][e] * dts[j]);
       }
+#pragma unroll
+    for (int j = 0; j < QJw; ++j)
+      lds_put4<IO>(sM + (s0 + 16 * j + acc_col()) * ldQ + m0 + acc_row(0), cb[j][0] * lt[j][0] * dts[j],
+                   cb[j][1] * lt[j][1] * dts[j], cb[j][2] * lt[j][2] * dts[j], cb[j][3] * lt[j][3] * dts[j]);
     f32x4 yacc[PJw];
 #pragma unroll
     for (int j = 0; j < PJw; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -546,7 +551,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    mma_strip<Lt, true, false, PJw, kEarlyUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
+    mma_strip<Lt, false, false, PJw, kEarlyUnroll>(yacc, sM, ldQ, m0, sX, ldP, p0, kQ);
     float dD_part = 0.f;
     {
       E* dzp = a.dz.p ? static_cast<E*>(a.dz.p) + b * a.dz.sb + t0 * a.dz.st + h * P : nullptr;
@@ -591,17 +596,17 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < QJw; ++j) {
-        float csum = 0.f;
+        float csum = 0.f, wv[4];
         const int s = s0 + 16 * j + acc_col();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = m0 + acc_row(e);
           const float wp = dyx[j][e] * lt[j][e];  // (dy_t.x_s) e^{cs_t-cs_s}, masked
           const float m2 = wp * cb[j][e];
           rs[e] += m2 * dts[j];
           csum += m2;
-          sW[t * ldQ + s] = T::to_lds(wp * dts[j]);
+          wv[e] = wp * dts[j];
         }
+        lds_put4<IO>(sW + s * ldQ + m0 + acc_row(0), wv[0], wv[1], wv[2], wv[3]);
         csum = col_sum4(csum);
         if (lane < 16) s_col[strip][s] = csum;
       }
@@ -625,7 +630,7 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
         dxd[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         dxs[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      mma_strip<Lt, false, false, PJw, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, p0, kQ);
+      mma_strip<Lt, true, false, PJw, kMainUnroll>(dxd, sM, ldQ, m0, sDY, ldP, p0, kQ);
       mma_strip<Lt, true, true, PJw, kMainUnroll>(dxs, sB, ldN, m0, sdH, ldN, p0, N);
       E* dxp = static_cast<E*>(a.dx.p) + b * a.dx.sb + t0 * a.dx.st + h * P;
       float dxv[PJw][4];
@@ -666,12 +671,12 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
       if (acc_col() == 0)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s_v[hf][m0 + acc_row(e)] = dqe[e] * vp[e];
-      mma_strip<Lt, false, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
+      mma_strip<Lt, true, false, NTw, kMainUnroll>(accdB, sW, ldQ, m0, sC, ldN, n0, kQ);
     }
     prefetch(h_first + hn, 2);
     // (e) dC rows t: W B + exp(cs_t) dY H
     {
-      mma_strip<Lt, true, false, NTw, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, n0, kQ);
+      mma_strip<Lt, false, false, NTw, kMainUnroll>(accdC, sW, ldQ, m0, sB, ldN, n0, kQ);
       f32x4 tmp[NTw];
 #pragma unroll
       for (int j = 0; j < NTw; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};

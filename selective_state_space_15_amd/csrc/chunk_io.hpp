@@ -363,6 +363,15 @@ __device__ __forceinline__ void plain_rows(const View& vw, int64_t L, int b, int
   }
 }
 
+// Four consecutive LDS operand elements from floats: 8 bytes (bf16) or 16 (fp32).
+template <typename IO>
+__device__ __forceinline__ void lds_put4(typename io_traits<IO>::lds* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(typename io_traits<IO>::lds) == 2)
+    *reinterpret_cast<uint2*>(dst) = make_uint2(f2bf2(a, b), f2bf2(c, d));
+  else
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
 // Store 16 bytes worth of floats into an LDS row as I/O-typed operand elements.
 template <typename IO>
 __device__ __forceinline__ void lds_put_row(typename io_traits<IO>::lds* dst, const float* v) {
