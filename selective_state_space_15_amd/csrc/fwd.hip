@@ -376,12 +376,14 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         for (int j = 0; j < CBJ; ++j) {
           const int s = 16 * CBJ * half + 16 * j + acc_col();
           const float css = s_cs[s], dts = s_dt[s];
+          float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = m0 + acc_row(e);
-            const float v = cb[j][e] * __expf(s <= t ? cst[e] - css : -__builtin_inff()) * dts;
-            sM[t * ldQ + s] = T::to_lds(v);
+            v[e] = cb[j][e] * __expf(s <= t ? cst[e] - css : -__builtin_inff()) * dts;
           }
+          // Mt stored transposed, [s][t]: the lane's four rows are one packed piece
+          lds_put4<IO>(sM + s * ldQ + m0 + acc_row(0), v[0], v[1], v[2], v[3]);
         }
       }
 #pragma unroll
@@ -391,7 +393,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
       }
       __syncthreads();
-      mma_strip<Lt, true, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
+      mma_strip<Lt, false, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
       // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
       // out = y * silu(z) on 16-byte rows
       float xg[YJ][4];
