@@ -23,6 +23,8 @@
 //      the gated output, the optional sequence checkpoints and h_final.
 // The state stays in registers (MFMA accumulator layout) along each walk, so
 // the only state traffic through memory is one state per sub-segment.
+#include <type_traits>
+
 #include "chunk_io.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -320,30 +322,46 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       uint4 raw[XPT + 3];
 #pragma unroll
       for (int i = 0; i < XPT + 3; ++i) raw[i] = sRaw[(r0 + i) * XV + cg];
-      const bool conv = pr.K > 0;
-      float w4[4][V], bias[V];
+      // with or without conv as one uniform branch around the whole tile: a branch per
+      // element would cut the tile into blocks, and with it the overlap of the
+      // elements' exp / reciprocal latencies
+      auto tile = [&](auto conv_tag) __attribute__((always_inline)) {
+        constexpr bool CONV = decltype(conv_tag)::value;
+        float w4[4][V], bias[V];
+        if constexpr (CONV)
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
+          for (int v = 0; v < V; ++v) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w4[j][v] = s_conv[(cl + v) * 5 + j];
-        bias[v] = s_conv[(cl + v) * 5 + 4];
-      }
+            for (int j = 0; j < 4; ++j) w4[j][v] = s_conv[(cl + v) * 5 + j];
+            bias[v] = s_conv[(cl + v) * 5 + 4];
+          }
 #pragma unroll
-      for (int r = 0; r < XPT; ++r) {
-        float o[V], ow[V];
-        const float ws = t0 + r0 + r < pr.L ? (OUT ? s_w[r0 + r] : s_wall[c * kQ + r0 + r]) : 0.f;
+        for (int r = 0; r < XPT; ++r) {
+          float o[V], ow[V];
+          const bool live = t0 + r0 + r < pr.L;
+          const float ws = live ? (OUT ? s_w[r0 + r] : s_wall[c * kQ + r0 + r]) : 0.f;
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          float pre = bias[v];
+          for (int v = 0; v < V; ++v) {
+            float val;
+            if constexpr (CONV) {
+              float pre = bias[v];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
-          o[v] = conv ? siluf_(pre) : raw_elem<IO>(raw[r + 3], v);
-          if (t0 + r0 + r >= pr.L) o[v] = 0.f;
-          ow[v] = o[v] * ws;
+              for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
+              val = siluf_(pre);
+            } else {
+              val = raw_elem<IO>(raw[r + 3], v);
+            }
+            o[v] = live ? val : 0.f;
+            ow[v] = o[v] * ws;
+          }
+          if constexpr (OUT) lds_put_row<IO>(sX + (r0 + r) * ldP + cl, o);
+          lds_put_row<IO>(sXw + (r0 + r) * ldP + cl, ow);
         }
-        if constexpr (OUT) lds_put_row<IO>(sX + (r0 + r) * ldP + cl, o);
-        lds_put_row<IO>(sXw + (r0 + r) * ldP + cl, ow);
-      }
+      };
+      if (pr.K > 0)
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
     // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
     // the row loads in flight); the last chunk reloads its own rows
