@@ -128,8 +128,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
 def test_workspace_scaling_is_linear_and_modest():
     f16k = bd.ssd_fwd_workspace(bd.make_dims(1, 16384, 32, 64, 128, 1, 0, 4), bd.SSD_BF16)
     f1m = bd.ssd_fwd_workspace(bd.make_dims(1, 1 << 20, 32, 64, 128, 1, 0, 4), bd.SSD_BF16)
-    # post-conv B|C rows (512 B/token) + one fp32 state per sub-segment of <= 4096 tokens
-    assert f1m <= (1 << 20) * 512 + 256 * (1 << 20) + (1 << 22)
+    # post-conv B|C rows (512 B/token) + the fp32 dt table (4 B per token and head) + one
+    # fp32 state per sub-segment of <= 4096 tokens
+    assert f1m <= (1 << 20) * (512 + 32 * 4) + 256 * (1 << 20) + (1 << 22)
     b16k = bd.ssd_bwd_workspace(bd.make_dims(1, 16384, 32, 64, 128, 1, 0, 4), bd.SSD_BF16)
     b32k = bd.ssd_bwd_workspace(bd.make_dims(1, 32768, 32, 64, 128, 1, 0, 4), bd.SSD_BF16)
     assert abs(b32k - 2 * b16k) <= 8192       # linear in the segment length
