@@ -15,8 +15,9 @@
 // Shape of the work: one workgroup of 4 waves computes a BM x BN block of y; the waves
 // form a 2 x 2 grid of WM x WN sub-blocks of 16 x 16 MFMA tiles
 // (v_mfma_f32_16x16x32_bf16).  Each K-tile of 64 is staged in LDS row-major (K
-// contiguous, rows padded by 16 bytes against bank conflicts); the next tile's 16-byte
-// row pieces are loaded into registers while the MFMAs run on the current one.  Row
+// contiguous, rows padded by 16 bytes against bank conflicts), in two buffers so that a
+// tile is staged while the other is read; the 16-byte row pieces of the tile two ahead
+// are loaded into registers while the MFMAs run on the current one.  Row
 // and column indices past M / N are clamped for the loads and masked at the store.
 #include <hip/hip_runtime.h>
 
@@ -194,13 +195,17 @@ linear_kernel(LinArgs a) {
   using OA = OpTile<BM, TA>;
   using OB = OpTile<BN, TB>;
   constexpr int AV = OA::pieces, BV = OB::pieces;
-  // operand tiles during the K loop; the bf16 output block afterwards
-  constexpr int kOpElems = OA::elems + OB::elems;
+  // operand tiles during the K loop, double-buffered (even K-tiles in buffer 0, odd in
+  // buffer 1: a tile is staged while the waves may still read the other, one barrier per
+  // K-tile); the bf16 output block afterwards
+  constexpr int kOpElems = 2 * (OA::elems + OB::elems);
   constexpr int kOutElems = OF32 ? 8 : BM * (BN + 8);
   __shared__ __align__(16) uint16_t smem[kOpElems > kOutElems ? kOpElems : kOutElems];
   __shared__ float s_rstd[NORM ? BM : 1];
-  uint16_t* sA = smem;
-  uint16_t* sB = smem + OA::elems;
+  uint16_t* const sA0 = smem;
+  uint16_t* const sB0 = smem + OA::elems;
+  uint16_t* const sA1 = smem + OA::elems + OB::elems;
+  uint16_t* const sB1 = sA1 + OA::elems;
 
   const int tid = threadIdx.x, wave = tid >> 6;
   // Tile order: consecutive logical ids run on one XCD (xcd_remap); they walk groups of
@@ -228,18 +233,19 @@ linear_kernel(LinArgs a) {
   const int lane = tid & 63, r = lane & 15, kg = lane >> 4;
   const int64_t nk = (a.K + kBK - 1) / kBK;
 
-  // One K-tile: norm bookkeeping, stage to LDS, refill the registers with the tile two
-  // ahead (clamped to the last: no branch), then the MFMAs on the staged tile.
-#define SSD_LINEAR_STEP(ra, rb, ka, kb, kt)                                                      \
+  // One K-tile: norm bookkeeping, stage to its LDS buffer, one barrier (the tile is
+  // visible, and every wave is past the MFMAs of the tile two back, which used this
+  // buffer), refill the registers with the tile two ahead (clamped to the last: no
+  // branch), then the MFMAs on the staged tile.
+#define SSD_LINEAR_STEP(ra, rb, ka, kb, kt, sA, sB)                                              \
   do {                                                                                           \
     if constexpr (NORM) norm_pieces<AV>(ra, ss, a.g + (kt) * kBK + OA::kk(tid, 0));              \
-    __syncthreads(); /* every wave is done reading the previous tile */                         \
-    store_op<BM, TA, RAG>(ra, ka, sA);                                                                \
-    store_op<BN, TB, RAG>(rb, kb, sB);                                                                \
+    store_op<BM, TA, RAG>(ra, ka, sA);                                                           \
+    store_op<BN, TB, RAG>(rb, kb, sB);                                                           \
     __syncthreads();                                                                             \
     const int64_t kn_ = (kt) + 2 < nk ? (kt) + 2 : nk - 1;                                      \
-    load_op<BM, TA, RAG>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                                \
-    load_op<BN, TB, RAG>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                                \
+    load_op<BM, TA, RAG>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                           \
+    load_op<BN, TB, RAG>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                           \
     mma_tile<TM, TN, BM, BN, TA, TB>(acc, sA, sB, wm, wn, r, kg);                                \
   } while (0)
 
@@ -252,10 +258,10 @@ linear_kernel(LinArgs a) {
   load_op<BN, TB, RAG>(b1, kb1, a.w, a.ldw, n0, a.N, (nk > 1 ? 1 : 0) * kBK, a.K);
   int64_t kt = 0;
   for (; kt + 1 < nk; kt += 2) {
-    SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt);
-    SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1);
+    SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
+    SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1, sA1, sB1);
   }
-  if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt);
+  if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
 #undef SSD_LINEAR_STEP
 
   if constexpr (NORM) {
