@@ -44,6 +44,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #ifndef SSD_LINEAR_WAVES
 #define SSD_LINEAR_WAVES 2
 #endif
+// 256 x 256 blocks for large problems (0: the small blocks everywhere)
+#ifndef SSD_LINEAR_BIG
+#define SSD_LINEAR_BIG 1
+#endif
 
 struct LinArgs {
   const uint16_t* x;  // A operand: [M][ldx] (K contiguous) or, transposed, [K][ldx]
@@ -74,17 +78,18 @@ __device__ __forceinline__ float sum8(float v) {
 // LDS tile of one operand for one K-tile of 64: K-contiguous operands are staged as
 // [rows][64 + 8], transposed ones (stored [K][rows] in memory) as [64][rows + 8]; the
 // MFMA fragments of the latter are read with the gfx950 LDS transpose loads.
-template <int ROWS, bool TR>
+template <int ROWS, bool TR, int NT = kLinThreads>
 struct OpTile {
   static constexpr int ld = TR ? ROWS + 8 : kLd;
   static constexpr int elems = TR ? kBK * ld : ROWS * kLd;
-  static constexpr int pieces = ROWS * kBK / 8 / kLinThreads;  // 16-byte pieces per thread
+  static constexpr int pieces = ROWS * kBK / 8 / NT;  // 16-byte pieces per thread
+  static_assert(pieces * 8 * NT == ROWS * kBK, "the tile splits evenly over the threads");
   // piece i of thread t: (row, k) of the tile it covers
   __device__ static __forceinline__ int row(int t, int i) {
-    return TR ? 8 * ((t + kLinThreads * i) % (ROWS / 8)) : (t + kLinThreads * i) / 8;
+    return TR ? 8 * ((t + NT * i) % (ROWS / 8)) : (t + NT * i) / 8;
   }
   __device__ static __forceinline__ int kk(int t, int i) {
-    return TR ? (t + kLinThreads * i) / (ROWS / 8) : 8 * ((t + kLinThreads * i) % 8);
+    return TR ? (t + NT * i) / (ROWS / 8) : 8 * ((t + NT * i) % 8);
   }
   __device__ static __forceinline__ int lds_off(int t, int i) {
     return TR ? kk(t, i) * ld + row(t, i) : row(t, i) * kLd + kk(t, i);
@@ -94,10 +99,10 @@ struct OpTile {
 // One K-tile's pieces of an operand into registers.  rows: the block's first row r0
 // and the operand's row count R (rows past it are clamped: their products land in
 // masked outputs); K-tile k0 of K (reduction entries past K read as zero).
-template <int ROWS, bool TR, bool RAG, int NP>
+template <int ROWS, bool TR, bool RAG, int NT, int NP>
 __device__ __forceinline__ void load_op(u32x4 (&v)[NP], uint32_t& keep, const uint16_t* base,
                                         int64_t ld, int64_t r0, int64_t R, int64_t k0, int64_t K) {
-  using OT = OpTile<ROWS, TR>;
+  using OT = OpTile<ROWS, TR, NT>;
   const int t = threadIdx.x;
   keep = 0;
   if constexpr (TR) {
@@ -133,9 +138,9 @@ __device__ __forceinline__ void load_op(u32x4 (&v)[NP], uint32_t& keep, const ui
 
 // The pieces into the LDS tile; pieces past K (clear bits of keep) become zeros here,
 // where the values are consumed, not right after their loads.
-template <int ROWS, bool TR, bool RAG, int NP>
+template <int ROWS, bool TR, bool RAG, int NT, int NP>
 __device__ __forceinline__ void store_op(const u32x4 (&v)[NP], uint32_t keep, uint16_t* s) {
-  using OT = OpTile<ROWS, TR>;
+  using OT = OpTile<ROWS, TR, NT>;
 #pragma unroll
   for (int i = 0; i < OT::pieces; ++i) {
     const bool k = !RAG || ((keep >> i) & 1u);
@@ -185,15 +190,32 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[TM][TN], const uint16_t* s
   }
 }
 
-template <int BM, int BN, bool TA, bool TB, bool NORM, bool RES, bool OF32, bool RAG>
-__global__ void __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(SSD_LINEAR_WAVES, SSD_LINEAR_WAVES)))
+// Launch shapes: block tile BM x BN computed by a WGM x WGN grid of waves, WPS waves per
+// SIMD of register budget, and DEPTH K-tiles loaded ahead into registers.
+// RAG: a ragged K (not whole K-tiles) is supported.
+template <int BM_, int BN_, int WGM_, int WGN_, int WPS_, int DEPTH_, bool RAG_>
+struct LinShape {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, WPS = WPS_, DEPTH = DEPTH_;
+  static constexpr bool rag = RAG_;
+  static constexpr int threads = 64 * WGM * WGN;
+};
+// 128 x 128 blocks of 4 waves (two workgroups per CU), two K-tiles ahead
+using LinSmall = LinShape<SSD_LINEAR_BM, SSD_LINEAR_BN, 2, 2, SSD_LINEAR_WAVES, 2, true>;
+// 256 x 256 blocks of 8 waves with 128 x 64 wave tiles (one workgroup per CU, 147 KB of
+// double-buffered LDS), one K-tile ahead: 2.7 times fewer LDS bytes per flop than the
+// 64 x 64 wave tiles, for problems with enough blocks to fill the GPU
+using LinBig = LinShape<256, 256, 2, 4, 2, 1, false>;
+
+template <typename S, bool TA, bool TB, bool NORM, bool RES, bool OF32, bool RAG>
+__global__ void __launch_bounds__(S::threads) __attribute__((amdgpu_waves_per_eu(S::WPS, S::WPS)))
 linear_kernel(LinArgs a) {
   static_assert(!(NORM && TA), "the norm prologue needs K-contiguous rows");
   static_assert(!(NORM && RAG), "the norm prologue needs whole K-tiles");
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-block
-  constexpr int TM = WM / 16, TN = WN / 16;  // MFMA tiles per wave
-  using OA = OpTile<BM, TA>;
-  using OB = OpTile<BN, TB>;
+  constexpr int BM = S::BM, BN = S::BN, NT = S::threads;
+  constexpr int WM = BM / S::WGM, WN = BN / S::WGN;  // wave sub-block
+  constexpr int TM = WM / 16, TN = WN / 16;            // MFMA tiles per wave
+  using OA = OpTile<BM, TA, NT>;
+  using OB = OpTile<BN, TB, NT>;
   constexpr int AV = OA::pieces, BV = OB::pieces;
   // operand tiles during the K loop, double-buffered (even K-tiles in buffer 0, odd in
   // buffer 1: a tile is staged while the waves may still read the other, one barrier per
@@ -219,7 +241,7 @@ linear_kernel(LinArgs a) {
   const int64_t gm_rows = tiles_m - grp * kGroupM < kGroupM ? tiles_m - grp * kGroupM : kGroupM;
   const int64_t m0 = (grp * kGroupM + in_grp % gm_rows) * BM;
   const int64_t n0 = (in_grp / gm_rows) * BN;
-  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int wm = (wave / S::WGN) * WM, wn = (wave % S::WGN) * WN;
 
   float ss[AV];
 #pragma unroll
@@ -240,28 +262,41 @@ linear_kernel(LinArgs a) {
 #define SSD_LINEAR_STEP(ra, rb, ka, kb, kt, sA, sB)                                              \
   do {                                                                                           \
     if constexpr (NORM) norm_pieces<AV>(ra, ss, a.g + (kt) * kBK + OA::kk(tid, 0));              \
-    store_op<BM, TA, RAG>(ra, ka, sA);                                                           \
-    store_op<BN, TB, RAG>(rb, kb, sB);                                                           \
+    store_op<BM, TA, RAG, NT>(ra, ka, sA);                                                       \
+    store_op<BN, TB, RAG, NT>(rb, kb, sB);                                                       \
     __syncthreads();                                                                             \
-    const int64_t kn_ = (kt) + 2 < nk ? (kt) + 2 : nk - 1;                                      \
-    load_op<BM, TA, RAG>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                           \
-    load_op<BN, TB, RAG>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                           \
+    const int64_t kn_ = (kt) + S::DEPTH < nk ? (kt) + S::DEPTH : nk - 1;                        \
+    load_op<BM, TA, RAG, NT>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                       \
+    load_op<BN, TB, RAG, NT>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                       \
     mma_tile<TM, TN, BM, BN, TA, TB>(acc, sA, sB, wm, wn, r, kg);                                \
   } while (0)
 
-  // two tiles in flight: buffer 0 holds even tiles, buffer 1 odd ones
-  u32x4 a0[AV], b0[BV], a1[AV], b1[BV];
-  uint32_t ka0, kb0, ka1, kb1;
-  load_op<BM, TA, RAG>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
-  load_op<BN, TB, RAG>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
-  load_op<BM, TA, RAG>(a1, ka1, a.x, a.ldx, m0, a.M, (nk > 1 ? 1 : 0) * kBK, a.K);
-  load_op<BN, TB, RAG>(b1, kb1, a.w, a.ldw, n0, a.N, (nk > 1 ? 1 : 0) * kBK, a.K);
   int64_t kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
-    SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1, sA1, sB1);
+  if constexpr (S::DEPTH == 2) {
+    // two tiles in flight: register set 0 holds even tiles, set 1 odd ones
+    u32x4 a0[AV], b0[BV], a1[AV], b1[BV];
+    uint32_t ka0, kb0, ka1, kb1;
+    load_op<BM, TA, RAG, NT>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
+    load_op<BN, TB, RAG, NT>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
+    load_op<BM, TA, RAG, NT>(a1, ka1, a.x, a.ldx, m0, a.M, (nk > 1 ? 1 : 0) * kBK, a.K);
+    load_op<BN, TB, RAG, NT>(b1, kb1, a.w, a.ldw, n0, a.N, (nk > 1 ? 1 : 0) * kBK, a.K);
+    for (; kt + 1 < nk; kt += 2) {
+      SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
+      SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1, sA1, sB1);
+    }
+    if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
+  } else {
+    // one tile in flight; the LDS buffers still alternate
+    u32x4 a0[AV], b0[BV];
+    uint32_t ka0, kb0;
+    load_op<BM, TA, RAG, NT>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
+    load_op<BN, TB, RAG, NT>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
+    for (; kt + 1 < nk; kt += 2) {
+      SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
+      SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt + 1, sA1, sB1);
+    }
+    if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
   }
-  if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
 #undef SSD_LINEAR_STEP
 
   if constexpr (NORM) {
@@ -321,8 +356,8 @@ linear_kernel(LinArgs a) {
     uint16_t* y = static_cast<uint16_t*>(a.y);
     constexpr int kPieces = BM * BN / 8;
 #pragma unroll
-    for (int q = 0; q < kPieces / kLinThreads; ++q) {
-      const int p = tid + kLinThreads * q;
+    for (int q = 0; q < kPieces / NT; ++q) {
+      const int p = tid + NT * q;
       const int row = p / (BN / 8), c8 = 8 * (p % (BN / 8));
       const int64_t gm = m0 + row;
       const int64_t gn = n0 + c8;
@@ -332,20 +367,32 @@ linear_kernel(LinArgs a) {
   }
 }
 
-template <bool TA, bool TB, bool NORM, bool RES, bool OF32>
-hipError_t launch_linear_t(const LinArgs& a0, hipStream_t s) {
-  constexpr int BM = SSD_LINEAR_BM, BN = SSD_LINEAR_BN;
+template <typename S, bool TA, bool TB, bool NORM, bool RES, bool OF32>
+hipError_t launch_linear_s(const LinArgs& a0, hipStream_t s) {
   LinArgs a = a0;
-  a.tiles_n = static_cast<int>((a.N + BN - 1) / BN);
-  a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
-  const dim3 grid(static_cast<unsigned>(a.tiles)), block(kLinThreads);
+  a.tiles_n = static_cast<int>((a.N + S::BN - 1) / S::BN);
+  a.tiles = ((a.M + S::BM - 1) / S::BM) * a.tiles_n;
+  const dim3 grid(static_cast<unsigned>(a.tiles)), block(S::threads);
   if (a.K % kBK == 0)
-    hipLaunchKernelGGL((linear_kernel<BM, BN, TA, TB, NORM, RES, OF32, false>), grid, block, 0, s, a);
-  else if constexpr (!NORM)
-    hipLaunchKernelGGL((linear_kernel<BM, BN, TA, TB, NORM, RES, OF32, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((linear_kernel<S, TA, TB, NORM, RES, OF32, false>), grid, block, 0, s, a);
+  else if constexpr (!NORM && S::rag)
+    hipLaunchKernelGGL((linear_kernel<S, TA, TB, NORM, RES, OF32, true>), grid, block, 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// The big blocks where they make at least four full waves of workgroups (one per CU),
+// no operand is smaller than a block, K is whole K-tiles and there is no norm prologue
+// (those variants do not fit the big blocks' registers); the small ones otherwise.
+template <bool TA, bool TB, bool NORM, bool RES, bool OF32>
+hipError_t launch_linear_t(const LinArgs& a, hipStream_t s) {
+  if constexpr (!NORM) {
+    const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    if (SSD_LINEAR_BIG && a.M >= 256 && a.N >= 256 && a.K % kBK == 0 && big_tiles >= 4 * 256)
+      return launch_linear_s<LinBig, TA, TB, NORM, RES, OF32>(a, s);
+  }
+  return launch_linear_s<LinSmall, TA, TB, NORM, RES, OF32>(a, s);
 }
 
 }  // namespace
