@@ -128,6 +128,7 @@ PROBE_TOKENS = 16384
 PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
     ("conv_fwd_kernel<bf16_t, 4>", 0): "conv pre-pass (fwd: B, C)",
     ("conv_fwd_kernel<bf16_t, 4>", 1): "conv pre-pass (bwd: x, B, C)",
+    ("dt_prepass_kernel<bf16_t>", 0): "dt table (fwd)",
     ("walk_kernel<bf16_t, 64, 128, 0>", 0): "walk_state (fwd)",
     ("walk_kernel<bf16_t, 64, 128, 1>", 0): "walk_out (fwd)",
     ("scan_kernel", 0): "scan (fwd, sub-segments)",
@@ -137,8 +138,10 @@ PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
     ("scan_rev_kernel", 0): "scan_rev (bwd)",
     ("bwd_main_kernel<bf16_t, 64, 128, 8>", 0): "bwd_main (bwd)",
     ("conv_bwd_kernel<bf16_t, true>", 0): "conv_bwd (bwd)",
-    ("linear_kernel<128, 128, false, false, false, false, false, false>", 0): "in_proj 8192x4384x1024",
-    ("linear_kernel<128, 128, false, false, false, false, false, false>", 1): "out_proj 8192x1024x2048",
+    ("linear_kernel<LinShape<128, 128, 2, 2, 2, 2, true>, false, false, false, false, false, false>", 0):
+        "in_proj 8192x4384x1024",
+    ("linear_kernel<LinShape<128, 128, 2, 2, 2, 2, true>, false, false, false, false, false, false>", 1):
+        "out_proj 8192x1024x2048",
 }
 # algorithmic bytes per token of each kernel's own inputs and outputs (bf16, d_model 1024
 # shapes; fp16 in-group states of 64 x 128 per chunk of 64 and head, 32 heads)
@@ -146,8 +149,9 @@ _STATE = 32 * 64 * 128 * 2 // 64
 PROBE_ALG_BYTES_PER_TOKEN = {
     "conv pre-pass (fwd: B, C)": 512 + 512,
     "conv pre-pass (bwd: x, B, C)": 4608 + 4096 + 512 + 512,
-    "walk_state (fwd)": 4096 + 256 + 64,
-    "walk_out (fwd)": 4608 + 4096 + 64 + 4096,
+    "dt table (fwd)": 64 + 128,
+    "walk_state (fwd)": 4096 + 256 + 128,
+    "walk_out (fwd)": 4608 + 4096 + 128 + 4096,
     "chunk_states (bwd)": 4096 + 256 + 64 + _STATE,
     "dstate (bwd)": 512 + 4096 + 4096 + 64 + _STATE,
     "bwd_main (bwd)": 4096 + 768 + 4096 + 4096 + 64 + 2 * _STATE + 4096 + 4096 + 64 + 1024,
