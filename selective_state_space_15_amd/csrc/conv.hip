@@ -67,7 +67,11 @@ __global__ void __launch_bounds__(256) conv_fwd_kernel(ConvFwdArgs a) {
   static_assert(K >= 1 && K <= 4, "taps are right-aligned on 4");
   const int ncv = a.C / V;
   const int64_t ntile = (a.L + kRowsF - 1) / kRowsF;
-  const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  // consecutive workgroups (consecutive row tiles) on one XCD: each XCD writes one
+  // contiguous token range, the range the chunk kernels after it (xcd_remap over
+  // chunks or chunk groups) give to the same XCD, so part of what they read of these
+  // rows is still in that XCD's L2
+  const int64_t gid = xcd_remap(blockIdx.x, gridDim.x) * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (gid >= a.B * ntile * ncv) return;
   const int cv = static_cast<int>(gid % ncv);
   const int64_t tile = (gid / ncv) % ntile;
@@ -245,7 +249,9 @@ __global__ void __launch_bounds__(256) conv_bwd_kernel(ConvBwdArgs a) {
   const int nxb = (xlim + kTileCh - 1) / kTileCh;
   const int ncb = nxb + (FUSED ? (a.C - a.hp + kTileCh - 1) / kTileCh : 0);
   const int64_t ntile = (a.L + kTileRows - 1) / kTileRows;
-  const int64_t wg = blockIdx.x;
+  // consecutive workgroups on one XCD: one contiguous token range per XCD, as in the
+  // chunk kernels before it
+  const int64_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int cb = static_cast<int>(wg % ncb);
   const int64_t tile = (wg / ncb) % ntile;
   const int64_t b = wg / (static_cast<int64_t>(ncb) * ntile);
