@@ -343,19 +343,32 @@ __global__ void __launch_bounds__(NW * kWave) bwd_main_kernel(BwdArgs a) {
     lds_put_row<IO>((seg == 1 ? sB : sC) + s * ldN + cl, o);
   });
   const bool clo = SPLIT && pr.bc_lo.p != nullptr;
+  // B's low part too, where the dout silu'(z) tile (not yet in use) can hold a B tile:
+  // C B^T, shared by every head of the block, is then (C + C_lo)(B + B_lo)^T less the
+  // C_lo B_lo^T term, at about 16 bits
+  constexpr bool kBlo = SPLIT && kQ * ldG * sizeof(float) >= kQ * ldN * sizeof(Lt);
+  Lt* const sBlo = reinterpret_cast<Lt*>(sG2);
   if (clo) {
     Problem prl = pr;
     prl.bc = pr.bc_lo;
     conv_rows<IO, P, N, false, false, true, kThreads>(prl, b, 0, g, t0, [&](int, int s, int cl, const float* o) {
       lds_put_row<IO>(sClo + s * ldN + cl, o);
     });
+    if constexpr (kBlo)
+      conv_rows<IO, P, N, false, true, false, kThreads>(prl, b, 0, g, t0, [&](int, int s, int cl, const float* o) {
+        lds_put_row<IO>(sBlo + s * ldN + cl, o);
+      });
   }
   __syncthreads();
   f32x4 cb[QJw];  // (C B^T)[t in rows m0.., s in this wave's half]
 #pragma unroll
   for (int j = 0; j < QJw; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sC, ldN, m0, sB, ldN, s0, N);
-  if (clo) mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sClo, ldN, m0, sB, ldN, s0, N);
+  if (clo) {
+    mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sClo, ldN, m0, sB, ldN, s0, N);
+    if constexpr (kBlo) mma_strip<Lt, true, true, QJw, kMainUnroll>(cb, sC, ldN, m0, sBlo, ldN, s0, N);
+  }
+  if constexpr (kBlo) __syncthreads();  // the first head's staging rewrites the B_lo tile
 
   f32x4 accdB[NTw], accdC[NTw];
 #pragma unroll
