@@ -101,14 +101,34 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   const float dtb = pr.dt_bias ? pr.dt_bias[h] : 0.f;
   const E* xbc = static_cast<const E*>(pr.xbc.p);
   const E* dtp = static_cast<const E*>(pr.dt.p);
-  const E* zp = static_cast<const E*>(pr.z.p);
+  const bool gate = pr.z.p != nullptr;
+  // without a gate the (unused) z loads read this row's x channel, always valid
+  const E* zsrc = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb + h * P + p
+                       : xbc + b * pr.xbc.sb + h * P + p;
+  const int64_t zst = gate ? pr.z.st : pr.xbc.st;
+  // A token's raw row, dt and z are loaded one token ahead, unconditionally (the last
+  // token reloads itself): with the state loads above they are all in flight at once,
+  // instead of dt and z each waiting a memory round trip after the conv.
+  E rawn[CPT], dtn, zn;
+  auto issue_tok = [&](int64_t t) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) rawn[i] = xbc[b * pr.xbc.sb + t * pr.xbc.st + ch[i]];
+    dtn = dtp[b * pr.dt.sb + t * pr.dt.st + h];
+    zn = zsrc[t * zst];
+  };
+  issue_tok(0);
 
   for (int64_t t = 0; t < pr.L; ++t) {
+    E rawc[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) rawc[i] = rawn[i];
+    const E dtc = dtn, zc = zn;
+    issue_tok(t + 1 < pr.L ? t + 1 : t);
     // post-conv x, B, C of token t
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       if (!live[i]) continue;
-      const float raw = io_traits<IO>::to_f(xbc[b * pr.xbc.sb + t * pr.xbc.st + ch[i]]);
+      const float raw = io_traits<IO>::to_f(rawc[i]);
       float v = raw;
       if constexpr (K > 0) {
         float pre = bias[i] + wk[i][K - 1] * raw;
@@ -125,7 +145,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
       else s_C[j - kRows - N] = v;
     }
     __syncthreads();
-    float dt = io_traits<IO>::to_f(dtp[b * pr.dt.sb + t * pr.dt.st + h]) + dtb;
+    float dt = io_traits<IO>::to_f(dtc) + dtb;
     if (pr.softplus) dt = softplusf_(dt);
     const float decay = __expf(dt * A);
     const float dtx = dt * s_x[pl];
@@ -138,7 +158,7 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
     const float y = sum_lanes<NT>(acc) + Dh * s_x[pl];
     if (tid % NT == 0) {
       float o = y;
-      if (zp) o *= siluf_(io_traits<IO>::to_f(zp[b * pr.z.sb + t * pr.z.st + h * P + p]));
+      if (gate) o *= siluf_(io_traits<IO>::to_f(zc));
       static_cast<E*>(a.out.p)[b * a.out.sb + t * a.out.st + h * P + p] = io_traits<IO>::from_f(o);
     }
     __syncthreads();  // the next token rewrites s_x / s_B / s_C

@@ -94,3 +94,56 @@ def test_decode_c4_shapes_batch16():
     """d_model 2560 shapes (80 heads), batch 16, 40 tokens one at a time."""
     d = synth.CONFIGS["c4"].with_(L=40)
     check_decode(Case(d, seed=84, states=True), [1] * 40)
+
+
+def test_decode_steps_replayed_from_a_hip_graph():
+    """A serving loop's form of decode: 16 one-token ssd_decode calls captured once in a
+    HIP graph (torch.cuda.CUDAGraph; the library launches on the stream it is given),
+    then replayed from three different carried states, each written into the captured
+    buffers by eager copies between replays.  Every replay must equal the same 16 calls
+    made eagerly from that state, bitwise: the same kernels on the same inputs."""
+    d = synth.CONFIGS["c1"].with_(B=2, L=16)
+    case = Case(d, seed=85, states=True)
+    _, z, xbc, dt = case.dev_inputs()
+    p = {k: fdev(v) for k, v in case.p.items()}
+    dims = bd.make_dims(d.B, 1, d.H, d.P, d.N, d.G, 0, d.K)
+
+    def steps(h, cs, out):
+        for t in range(d.L):
+            sl = slice(t, t + 1)
+            bd.ssd_decode(dims, xbc[:, sl], p["A"], dt[:, sl], out[:, sl], h, conv_w=p["conv_w"],
+                          conv_b=p["conv_b"], conv_state_in=cs[t % 2], conv_state_out=cs[(t + 1) % 2],
+                          dt_bias=p["dt_bias"], D=p["D"], z=z[:, sl], h_in=h)
+
+    def buffers():
+        return (torch.zeros(d.B, d.H, d.P, d.N, device="cuda"),
+                [torch.zeros(d.B, d.K - 1, d.cd, dtype=torch.bfloat16, device="cuda") for _ in range(2)],
+                torch.zeros(d.B, d.L, d.hp, dtype=torch.bfloat16, device="cuda"))
+
+    h, cs, out = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        steps(*buffers())  # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(h, cs, out)
+    gen = torch.Generator().manual_seed(86)
+    for r in range(3):
+        h0 = torch.randn(d.B, d.H, d.P, d.N, generator=gen).mul_(0.5 * (r + 1)).cuda()
+        c0 = torch.randn(d.B, d.K - 1, d.cd, generator=gen).to(torch.bfloat16).cuda()
+        h.copy_(h0)
+        cs[0].copy_(c0)
+        graph.replay()
+        torch.cuda.synchronize()
+        he, cse, oute = buffers()
+        he.copy_(h0)
+        cse[0].copy_(c0)
+        steps(he, cse, oute)
+        torch.cuda.synchronize()
+        last = d.L % 2
+        print(f"[decode graph] replay {r}: out max |diff| {(out.float() - oute.float()).abs().max().item():.3e}",
+              flush=True)
+        assert torch.equal(out, oute) and torch.equal(h, he) and torch.equal(cs[last], cse[last]), r
+        assert torch.isfinite(out.float()).all()
