@@ -13,8 +13,8 @@
 // which is the recurrence of the forward pass taken one step at a time.
 //
 // The rows p of a head's state are independent given B, C and dt, so one workgroup of
-// 256 threads owns kRows rows of one (batch, head): those rows of the fp32 state live
-// in registers for the whole call (N / (256 / kRows) elements per thread), each conv
+// 16 threads per row owns ROWS rows of one (batch, head): those rows of the fp32 state
+// live in registers for the whole call (N / 16 elements per thread), each conv
 // channel keeps its window of K-1 raw inputs in registers, and the post-conv x, B and C
 // of the current token pass through LDS.  The state is read once and written once per
 // call, whatever the number of tokens.  The B / C conv runs in every workgroup of the
@@ -25,8 +25,11 @@
 namespace ssd {
 namespace {
 
-constexpr int kDecThreads = 256;
-constexpr int kRows = 16;  // state rows (head channels p) per workgroup
+// 16 lanes per state row; ROWS state rows (head channels p) per workgroup: 16 (P/16
+// workgroups per head) for few (batch, head) pairs, all P (one workgroup per head, 16 P
+// threads) when there are enough heads to fill the GPU, which repeats the B / C conv
+// P/16 times less
+constexpr int kRowLanes = 16;
 
 struct DecodeArgs {
   Problem pr;          // L = tokens in this call; h0 = state in (null = zeros)
@@ -45,8 +48,10 @@ __device__ __forceinline__ float sum_lanes(float v) {
   return v;
 }
 
-template <typename IO, int P, int N, int K>
-__global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
+template <typename IO, int P, int N, int K, int ROWS>
+__global__ void __launch_bounds__(kRowLanes * ROWS) decode_kernel(DecodeArgs a) {
+  constexpr int kDecThreads = kRowLanes * ROWS;
+  constexpr int kRows = ROWS;
   using E = typename io_traits<IO>::elem;
   constexpr int SPLIT = P / kRows;      // workgroups per (batch, head)
   constexpr int NT = kDecThreads / kRows;  // threads per state row p
@@ -180,17 +185,24 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(DecodeArgs a) {
   }
 }
 
-template <typename IO, int P, int N>
-hipError_t launch_decode_pn(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H * (P / kRows)));
+template <typename IO, int P, int N, int ROWS>
+hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H * (P / ROWS))), block(kRowLanes * ROWS);
   switch (a.pr.K) {
-    case 0: hipLaunchKernelGGL((decode_kernel<IO, P, N, 0>), grid, dim3(kDecThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<IO, P, N, 2>), grid, dim3(kDecThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<IO, P, N, 3>), grid, dim3(kDecThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<IO, P, N, 4>), grid, dim3(kDecThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((decode_kernel<IO, P, N, 0, ROWS>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<IO, P, N, 2, ROWS>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<IO, P, N, 3, ROWS>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<IO, P, N, 4, ROWS>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename IO, int P, int N>
+hipError_t launch_decode_pn(const DecodeArgs& a, hipStream_t s) {
+  // whole heads from 512 (batch, head) pairs on (two or more workgroups per CU)
+  if (static_cast<int64_t>(a.pr.B) * a.pr.H >= 512) return launch_decode_rows<IO, P, N, P>(a, s);
+  return launch_decode_rows<IO, P, N, 16>(a, s);
 }
 
 template <typename IO>

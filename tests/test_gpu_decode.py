@@ -84,6 +84,13 @@ def test_decode_other_shapes(P, N, G):
     check_decode(Case(d, seed=82, states=True), [1] * 64 + [66])
 
 
+def test_decode_whole_head_workgroups_p32():
+    """512 (batch, head) pairs take one workgroup per head (16 P threads); here with
+    P = 32, N = 64 and two groups, one token per call and a multi-token call."""
+    d = synth.Dims(B=8, L=12, H=64, P=32, N=64, G=2, K=4, d_model=1024)
+    check_decode(Case(d, seed=87, states=True), [1] * 8 + [4])
+
+
 def test_decode_fp32_no_conv_no_gate():
     """The fp32 single-scan configuration (4 heads x 32, d_state 16, no conv, no gate)."""
     d = synth.CONFIGS["c0"].with_(L=96)
