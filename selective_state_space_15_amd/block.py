@@ -22,6 +22,21 @@ from . import binding as bd
 
 EPS = 1e-5
 
+# A projection whose plain form (no norm prologue) runs on mixer_proj's 256 x 256 MFMA
+# blocks -- at least 1,024 of them, both dimensions >= 256, K a multiple of 64 -- is
+# faster as a norm pass of its own followed by the plain product than with the norm
+# folded into the product (whose registers only fit the 128 x 128 blocks).
+BIG_BLOCKS = 1024
+
+
+def _big_blocks(M: int, N: int, K: int) -> bool:
+    return M >= 256 and N >= 256 and K % 64 == 0 and -(-M // 256) * -(-N // 256) >= BIG_BLOCKS
+
+
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
 
 @dataclass
 class Shape:
@@ -104,20 +119,32 @@ def _hot_views(sh: Shape, zx: torch.Tensor, B: int, L: int):
 def block_fwd(sh: Shape, w: Weights, u: torch.Tensor, final: torch.Tensor, sc: Scratch, *, h0=None,
               conv_state=None, h_final=None, conv_state_out=None, eps=EPS):
     """final [B, L, d_model] = block(u [B, L, d_model]); the norm before in_proj is fused
-    into the projection's operand load, the gated norm and the residual into out_proj."""
+    into the projection's operand load, the gated norm and the residual into out_proj --
+    or, for projections large enough for the big MFMA blocks, each norm is a pass of its
+    own: u's into final's buffer (unused until out_proj writes it; final must then not
+    overlap u), the output's in place in the scratch."""
     B, L, dm = u.shape
     _contig(u, final)
     n = B * L
     if n > sc.B * sc.T:
         raise ValueError(f"{n} tokens exceed the scratch of {sc.B * sc.T}")
     zx = sc.zx[:n]
-    bd.mixer_proj(u.reshape(n, dm), w.w_in, zx, norm_w=w.norm_in, norm_eps=eps)
+    u2, f2 = u.reshape(n, dm), final.reshape(n, dm)
+    if _big_blocks(n, sh.dip, dm) and not _overlap(u, final):
+        bd.rmsnorm_fwd(u2, w.norm_in, f2, eps=eps)
+        bd.mixer_proj(f2, w.w_in, zx)
+    else:
+        bd.mixer_proj(u2, w.w_in, zx, norm_w=w.norm_in, norm_eps=eps)
     z, xbc, dt = _hot_views(sh, zx, B, L)
     out = sc.out[:n].view(B, L, sh.hp)
     bd.ssd_fwd(_dims(sh, B, L), xbc, w.A, dt, out, conv_w=w.conv_w, conv_b=w.conv_b, conv_state_in=conv_state,
                conv_state_out=conv_state_out, dt_bias=w.dt_bias, D=w.D, z=z, h0=h0, h_final=h_final, ws=sc.fws)
-    bd.mixer_proj(out.view(n, sh.hp), w.w_out, final.reshape(n, dm), norm_w=w.norm_out, norm_eps=eps,
-                  residual=u.reshape(n, dm))
+    o2 = out.view(n, sh.hp)
+    if _big_blocks(n, dm, sh.hp):
+        bd.rmsnorm_fwd(o2, w.norm_out, o2, eps=eps)
+        bd.mixer_proj(o2, w.w_out, f2, residual=u2)
+    else:
+        bd.mixer_proj(o2, w.w_out, f2, norm_w=w.norm_out, norm_eps=eps, residual=u2)
 
 
 def block_bwd(sh: Shape, w: Weights, u: torch.Tensor, dfinal: torch.Tensor, du: torch.Tensor, grads: dict,

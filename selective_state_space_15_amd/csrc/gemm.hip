@@ -382,14 +382,19 @@ hipError_t launch_linear_s(const LinArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The big blocks where they make at least four full waves of workgroups (one per CU),
-// no operand is smaller than a block, K is whole K-tiles and there is no norm prologue
-// (those variants do not fit the big blocks' registers); the small ones otherwise.
+// The big blocks where they make at least four full waves of workgroups (one per CU), or
+// half a wave for long K, no operand is smaller than a block, K is whole K-tiles and
+// there is no norm prologue (those variants do not fit the big blocks' registers); the
+// small ones otherwise.
 template <bool TA, bool TB, bool NORM, bool RES, bool OF32>
 hipError_t launch_linear_t(const LinArgs& a, hipStream_t s) {
   if constexpr (!NORM) {
     const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    if (SSD_LINEAR_BIG && a.M >= 256 && a.N >= 256 && a.K % kBK == 0 && big_tiles >= 4 * 256)
+    // long K (the weight gradients over a whole batch of tokens): a block's work is long
+    // enough that half the CUs with big blocks beat the small ones (65,536 tokens: 650 ->
+    // 930 TFLOP/s at 200 and 420 blocks)
+    const bool enough = big_tiles >= 4 * 256 || (a.K >= 16384 && big_tiles >= 128);
+    if (SSD_LINEAR_BIG && a.M >= 256 && a.N >= 256 && a.K % kBK == 0 && enough)
       return launch_linear_s<LinBig, TA, TB, NORM, RES, OF32>(a, s);
   }
   return launch_linear_s<LinSmall, TA, TB, NORM, RES, OF32>(a, s);

@@ -87,11 +87,15 @@ def oracle_block_bwd(d, u, wts, prm, dF, st):
                          dconv_state_out=f(st["dconv_state"]))
 
 
-@pytest.mark.parametrize("name", ["small", "c1", "c4"])
-def test_block_fwd_bwd(name):
+@pytest.mark.parametrize("name", ["small", "c1", "c4", "c1-prenorm"])
+def test_block_fwd_bwd(name, monkeypatch):
+    if name == "c1-prenorm":
+        # the forward's norms as passes of their own (rmsnorm_fwd, then plain products),
+        # the form large projections take
+        monkeypatch.setattr(block, "BIG_BLOCKS", 1)
     if name == "small":
         d = synth.Dims(B=2, L=777, H=8, P=32, N=64, G=1, K=4, d_model=256)
-    elif name == "c1":
+    elif name in ("c1", "c1-prenorm"):
         d = synth.CONFIGS["c1"]
     else:  # the batched 2.7B-style shapes (d_model 2560, 80 heads) at batch 2, L = 1000
         d = synth.CONFIGS["c4"].with_(B=2, L=1000)
