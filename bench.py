@@ -15,6 +15,10 @@ measurements that are not the headline:
   c1_mixer in_proj -> hot path -> out_proj at L = 8192 (MFMA projections; the working
            set fits the 256 MB last-level cache)
   decode   one-token streaming decode latency at d_model 1024 and the 80-head shapes
+           (per call from Python, and per step replayed from a HIP graph)
+  magc     peak memory and training rate of a 48-block stack under multi-axis
+           gradient checkpointing
+  copy_ceiling  a plain 4 GiB device copy and fill, the practical HBM ceiling
 and the fp64 oracle timed on a bounded prefix on the host cores (all of them, and one).
 """
 from __future__ import annotations
@@ -284,6 +288,8 @@ def main():
         print("[bench] decode done", file=sys.stderr, flush=True)
         res["magc"] = bench_magc(args, stream)
         print("[bench] magc done", file=sys.stderr, flush=True)
+        res["copy_ceiling"] = bench_copy(stream)
+        print("[bench] copy ceiling done", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if args.cpu_sample > 0:
@@ -511,6 +517,25 @@ def bench_decode(args, stream):
                              "us_per_call); us_per_token_graph: 32 such steps captured in a HIP graph "
                              "and replayed; the kernel reads and writes the state once per call"}
     return res
+
+
+def bench_copy(stream):
+    """The practical HBM ceiling: a plain device copy of 4 GiB (reads plus writes) and a
+    4 GiB fill, median of 5 (torch's own copy and fill kernels)."""
+    import numpy as np
+    import torch
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=stream.device)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    cp = timed(lambda: dst.copy_(src), 5, stream)
+    fl = timed(lambda: dst.fill_(2), 5, stream)
+    del src, dst
+    torch.cuda.empty_cache()
+    c_ms, f_ms = float(np.median(cp)), float(np.median(fl))
+    return {"copy_bytes": n, "copy_GBs": 2 * n / (c_ms * 1e-3) / 1e9, "fill_GBs": n / (f_ms * 1e-3) / 1e9,
+            "peak_GBs": 8000.0, "note": "reads plus writes of a 4 GiB device copy; a context ceiling, "
+                                         "the rooflines use the published 8 TB/s"}
 
 
 def bench_magc(args, stream):

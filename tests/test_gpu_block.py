@@ -24,7 +24,9 @@ def bits_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 4384, 1024), (777, 1024, 2048), (333, 648, 256)])
+# the last case's weight gradient (K = 16,384 tokens, 17 x 9 blocks of 256 with ragged
+# edges) takes the big 256 x 256 blocks of the long-K rule
+@pytest.mark.parametrize("M,N,K", [(1000, 4384, 1024), (777, 1024, 2048), (333, 648, 256), (16384, 4104, 2104)])
 def test_mixer_proj_bwd(M, N, K):
     r = np.random.default_rng(M + N)
     dy = synth.bf16_bits(r.standard_normal((M, N)).astype(np.float32))
