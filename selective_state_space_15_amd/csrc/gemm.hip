@@ -21,6 +21,8 @@
 // and column indices past M / N are clamped for the loads and masked at the store.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -204,7 +206,7 @@ using LinSmall = LinShape<SSD_LINEAR_BM, SSD_LINEAR_BN, 2, 2, SSD_LINEAR_WAVES, 
 // 256 x 256 blocks of 8 waves with 128 x 64 wave tiles (one workgroup per CU, 147 KB of
 // double-buffered LDS), one K-tile ahead: 2.7 times fewer LDS bytes per flop than the
 // 64 x 64 wave tiles, for problems with enough blocks to fill the GPU
-using LinBig = LinShape<256, 256, 2, 4, 2, 1, false>;
+using LinBig = LinShape<256, 256, 2, 4, 2, 1, true>;
 
 template <typename S, bool TA, bool TB, bool NORM, bool RES, bool OF32, bool RAG>
 __global__ void __launch_bounds__(S::threads) __attribute__((amdgpu_waves_per_eu(S::WPS, S::WPS)))
@@ -259,17 +261,18 @@ linear_kernel(LinArgs a) {
   // visible, and every wave is past the MFMAs of the tile two back, which used this
   // buffer), refill the registers with the tile two ahead (clamped to the last: no
   // branch), then the MFMAs on the staged tile.
-#define SSD_LINEAR_STEP(ra, rb, ka, kb, kt, sA, sB)                                              \
+#define SSD_LINEAR_STEPR(ra, rb, ka, kb, kt, sA, sB, R, NKT)                                     \
   do {                                                                                           \
     if constexpr (NORM) norm_pieces<AV>(ra, ss, a.g + (kt) * kBK + OA::kk(tid, 0));              \
-    store_op<BM, TA, RAG, NT>(ra, ka, sA);                                                       \
-    store_op<BN, TB, RAG, NT>(rb, kb, sB);                                                       \
+    store_op<BM, TA, R, NT>(ra, ka, sA);                                                         \
+    store_op<BN, TB, R, NT>(rb, kb, sB);                                                         \
     __syncthreads();                                                                             \
-    const int64_t kn_ = (kt) + S::DEPTH < nk ? (kt) + S::DEPTH : nk - 1;                        \
-    load_op<BM, TA, RAG, NT>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                       \
-    load_op<BN, TB, RAG, NT>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                       \
+    const int64_t kn_ = (kt) + S::DEPTH < (NKT) ? (kt) + S::DEPTH : (NKT) - 1;                  \
+    load_op<BM, TA, R, NT>(ra, ka, a.x, a.ldx, m0, a.M, kn_ * kBK, a.K);                         \
+    load_op<BN, TB, R, NT>(rb, kb, a.w, a.ldw, n0, a.N, kn_ * kBK, a.K);                         \
     mma_tile<TM, TN, BM, BN, TA, TB>(acc, sA, sB, wm, wn, r, kg);                                \
   } while (0)
+#define SSD_LINEAR_STEP(ra, rb, ka, kb, kt, sA, sB) SSD_LINEAR_STEPR(ra, rb, ka, kb, kt, sA, sB, RAG, nk)
 
   int64_t kt = 0;
   if constexpr (S::DEPTH == 2) {
@@ -285,19 +288,43 @@ linear_kernel(LinArgs a) {
       SSD_LINEAR_STEP(a1, b1, ka1, kb1, kt + 1, sA1, sB1);
     }
     if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
-  } else {
+  } else if constexpr (!RAG) {
     // one tile in flight; the LDS buffers still alternate
     u32x4 a0[AV], b0[BV];
     uint32_t ka0, kb0;
-    load_op<BM, TA, RAG, NT>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
-    load_op<BN, TB, RAG, NT>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
+    load_op<BM, TA, false, NT>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
+    load_op<BN, TB, false, NT>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
     for (; kt + 1 < nk; kt += 2) {
       SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
       SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt + 1, sA1, sB1);
     }
     if (kt < nk) SSD_LINEAR_STEP(a0, b0, ka0, kb0, kt, sA0, sB0);
+  } else {
+    // ragged K, one tile in flight: every K-tile but the last is whole, so the loop runs
+    // over those with the whole-tile loads and stores (the masked forms do not fit these
+    // blocks' registers), and the last tile is loaded, masked and multiplied after it.
+    u32x4 a0[AV], b0[BV];
+    uint32_t ka0 = 0, kb0 = 0;
+    const int64_t nw = nk - 1;  // whole K-tiles
+    if (nw > 0) {
+      load_op<BM, TA, false, NT>(a0, ka0, a.x, a.ldx, m0, a.M, 0, a.K);
+      load_op<BN, TB, false, NT>(b0, kb0, a.w, a.ldw, n0, a.N, 0, a.K);
+      for (; kt + 1 < nw; kt += 2) {
+        SSD_LINEAR_STEPR(a0, b0, ka0, kb0, kt, sA0, sB0, false, nw);
+        SSD_LINEAR_STEPR(a0, b0, ka0, kb0, kt + 1, sA1, sB1, false, nw);
+      }
+      if (kt < nw) SSD_LINEAR_STEPR(a0, b0, ka0, kb0, kt, sA0, sB0, false, nw);
+    }
+    load_op<BM, TA, true, NT>(a0, ka0, a.x, a.ldx, m0, a.M, nw * kBK, a.K);
+    load_op<BN, TB, true, NT>(b0, kb0, a.w, a.ldw, n0, a.N, nw * kBK, a.K);
+    __syncthreads();  // every wave is past the MFMAs that read buffer 0
+    store_op<BM, TA, true, NT>(a0, ka0, sA0);
+    store_op<BN, TB, true, NT>(b0, kb0, sB0);
+    __syncthreads();
+    mma_tile<TM, TN, BM, BN, TA, TB>(acc, sA0, sB0, wm, wn, r, kg);
   }
 #undef SSD_LINEAR_STEP
+#undef SSD_LINEAR_STEPR
 
   if constexpr (NORM) {
 #pragma unroll
@@ -383,9 +410,8 @@ hipError_t launch_linear_s(const LinArgs& a0, hipStream_t s) {
 }
 
 // The big blocks where they make at least four full waves of workgroups (one per CU), or
-// half a wave for long K, no operand is smaller than a block, K is whole K-tiles and
-// there is no norm prologue (those variants do not fit the big blocks' registers); the
-// small ones otherwise.
+// half a wave for long K, no operand is smaller than a block and there is no norm
+// prologue (it does not fit the big blocks' registers); the small ones otherwise.
 template <bool TA, bool TB, bool NORM, bool RES, bool OF32>
 hipError_t launch_linear_t(const LinArgs& a, hipStream_t s) {
   if constexpr (!NORM) {
@@ -394,7 +420,7 @@ hipError_t launch_linear_t(const LinArgs& a, hipStream_t s) {
     // enough that half the CUs with big blocks beat the small ones (65,536 tokens: 650 ->
     // 930 TFLOP/s at 200 and 420 blocks)
     const bool enough = big_tiles >= 4 * 256 || (a.K >= 16384 && big_tiles >= 128);
-    if (SSD_LINEAR_BIG && a.M >= 256 && a.N >= 256 && a.K % kBK == 0 && enough)
+    if (SSD_LINEAR_BIG && a.M >= 256 && a.N >= 256 && enough)
       return launch_linear_s<LinBig, TA, TB, NORM, RES, OF32>(a, s);
   }
   return launch_linear_s<LinSmall, TA, TB, NORM, RES, OF32>(a, s);

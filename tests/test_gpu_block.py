@@ -24,9 +24,10 @@ def bits_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
-# the last case's weight gradient (K = 16,384 tokens, 17 x 9 blocks of 256 with ragged
-# edges) takes the big 256 x 256 blocks of the long-K rule
-@pytest.mark.parametrize("M,N,K", [(1000, 4384, 1024), (777, 1024, 2048), (333, 648, 256), (16384, 4104, 2104)])
+# the last two cases' weight gradients (K = 16,384 and a ragged 16,392 tokens, 17 x 9
+# blocks of 256 with ragged edges) take the big 256 x 256 blocks of the long-K rule
+@pytest.mark.parametrize("M,N,K", [(1000, 4384, 1024), (777, 1024, 2048), (333, 648, 256), (16384, 4104, 2104),
+                                   (16392, 4104, 2104)])
 def test_mixer_proj_bwd(M, N, K):
     r = np.random.default_rng(M + N)
     dy = synth.bf16_bits(r.standard_normal((M, N)).astype(np.float32))
@@ -43,6 +44,24 @@ def test_mixer_proj_bwd(M, N, K):
     e = dict(dx=rel_l2(to_host(dx), rdx), dw=rel_l2(to_host(dw), rdw))
     print(f"[proj_bwd] M={M} N={N} K={K} " + " ".join(f"{k}={v:.2e}" for k, v in e.items()), flush=True)
     assert all(v <= TOL["bf16"] for v in e.values()), e
+
+
+@pytest.mark.parametrize("K", [8, 72, 200])
+def test_mixer_proj_big_blocks_ragged_k(K):
+    """dx = dy w with 8,192 x 8,192 outputs (1,024 blocks of 256 x 256: the big blocks) and
+    a reduction (the projection's output width) that ends inside its last K-tile of 64:
+    none, one or three whole tiles before it."""
+    M = N = 8192
+    r = np.random.default_rng(K)
+    dy = synth.bf16_bits(r.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((0.1 * r.standard_normal((K, N))).astype(np.float32))
+    dx = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    bd.mixer_proj_bwd(bits_dev(dy), w=bits_dev(w), dx=dx)
+    torch.cuda.synchronize()
+    f = lambda a: synth.bf16_to_f32(a).astype(np.float64)
+    e = rel_l2(to_host(dx), f(dy) @ f(w))
+    print(f"[proj ragged K] K={K} dx={e:.2e}", flush=True)
+    assert e <= TOL["bf16"], e
 
 
 def test_rmsnorm_fwd_bwd():
