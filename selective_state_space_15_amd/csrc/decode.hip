@@ -185,6 +185,119 @@ __global__ void __launch_bounds__(kRowLanes * ROWS) decode_kernel(DecodeArgs a) 
   }
 }
 
+// One token (T = 1) for many (batch, head) pairs: a grid of resident workgroups, each
+// taking whole heads in turn (head q, q + grid, ...).  A head's inputs -- its state
+// rows, conv window, taps, raw row, dt and z -- are loaded while the head before it
+// computes and stores, so the state stream does not stop between heads (a workgroup per
+// head would stream in rounds, each waiting for its loads).  Thread tid owns state row
+// tid / 16, columns 16-wide interleaved as in decode_kernel, and conv channel tid (the
+// head's P x channels, then the group's B and C channels).
+template <typename IO, int P, int N, int K>
+__global__ void __launch_bounds__(kRowLanes * P) decode_step_kernel(DecodeArgs a) {
+  constexpr int NTHR = kRowLanes * P;
+  using E = typename io_traits<IO>::elem;
+  constexpr int NT = kRowLanes, NPT = N / NT;
+  constexpr int NCH = P + 2 * N;  // conv channels of a head: its x rows, B, C
+  constexpr int KW = K > 1 ? K - 1 : 1;
+  static_assert(NCH <= NTHR, "one conv channel per thread");
+  const Problem& pr = a.pr;
+  __shared__ float s_x[P], s_B[N], s_C[N];
+  const int tid = threadIdx.x;
+  const int pl = tid / NT, n0 = (tid % NT) * NPT;
+  const bool live = tid < NCH;
+  const int jj = live ? tid : 0;
+  const int hpg = pr.H / pr.G;
+  const int64_t HP = static_cast<int64_t>(pr.H) * P;
+  const int64_t GN = static_cast<int64_t>(pr.G) * N;
+  const int64_t nblk = static_cast<int64_t>(pr.B) * pr.H;
+  const E* xbc = static_cast<const E*>(pr.xbc.p);
+  const E* dtp = static_cast<const E*>(pr.dt.p);
+  const E* csi = static_cast<const E*>(pr.cs_in.p);
+  const bool gate = pr.z.p != nullptr;
+  const bool has_cs = K > 1 && csi != nullptr;
+
+  // one head's inputs (every load unconditional, from a valid address)
+  struct In {
+    float st[NPT];
+    float wk[K > 0 ? K : 1], bias;
+    E win[KW], raw, dt, z;
+  };
+  auto chan = [&](int b, int h) -> int64_t {
+    const int g = h / hpg;
+    return jj < P ? h * P + jj : jj < P + N ? HP + g * N + (jj - P) : HP + GN + g * N + (jj - P - N);
+  };
+  auto load = [&](int64_t q, In& in) __attribute__((always_inline)) {
+    const int b = static_cast<int>(q / pr.H), h = static_cast<int>(q % pr.H);
+    const int64_t soff = ((static_cast<int64_t>(b) * pr.H + h) * P + pl) * N + n0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) in.st[j] = pr.h0 ? pr.h0[soff + j] : 0.f;
+    const int64_t c = chan(b, h);
+    if constexpr (K > 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) in.wk[k] = pr.conv_w[c * K + k];
+      in.bias = pr.conv_b ? pr.conv_b[c] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < KW; ++k) in.win[k] = has_cs ? csi[b * pr.cs_in.sb + k * pr.cs_in.st + c] : E{};
+    in.raw = xbc[b * pr.xbc.sb + c];
+    in.dt = dtp[b * pr.dt.sb + h];
+    in.z = gate ? static_cast<const E*>(pr.z.p)[b * pr.z.sb + h * P + pl] : in.raw;
+  };
+
+  In nx;
+  int64_t q = blockIdx.x;
+  load(q < nblk ? q : 0, nx);
+  for (; q < nblk; q += gridDim.x) {
+    const In cur = nx;
+    load(q + gridDim.x < nblk ? q + gridDim.x : q, nx);
+    const int b = static_cast<int>(q / pr.H), h = static_cast<int>(q % pr.H);
+    // post-conv x, B, C of the token
+    const float raw = io_traits<IO>::to_f(cur.raw);
+    float v = raw;
+    if constexpr (K > 0) {
+      float pre = cur.bias + cur.wk[K - 1] * raw;
+#pragma unroll
+      for (int k = 0; k < K - 1; ++k) pre += cur.wk[k] * io_traits<IO>::to_f(cur.win[k]);
+      v = siluf_(pre);
+    }
+    if (live) {
+      if (tid < P) s_x[tid] = v;
+      else if (tid < P + N) s_B[tid - P] = v;
+      else s_C[tid - P - N] = v;
+    }
+    __syncthreads();
+    float dt = io_traits<IO>::to_f(cur.dt) + (pr.dt_bias ? pr.dt_bias[h] : 0.f);
+    if (pr.softplus) dt = softplusf_(dt);
+    const float decay = __expf(dt * pr.A[h]);
+    const float xv = s_x[pl];
+    const float dtx = dt * xv;
+    float st[NPT], acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      st[j] = decay * cur.st[j] + dtx * s_B[n0 + j];
+      acc += st[j] * s_C[n0 + j];
+    }
+    const float y = sum_lanes<NT>(acc) + (pr.D ? pr.D[h] : 0.f) * xv;
+    if (tid % NT == 0) {
+      float o = y;
+      if (gate) o *= siluf_(io_traits<IO>::to_f(cur.z));
+      static_cast<E*>(a.out.p)[b * a.out.sb + h * P + pl] = io_traits<IO>::from_f(o);
+    }
+    const int64_t soff = ((static_cast<int64_t>(b) * pr.H + h) * P + pl) * N + n0;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) a.h_out[soff + j] = st[j];
+    // the conv window after the token: the carried rows shifted by one, then the raw row;
+    // B / C rows by the group's first head
+    if (K > 1 && a.cs_out.p && live && (tid < P || h % hpg == 0)) {
+      const int64_t c = chan(b, h);
+#pragma unroll
+      for (int k = 0; k < KW; ++k)
+        static_cast<E*>(a.cs_out.p)[b * a.cs_out.sb + k * a.cs_out.st + c] = k + 1 < KW ? cur.win[k + 1] : cur.raw;
+    }
+    __syncthreads();  // the next head rewrites s_x / s_B / s_C
+  }
+}
+
 template <typename IO, int P, int N, int ROWS>
 hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.pr.B * a.pr.H * (P / ROWS))), block(kRowLanes * ROWS);
@@ -198,10 +311,33 @@ hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename IO, int P, int N, int K>
+hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t s) {
+  const void* kf = reinterpret_cast<const void*>(&decode_step_kernel<IO, P, N, K>);
+  const int64_t nblk = static_cast<int64_t>(a.pr.B) * a.pr.H;
+  const int64_t res = resident_blocks(kf, kRowLanes * P);
+  if (res <= 0) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nblk < res ? nblk : res)), block(kRowLanes * P);
+  hipLaunchKernelGGL((decode_step_kernel<IO, P, N, K>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename IO, int P, int N>
 hipError_t launch_decode_pn(const DecodeArgs& a, hipStream_t s) {
-  // whole heads from 512 (batch, head) pairs on (two or more workgroups per CU)
-  if (static_cast<int64_t>(a.pr.B) * a.pr.H >= 512) return launch_decode_rows<IO, P, N, P>(a, s);
+  // whole heads from 512 (batch, head) pairs on (two or more workgroups per CU); one
+  // token there streams the heads through resident workgroups
+  if (static_cast<int64_t>(a.pr.B) * a.pr.H >= 512) {
+    if (a.pr.L == 1) {
+      switch (a.pr.K) {
+        case 0: return launch_decode_step<IO, P, N, 0>(a, s);
+        case 2: return launch_decode_step<IO, P, N, 2>(a, s);
+        case 3: return launch_decode_step<IO, P, N, 3>(a, s);
+        case 4: return launch_decode_step<IO, P, N, 4>(a, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    return launch_decode_rows<IO, P, N, P>(a, s);
+  }
   return launch_decode_rows<IO, P, N, 16>(a, s);
 }
 
