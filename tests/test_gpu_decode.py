@@ -103,13 +103,15 @@ def test_decode_c4_shapes_batch16():
     check_decode(Case(d, seed=84, states=True), [1] * 40)
 
 
-def test_decode_steps_replayed_from_a_hip_graph():
-    """A serving loop's form of decode: 16 one-token ssd_decode calls captured once in a
-    HIP graph (torch.cuda.CUDAGraph; the library launches on the stream it is given),
-    then replayed from three different carried states, each written into the captured
-    buffers by eager copies between replays.  Every replay must equal the same 16 calls
-    made eagerly from that state, bitwise: the same kernels on the same inputs."""
-    d = synth.CONFIGS["c1"].with_(B=2, L=16)
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_decode_steps_replayed_from_a_hip_graph(name):
+    """A serving loop's form of decode: one-token ssd_decode calls captured once in a HIP
+    graph (torch.cuda.CUDAGraph; the library launches on the stream it is given), then
+    replayed from three different carried states, each written into the captured
+    buffers by eager copies between replays.  Every replay must equal the same calls
+    made eagerly from that state, bitwise: the same kernels on the same inputs.  c4
+    (batch 16, 80 heads) takes the resident-workgroup kernel."""
+    d = synth.CONFIGS["c1"].with_(B=2, L=16) if name == "c1" else synth.CONFIGS["c4"].with_(L=6)
     case = Case(d, seed=85, states=True)
     _, z, xbc, dt = case.dev_inputs()
     p = {k: fdev(v) for k, v in case.p.items()}
