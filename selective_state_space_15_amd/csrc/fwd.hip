@@ -410,7 +410,22 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
 #pragma unroll
         for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
       }
+      // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B in the registers now: the products
+      // above took H_{c-1} from its LDS copy, which is replaced after the barrier, while
+      // M X runs (one barrier per chunk fewer than replacing it at the chunk's end)
+      if (s_owns) {
+        const float decay = __expf(cs_last);
+#pragma unroll
+        for (int j = 0; j < NJS; ++j) accH[j] *= decay;
+        mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+      }
       __syncthreads();
+      if (s_owns)
+#pragma unroll
+        for (int j = 0; j < NJS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
       mma_strip<Lt, false, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
       // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
       // out = y * silu(z) on 16-byte rows
@@ -443,23 +458,17 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         }
       }
     }
-    // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B
-    if (s_owns) {
-      const float decay = __expf(cs_last);
+    // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B (the state walk; the output walk
+    // did it above)
+    if constexpr (!OUT) {
+      if (s_owns) {
+        const float decay = __expf(cs_last);
 #pragma unroll
-      for (int j = 0; j < NJS; ++j) accH[j] *= decay;
-      mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+        for (int j = 0; j < NJS; ++j) accH[j] *= decay;
+        mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+      }
     }
-    __syncthreads();
-    if constexpr (OUT) {
-      if (s_owns)
-#pragma unroll
-        for (int j = 0; j < NJS; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
-      __syncthreads();
-    }
+    __syncthreads();  // the next chunk's staging rewrites the tiles read above
   }
 
   if constexpr (!OUT) {
