@@ -412,7 +412,6 @@ __device__ __forceinline__ float block_colsum(const float* m, int64_t rows, int6
   return s_part[0][lane] + s_part[1][lane] + s_part[2][lane] + s_part[3][lane];
 }
 
-// Row / column of accumulator element e (0..3) of this lane inside a 16x16 tile.
 // base + `bytes`, with the byte offset held as an opaque 32-bit vector value: the
 // address is then formed at the access as a scalar base plus a 32-bit offset (one
 // vector register), instead of a 64-bit per-thread pointer that the compiler would
@@ -424,6 +423,7 @@ __device__ __forceinline__ Ptr byte_off(Ptr base, uint32_t bytes) {
   return reinterpret_cast<Ptr>(reinterpret_cast<C>(base) + bytes);
 }
 
+// Row / column of accumulator element e (0..3) of this lane inside a 16x16 tile.
 __device__ __forceinline__ int acc_row(int e) { return 4 * ((threadIdx.x & 63) >> 4) + e; }
 __device__ __forceinline__ int acc_col() { return threadIdx.x & 15; }
 
