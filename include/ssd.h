@@ -160,7 +160,7 @@ ssd_status ssd_fwd(const ssd_dims* d, ssd_dtype io, ssd_view xbc, const float* c
  *
  *   Limit    dims whose ssd_fwd_workspace() exceeds SSD_FWD_NOALLOC_SCRATCH_BYTES
  *            return SSD_ERR_WORKSPACE before anything is enqueued (at d_model 1024
- *            shapes -- 32 heads x 64, d_state 128, batch 1 -- up to about 130K tokens
+ *            shapes -- 32 heads x 64, d_state 128, batch 1 -- up to about 149K tokens
  *            per call; longer sequences run as several calls with carried state, or
  *            through ssd_fwd).
  *   Device   the scratch of the *current* device is used; `stream` must belong to it.

@@ -634,7 +634,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 Plan make_plan(int64_t B, int64_t L, int H) {
   Plan pl{};
   pl.nchunks = (L + kQ - 1) / kQ;
-  const int64_t target = 2048;  // workgroups: 8 per CU on 256 CUs
+  // workgroups: one round of resident walks (two per CU on 256 CUs).  More, shorter
+  // sub-segments only add rounds, prologues and scan steps: at 8,192 tokens, 32 heads,
+  // 2,048 walks of 2 chunks took 0.173 ms, 512 walks of 8 chunks 0.121 ms; at the
+  // 80-head batch-16 shapes one walk per (batch, head) drops the state walk and the
+  // scan (1.54 -> 1.12 ms at 4,096 tokens)
+  const int64_t target = 512;
   int64_t want = (target + B * H - 1) / (B * H);
   if (want < 1) want = 1;
   int64_t cps = (pl.nchunks + want - 1) / want;
