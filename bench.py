@@ -438,6 +438,12 @@ def bench_c1_mixer(args, stream):
     t_in = float(np.median(timed(in_proj, n, stream)))
     t_out = float(np.median(timed(out_proj, n, stream)))
     t_hot = float(np.median(timed(hot, n, stream)))
+    # context: the vendor library (torch.matmul -> hipBLASLt) on the same two products
+    # (plain products, no fused epilogue; the weights pre-transposed once)
+    w_in_t, w_out_t = w_in.t().contiguous(), w_out.t().contiguous()
+    out2 = out.view(B * L, hp)
+    t_in_lib = float(np.median(timed(lambda: torch.matmul(u, w_in_t, out=zx.view(B * L, dip)), n, stream)))
+    t_out_lib = float(np.median(timed(lambda: torch.matmul(out2, w_out_t, out=final), n, stream)))
     tok = B * L
     hot_fwd_bytes = hot_bytes(d)[0]
     hot_gbs = hot_fwd_bytes * tok / (t_hot * 1e-3) / 1e9
@@ -457,7 +463,9 @@ def bench_c1_mixer(args, stream):
                                      "the 105 MB working set stays in the 256 MB MALL"},
             "gemm_roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                               "frac": tf / MFMA_BF16_PEAK_TFS, "in_proj_tflops": tf_in,
-                              "out_proj_tflops": tf_out, "flops_per_token": (f_in + f_out) / tok}}
+                              "out_proj_tflops": tf_out, "flops_per_token": (f_in + f_out) / tok,
+                              "hipblaslt_in_proj_tflops": f_in / (t_in_lib * 1e-3) / 1e12,
+                              "hipblaslt_out_proj_tflops": f_out / (t_out_lib * 1e-3) / 1e12}}
 
 
 def bench_decode(args, stream):
