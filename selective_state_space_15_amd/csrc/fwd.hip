@@ -173,6 +173,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
                           ? (OUT ? 2 : 1) * (N / (16 / static_cast<int>(sizeof(E)))) * kQ / NTHR
                           : 1;
   ChunkLoader<IO, P, N, false, true, OUT, NTHR, 1, RBL, false> ld;  // B (and C) rows
+  // the state walk's second register set of B rows (it loads two chunks ahead)
+  ChunkLoader<IO, P, N, false, true, OUT, NTHR, 1, RBL, false> ld2;
   // x rows: thread tid loads the XPT 16-byte vectors v = tid + NTHR i of the chunk's raw
   // 64 x P rows (row v / XV, columns V (v % XV)), one chunk ahead.  At the chunk they go
   // to LDS staging rows 3 .., behind the 3 rows before the chunk (the conv halo, kept
@@ -183,8 +185,8 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   constexpr int XPT = kQ * XV / NTHR;
   static_assert(kQ * XV % NTHR == 0 && 3 * XV <= NTHR, "x vectors tile the threads");
   const E* xsrc = static_cast<const E*>(pr.xbc.p) + b * pr.xbc.sb + h * P;
-  uint4 xr[XPT];
-  uint32_t xok = 0;
+  uint4 xr[XPT], xr2[XPT];  // xr2: the state walk's second set
+  uint32_t xok = 0, xok2 = 0;
   uint4 xhalo = make_uint4(0u, 0u, 0u, 0u);
   const int vlast = static_cast<int>(threadIdx.x) + NTHR * (XPT - 1);
   const bool holds_halo = vlast >= (kQ - 3) * XV;  // rows kQ-3 .. kQ-1 of the chunk
@@ -198,6 +200,18 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
       xr[i] = *reinterpret_cast<const uint4*>(xsrc + (t < pr.L ? t : pr.L - 1) * pr.xbc.st + (v % XV) * V);
     }
     xok = m;
+  };
+  // the same into a given register set (the state walk's two sets)
+  auto issue_x_into = [&](int64_t tn, uint4 (&xd)[XPT], uint32_t& okd) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int v = static_cast<int>(threadIdx.x) + NTHR * i;
+      const int64_t t = tn + v / XV;
+      m |= (t < pr.L ? 1u : 0u) << i;
+      xd[i] = *reinterpret_cast<const uint4*>(xsrc + (t < pr.L ? t : pr.L - 1) * pr.xbc.st + (v % XV) * V);
+    }
+    okd = m;
   };
   // the halo of the walk's first chunk: rows tbeg-3 .. tbeg-1 of x, or of the carried
   // conv state before the sequence (zero before that, and without conv)
@@ -266,10 +280,61 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     }
     __syncthreads();
   }
+  // post-conv x (SiLU; taps right-aligned on 4 in s_conv) of XPT rows per task from
+  // the staged raw rows of chunk c: sX = x (output walk), sXw = x * w_s; rows past the
+  // end are zero
+  auto conv_rows = [&](int64_t c, int64_t t0) __attribute__((always_inline)) {
+    const int cg = static_cast<int>(threadIdx.x) % XV, r0 = (static_cast<int>(threadIdx.x) / XV) * XPT;
+    const int cl = cg * V;
+    uint4 raw[XPT + 3];
+#pragma unroll
+    for (int i = 0; i < XPT + 3; ++i) raw[i] = sRaw[(r0 + i) * XV + cg];
+    // with or without conv as one uniform branch around the whole tile: a branch per
+    // element would cut the tile into blocks, and with it the overlap of the
+    // elements' exp / reciprocal latencies
+    auto tile = [&](auto conv_tag) __attribute__((always_inline)) {
+      constexpr bool CONV = decltype(conv_tag)::value;
+      float w4[4][V], bias[V];
+      if constexpr (CONV)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w4[j][v] = s_conv[(cl + v) * 5 + j];
+          bias[v] = s_conv[(cl + v) * 5 + 4];
+        }
+#pragma unroll
+      for (int r = 0; r < XPT; ++r) {
+        float o[V], ow[V];
+        const bool live = t0 + r0 + r < pr.L;
+        const float ws = live ? (OUT ? s_w[r0 + r] : s_wall[c * kQ + r0 + r]) : 0.f;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float val;
+          if constexpr (CONV) {
+            float pre = bias[v];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
+            val = siluf_(pre);
+          } else {
+            val = raw_elem<IO>(raw[r + 3], v);
+          }
+          o[v] = live ? val : 0.f;
+          ow[v] = o[v] * ws;
+        }
+        if constexpr (OUT) lds_put_row<IO>(sX + (r0 + r) * ldP + cl, o);
+        lds_put_row<IO>(sXw + (r0 + r) * ldP + cl, ow);
+      }
+    };
+    if (pr.K > 0)
+      tile(std::true_type{});
+    else
+      tile(std::false_type{});
+  };
   issue_x(tbeg);
   ld.issue_raw(pr, b, h, g, tbeg);
 
   float lsum = 0.f;
+  if constexpr (OUT)
   for (int64_t c = 0; c < a.cps; ++c) {
     const int64_t t0 = tbeg + c * kQ;
     if (t0 >= pr.L) break;
@@ -314,55 +379,7 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
     __syncthreads();
     const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
     lsum += cs_last;
-    // post-conv x (SiLU; taps right-aligned on 4 in s_conv) of XPT rows per task:
-    // sX = x (output walk), sXw = x * w_s; rows past the end are zero
-    {
-      const int cg = static_cast<int>(threadIdx.x) % XV, r0 = (static_cast<int>(threadIdx.x) / XV) * XPT;
-      const int cl = cg * V;
-      uint4 raw[XPT + 3];
-#pragma unroll
-      for (int i = 0; i < XPT + 3; ++i) raw[i] = sRaw[(r0 + i) * XV + cg];
-      // with or without conv as one uniform branch around the whole tile: a branch per
-      // element would cut the tile into blocks, and with it the overlap of the
-      // elements' exp / reciprocal latencies
-      auto tile = [&](auto conv_tag) __attribute__((always_inline)) {
-        constexpr bool CONV = decltype(conv_tag)::value;
-        float w4[4][V], bias[V];
-        if constexpr (CONV)
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w4[j][v] = s_conv[(cl + v) * 5 + j];
-            bias[v] = s_conv[(cl + v) * 5 + 4];
-          }
-#pragma unroll
-        for (int r = 0; r < XPT; ++r) {
-          float o[V], ow[V];
-          const bool live = t0 + r0 + r < pr.L;
-          const float ws = live ? (OUT ? s_w[r0 + r] : s_wall[c * kQ + r0 + r]) : 0.f;
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-            float val;
-            if constexpr (CONV) {
-              float pre = bias[v];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
-              val = siluf_(pre);
-            } else {
-              val = raw_elem<IO>(raw[r + 3], v);
-            }
-            o[v] = live ? val : 0.f;
-            ow[v] = o[v] * ws;
-          }
-          if constexpr (OUT) lds_put_row<IO>(sX + (r0 + r) * ldP + cl, o);
-          lds_put_row<IO>(sXw + (r0 + r) * ldP + cl, ow);
-        }
-      };
-      if (pr.K > 0)
-        tile(std::true_type{});
-      else
-        tile(std::false_type{});
-    }
+    conv_rows(c, t0);
     // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
     // the row loads in flight); the last chunk reloads its own rows
     {
@@ -458,17 +475,60 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
         }
       }
     }
-    // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B (the state walk; the output walk
-    // did it above)
-    if constexpr (!OUT) {
+    __syncthreads();  // the next chunk's staging rewrites the tiles read above
+  }
+  else {
+    // The state walk: the rows of each chunk are loaded two chunks ahead, into two
+    // register sets (it has the registers: under 200 of 256), set 1 for odd chunks.  The
+    // chunks run in pairs with no branch between the two calls, so the compiler's load
+    // counters see each set's loads in issue order and each chunk waits only for its
+    // own set (a branch merging registers with loads in flight makes it wait for all).
+    const int64_t nc = min(a.cps, (pr.L - tbeg + kQ - 1) / kQ);  // chunks of this walk
+    {
+      const int64_t t1 = nc > 1 ? tbeg + kQ : tbeg;  // (a one-chunk walk reloads its own)
+      issue_x_into(t1, xr2, xok2);
+      ld2.issue_raw(pr, b, h, g, t1);
+    }
+    auto step = [&](int64_t c, uint4 (&xd)[XPT], uint32_t& okd, auto& ldd) __attribute__((always_inline)) {
+      const int64_t t0 = tbeg + c * kQ;
+      // raw x rows (masked past the end) and the halo to the staging rows; B rows to LDS
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int v = static_cast<int>(threadIdx.x) + NTHR * i;
+        sRaw[(3 + v / XV) * XV + v % XV] = keep_if((okd >> i) & 1u, xd[i]);
+      }
+      if (holds_halo) sRaw[(vlast / XV - (kQ - 3)) * XV + vlast % XV] = xhalo;
+      xhalo = keep_if((okd >> (XPT - 1)) & 1u, xd[XPT - 1]);  // the next chunk's halo
+      ldd.consume_bc_raw([&](int seg, int s, int cl, const uint4& v) {
+        *reinterpret_cast<uint4*>(sB + s * ldN + cl) = v;
+      });
+      __syncthreads();
+      const float cs_last = s_lall[c];
+      lsum += cs_last;
+      conv_rows(c, t0);
+      // the rows two chunks ahead into the set just read (past the walk's last chunk
+      // they reload this chunk's rows, which nothing reads)
+      {
+        const int64_t tn = c + 2 < nc ? t0 + 2 * kQ : t0;
+        issue_x_into(tn, xd, okd);
+        ldd.issue_raw(pr, b, h, g, tn);
+      }
+      __syncthreads();
+      // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B
       if (s_owns) {
         const float decay = __expf(cs_last);
 #pragma unroll
         for (int j = 0; j < NJS; ++j) accH[j] *= decay;
         mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
       }
+      __syncthreads();  // the next chunk's staging rewrites the tiles read above
+    };
+    int64_t c = 0;
+    for (; c + 1 < nc; c += 2) {
+      step(c, xr, xok, ld);
+      step(c + 1, xr2, xok2, ld2);
     }
-    __syncthreads();  // the next chunk's staging rewrites the tiles read above
+    if (c < nc) step(c, xr, xok, ld);
   }
 
   if constexpr (!OUT) {
