@@ -895,16 +895,19 @@ hipError_t run_bwd(const Problem& pr, const BwdIn& in, const BwdOut& o, char* ws
   a.ddt = o.ddt;
   a.dbc_part = reinterpret_cast<float*>(ws + l.dbc);
   a.par_part = reinterpret_cast<float*>(ws + l.par);
+  const int64_t hp = static_cast<int64_t>(pr.H) * pr.P;
   if (pr.K > 0) {
-    const int64_t hp = static_cast<int64_t>(pr.H) * pr.P;
     a.dx = MView{ws + l.dx, pr.L * hp, hp};
   } else {
     a.dx = o.dxbc;  // x channels come first in dxbc rows
   }
   const int64_t PN = static_cast<int64_t>(P) * N;
   const int64_t ne = pr.B * pr.H * PN;
-  // 1. in-group prefix states and, by a scan over groups, the state entering each group
-  hipError_t e = launch_group_chunk_states(pr, l.nch, Ps, Psc, Hg, lsum, glsum, s);
+  // 1. in-group prefix states and, by a scan over groups, the state entering each group;
+  // with bf16 I/O and a conv the state walk also convolves x and writes the post-conv
+  // rows that step 4 reads
+  const MView xp_out = pr.bf16 && pr.K > 0 ? MView{ws + l.xp, pr.L * hp, hp} : MView{nullptr, 0, 0};
+  hipError_t e = launch_group_chunk_states(pr, l.nch, Ps, Psc, Hg, lsum, glsum, xp_out, s);
   if (e != hipSuccess) return e;
   // 2. in-group suffix gradients, 3. reverse scan over groups -> gradient leaving each
   // group, dh0
@@ -967,7 +970,10 @@ hipError_t launch_bwd(const Problem& pr_in, const BwdIn& in, const BwdOut& o, vo
   char* ws = static_cast<char*>(ws_v);
   const BwdLayout l = bwd_layout(pr);
   if (pr.K > 0) {
-    const hipError_t e = launch_xbc_prepass(pr, ws + l.xp, ws + l.bc, ws + l.bc_lo, s);
+    // bf16 I/O: the pre-pass convolves B and C only (the state walk convolves x);
+    // fp32 I/O: x, B and C
+    const hipError_t e = pr.bf16 ? launch_bc_prepass(pr, ws + l.bc, ws + l.bc_lo, s, kKXbcPrepass)
+                                 : launch_xbc_prepass(pr, ws + l.xp, ws + l.bc, ws + l.bc_lo, s);
     if (e != hipSuccess) return e;
     const int64_t gn2 = 2LL * pr.G * pr.N;
     pr.bc = View{ws + l.bc, pr.L * gn2, gn2};

@@ -61,6 +61,7 @@ struct GroupArgs {
   float* grp;     // [B][ngr][H][P][N]: E_g (S) or F_g (dS)
   float* lsum;    // S only: [B][nch][H] chunk log-decay
   float* glsum;   // S only: [B][ngr][H] group log-decay
+  MView xp_out;   // S walk that convolves x itself: post-conv x rows [B][L][H*P] (bf16)
 };
 
 template <bool DS>
@@ -75,7 +76,10 @@ struct GroupShape {
 
 // HB heads per workgroup (a template parameter: the head loop is unrolled, so each
 // head's state tiles are addressed statically, with no branch around the products)
-template <typename IO, int P, int N, bool DS, int HB>
+// CX: the S walk reads raw x rows, convolves them (SiLU) itself and writes the
+// post-conv rows to xp_out for the main backward kernel (bf16 I/O with a conv; the
+// pre-pass then convolves only B and C).
+template <typename IO, int P, int N, bool DS, int HB, bool CX = false>
 __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     __attribute__((amdgpu_waves_per_eu(GroupShape<DS>::waves_per_simd)))
     group_state_kernel(GroupArgs a) {
@@ -98,6 +102,14 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   __shared__ __align__(16) Lt sAlo[SPLIT ? 2 : 1][SPLIT ? kQ * ldP : 8];
   __shared__ float s_w[HBM][kQ];                                  // w_s (S) or exp(cs_t) (dS)
   __shared__ float s_l[HBM];                                      // chunk log-decay per head
+  // CX: a step's raw x rows behind the 3 rows before its chunk, and the block's conv
+  // taps (right-aligned on 4) and biases
+  constexpr int XVR = P / V;                    // 16-byte vectors per x row
+  constexpr int CR = CX ? kQ * XVR / NTHR : 1;  // conv rows per task
+  static_assert(!CX || (!DS && sizeof(E) == 2 && kQ * XVR % NTHR == 0 && 3 * XVR <= NTHR),
+                "conv tasks tile the workgroup");
+  __shared__ __align__(16) uint4 sRawG[CX ? (kQ + 3) * XVR : 1];
+  __shared__ float s_cvw[CX ? HB * P * 5 : 1];
 
   const Problem& pr = a.pr;
   const int nhb = pr.H / HB;
@@ -122,12 +134,17 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
 
   constexpr int NDT = ((P / V) * kQ + NTHR - 1) / NTHR;
   uint4 dvr[NDT], zvr[DS ? NDT : 1];
-  const View rows = DS ? a.dout : (pr.K > 0 ? pr.xp : pr.xbc);
+  const View rows = DS ? a.dout : (pr.K > 0 && !CX ? pr.xp : pr.xbc);
   const E* dbase = static_cast<const E*>(rows.p) + b * rows.sb;
   const bool gate = DS && pr.z.p != nullptr;
   const float gw = gate ? 1.f : 0.f;
   const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
   const int64_t zst = gate ? pr.z.st : rows.st;
+  // CX: the conv halo of a step (the 3 x rows before its chunk: raw rows, or the
+  // carried conv state before the sequence, zero before that), one vector per thread
+  uint4 hvr = make_uint4(0u, 0u, 0u, 0u);
+  bool hok = false;
+  const E* csb = CX && pr.cs_in.p ? static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb : nullptr;
   // rows of step k (unconditional loads from clamped rows; masked when staged)
   auto issue_step = [&](int k) {
     const int64_t c = chunk_of(k);
@@ -141,12 +158,67 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
       dvr[q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col);
       if constexpr (DS) zvr[q] = *reinterpret_cast<const uint4*>(zbase + t * zst + h * P + col);
     }
+    if constexpr (CX) {
+      const int i = min(static_cast<int>(threadIdx.x), 3 * XVR - 1);
+      const int64_t t = t0 - 3 + i / XVR;
+      const int col = h * P + (i % XVR) * V;
+      const bool from_state = t < 0 && csb && t >= -(pr.K - 1);
+      // the address is chosen, not the loaded value (a select after the load would wait)
+      const E* src = from_state ? csb + (t + pr.K - 1) * pr.cs_in.st + col
+                                : dbase + (t >= 0 ? t : 0) * rows.st + col;
+      hvr = *reinterpret_cast<const uint4*>(src);
+      hok = static_cast<int>(threadIdx.x) < 3 * XVR && (t >= 0 || from_state);
+    }
   };
   auto stage = [&](int k, int buf) __attribute__((always_inline)) {
     const int hh = k % HB;
     const int64_t t0 = chunk_of(k) * kQ;
     Lt* A = sA[buf];
     Lt* Alo = sAlo[SPLIT ? buf : 0];
+    if constexpr (CX) {
+      // raw rows (zero past the end) and the halo to LDS; then the conv + SiLU of CR
+      // rows per task: w_s x to the product tile, x to the post-conv rows
+#pragma unroll
+      for (int q = 0; q < NDT; ++q) {
+        const int task = threadIdx.x + q * NTHR;
+        if ((P / V) * kQ % NTHR != 0 && task >= (P / V) * kQ) continue;
+        const int r = task / XVR;
+        sRawG[(3 + r) * XVR + task % XVR] = keep_if(t0 + r < pr.L, dvr[q]);
+      }
+      if (static_cast<int>(threadIdx.x) < 3 * XVR) sRawG[threadIdx.x] = keep_if(hok, hvr);
+      __syncthreads();
+      const int cg = static_cast<int>(threadIdx.x) % XVR, r0 = (static_cast<int>(threadIdx.x) / XVR) * CR;
+      const int cl = cg * V;
+      uint4 raw[CR + 3];
+#pragma unroll
+      for (int i = 0; i < CR + 3; ++i) raw[i] = sRawG[(r0 + i) * XVR + cg];
+      float w4[4][V], bias[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w4[j][v] = s_cvw[(hh * P + cl + v) * 5 + j];
+        bias[v] = s_cvw[(hh * P + cl + v) * 5 + 4];
+      }
+      E* xo = static_cast<E*>(a.xp_out.p) + b * a.xp_out.sb + (hfirst + hh) * P + cl;
+#pragma unroll
+      for (int r = 0; r < CR; ++r) {
+        const int row = r0 + r;
+        const bool live = t0 + row < pr.L;
+        const float sc = s_w[hh][row];
+        float o[V], ow[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float pre = bias[v];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
+          o[v] = live ? siluf_(pre) : 0.f;
+          ow[v] = o[v] * sc;
+        }
+        lds_put_row<IO>(A + row * ldP + cl, ow);
+        if (live) store_vec16<IO>(xo + (t0 + row) * a.xp_out.st, o);
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < NDT; ++q) {
       const int task = threadIdx.x + q * NTHR;
@@ -286,6 +358,13 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   // group rows and dt, and after its product they go to LDS.  Every load is consumed in
   // the iteration that issues it, so each wait counts exactly the loads it needs and
   // leaves the state stores in flight.  (The last chunk reloads itself.)
+  if constexpr (CX)
+    for (int i = threadIdx.x; i < HB * P * 5; i += NTHR) {
+      const int hh = i / (P * 5), cl = (i / 5) % P, j = i % 5;
+      const int c = (hfirst + hh) * P + cl;
+      const int kk = j - (4 - pr.K);
+      s_cvw[i] = j == 4 ? (pr.conv_b ? pr.conv_b[c] : 0.f) : (kk >= 0 ? pr.conv_w[c * pr.K + kk] : 0.f);
+    }
   issue_rows(chunk_of(0));
   issue_dt(chunk_of(0));
   issue_step(0);
@@ -459,9 +538,18 @@ int heads_per_group_block(const Problem& pr, int max_heads) {
   return hb;
 }
 
+template <typename IO, int PP, int NN, bool DS, bool CX>
+hipError_t launch_group_kernel(const GroupArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.hb == 2)
+    hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 2, CX>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 1, CX>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <bool DS>
 hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, void* out, float* oscale,
-                         float* grp, float* lsum, float* glsum, hipStream_t s) {
+                         float* grp, float* lsum, float* glsum, MView xp_out, hipStream_t s) {
   GroupArgs a{};
   a.pr = pr;
   a.nch = nch;
@@ -473,19 +561,18 @@ hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, void* out, f
   a.grp = grp;
   a.lsum = lsum;
   a.glsum = glsum;
+  a.xp_out = xp_out;
+  static_assert(GroupShape<DS>::max_heads == 2, "head blocks of 2 or 1");
   const dim3 grid(static_cast<unsigned>(pr.B * a.ngr * (pr.H / a.hb)));
   const dim3 block(GroupShape<DS>::waves * 64);
   TimingScope ts(DS ? kKDstate : kKChunkStates, s);
+  // the S walk convolves x itself where it is given the post-conv rows to write
+  const bool cx = !DS && pr.bf16 && pr.K > 0 && xp_out.p != nullptr;
 #define SSD_CASE(IO, PP, NN)                                                                     \
   if (pr.P == PP && pr.N == NN) {                                                                \
-    if (a.hb == GroupShape<DS>::max_heads)                                                       \
-      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, GroupShape<DS>::max_heads>), grid,   \
-                         block, 0, s, a);                                                        \
-    else if (a.hb >= 2)                                                                          \
-      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 2>), grid, block, 0, s, a);        \
-    else                                                                                         \
-      hipLaunchKernelGGL((group_state_kernel<IO, PP, NN, DS, 1>), grid, block, 0, s, a);        \
-    return hipGetLastError();                                                                    \
+    if constexpr (!DS && sizeof(IO) == 2)                                                        \
+      if (cx) return launch_group_kernel<IO, PP, NN, DS, true>(a, grid, block, s);               \
+    return launch_group_kernel<IO, PP, NN, DS, false>(a, grid, block, s);                        \
   }
   if (pr.bf16) {
     SSD_CASE(bf16_t, 64, 128) SSD_CASE(bf16_t, 64, 64) SSD_CASE(bf16_t, 64, 32)
@@ -502,14 +589,17 @@ hipError_t launch_groups(const Problem& pr, int64_t nch, View dout, void* out, f
 }  // namespace
 
 hipError_t launch_group_local_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
-                                     float* Eg, float* lsum, float* glsum, hipStream_t s) {
-  if (pr.K > 0 && !pr.xp.p) return hipErrorInvalidValue;  // post-conv x comes from the pre-pass
-  return launch_groups<false>(pr, nch, View{nullptr, 0, 0}, Pst, Psc, Eg, lsum, glsum, s);
+                                     float* Eg, float* lsum, float* glsum, MView xp_out,
+                                     hipStream_t s) {
+  // post-conv x: written here from the raw rows (xp_out, bf16 I/O) or read from the
+  // pre-pass's rows (pr.xp, fp32 I/O)
+  if (pr.K > 0 && !pr.xp.p && !xp_out.p) return hipErrorInvalidValue;
+  return launch_groups<false>(pr, nch, View{nullptr, 0, 0}, Pst, Psc, Eg, lsum, glsum, xp_out, s);
 }
 
 hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, void* Qst,
                                 float* Qsc, float* Fg, hipStream_t s) {
-  return launch_groups<true>(pr, nch, dout, Qst, Qsc, Fg, nullptr, nullptr, s);
+  return launch_groups<true>(pr, nch, dout, Qst, Qsc, Fg, nullptr, nullptr, MView{nullptr, 0, 0}, s);
 }
 
 }  // namespace ssd

@@ -698,8 +698,8 @@ size_t bc_prepass_bytes(const Problem& pr) {
   return (n + 255) & ~static_cast<size_t>(255);
 }
 
-hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s) {
-  TimingScope ts(kKBcPrepass, s);
+hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s, int kind) {
+  TimingScope ts(kind, s);
   const int hp = pr.H * pr.P, gn2 = 2 * pr.G * pr.N;
   const MView out{dst, pr.L * gn2, gn2};
   return launch_conv_fwd_range(pr.bf16, pr.B, pr.L, gn2, pr.K, 1, pr.xbc, hp, pr.cs_in, hp,

@@ -71,7 +71,8 @@ struct Problem {
   const float* h0;
   View bc;     // post-conv B|C rows [B][L][2*G*N] from the conv pre-pass (p null: read xbc)
   View bc_lo;  // bf16 I/O backward: post-conv B|C minus its bf16 rounding (p null: none)
-  View xp;     // post-conv x rows [B][L][H*P] from a pre-pass (p null: conv in the loaders)
+  View xp;     // post-conv x rows [B][L][H*P] from a pre-pass or the backward's state
+               // walk (p null: conv in the loaders)
   const float* dtsp;  // forward: dt = softplus(dt_raw + dt_bias) (or the sum alone without
                       // softplus) as fp32 [B][L][H], from the dt pre-pass
 };
@@ -106,13 +107,17 @@ constexpr int state_scale_cols(int P, int N) {
   return 16 * ((N / 16 + 8 / (P / 16) - 1) / (8 / (P / 16)));
 }
 constexpr int state_scale_blocks(int P, int N) { return (P / 16) * (N / state_scale_cols(P, N)); }
+// xp_out (bf16 I/O with a conv): the S walk convolves the raw x rows itself and writes
+// the post-conv rows there; otherwise (p null) it reads them from pr.xp.
 hipError_t launch_group_local_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
-                                     float* Eg, float* lsum, float* glsum, hipStream_t s);
+                                     float* Eg, float* lsum, float* glsum, MView xp_out,
+                                     hipStream_t s);
 hipError_t launch_group_dstates(const Problem& pr, int64_t nch, View dout, void* Qst,
                                 float* Qsc, float* Fg, hipStream_t s);
 // group_local_states, then the scan over groups: Eg[b][g][h] <- H_in(g)
 hipError_t launch_group_chunk_states(const Problem& pr, int64_t nch, void* Pst, float* Psc,
-                                     float* Eg, float* lsum, float* glsum, hipStream_t s);
+                                     float* Eg, float* lsum, float* glsum, MView xp_out,
+                                     hipStream_t s);
 
 // ---------------------------------------------------------------- backward
 struct BwdIn {
@@ -148,15 +153,17 @@ hipError_t launch_conv_fwd_range(int bf16, int64_t B, int64_t L, int C, int K, i
                                  int x_c0, View st, int st_c0, const float* w, const float* bias,
                                  MView out, int o_c0, hipStream_t s, void* out_lo);
 // B|C post-conv pre-pass of the SSD entry points: channels [H*P, Cd) of xbc -> dst,
-// and (dst_lo != null, bf16 I/O) the rounding residual v - bf16(v) -> dst_lo
-hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s);
+// and (dst_lo != null, bf16 I/O) the rounding residual v - bf16(v) -> dst_lo; `kind`
+// names it for the timing instrumentation (the forward's or the backward's pre-pass)
+hipError_t launch_bc_prepass(const Problem& pr, void* dst, void* dst_lo, hipStream_t s,
+                             int kind = kKBcPrepass);
 size_t bc_prepass_bytes(const Problem& pr);
 // Workgroups of `threads` threads of `kernel` resident on the current device at once
 // (all CUs; cached per device and kernel); 0 if the runtime cannot tell.
 int64_t resident_blocks(const void* kernel, int threads);
-// Both pre-passes of the backward in one launch: post-conv x channels -> xp
-// ([B][L][H*P]), post-conv B|C -> bc ([B][L][2GN]) and (bf16 I/O) its rounding
-// residual -> bc_lo.
+// Both pre-passes of the backward in one launch (fp32 I/O; with bf16 I/O the state
+// group walk convolves x): post-conv x channels -> xp ([B][L][H*P]), post-conv B|C ->
+// bc ([B][L][2GN]) and (bf16 I/O) its rounding residual -> bc_lo.
 hipError_t launch_xbc_prepass(const Problem& pr, void* xp, void* bc, void* bc_lo, hipStream_t s);
 size_t x_prepass_bytes(const Problem& pr);
 size_t conv_bwd_workspace_bytes(int64_t B, int64_t L, int64_t C);

@@ -49,7 +49,7 @@ hipEvent_t take_event(TimingState& s) {
 const char* const kNames[kKernelKinds] = {
     "prepass", "walk_state", "scan", "walk_out", "conv_state_out", "conv_fwd",
     "chunk_states", "dstate", "scan_rev", "bwd_main", "conv_bwd", "dbc_reduce", "params",
-    "scan_groups", "xbc_prepass", "linear", "decode", "rmsnorm"};
+    "scan_groups", "bwd_prepass", "linear", "decode", "rmsnorm"};
 
 }  // namespace
 

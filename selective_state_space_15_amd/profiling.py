@@ -127,7 +127,7 @@ def report_bytes(fetch_db, write_db, kernel, copy_bytes, cmd_fetch, cmd_write, t
 PROBE_TOKENS = 16384
 PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
     ("conv_fwd_kernel<bf16_t, 4>", 0): "conv pre-pass (fwd: B, C)",
-    ("conv_fwd_kernel<bf16_t, 4>", 1): "conv pre-pass (bwd: x, B, C)",
+    ("conv_fwd_kernel<bf16_t, 4>", 1): "conv pre-pass (bwd: B, C)",
     ("dt_prepass_kernel<bf16_t>", 0): "dt table (fwd)",
     ("walk_kernel<bf16_t, 64, 128, 0>", 0): "walk_state (fwd)",
     ("walk_kernel<bf16_t, 64, 128, 1>", 0): "walk_out (fwd)",
@@ -148,11 +148,12 @@ PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
 _STATE = 32 * 64 * 128 * 2 // 64
 PROBE_ALG_BYTES_PER_TOKEN = {
     "conv pre-pass (fwd: B, C)": 512 + 512,
-    "conv pre-pass (bwd: x, B, C)": 4608 + 4096 + 512 + 512,
+    "conv pre-pass (bwd: B, C)": 512 + 512 + 512,
     "dt table (fwd)": 64 + 128,
     "walk_state (fwd)": 4096 + 256 + 128,
     "walk_out (fwd)": 4608 + 4096 + 128 + 4096,
-    "chunk_states (bwd)": 4096 + 256 + 64 + _STATE,
+    # raw x in, post-conv x out (the S walk convolves x for the main backward kernel)
+    "chunk_states (bwd)": 4096 + 256 + 64 + _STATE + 4096,
     "dstate (bwd)": 512 + 4096 + 4096 + 64 + _STATE,
     "bwd_main (bwd)": 4096 + 768 + 4096 + 4096 + 64 + 2 * _STATE + 4096 + 4096 + 64 + 1024,
     "conv_bwd (bwd)": 4608 + 4096 + 1024 + 4608,
