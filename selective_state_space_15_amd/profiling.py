@@ -133,8 +133,8 @@ PROBE_LABELS = {  # (kernel, occurrence in the step) -> label
     ("walk_kernel<bf16_t, 64, 128, 1>", 0): "walk_out (fwd)",
     ("scan_kernel", 0): "scan (fwd, sub-segments)",
     ("scan_kernel", 1): "scan (bwd, chunk groups)",
-    ("group_state_kernel<bf16_t, 64, 128, false, 2>", 0): "chunk_states (bwd)",
-    ("group_state_kernel<bf16_t, 64, 128, true, 2>", 0): "dstate (bwd)",
+    ("group_state_kernel<bf16_t, 64, 128, false, 2, true>", 0): "chunk_states (bwd)",
+    ("group_state_kernel<bf16_t, 64, 128, true, 2, false>", 0): "dstate (bwd)",
     ("scan_rev_kernel", 0): "scan_rev (bwd)",
     ("bwd_main_kernel<bf16_t, 64, 128, 8>", 0): "bwd_main (bwd)",
     ("conv_bwd_kernel<bf16_t, true>", 0): "conv_bwd (bwd)",
