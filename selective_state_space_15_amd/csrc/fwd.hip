@@ -334,150 +334,151 @@ __global__ void __launch_bounds__(WalkShape<MODE>::waves * 64)
   ld.issue_raw(pr, b, h, g, tbeg);
 
   float lsum = 0.f;
-  if constexpr (OUT)
-  for (int64_t c = 0; c < a.cps; ++c) {
-    const int64_t t0 = tbeg + c * kQ;
-    if (t0 >= pr.L) break;
-    if constexpr (OUT) {
-      if (a.h_ckpt && t0 % a.ckpt_every == 0 && s_owns) {
-        float* dst = a.h_ckpt + ((t0 / a.ckpt_every) * pr.B + b) * pr.H * PN + h * PN;
+  if constexpr (OUT) {
+    // the output walk: each chunk's rows loaded one chunk ahead (its registers hold one set)
+    for (int64_t c = 0; c < a.cps; ++c) {
+      const int64_t t0 = tbeg + c * kQ;
+      if (t0 >= pr.L) break;
+      if constexpr (OUT) {
+        if (a.h_ckpt && t0 % a.ckpt_every == 0 && s_owns) {
+          float* dst = a.h_ckpt + ((t0 / a.ckpt_every) * pr.B + b) * pr.H * PN + h * PN;
 #pragma unroll
-        for (int j = 0; j < NJS; ++j)
+          for (int j = 0; j < NJS; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
+            for (int e = 0; e < 4; ++e)
+              dst[(s_pi * 16 + acc_row(e)) * N + (s_nj0 + j) * 16 + acc_col()] = accH[j][e];
+        }
       }
-    }
-    // (1) dt (softplus applied by the pre-pass), l = dt * A, chunk-local cumsum (wave 0)
-    if (OUT && wave == 0) {
-      const float dtv = t0 + lane < pr.L ? dt_pre : 0.f;
-      const float cs = wave_incl_scan(dtv * Ah);
-      const float csl = lane_value(cs, kWave - 1);
-      s_dt[lane] = dtv;
-      s_cs[lane] = cs;
-      s_w[lane] = dtv * __expf(csl - cs);
-    }
-    // (2) conv + stores into LDS (the raw rows are staged while wave 0 finishes (1);
-    // one barrier then covers both)
-    //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
-    // z first: the epilogue's wait for it then leaves the next chunk's loads, issued
-    // after it, in flight
-    prefetch_z(t0);
-    // raw x rows (masked past the end) and the halo to the staging rows
+      // (1) dt (softplus applied by the pre-pass), l = dt * A, chunk-local cumsum (wave 0)
+      if (OUT && wave == 0) {
+        const float dtv = t0 + lane < pr.L ? dt_pre : 0.f;
+        const float cs = wave_incl_scan(dtv * Ah);
+        const float csl = lane_value(cs, kWave - 1);
+        s_dt[lane] = dtv;
+        s_cs[lane] = cs;
+        s_w[lane] = dtv * __expf(csl - cs);
+      }
+      // (2) conv + stores into LDS (the raw rows are staged while wave 0 finishes (1);
+      // one barrier then covers both)
+      //   sX[s][p] = x (OUT only), sXw[s][p] = x * w_s, sB[s][n], sC[s][n] (OUT only)
+      // z first: the epilogue's wait for it then leaves the next chunk's loads, issued
+      // after it, in flight
+      prefetch_z(t0);
+      // raw x rows (masked past the end) and the halo to the staging rows
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int v = static_cast<int>(threadIdx.x) + NTHR * i;
-      sRaw[(3 + v / XV) * XV + v % XV] = keep_if((xok >> i) & 1u, xr[i]);
-    }
-    if (holds_halo) sRaw[(vlast / XV - (kQ - 3)) * XV + vlast % XV] = xhalo;
-    xhalo = keep_if((xok >> (XPT - 1)) & 1u, xr[XPT - 1]);  // the next chunk's halo
-    // B / C rows go to LDS as loaded (the tiles keep the I/O element type)
-    static_assert(sizeof(Lt) == sizeof(E), "LDS tiles hold I/O elements");
-    ld.consume_bc_raw([&](int seg, int s, int cl, const uint4& v) {
-      *reinterpret_cast<uint4*>((seg == 1 ? sB : sC) + s * ldN + cl) = v;
-    });
-    __syncthreads();
-    const float cs_last = OUT ? s_cs[kQ - 1] : s_lall[c];
-    lsum += cs_last;
-    conv_rows(c, t0);
-    // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
-    // the row loads in flight); the last chunk reloads its own rows
-    {
-      const int64_t tn = c + 1 < a.cps && t0 + kQ < pr.L ? t0 + kQ : t0;
-      if constexpr (OUT) prefetch(tn);
-      issue_x(tn);
-      ld.issue_raw(pr, b, h, g, tn);
-    }
-    __syncthreads();
-
-    if constexpr (OUT) {
-      // C B^T (-> masked, decayed, dt-scaled intra-chunk matrix Mt) and the carried-state
-      // term C H_{c-1}^T in one pass over the C strip
-      f32x4 yacc[YJ];
-#pragma unroll
-      for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float cst[4];
+      for (int i = 0; i < XPT; ++i) {
+        const int v = static_cast<int>(threadIdx.x) + NTHR * i;
+        sRaw[(3 + v / XV) * XV + v % XV] = keep_if((xok >> i) & 1u, xr[i]);
+      }
+      if (holds_halo) sRaw[(vlast / XV - (kQ - 3)) * XV + vlast % XV] = xhalo;
+      xhalo = keep_if((xok >> (XPT - 1)) & 1u, xr[XPT - 1]);  // the next chunk's halo
+      // B / C rows go to LDS as loaded (the tiles keep the I/O element type)
+      static_assert(sizeof(Lt) == sizeof(E), "LDS tiles hold I/O elements");
+      ld.consume_bc_raw([&](int seg, int s, int cl, const uint4& v) {
+        *reinterpret_cast<uint4*>((seg == 1 ? sB : sC) + s * ldN + cl) = v;
+      });
+      __syncthreads();
+      const float cs_last = s_cs[kQ - 1];
+      lsum += cs_last;
+      conv_rows(c, t0);
+      // the next chunk's loads go in flight now, dt first (its wait in (1) then leaves
+      // the row loads in flight); the last chunk reloads its own rows
       {
-        f32x4 cb[CBJ];
-#pragma unroll
-        for (int j = 0; j < CBJ; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma_strip_ab<Lt, true, true, CBJ, YJ>(cb, yacc, sC, ldN, m0, sB, ldN, 16 * CBJ * half, sH, ldN,
-                                             16 * YJ * half, N);
-        // cs at this lane's rows t = m0 + acc_row(e) (four consecutive) and cs, dt at its
-        // columns s; the decay mask without a branch (exp(-inf) = 0 above the diagonal)
-        const float4 c4 = *reinterpret_cast<const float4*>(s_cs + m0 + acc_row(0));
-        cst[0] = c4.x; cst[1] = c4.y; cst[2] = c4.z; cst[3] = c4.w;
-#pragma unroll
-        for (int j = 0; j < CBJ; ++j) {
-          const int s = 16 * CBJ * half + 16 * j + acc_col();
-          const float css = s_cs[s], dts = s_dt[s];
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = m0 + acc_row(e);
-            v[e] = cb[j][e] * __expf(s <= t ? cst[e] - css : -__builtin_inff()) * dts;
-          }
-          // Mt stored transposed, [s][t]: the lane's four rows are one packed piece
-          lds_put4<IO>(sM + s * ldQ + m0 + acc_row(0), v[0], v[1], v[2], v[3]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ecs = __expf(cst[e]);
-#pragma unroll
-        for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
-      }
-      // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B in the registers now: the products
-      // above took H_{c-1} from its LDS copy, which is replaced after the barrier, while
-      // M X runs (one barrier per chunk fewer than replacing it at the chunk's end)
-      if (s_owns) {
-        const float decay = __expf(cs_last);
-#pragma unroll
-        for (int j = 0; j < NJS; ++j) accH[j] *= decay;
-        mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+        const int64_t tn = c + 1 < a.cps && t0 + kQ < pr.L ? t0 + kQ : t0;
+        if constexpr (OUT) prefetch(tn);
+        issue_x(tn);
+        ld.issue_raw(pr, b, h, g, tn);
       }
       __syncthreads();
-      if (s_owns)
+
+      if constexpr (OUT) {
+        // C B^T (-> masked, decayed, dt-scaled intra-chunk matrix Mt) and the carried-state
+        // term C H_{c-1}^T in one pass over the C strip
+        f32x4 yacc[YJ];
 #pragma unroll
-        for (int j = 0; j < NJS; ++j)
+        for (int j = 0; j < YJ; ++j) yacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float cst[4];
+        {
+          f32x4 cb[CBJ];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
-      mma_strip<Lt, false, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
-      // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
-      // out = y * silu(z) on 16-byte rows
-      float xg[YJ][4];
+          for (int j = 0; j < CBJ; ++j) cb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mma_strip_ab<Lt, true, true, CBJ, YJ>(cb, yacc, sC, ldN, m0, sB, ldN, 16 * CBJ * half, sH, ldN,
+                                               16 * YJ * half, N);
+          // cs at this lane's rows t = m0 + acc_row(e) (four consecutive) and cs, dt at its
+          // columns s; the decay mask without a branch (exp(-inf) = 0 above the diagonal)
+          const float4 c4 = *reinterpret_cast<const float4*>(s_cs + m0 + acc_row(0));
+          cst[0] = c4.x; cst[1] = c4.y; cst[2] = c4.z; cst[3] = c4.w;
 #pragma unroll
-      for (int j = 0; j < YJ; ++j) acc_gather(xg[j], sX, ldP, m0, 16 * (YJ * half + j));
+          for (int j = 0; j < CBJ; ++j) {
+            const int s = 16 * CBJ * half + 16 * j + acc_col();
+            const float css = s_cs[s], dts = s_dt[s];
+            float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = m0 + acc_row(e);
-#pragma unroll
-        for (int j = 0; j < YJ; ++j) {
-          const int p = 16 * (YJ * half + j) + acc_col();
-          sY[t * ldY + p] = yacc[j][e] + Dh * xg[j][e];
-        }
-      }
-      __syncthreads();
-      E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
-#pragma unroll
-      for (int q = 0; q < NYV; ++q) {
-        const int k = static_cast<int>(threadIdx.x) + NTHR * q;
-        const int r = k / (P / V), col = (k % (P / V)) * V;
-        if ((kQ * P / V) % NTHR == 0 || k < kQ * P / V) {
-          float y[V];
-#pragma unroll
-          for (int v = 0; v < V; ++v) {
-            y[v] = sY[r * ldY + col + v];
-            if (gate) y[v] *= siluf_(raw_elem<IO>(zr[q], v));
+            for (int e = 0; e < 4; ++e) {
+              const int t = m0 + acc_row(e);
+              v[e] = cb[j][e] * __expf(s <= t ? cst[e] - css : -__builtin_inff()) * dts;
+            }
+            // Mt stored transposed, [s][t]: the lane's four rows are one packed piece
+            lds_put4<IO>(sM + s * ldQ + m0 + acc_row(0), v[0], v[1], v[2], v[3]);
           }
-          if (t0 + r < pr.L) store_vec16<IO>(op + (t0 + r) * a.out.st + col, y);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ecs = __expf(cst[e]);
+#pragma unroll
+          for (int j = 0; j < YJ; ++j) yacc[j][e] *= ecs;
+        }
+        // (3) H_c = exp(cs_last) H_{c-1} + (w o x)^T B in the registers now: the products
+        // above took H_{c-1} from its LDS copy, which is replaced after the barrier, while
+        // M X runs (one barrier per chunk fewer than replacing it at the chunk's end)
+        if (s_owns) {
+          const float decay = __expf(cs_last);
+#pragma unroll
+          for (int j = 0; j < NJS; ++j) accH[j] *= decay;
+          mma_strip<Lt, false, false, NJS>(accH, sXw, ldP, s_pi * 16, sB, ldN, s_nj0 * 16, kQ);
+        }
+        __syncthreads();
+        if (s_owns)
+#pragma unroll
+          for (int j = 0; j < NJS; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sH[(s_pi * 16 + acc_row(e)) * ldN + (s_nj0 + j) * 16 + acc_col()] = T::to_lds(accH[j][e]);
+        mma_strip<Lt, false, false, YJ>(yacc, sM, ldQ, m0, sX, ldP, 16 * YJ * half, kQ);
+        // y = Ydiag + exp(cs_t) Yoff + D x (fp32, through the dead C tile), then
+        // out = y * silu(z) on 16-byte rows
+        float xg[YJ][4];
+#pragma unroll
+        for (int j = 0; j < YJ; ++j) acc_gather(xg[j], sX, ldP, m0, 16 * (YJ * half + j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = m0 + acc_row(e);
+#pragma unroll
+          for (int j = 0; j < YJ; ++j) {
+            const int p = 16 * (YJ * half + j) + acc_col();
+            sY[t * ldY + p] = yacc[j][e] + Dh * xg[j][e];
+          }
+        }
+        __syncthreads();
+        E* op = static_cast<E*>(a.out.p) + b * a.out.sb + h * P;
+#pragma unroll
+        for (int q = 0; q < NYV; ++q) {
+          const int k = static_cast<int>(threadIdx.x) + NTHR * q;
+          const int r = k / (P / V), col = (k % (P / V)) * V;
+          if ((kQ * P / V) % NTHR == 0 || k < kQ * P / V) {
+            float y[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+              y[v] = sY[r * ldY + col + v];
+              if (gate) y[v] *= siluf_(raw_elem<IO>(zr[q], v));
+            }
+            if (t0 + r < pr.L) store_vec16<IO>(op + (t0 + r) * a.out.st + col, y);
+          }
         }
       }
+      __syncthreads();  // the next chunk's staging rewrites the tiles read above
     }
-    __syncthreads();  // the next chunk's staging rewrites the tiles read above
-  }
-  else {
+  } else {
     // The state walk: the rows of each chunk are loaded two chunks ahead, into two
     // register sets (it has the registers: under 200 of 256), set 1 for odd chunks.  The
     // chunks run in pairs with no branch between the two calls, so the compiler's load
