@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   constexpr int CR = CX ? kQ * XVR / NTHR : 1;  // conv rows per task
   static_assert(!CX || (!DS && sizeof(E) == 2 && kQ * XVR % NTHR == 0 && 3 * XVR <= NTHR),
                 "conv tasks tile the workgroup");
-  __shared__ __align__(16) uint4 sRawG[CX ? (kQ + 3) * XVR : 1];
+  __shared__ __align__(16) uint4 sRawG[CX ? HB : 1][CX ? (kQ + 3) * XVR : 1];
   __shared__ float s_cvw[CX ? HB * P * 5 : 1];
 
   const Problem& pr = a.pr;
@@ -140,11 +140,6 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   const float gw = gate ? 1.f : 0.f;
   const E* zbase = gate ? static_cast<const E*>(pr.z.p) + b * pr.z.sb : dbase;
   const int64_t zst = gate ? pr.z.st : rows.st;
-  // CX: the conv halo of a step (the 3 x rows before its chunk: raw rows, or the
-  // carried conv state before the sequence, zero before that), one vector per thread
-  uint4 hvr = make_uint4(0u, 0u, 0u, 0u);
-  bool hok = false;
-  const E* csb = CX && pr.cs_in.p ? static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb : nullptr;
   // rows of step k (unconditional loads from clamped rows; masked when staged)
   auto issue_step = [&](int k) {
     const int64_t c = chunk_of(k);
@@ -158,67 +153,12 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
       dvr[q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + col);
       if constexpr (DS) zvr[q] = *reinterpret_cast<const uint4*>(zbase + t * zst + h * P + col);
     }
-    if constexpr (CX) {
-      const int i = min(static_cast<int>(threadIdx.x), 3 * XVR - 1);
-      const int64_t t = t0 - 3 + i / XVR;
-      const int col = h * P + (i % XVR) * V;
-      const bool from_state = t < 0 && csb && t >= -(pr.K - 1);
-      // the address is chosen, not the loaded value (a select after the load would wait)
-      const E* src = from_state ? csb + (t + pr.K - 1) * pr.cs_in.st + col
-                                : dbase + (t >= 0 ? t : 0) * rows.st + col;
-      hvr = *reinterpret_cast<const uint4*>(src);
-      hok = static_cast<int>(threadIdx.x) < 3 * XVR && (t >= 0 || from_state);
-    }
   };
   auto stage = [&](int k, int buf) __attribute__((always_inline)) {
     const int hh = k % HB;
     const int64_t t0 = chunk_of(k) * kQ;
     Lt* A = sA[buf];
     Lt* Alo = sAlo[SPLIT ? buf : 0];
-    if constexpr (CX) {
-      // raw rows (zero past the end) and the halo to LDS; then the conv + SiLU of CR
-      // rows per task: w_s x to the product tile, x to the post-conv rows
-#pragma unroll
-      for (int q = 0; q < NDT; ++q) {
-        const int task = threadIdx.x + q * NTHR;
-        if ((P / V) * kQ % NTHR != 0 && task >= (P / V) * kQ) continue;
-        const int r = task / XVR;
-        sRawG[(3 + r) * XVR + task % XVR] = keep_if(t0 + r < pr.L, dvr[q]);
-      }
-      if (static_cast<int>(threadIdx.x) < 3 * XVR) sRawG[threadIdx.x] = keep_if(hok, hvr);
-      __syncthreads();
-      const int cg = static_cast<int>(threadIdx.x) % XVR, r0 = (static_cast<int>(threadIdx.x) / XVR) * CR;
-      const int cl = cg * V;
-      uint4 raw[CR + 3];
-#pragma unroll
-      for (int i = 0; i < CR + 3; ++i) raw[i] = sRawG[(r0 + i) * XVR + cg];
-      float w4[4][V], bias[V];
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w4[j][v] = s_cvw[(hh * P + cl + v) * 5 + j];
-        bias[v] = s_cvw[(hh * P + cl + v) * 5 + 4];
-      }
-      E* xo = static_cast<E*>(a.xp_out.p) + b * a.xp_out.sb + (hfirst + hh) * P + cl;
-#pragma unroll
-      for (int r = 0; r < CR; ++r) {
-        const int row = r0 + r;
-        const bool live = t0 + row < pr.L;
-        const float sc = s_w[hh][row];
-        float o[V], ow[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          float pre = bias[v];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
-          o[v] = live ? siluf_(pre) : 0.f;
-          ow[v] = o[v] * sc;
-        }
-        lds_put_row<IO>(A + row * ldP + cl, ow);
-        if (live) store_vec16<IO>(xo + (t0 + row) * a.xp_out.st, o);
-      }
-      return;
-    }
 #pragma unroll
     for (int q = 0; q < NDT; ++q) {
       const int task = threadIdx.x + q * NTHR;
@@ -358,6 +298,90 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
   // group rows and dt, and after its product they go to LDS.  Every load is consumed in
   // the iteration that issues it, so each wait counts exactly the loads it needs and
   // leaves the state stores in flight.  (The last chunk reloads itself.)
+  // CX: a chunk's raw x rows of every head of the block and each head's conv halo (the
+  // 3 rows before the chunk: raw rows, or the carried conv state before the sequence,
+  // zero before that), loaded a chunk ahead with the B rows; staged in LDS and convolved
+  // for all heads at once, so a chunk needs one staging barrier and one conv barrier.
+  uint4 cxr[CX ? HB : 1][CX ? NDT : 1], chv[CX ? HB : 1];
+  bool chok[CX ? HB : 1];
+  const E* csb = CX && pr.cs_in.p ? static_cast<const E*>(pr.cs_in.p) + b * pr.cs_in.sb : nullptr;
+  auto issue_cx = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+#pragma unroll
+    for (int hh = 0; hh < (CX ? HB : 0); ++hh) {
+      const int h = hfirst + hh;
+#pragma unroll
+      for (int q = 0; q < NDT; ++q) {
+        const int task = min(static_cast<int>(threadIdx.x) + q * NTHR, XVR * kQ - 1);
+        const int r = task / XVR;
+        const int64_t t = t0 + r < pr.L ? t0 + r : t0;
+        cxr[hh][q] = *reinterpret_cast<const uint4*>(dbase + t * rows.st + h * P + (task % XVR) * V);
+      }
+      const int i = min(static_cast<int>(threadIdx.x), 3 * XVR - 1);
+      const int64_t t = t0 - 3 + i / XVR;
+      const int col = h * P + (i % XVR) * V;
+      const bool from_state = t < 0 && csb && t >= -(pr.K - 1);
+      // the address is chosen, not the loaded value (a select after the load would wait)
+      const E* src = from_state ? csb + (t + pr.K - 1) * pr.cs_in.st + col
+                                : dbase + (t >= 0 ? t : 0) * rows.st + col;
+      chv[hh] = *reinterpret_cast<const uint4*>(src);
+      chok[hh] = static_cast<int>(threadIdx.x) < 3 * XVR && (t >= 0 || from_state);
+    }
+  };
+  // the loaded rows (zero past the end) and halos to LDS
+  auto put_cx = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+#pragma unroll
+    for (int hh = 0; hh < (CX ? HB : 0); ++hh) {
+#pragma unroll
+      for (int q = 0; q < NDT; ++q) {
+        const int task = threadIdx.x + q * NTHR;
+        if (XVR * kQ % NTHR != 0 && task >= XVR * kQ) continue;
+        const int r = task / XVR;
+        sRawG[hh][(3 + r) * XVR + task % XVR] = keep_if(t0 + r < pr.L, cxr[hh][q]);
+      }
+      if (static_cast<int>(threadIdx.x) < 3 * XVR) sRawG[hh][threadIdx.x] = keep_if(chok[hh], chv[hh]);
+    }
+  };
+  // conv + SiLU of CR rows per task and head: w_s x to head hh's product tile sA[hh],
+  // x to the post-conv rows
+  auto conv_cx = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
+    const int cg = static_cast<int>(threadIdx.x) % XVR, r0 = (static_cast<int>(threadIdx.x) / XVR) * CR;
+    const int cl = cg * V;
+#pragma unroll
+    for (int hh = 0; hh < (CX ? HB : 0); ++hh) {
+      uint4 raw[CR + 3];
+#pragma unroll
+      for (int i = 0; i < CR + 3; ++i) raw[i] = sRawG[hh][(r0 + i) * XVR + cg];
+      float w4[4][V], bias[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w4[j][v] = s_cvw[(hh * P + cl + v) * 5 + j];
+        bias[v] = s_cvw[(hh * P + cl + v) * 5 + 4];
+      }
+      E* xo = static_cast<E*>(a.xp_out.p) + b * a.xp_out.sb + (hfirst + hh) * P + cl;
+#pragma unroll
+      for (int r = 0; r < CR; ++r) {
+        const int row = r0 + r;
+        const bool live = t0 + row < pr.L;
+        const float sc = s_w[hh][row];
+        float o[V], ow[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          float pre = bias[v];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pre = fmaf(w4[j][v], raw_elem<IO>(raw[r + j], v), pre);
+          o[v] = live ? siluf_(pre) : 0.f;
+          ow[v] = o[v] * sc;
+        }
+        lds_put_row<IO>(sA[hh] + row * ldP + cl, ow);
+        if (live) store_vec16<IO>(xo + (t0 + row) * a.xp_out.st, o);
+      }
+    }
+  };
+
   if constexpr (CX)
     for (int i = threadIdx.x; i < HB * P * 5; i += NTHR) {
       const int hh = i / (P * 5), cl = (i / 5) % P, j = i % 5;
@@ -367,11 +391,18 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     }
   issue_rows(chunk_of(0));
   issue_dt(chunk_of(0));
-  issue_step(0);
+  if constexpr (CX)
+    issue_cx(chunk_of(0));
+  else
+    issue_step(0);
   put_rows(chunk_of(0));
   put_dt(chunk_of(0), true);
+  if constexpr (CX) put_cx(chunk_of(0));
   __syncthreads();
-  stage(0, 0);
+  if constexpr (CX)
+    conv_cx(chunk_of(0));
+  else
+    stage(0, 0);
   __syncthreads();
   for (int i = 0; i < ng; ++i) {
     const int64_t c = chunk_of(i * HB);
@@ -380,13 +411,22 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     for (int hh = 0; hh < HB; ++hh) {
       const int k = i * HB + hh;
       const int h = hfirst + hh;
-      issue_step(k + 1 < nsteps ? k + 1 : k);
-      if (hh == HB - 1) {
-        issue_rows(cn);
-        issue_dt(cn);
+      if constexpr (CX) {
+        // the next chunk's rows, a chunk ahead (the last chunk reloads its own)
+        if (hh == 0) {
+          issue_rows(cn);
+          issue_dt(cn);
+          issue_cx(cn);
+        }
+      } else {
+        issue_step(k + 1 < nsteps ? k + 1 : k);
+        if (hh == HB - 1) {
+          issue_rows(cn);
+          issue_dt(cn);
+        }
       }
       if (owns) {
-        const Lt* A = sA[k & 1];
+        const Lt* A = sA[CX ? hh : (k & 1)];
         const Lt* Alo = sAlo[SPLIT ? (k & 1) : 0];
         const float dec = __expf(s_l[hh]);
 #pragma unroll
@@ -486,13 +526,21 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
         }
       }
       if (hh == HB - 1) {
-        __syncthreads();  // every product of chunk c is done with sK, s_w, s_l
+        __syncthreads();  // every product of chunk c is done with sK, s_w, s_l (and sA)
         put_rows(cn);
         put_dt(cn, i + 1 < ng);
+        if constexpr (CX) put_cx(cn);
         __syncthreads();
       }
-      stage(k + 1 < nsteps ? k + 1 : k, (k + 1) & 1);
-      __syncthreads();
+      if constexpr (CX) {
+        if (hh == HB - 1) {
+          conv_cx(cn);
+          __syncthreads();
+        }
+      } else {
+        stage(k + 1 < nsteps ? k + 1 : k, (k + 1) & 1);
+        __syncthreads();
+      }
     }
   }
   // E_g (S: the state after the group's last chunk) or F_g (dS: the gradient after its
