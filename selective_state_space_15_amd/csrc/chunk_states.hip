@@ -20,7 +20,10 @@
 // channels.  Each chunk's B rows (S) or C rows (dS) are staged in LDS once and reused
 // by every head of the block; each (chunk, head) step's own rows (x, or dout and z)
 // are loaded one step ahead, so they are in flight while the previous step's MFMA
-// product is computed and stored.  bf16 I/O: dS is accumulated from split operands
+// product is computed and stored.  With bf16 I/O and a conv, the S walk reads the raw
+// x rows of all heads of its block a chunk ahead instead, convolves them (SiLU) at the
+// chunk boundary and writes the post-conv rows for the main backward kernel, so the
+// backward's pre-pass only convolves B and C.  bf16 I/O: dS is accumulated from split operands
 // (dy_hi C_hi + dy_lo C_hi + dy_hi C_lo), since the state gradient feeds the
 // log-decay gradient through an fp32 dot with H.
 #include "chunk_io.hpp"
@@ -294,10 +297,11 @@ __global__ void __launch_bounds__(GroupShape<DS>::waves * 64)
     }
   };
 
-  // Per chunk: the HB head steps (unrolled); the last one also issues the next chunk's
-  // group rows and dt, and after its product they go to LDS.  Every load is consumed in
-  // the iteration that issues it, so each wait counts exactly the loads it needs and
-  // leaves the state stores in flight.  (The last chunk reloads itself.)
+  // Per chunk: the HB head steps (unrolled); the last one (CX: the first) also issues
+  // the next chunk's group rows and dt (CX: and x rows), and after its product they go
+  // to LDS.  Every load is consumed in the iteration that issues it, so each wait counts
+  // exactly the loads it needs and leaves the state stores in flight.  (The last chunk
+  // reloads itself.)
   // CX: a chunk's raw x rows of every head of the block and each head's conv halo (the
   // 3 rows before the chunk: raw rows, or the carried conv state before the sequence,
   // zero before that), loaded a chunk ahead with the B rows; staged in LDS and convolved
